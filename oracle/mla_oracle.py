@@ -1,0 +1,341 @@
+"""fp64 CPU oracle for one Ulysses rank's share of Multi-head Latent Attention.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The HIP
+library never imports, links or calls it, and it shares no code with the HIP
+library: the only module both sides use is ``mla_inputs`` (seeded random draws).
+
+Every function is the plain definition of what the pages compute, written in
+NumPy float64, with no blocking or fusion beyond what that definition states:
+
+* head shard lists      -- DeepSpeed PR #8316 "[Ulysses] Carry the KV head count
+                           per DistributedAttention", sections "What breaks" and
+                           "The change" (KV-following split, GQA groups), and the
+                           review thread (reject fewer KV heads than ranks before
+                           any collective).
+* token<->head pack     -- torchtitan PR #5445 carrying the "MLA CP optimization"
+                           commit message, section "Ulysses CP" (one exchange of
+                           concat(q_THK, kv_THP)); hyper-parallel
+                           mla_context_parallel.py, ``_expanded``/``restore_output``.
+* latent up-projection  -- torchtitan "MLA CP optimization", sections "K/V
+                           all-gather CP" and "Ulysses CP" (``wkv_b`` then
+                           ``unpack``); hyper-parallel ``_head_projection_request``
+                           (contiguous head rows) and ``_assemble_key_value``.
+* attention             -- the same sections (``attention(q_THK, k_THK, v_THV)``
+                           with ``k_THK = concat(k_nope, expand_per_head(k_shared))``);
+                           hyper-parallel ``MLAContextParallel.__call__`` (scaling,
+                           causal with no look-ahead) and ``_causal_partition``
+                           (documents as cumulative ends).
+* split-KV decode       -- DeepSpeed PR #8602, "Components" table (decode
+                           attention with KV split-K and an online softmax).
+
+Readings where the pages are silent (each also listed in the design doc):
+the scale is an explicit argument; key j is visible to query t iff j <= t in the
+same document; documents are given as cu_seqlens with a leading 0; inputs are
+post-RoPE; the weight is row-major [L][heads_total*(N+V)] with each head's
+column block [k_nope N | v V]; the packed row is [q_nope | q_rope | k_nope | v].
+
+Parity status: every function below is pinned by tests in ``tests/`` against
+worked examples printed on the pages, closed forms, library routines or brute
+force (see ``tests/test_oracle_*.py``). None is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "widen", "head_shard_rule", "head_shard_sizes", "head_offsets",
+    "pack_heads", "unpack_heads", "latent_up_proj", "attention_probs",
+    "attention", "decode_split_kv", "decode_reference", "doc_bounds",
+    "ulysses_materialise_k_first", "ulysses_latent_first",
+]
+
+
+def widen(x) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) or fp32 arrays to float64."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Head shard lists (DeepSpeed PR #8316)
+# --------------------------------------------------------------------------
+
+def head_shard_rule(q_heads: int, kv_heads: int, sp: int) -> list[int]:
+    """The split rule alone, without the guard.
+
+    KV heads are dealt out as evenly as possible with the remainder going to the
+    lowest ranks, and every KV head carries its whole group of q_heads/kv_heads
+    query heads, so a query head always lands on the rank that holds its KV head
+    (PR #8316, "The change": Q=6/KV=3 over sp=2 must give [4, 2]).
+    """
+    group = q_heads // kv_heads
+    base, extra = divmod(kv_heads, sp)
+    return [(base + (1 if r < extra else 0)) * group for r in range(sp)]
+
+
+def head_shard_sizes(q_heads: int, kv_heads: int, sp: int) -> list[int]:
+    """Validated shard list: query heads per rank, ranks in order.
+
+    Rejected before any exchange (PR #8316 review thread): sp < 1, q_heads < 1,
+    kv_heads < 1, a query count that is not a whole number of KV groups, and
+    fewer KV heads than ranks (a rank would receive zero heads).
+    """
+    if sp < 1 or q_heads < 1 or kv_heads < 1:
+        raise ValueError(f"heads and sp must be positive (q={q_heads}, kv={kv_heads}, sp={sp})")
+    if q_heads % kv_heads:
+        raise ValueError(f"q_heads ({q_heads}) is not a multiple of kv_heads ({kv_heads})")
+    if kv_heads < sp:
+        raise ValueError(f"kv_heads ({kv_heads}) < sp ({sp}): some rank would own no KV head")
+    return head_shard_rule(q_heads, kv_heads, sp)
+
+
+def head_offsets(sizes) -> list[int]:
+    """First head of each rank: rank r owns heads [off_r, off_r + sizes[r])."""
+    offs, acc = [], 0
+    for s in sizes:
+        offs.append(acc)
+        acc += s
+    return offs
+
+
+# --------------------------------------------------------------------------
+# Token <-> head pack (torchtitan "Ulysses CP"; hyper-parallel _expanded)
+# --------------------------------------------------------------------------
+
+def pack_heads(x: np.ndarray, sizes) -> np.ndarray:
+    """Send side of the token->head exchange.
+
+    x is [T][heads_total][F]. The result is the concatenation over ranks r of
+    the slab x[:, off_r:off_r+sizes[r], :], each slab laid out [T][sizes[r]][F]:
+    send[base_r + (t*q_r + h')*F + f] = x[t][off_r + h'][f], base_r = T*off_r*F.
+    Returned flat (1-D), in the dtype of x (a pure permutation of elements).
+    """
+    T, H, F = x.shape
+    assert sum(sizes) == H
+    slabs = [np.ascontiguousarray(x[:, o:o + q, :]).reshape(-1)
+             for o, q in zip(head_offsets(sizes), sizes)]
+    return np.concatenate(slabs) if slabs else np.zeros(0, x.dtype)
+
+
+def unpack_heads(send: np.ndarray, sizes, tokens: int, feat: int) -> np.ndarray:
+    """Exact inverse of ``pack_heads``: back to [T][heads_total][F]."""
+    H = sum(sizes)
+    out = np.empty((tokens, H, feat), dtype=send.dtype)
+    for o, q in zip(head_offsets(sizes), sizes):
+        base = tokens * o * feat
+        out[:, o:o + q, :] = send[base:base + tokens * q * feat].reshape(tokens, q, feat)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Latent up-projection (torchtitan wkv_b; hyper-parallel head-range rows)
+# --------------------------------------------------------------------------
+
+def latent_up_proj(latent, w_kvb, head_begin: int, heads: int, N: int, V: int) -> np.ndarray:
+    """kv[t][h][j] = sum_l latent[t][l] * W[l][(head_begin+h)*(N+V) + j].
+
+    latent [T][L], W [L][heads_total*(N+V)] -> kv [T][heads][N+V] (float64);
+    kv[..., :N] is k_nope and kv[..., N:] is v. The head range must lie inside W.
+    """
+    c = widen(latent)
+    W = widen(w_kvb)
+    P = N + V
+    if not (0 <= head_begin and heads >= 1 and (head_begin + heads) * P <= W.shape[1]):
+        raise ValueError("head range outside the projection weight")
+    cols = W[:, head_begin * P:(head_begin + heads) * P]
+    return (c @ cols).reshape(c.shape[0], heads, P)
+
+
+# --------------------------------------------------------------------------
+# Attention with a head-shared RoPE key band
+# --------------------------------------------------------------------------
+
+def doc_bounds(cu_seqlens=None, T: int | None = None, ends=None) -> list[tuple[int, int]]:
+    """Document [start, end) ranges.
+
+    Accepts cu_seqlens with a leading 0 (n+1 entries) or, as hyper-parallel's
+    ``_causal_partition`` passes them, cumulative document ends without the 0.
+    With neither, the whole sequence of length T is one document.
+    """
+    if cu_seqlens is None and ends is None:
+        return [(0, int(T))]
+    if ends is not None:
+        cu = [0] + [int(e) for e in ends]
+    else:
+        cu = [int(e) for e in cu_seqlens]
+        if cu[0] != 0:
+            raise ValueError("cu_seqlens must start at 0")
+    if any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    return [(a, b) for a, b in zip(cu, cu[1:])]
+
+
+def _scores(q, kv, k_rope, h, rows, cols, N, scale):
+    """s[t][j] = scale * (q_nope[t]·k_nope[j] + q_rope[t]·k_rope[j]) for head h."""
+    qn, qr = q[rows, h, :N], q[rows, h, N:]
+    kn = kv[cols, h, :N]
+    kr = k_rope[cols]
+    return scale * (qn @ kn.T + qr @ kr.T)
+
+
+def attention_probs(q, kv, k_rope, N, scale, causal=True, cu_seqlens=None, h=0):
+    """Full [T][T] probability matrix of head h (0 where a key is not visible)."""
+    q, kv, k_rope = widen(q), widen(kv), widen(k_rope)
+    T = q.shape[0]
+    Pm = np.zeros((T, T))
+    for a, b in doc_bounds(cu_seqlens, T):
+        if b == a:
+            continue
+        s = _scores(q, kv, k_rope, h, slice(a, b), slice(a, b), N, scale)
+        if causal:
+            s = np.where(np.tril(np.ones((b - a, b - a), bool)), s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        Pm[a:b, a:b] = e / e.sum(axis=1, keepdims=True)
+    return Pm
+
+
+def attention(q, kv, k_rope, N: int, scale: float, causal: bool = True, cu_seqlens=None,
+              rows=None):
+    """Causal (or full) softmax attention of one rank's heads.
+
+    q [T][H][N+R] (= [q_nope | q_rope]), kv [T][H][N+V] (= [k_nope | v]),
+    k_rope [T][R] shared by every head. Query t of a document attends to keys j
+    of the same document with j <= t when causal. Returns out [T][H][V] and
+    lse [H][T] (natural log of the softmax denominator, including the max).
+    ``rows`` optionally restricts the computation to those query rows (the rest
+    of ``out``/``lse`` is NaN) so large workloads can be sampled.
+    """
+    q, kv, k_rope = widen(q), widen(kv), widen(k_rope)
+    T, H, _ = q.shape
+    V = kv.shape[2] - N
+    out = np.full((T, H, V), np.nan)
+    lse = np.full((H, T), np.nan)
+    want = None if rows is None else np.zeros(T, bool)
+    if want is not None:
+        want[np.asarray(rows)] = True
+    for a, b in doc_bounds(cu_seqlens, T):
+        if b == a:
+            continue
+        qi = np.arange(a, b) if want is None else np.arange(a, b)[want[a:b]]
+        if qi.size == 0:
+            continue
+        for h in range(H):
+            s = _scores(q, kv, k_rope, h, qi, slice(a, b), N, scale)
+            if causal:
+                s = np.where(np.arange(a, b)[None, :] <= qi[:, None], s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            den = e.sum(axis=1, keepdims=True)
+            out[qi, h, :] = (e / den) @ kv[a:b, h, N:]
+            lse[h, qi] = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Latent-cache decode with a split-KV online-softmax reduction
+# --------------------------------------------------------------------------
+
+def decode_split_kv(q, latent, k_rope, w_kvb, N: int, V: int, scale: float, splits: int,
+                    seqs=None):
+    """One new query per sequence over its whole cached latent, in ``splits`` chunks.
+
+    For each sequence b: up-project the cached latent for all heads (the
+    latent-first projection), score every cached position (no mask: the query
+    is the newest token), and reduce chunk by chunk. Chunk c yields its own max
+    m_c, denominator l_c and normalised output o_c; the chunks combine as
+    m = max_c m_c, l = sum_c l_c e^(m_c-m), o = sum_c l_c e^(m_c-m) o_c / l.
+    q [B][H][N+R], latent [B][S][L], k_rope [B][S][R] -> out [B][H][V] and the
+    partials (m, l [B][H][splits], o_c [B][H][splits][V]). ``seqs`` samples b.
+    """
+    q, c_all, kr_all = widen(q), widen(latent), widen(k_rope)
+    B, H, _ = q.shape
+    S = c_all.shape[1]
+    seqs = range(B) if seqs is None else seqs
+    out = np.full((B, H, V), np.nan)
+    m_p = np.full((B, H, splits), np.nan)
+    l_p = np.full((B, H, splits), np.nan)
+    o_p = np.full((B, H, splits, V), np.nan)
+    chunk = -(-S // splits)
+    for b in seqs:
+        kv = latent_up_proj(c_all[b], w_kvb, 0, H, N, V)          # [S][H][N+V]
+        for h in range(H):
+            s = scale * (kv[:, h, :N] @ q[b, h, :N] + kr_all[b] @ q[b, h, N:])   # [S]
+            for ci in range(splits):
+                lo, hi = ci * chunk, min(S, (ci + 1) * chunk)
+                if hi <= lo:
+                    m_p[b, h, ci], l_p[b, h, ci], o_p[b, h, ci] = -np.inf, 0.0, 0.0
+                    continue
+                mc = s[lo:hi].max()
+                e = np.exp(s[lo:hi] - mc)
+                m_p[b, h, ci], l_p[b, h, ci] = mc, e.sum()
+                o_p[b, h, ci] = (e @ kv[lo:hi, h, N:]) / e.sum()
+            m = m_p[b, h].max()
+            wgt = l_p[b, h] * np.exp(m_p[b, h] - m)
+            out[b, h] = (wgt[:, None] * o_p[b, h]).sum(axis=0) / wgt.sum()
+    return out, (m_p, l_p, o_p)
+
+
+def decode_reference(q, latent, k_rope, w_kvb, N: int, V: int, scale: float, seqs=None):
+    """Direct (unsplit) softmax for the decode step: the definition split-KV must reach."""
+    q, c_all, kr_all = widen(q), widen(latent), widen(k_rope)
+    B, H, _ = q.shape
+    seqs = range(B) if seqs is None else seqs
+    out = np.full((B, H, V), np.nan)
+    for b in seqs:
+        kv = latent_up_proj(c_all[b], w_kvb, 0, H, N, V)
+        for h in range(H):
+            s = scale * (kv[:, h, :N] @ q[b, h, :N] + kr_all[b] @ q[b, h, N:])
+            e = np.exp(s - s.max())
+            out[b, h] = (e / e.sum()) @ kv[:, h, N:]
+    return out
+
+
+# --------------------------------------------------------------------------
+# The two orders of the rank computation (torchtitan "MLA CP optimization")
+# --------------------------------------------------------------------------
+
+def ulysses_materialise_k_first(latent, w_kvb, q, k_rope, sizes, N, V, scale):
+    """Project every head on each rank's own tokens, pack [q | kv], exchange, attend.
+
+    Simulates sp ranks that each hold T/sp consecutive tokens of latent, q
+    (all heads) and k_rope. Each rank projects all heads, builds F-rows
+    [q_nope | q_rope | k_nope | v], packs them by the shard list; rank r then
+    receives slice r of every peer (in rank order, i.e. token order), splits
+    the rows and attends over the full sequence with the all-gathered k_rope.
+    Returns the per-rank outputs [T][sizes[r]][V].
+    """
+    latent, w_kvb, q, k_rope = widen(latent), widen(w_kvb), widen(q), widen(k_rope)
+    sp = len(sizes)
+    T, Htot, K = q.shape
+    P = N + V
+    F = K + P
+    Tl = T // sp
+    sends = []
+    for s in range(sp):
+        tok = slice(s * Tl, (s + 1) * Tl)
+        kv_loc = latent_up_proj(latent[tok], w_kvb, 0, Htot, N, V)
+        rows = np.concatenate([q[tok], kv_loc], axis=2)            # [Tl][Htot][F]
+        sends.append(pack_heads(rows, sizes))
+    outs = []
+    for r, (o, qr) in enumerate(zip(head_offsets(sizes), sizes)):
+        base, n = Tl * o * F, Tl * qr * F
+        recv = np.concatenate([snd[base:base + n].reshape(Tl, qr, F) for snd in sends], axis=0)
+        q_r, kv_r = recv[:, :, :K], recv[:, :, K:]
+        out, _ = attention(q_r, kv_r, k_rope, N, scale, causal=True)
+        outs.append(out)
+    return outs
+
+
+def ulysses_latent_first(latent, w_kvb, q, k_rope, sizes, N, V, scale):
+    """Gather the latents first, then project only the rank's own head range, attend."""
+    latent, w_kvb, q, k_rope = widen(latent), widen(w_kvb), widen(q), widen(k_rope)
+    outs = []
+    for o, qr in zip(head_offsets(sizes), sizes):
+        kv = latent_up_proj(latent, w_kvb, o, qr, N, V)
+        out, _ = attention(q[:, o:o + qr, :], kv, k_rope, N, scale, causal=True)
+        outs.append(out)
+    return outs

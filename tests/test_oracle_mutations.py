@@ -1,0 +1,149 @@
+"""Planted mistakes: each plausible slip in the oracle must fail at least one pin.
+
+Mistakes are planted in the oracle only, on the CPU, by monkeypatching.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mla_oracle as om
+import test_oracle_numerics as tn
+import test_oracle_shard_pack as ts
+from golden_io import shard_cases
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(om, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (Exception, pytest.fail.Exception):
+        return True
+    return False
+
+
+def _any_attention_pin_fails():
+    pins = [
+        lambda: tn.test_attention_matches_sdpa_with_expanded_key(True),
+        tn.test_attention_tiny_config_matches_sdpa,
+        tn.test_varlen_matches_sdpa_block_diagonal_mask_and_separate_runs,
+        tn.test_first_token_of_each_document_returns_its_value_row,
+        tn.test_zero_query_gives_running_mean_of_values,
+        tn.test_attention_brute_force_tiny,
+    ]
+    return any(_fails(p) for p in pins)
+
+
+def test_dropped_rope_term_is_caught(monkeypatch):
+    def bad(q, kv, k_rope, h, rows, cols, N, scale):
+        return scale * (q[rows, h, :N] @ kv[cols, h, :N].T)
+    _patch(monkeypatch, "_scores", bad)
+    assert _any_attention_pin_fails()
+
+
+def test_missing_scale_is_caught(monkeypatch):
+    def bad(q, kv, k_rope, h, rows, cols, N, scale):
+        return q[rows, h, :N] @ kv[cols, h, :N].T + q[rows, h, N:] @ k_rope[cols].T
+    _patch(monkeypatch, "_scores", bad)
+    assert _any_attention_pin_fails()
+
+
+def test_rope_band_taken_from_wrong_operand_is_caught(monkeypatch):
+    # q_rope paired with k_nope's tail instead of the shared band
+    def bad(q, kv, k_rope, h, rows, cols, N, scale):
+        R = k_rope.shape[1]
+        return scale * (q[rows, h, :N] @ kv[cols, h, :N].T + q[rows, h, N:] @ kv[cols, h, N - R:N].T)
+    _patch(monkeypatch, "_scores", bad)
+    assert _any_attention_pin_fails()
+
+
+def test_wrong_sign_is_caught(monkeypatch):
+    orig = om._scores
+    _patch(monkeypatch, "_scores", lambda *a: -orig(*a))
+    assert _any_attention_pin_fails()
+
+
+def test_strict_causal_mask_is_caught(monkeypatch):
+    # a query that may not see itself (j < t): the first-token pin must fail
+    orig = om.attention
+
+    def bad(q, kv, k_rope, N, scale, causal=True, cu_seqlens=None, rows=None):
+        out, lse = orig(q, kv, k_rope, N, scale, causal, cu_seqlens, rows)
+        qq, kk, rr = om.widen(q), om.widen(kv), om.widen(k_rope)
+        out = out.copy()
+        # shift by one key: o_t := o_{t-1} within each document (the j < t answer up to scale)
+        for a, b in om.doc_bounds(cu_seqlens, qq.shape[0]):
+            out[a + 1:b] = out[a:b - 1].copy()
+        return out, lse
+    _patch(monkeypatch, "attention", bad)
+    assert _any_attention_pin_fails()
+
+
+def test_value_and_key_swapped_in_projection_is_caught(monkeypatch):
+    orig = om.latent_up_proj
+
+    def bad(latent, w_kvb, head_begin, heads, N, V):
+        kv = orig(latent, w_kvb, head_begin, heads, N, V)
+        return np.concatenate([kv[..., V:], kv[..., :V]], axis=-1) if N == V else kv[..., ::-1].copy()
+    _patch(monkeypatch, "latent_up_proj", bad)
+    pins = [tn.test_up_proj_brute_force_tiny_config, tn.test_up_proj_one_hot_latent_returns_weight_rows,
+            tn.test_up_proj_matches_torch_linear_layout]
+    assert any(_fails(p) for p in pins)
+
+
+def test_transposed_head_blocks_in_projection_is_caught(monkeypatch):
+    # columns read as [j][head] instead of [head][j]
+    def bad(latent, w_kvb, head_begin, heads, N, V):
+        c, W = om.widen(latent), om.widen(w_kvb)
+        P = N + V
+        Ht = W.shape[1] // P
+        Wt = W.reshape(W.shape[0], P, Ht).transpose(0, 2, 1).reshape(W.shape[0], -1)
+        return (c @ Wt[:, head_begin * P:(head_begin + heads) * P]).reshape(c.shape[0], heads, P)
+    _patch(monkeypatch, "latent_up_proj", bad)
+    pins = [tn.test_up_proj_brute_force_tiny_config, tn.test_up_proj_one_hot_latent_returns_weight_rows,
+            tn.test_up_proj_matches_torch_linear_layout]
+    assert any(_fails(p) for p in pins)
+
+
+def test_remainder_to_last_ranks_is_caught(monkeypatch):
+    def bad(q_heads, kv_heads, sp):
+        g = q_heads // kv_heads
+        base, extra = divmod(kv_heads, sp)
+        return [(base + (1 if r >= sp - extra else 0)) * g for r in range(sp)]
+    _patch(monkeypatch, "head_shard_rule", bad)
+    assert any(_fails(ts.test_shard_lists_printed_on_pages, *c) for c in shard_cases())
+
+
+def test_query_side_split_is_caught(monkeypatch):
+    # splitting the query count instead of following the KV heads gives [3, 3] for Q6/KV3
+    def bad(q_heads, kv_heads, sp):
+        base, extra = divmod(q_heads, sp)
+        return [base + (1 if r < extra else 0) for r in range(sp)]
+    _patch(monkeypatch, "head_shard_rule", bad)
+    assert any(_fails(ts.test_shard_lists_printed_on_pages, *c) for c in shard_cases())
+
+
+def test_missing_guard_is_caught(monkeypatch):
+    _patch(monkeypatch, "head_shard_sizes", lambda q, kv, sp: om.head_shard_rule(q, kv, sp))
+    assert any(_fails(ts.test_shard_lists_printed_on_pages, *c) for c in shard_cases())
+
+
+def test_pack_token_major_slabs_is_caught(monkeypatch):
+    # interleaving ranks per token ([T][H][F] unchanged) instead of per-rank slabs
+    _patch(monkeypatch, "pack_heads", lambda x, sizes: np.ascontiguousarray(x).reshape(-1))
+    assert _fails(ts.test_pack_index_coded_brute_force, 3, [2, 1], 5)
+
+
+def test_split_combine_without_rescale_is_caught(monkeypatch):
+    orig = om.decode_split_kv
+
+    def bad(q, latent, k_rope, w_kvb, N, V, scale, splits, seqs=None):
+        out, (m, l, o) = orig(q, latent, k_rope, w_kvb, N, V, scale, splits, seqs)
+        out = (l[..., None] * o).sum(axis=2) / l.sum(axis=2)[..., None]   # forgets e^(m_c - m)
+        return out, (m, l, o)
+    _patch(monkeypatch, "decode_split_kv", bad)
+    assert _fails(tn.test_split_kv_equals_direct_softmax, 3)
