@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of one Ulysses rank's MLA shard on one MI355X.
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input, all in libmla.so:
+  1. pack      : token->head pack of the rank's local [q | kv] rows,
+                 [256 tokens][128 heads][448] -> 8 slabs of 16 heads
+  2. up-proj   : latent [2048][512] x wkv_b [512][16*256] -> kv [2048][16][256]
+  3. attention : causal, shared 64-wide RoPE band, q [2048][16][192] -> out [2048][16][128]
+  4. unpack    : head->token restore of the output, 8 x [256][16][128] -> [256][128][128]
+(the DeepSeek-V3-shaped rank of 128 heads over sp=8: T=2048, H=16, L=512,
+N=128, R=64, V=128, bf16 storage with fp32 accumulation).
+
+value = algorithmic FLOPs of the step (up-projection 2*T*L*H*(N+V) plus
+attention 2*H*T(T+1)/2*(N+R+V), unmasked pairs only) / measured step time.
+The timed region is K steps launched back to back on one stream, with the
+inputs resident in HBM, bracketed by HIP events after a synchronize.
+A second pass times every kernel on its own with events for the roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str, launches_per_unit=1):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "mla_attention_under_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or _sha(src) != rec["source_sha"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def _busy(torch, ms=30):
+    """Keep the GPU busy so the host can queue the timed launches ahead of it."""
+    try:
+        torch.cuda._sleep(int(ms * 2.4e6))
+    except Exception:  # pragma: no cover - the spin kernel is part of torch on ROCm
+        x = torch.empty(1 << 26, device="cuda")
+        for _ in range(max(1, ms // 2)):
+            x.fill_(1.0)
+
+
+def cpu_baseline(w, d, x_pack, sizes, flops_step):
+    """The fp64 oracle on the host cores over the same workload, for about 10 s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    scale = 1 / math.sqrt(w.K)
+    out_slabs = np.zeros((w.T, w.H, w.V), dtype=np.float64)
+
+    def one_step():
+        oracle.pack_heads(x_pack, sizes)
+        kv = oracle.latent_up_proj(d["latent"], d["w_kvb"], 0, w.H, w.N, w.V)
+        out, _ = oracle.attention(d["q"], kv, d["k_rope"], w.N, scale)
+        out_slabs[:] = out
+        oracle.unpack_heads(out_slabs.reshape(-1), [w.H] * 8, w.T // 8, w.V)
+
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        one_step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or (n >= 1 and el / n > 15.0):
+            break
+    return {"value": round(flops_step * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full step(s) of the same workload (pack, up-projection, attention of all "
+                      f"{w.H} heads, unpack) in float64 NumPy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the uneven22 pack/unpack HBM measurement")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this build has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(1)
+
+    import numpy as np
+    import torch
+
+    import mla_attention_under_amd as mla
+    import mla_inputs as mi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    mla.load_library()
+
+    w = mi.WORKLOADS["dsv3_rank"]
+    T, H, L, N, R, V, P, K = w.T, w.H, w.L, w.N, w.R, w.V, w.P, w.K
+    scale = 1 / math.sqrt(K)
+    sp, Ttok, Htot_pack = 8, w.pack_tokens, sum(w.pack_shards)
+    sizes = mla.mla_head_shard_sizes(Htot_pack, Htot_pack, sp)           # [16] * 8
+
+    d = mi.shard_inputs(w)
+    x_pack = mi.pack_payload(Ttok, Htot_pack, w.F, cfg=w.cfg)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    latent, W, q, kr = dev(d["latent"]), dev(d["w_kvb"]), dev(d["q"]), dev(d["k_rope"])
+    xp = dev(x_pack)
+    send = torch.empty(xp.numel(), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((T, H, P), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((T, H, V), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T // sp, sp * H, V), dtype=torch.bfloat16, device="cuda")
+    out_flat = out.view(-1)
+
+    kernels = ["pack", "up_proj", "attention", "unpack"]
+    calls = {
+        "pack": lambda: mla.mla_pack_heads(xp, send, sizes),
+        "up_proj": lambda: mla.mla_latent_up_proj(latent, W, kv, w.heads_total, 0, H, N, V),
+        "attention": lambda: mla.mla_attention_fwd(q, kv, kr, out, N, R, V, scale),
+        "unpack": lambda: mla.mla_unpack_heads(out_flat, y, [H] * sp),
+    }
+
+    def step():
+        for k in kernels:
+            calls[k]()
+
+    flops_up = 2.0 * T * L * H * P
+    pairs = T * (T + 1) / 2
+    flops_attn = 2.0 * H * pairs * (K + V)
+    flops_step = flops_up + flops_attn
+    bytes_pack = 2.0 * xp.numel() * 2
+    bytes_unpack = 2.0 * out.numel() * 2
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps back to back
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    _busy(torch)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # ---- per-kernel pass: events around every launch, on the launch stream
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for k in kernels}
+    torch.cuda.synchronize()
+    _busy(torch)
+    for i in range(args.steps):
+        for k in kernels:
+            ev[k][i][0].record()
+            calls[k]()
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    kern_us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in kernels}
+
+    attn_tflops = flops_attn / (kern_us["attention"] * 1e-6) / 1e12
+    extra = {
+        "kernel_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "up_proj_tflops": round(flops_up / (kern_us["up_proj"] * 1e-6) / 1e12, 2),
+        "attention_tflops": round(attn_tflops, 2),
+        "compute_only_tflops": round(flops_step / ((kern_us["up_proj"] + kern_us["attention"]) * 1e-6) / 1e12, 2),
+        "pack_gbps": round(bytes_pack / (kern_us["pack"] * 1e-6) / 1e9, 1),
+        "unpack_gbps": round(bytes_unpack / (kern_us["unpack"] * 1e-6) / 1e9, 1),
+        "pack_note": "dsv3_rank pack/unpack buffers (58.7 MB, 16.8 MB) fit the 256 MB Infinity Cache",
+    }
+
+    if not args.no_extra:
+        # uneven 22-head shard: [4096][128][448] <-> 6 slabs; 940 MB of traffic per direction, beyond the cache
+        sz6 = mla.mla_head_shard_sizes(128, 128, 6)
+        big = torch.randint(-32768, 32767, (4096, 128, 448), dtype=torch.int16, device="cuda")
+        big_send = torch.empty(big.numel(), dtype=torch.int16, device="cuda")
+        big_back = torch.empty_like(big)
+        for _ in range(3):
+            mla.mla_pack_heads(big, big_send, sz6)
+            mla.mla_unpack_heads(big_send, big_back, sz6)
+        reps = 20
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * reps)]
+        torch.cuda.synchronize()
+        _busy(torch)
+        for i in range(reps):
+            e[2 * i][0].record()
+            mla.mla_pack_heads(big, big_send, sz6)
+            e[2 * i][1].record()
+            e[2 * i + 1][0].record()
+            mla.mla_unpack_heads(big_send, big_back, sz6)
+            e[2 * i + 1][1].record()
+        torch.cuda.synchronize()
+        nbytes = 2.0 * big.numel() * 2
+        pk = sum(e[2 * i][0].elapsed_time(e[2 * i][1]) for i in range(reps)) / reps
+        up = sum(e[2 * i + 1][0].elapsed_time(e[2 * i + 1][1]) for i in range(reps)) / reps
+        extra["uneven22_pack_gbps"] = round(nbytes / (pk * 1e-3) / 1e9, 1)
+        extra["uneven22_unpack_gbps"] = round(nbytes / (up * 1e-3) / 1e9, 1)
+        extra["uneven22_pack_us"] = round(pk * 1e3, 2)
+        assert torch.equal(big_back, big), "uneven22 pack/unpack round trip failed"
+        del big, big_send, big_back
+
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    traffic = _traffic("attention", "dsv3_rank")
+    roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "kernel": "mla_attention_fwd (attn_fwd_kernel<128,64,128>)",
+            "algorithmic": f"{flops_attn / 1e9:.3f} GFLOP per launch = 2*H*T(T+1)/2*(N+R+V)"}
+    line = {
+        "metric": "MLA shard attention TFLOP/s (+pack GB/s), T=2048 H=16 bf16, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dsv3_rank", "T": T, "H": H, "L": L, "N": N, "R": R, "V": V, "heads_total": 128,
+                   "sp": sp, "pack": "[256][128][448] -> 8 x 16 heads", "causal": True,
+                   "step": "pack + up_proj + attention + unpack", "flops_per_step": flops_step},
+        "roofline": roof,
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, d, x_pack, sizes, flops_step)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

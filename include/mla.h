@@ -1,0 +1,199 @@
+/*
+ * mla.h -- C ABI of libmla.so: one Ulysses rank's share of Multi-head Latent
+ * Attention (MLA) on an AMD Instinct MI355X (gfx950).
+ *
+ * Notation (torchtitan PR #5445, "MLA CP optimization" commit message, opening
+ * paragraph): T tokens, H heads, L KV latent width, N non-positional key width,
+ * R shared (RoPE) key width, V value width; K = N+R, P = N+V, F = K+P.
+ *
+ * Conventions for every call
+ *  - All tensors are dense row-major arrays of the stated element type, passed
+ *    as plain device pointers; sizes and strides are in ELEMENTS.
+ *  - Element type: MLA_BF16 (bfloat16 storage, fp32 accumulation, outputs
+ *    rounded to nearest-even) or MLA_F32 (fp32 throughout).
+ *  - `stream` is a hipStream_t cast to void* (NULL = the null stream). Every
+ *    call is asynchronous on that stream; the library never synchronises.
+ *  - Ownership: the caller owns every buffer, including the workspace. The
+ *    library allocates no device memory and keeps no per-model state (no head
+ *    count is ever stored between calls).
+ *  - Errors: all arguments are validated on the host BEFORE anything is
+ *    launched. On failure the call returns a negative mla_status, launches
+ *    nothing, writes no output, and mla_last_error() describes the problem.
+ *    MLA_ELAUNCH reports a HIP launch error (the message names it).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_EINVAL = -1,       /* an argument is out of range or inconsistent      */
+  MLA_EUNSUPPORTED = -2, /* valid, but not a shape/alignment this build runs */
+  MLA_ELAUNCH = -3       /* the HIP runtime rejected a launch               */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Thread-local text of the last error on this thread ("" if none). Never NULL. */
+const char *mla_last_error(void);
+
+/* Library version string, e.g. "mla 0.1 gfx950". */
+const char *mla_version(void);
+
+/*
+ * Head shard list (host only, no GPU use).
+ * DeepSpeed PR #8316 "[Ulysses] Carry the KV head count per DistributedAttention",
+ * sections "What breaks" and "The change": the query heads of a sequence-parallel
+ * group follow the KV head count. KV heads are dealt out as evenly as possible,
+ * remainder to the lowest ranks, and each KV head takes its whole group of
+ * q_heads/kv_heads query heads: rank r gets
+ *     sizes_out[r] = (kv_heads / sp + (r < kv_heads % sp)) * (q_heads / kv_heads)
+ * heads, contiguous and ascending (rank r owns [sum_{s<r} sizes[s], +sizes[r])).
+ * Examples: (12,12,4) -> [3,3,3,3]; (3,3,2) -> [2,1]; (6,3,2) -> [4,2].
+ * Rejected with MLA_EINVAL (the same review thread: fail before any exchange):
+ * sp < 1, q_heads < 1, kv_heads < 1, q_heads % kv_heads != 0, kv_heads < sp.
+ * sizes_out: caller array of sp ints, written only on success.
+ */
+int mla_head_shard_sizes(int q_heads, int kv_heads, int sp, int *sizes_out);
+
+/*
+ * Token->head pack: the local send side of the Ulysses token->head exchange of
+ * concat(q_THK, kv_THP) (torchtitan "MLA CP optimization", section "Ulysses CP";
+ * hyper-parallel mla_context_parallel.py, `_expanded`).
+ *   x    : [tokens][heads_total][feat]
+ *   send : concatenation over ranks r of slabs [tokens][sizes[r]][feat]:
+ *          send[T*off_r*feat + (t*sizes[r] + h)*feat + f] = x[t][off_r + h][f]
+ *          with off_r = sizes[0] + ... + sizes[r-1].
+ * sizes: HOST array of sp positive ints summing to heads_total (e.g. from
+ * mla_head_shard_sizes). The copy is bit-exact; dtype only fixes the element
+ * size (MLA_BF16: 2 bytes, MLA_F32: 4 bytes). x and send must not overlap.
+ * tokens == 0 is a valid no-op. sp <= 1024.
+ */
+int mla_pack_heads(const void *x, void *send, int64_t tokens, int heads_total, int feat,
+                   const int *sizes, int sp, int dtype, void *stream);
+
+/*
+ * Head->token unpack: the exact inverse of mla_pack_heads (the receive side of
+ * the head->token exchange of the attention output, torchtitan "Ulysses CP"
+ * `all_to_all_head_to_token(out_THV)`; hyper-parallel `restore_output`).
+ *   recv : concatenation over r of slabs [tokens][sizes[r]][feat]
+ *   x    : [tokens][heads_total][feat], x[t][off_r + h][f] = slab_r[t][h][f]
+ * Same argument rules as mla_pack_heads.
+ */
+int mla_unpack_heads(const void *recv, void *x, int64_t tokens, int heads_total, int feat,
+                     const int *sizes, int sp, int dtype, void *stream);
+
+/*
+ * Latent up-projection through wkv_b for a contiguous head range
+ * (torchtitan "MLA CP optimization", sections "K/V all-gather CP" and "Ulysses CP":
+ * kv_THP = reshape_per_head(wkv_b(kv_c_normed_TL)); hyper-parallel
+ * `_head_projection_request`: only the rows of heads [head_begin, head_begin+heads)):
+ *   kv_out[t][h][j] = sum_l latent[t][l] * w_kvb[l][(head_begin + h)*(N+V) + j]
+ *   latent : [T][L]
+ *   w_kvb  : [L][heads_total*(N+V)]  (each head's column block is [k_nope N | v V];
+ *            note torch.nn.Linear stores the transpose of this)
+ *   kv_out : [T][heads][N+V]         (k_nope = [..., :N], v = [..., N:])
+ * Requires 0 <= head_begin, heads >= 1, head_begin + heads <= heads_total,
+ * L >= 1, N >= 1, V >= 1, T >= 0. MLA_BF16 additionally needs L, N+V and
+ * heads_total*(N+V) to be multiples of 8 and 16-byte aligned pointers.
+ */
+int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int64_t T, int L,
+                       int heads_total, int head_begin, int heads, int N, int V, int dtype,
+                       void *stream);
+
+/*
+ * Attention of one rank's heads with a head-shared RoPE key band
+ * (torchtitan "MLA CP optimization", section "Ulysses CP":
+ * k_THK = concat(k_nope_THN, expand_per_head(k_shared_TR)),
+ * out_THV = attention(q_THK, k_THK, v_THV); hyper-parallel
+ * `_assemble_key_value` and `MLAContextParallel.__call__`):
+ *   s[t][j] = scale * (q[t][h][:N] . kv[j][h][:N] + q[t][h][N:] . k_rope[j][:])
+ *   out[t][h][:] = sum_j softmax_j(s[t][.]) * kv[j][h][N:N+V]
+ * over the keys j of t's document, and with j <= t when causal (no look-ahead).
+ * The shared band is read once per key tile and never expanded in memory.
+ *   q      : [T][H][N+R] rows at q + t*q_stride_t + h*q_stride_h
+ *   kv     : [T][H][N+V] rows at kv + t*kv_stride_t + h*kv_stride_h
+ *   k_rope : [T][R]      rows at k_rope + t*kr_stride_t
+ *   out    : [T][H][V]   rows at out + t*o_stride_t + h*o_stride_h
+ *   lse    : optional fp32 [H][T] (NULL to skip): natural-log softmax denominator
+ *   cu_seqlens : optional DEVICE int32 array of n_seq+1 non-decreasing offsets
+ *            starting at 0 and ending at T (packed documents; hyper-parallel
+ *            `_causal_partition` uses the same ends without the leading 0).
+ *            NULL means one document of T tokens.
+ * The packed q+kv rows of mla_pack_heads can be read in place with
+ * q_stride_h = kv_stride_h = F and kv = q + K.
+ * Workspace: mla_attention_workspace_size() bytes of device memory, 256-byte
+ * aligned (0 when cu_seqlens is NULL); contents need not be initialised.
+ */
+typedef struct mla_attn_args {
+  const void *q;
+  int64_t q_stride_t, q_stride_h;
+  const void *kv;
+  int64_t kv_stride_t, kv_stride_h;
+  const void *k_rope;
+  int64_t kr_stride_t;
+  void *out;
+  int64_t o_stride_t, o_stride_h;
+  float *lse;
+  const int32_t *cu_seqlens;
+  int n_seq;
+  int64_t T;
+  int H, N, R, V;
+  float scale;
+  int causal;
+  int dtype;
+  void *workspace;
+  size_t workspace_bytes;
+} mla_attn_args;
+
+size_t mla_attention_workspace_size(const mla_attn_args *a);
+int mla_attention_fwd(const mla_attn_args *a, void *stream);
+
+/*
+ * Latent-cache decode: one new query token per sequence attends over its whole
+ * cached latent, reduced in num_splits KV chunks with an online softmax
+ * (DeepSpeed PR #8602, "Components": decode attention with KV split-K and an
+ * online softmax) and combined as m = max_c m_c, l = sum_c l_c e^(m_c - m),
+ * o = sum_c l_c e^(m_c - m) o_c / l.
+ * The keys and values are the latent-first up-projection of the cache
+ * (k_nope, v = latent_cache[b] @ w_kvb columns of each head) with the shared
+ * band rope_cache[b]; no mask (the query is the newest token).
+ *   q            : [B][H][N+R]
+ *   latent_cache : [B][S][L]
+ *   rope_cache   : [B][S][R]
+ *   w_kvb        : [L][heads_total*(N+V)], heads [head_begin, head_begin+H)
+ *   out          : [B][H][V]
+ *   lse          : optional fp32 [B][H]
+ * MLA_BF16 only. Workspace: mla_latent_decode_workspace_size() bytes, 256-byte
+ * aligned; contents need not be initialised.
+ */
+typedef struct mla_decode_args {
+  const void *q;
+  const void *latent_cache;
+  const void *rope_cache;
+  const void *w_kvb;
+  void *out;
+  float *lse;
+  int B;
+  int64_t S;
+  int L, H, heads_total, head_begin, N, R, V;
+  int num_splits;
+  float scale;
+  int dtype;
+  void *workspace;
+  size_t workspace_bytes;
+} mla_decode_args;
+
+size_t mla_latent_decode_workspace_size(const mla_decode_args *a);
+int mla_latent_decode_fwd(const mla_decode_args *a, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

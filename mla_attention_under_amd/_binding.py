@@ -1,0 +1,246 @@
+"""Thin ctypes binding of libmla.so (argument marshalling only).
+
+Every function has the name of the C entry point it wraps (include/mla.h).
+Tensors are torch tensors on the GPU; PyTorch supplies device memory and the
+current stream, and every step of the computation runs in libmla.so. There is
+no fallback: if the library is missing or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_OK, MLA_EINVAL, MLA_EUNSUPPORTED, MLA_ELAUNCH = 0, -1, -2, -3
+MLA_BF16, MLA_F32 = 0, 1
+
+# every symbol include/mla.h declares
+EXPORTS = (
+    "mla_last_error", "mla_version", "mla_head_shard_sizes", "mla_pack_heads", "mla_unpack_heads",
+    "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
+    "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+class mla_attn_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+        ("kv", ctypes.c_void_p), ("kv_stride_t", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
+        ("k_rope", ctypes.c_void_p), ("kr_stride_t", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
+        ("lse", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("n_seq", ctypes.c_int),
+        ("T", ctypes.c_int64), ("H", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int), ("V", ctypes.c_int),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class mla_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("latent_cache", ctypes.c_void_p), ("rope_cache", ctypes.c_void_p),
+        ("w_kvb", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("B", ctypes.c_int), ("S", ctypes.c_int64), ("L", ctypes.c_int), ("H", ctypes.c_int),
+        ("heads_total", ctypes.c_int), ("head_begin", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int),
+        ("V", ctypes.c_int), ("num_splits", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mla_attention_under_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_version.restype = ctypes.c_char_p
+    lib.mla_head_shard_sizes.argtypes = [i32, i32, i32, ctypes.POINTER(i32)]
+    for fn in (lib.mla_pack_heads, lib.mla_unpack_heads):
+        fn.argtypes = [vp, vp, i64, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
+    lib.mla_latent_up_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.mla_attention_workspace_size.argtypes = [ctypes.POINTER(mla_attn_args)]
+    lib.mla_attention_workspace_size.restype = sz
+    lib.mla_attention_fwd.argtypes = [ctypes.POINTER(mla_attn_args), vp]
+    lib.mla_latent_decode_workspace_size.argtypes = [ctypes.POINTER(mla_decode_args)]
+    lib.mla_latent_decode_workspace_size.restype = sz
+    lib.mla_latent_decode_fwd.argtypes = [ctypes.POINTER(mla_decode_args), vp]
+    for name in EXPORTS:
+        getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn, rc):
+    if rc != MLA_OK:
+        raise MlaError(fn, rc, load_library().mla_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t):
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def mla_head_shard_sizes(q_heads: int, kv_heads: int, sp: int) -> list[int]:
+    lib = load_library()
+    out = (ctypes.c_int * max(sp, 1))()
+    _check("mla_head_shard_sizes", lib.mla_head_shard_sizes(q_heads, kv_heads, sp, out))
+    return list(out)[:sp]
+
+
+def _pack(name, src, dst, sizes, tokens, heads_total, feat, stream):
+    lib = load_library()
+    _dev(src, dst)
+    if src.element_size() != dst.element_size():
+        raise ValueError("source and destination element sizes differ")
+    dt = {2: MLA_BF16, 4: MLA_F32}[src.element_size()]
+    arr = (ctypes.c_int * len(sizes))(*sizes)
+    _check(name, getattr(lib, name)(_ptr(src), _ptr(dst), tokens, heads_total, feat, arr, len(sizes), dt,
+                                    _stream(stream)))
+    return dst
+
+
+def mla_pack_heads(x, send, sizes, stream=None):
+    """x [T][heads_total][F] (contiguous) -> send (flat, concat_r [T][sizes[r]][F])."""
+    assert x.is_contiguous() and send.is_contiguous() and x.dim() == 3 and send.numel() == x.numel()
+    T, Ht, F = x.shape
+    return _pack("mla_pack_heads", x, send, sizes, T, Ht, F, stream)
+
+
+def mla_unpack_heads(recv, x, sizes, stream=None):
+    """recv (flat, concat_r [T][sizes[r]][F]) -> x [T][heads_total][F] (contiguous)."""
+    assert x.is_contiguous() and recv.is_contiguous() and x.dim() == 3 and recv.numel() == x.numel()
+    T, Ht, F = x.shape
+    return _pack("mla_unpack_heads", recv, x, sizes, T, Ht, F, stream)
+
+
+def mla_latent_up_proj(latent, w_kvb, kv_out, heads_total, head_begin, heads, N, V, stream=None):
+    """latent [T][L], w_kvb [L][heads_total*(N+V)] -> kv_out [T][heads][N+V]."""
+    lib = load_library()
+    _dev(latent, w_kvb, kv_out)
+    assert latent.is_contiguous() and w_kvb.is_contiguous() and kv_out.is_contiguous()
+    T, L = latent.shape
+    assert w_kvb.shape == (L, heads_total * (N + V)) and kv_out.numel() == T * heads * (N + V)
+    _check("mla_latent_up_proj", lib.mla_latent_up_proj(
+        _ptr(latent), _ptr(w_kvb), _ptr(kv_out), T, L, heads_total, head_begin, heads, N, V, _dtype(latent),
+        _stream(stream)))
+    return kv_out
+
+
+def _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace):
+    T, H = q.shape[0], q.shape[1]
+    a = mla_attn_args()
+    a.q, a.q_stride_t, a.q_stride_h = q.data_ptr(), q.stride(0), q.stride(1)
+    a.kv, a.kv_stride_t, a.kv_stride_h = kv.data_ptr(), kv.stride(0), kv.stride(1)
+    a.k_rope, a.kr_stride_t = k_rope.data_ptr(), k_rope.stride(0)
+    a.out, a.o_stride_t, a.o_stride_h = out.data_ptr(), out.stride(0), out.stride(1)
+    a.lse = None if lse is None else lse.data_ptr()
+    a.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    a.n_seq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.T, a.H, a.N, a.R, a.V = T, H, N, R, V
+    a.scale, a.causal, a.dtype = float(scale), int(bool(causal)), _dtype(q)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal=True, cu_seqlens=None) -> int:
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, None, cu_seqlens, None)
+    return int(load_library().mla_attention_workspace_size(ctypes.byref(a)))
+
+
+def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None, cu_seqlens=None,
+                      workspace=None, stream=None):
+    """q [T][H][N+R], kv [T][H][N+V], k_rope [T][R] (last dims unit-stride) -> out [T][H][V].
+
+    Strided views are passed through (e.g. q and kv read in place from a packed
+    [T][H][F] buffer). cu_seqlens: int32 device tensor [n_seq+1] or None.
+    The workspace, when needed and not given, is allocated through PyTorch.
+    """
+    lib = load_library()
+    _dev(q, kv, k_rope, out, lse, cu_seqlens, workspace)
+    for t in (q, kv, k_rope, out):
+        assert t.stride(-1) == 1
+    if cu_seqlens is not None:
+        assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    if workspace is None:
+        need = mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace)
+    _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def _decode_args(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits, scale,
+                 lse, workspace):
+    B, H = q.shape[0], q.shape[1]
+    a = mla_decode_args()
+    a.q, a.latent_cache, a.rope_cache = q.data_ptr(), latent_cache.data_ptr(), rope_cache.data_ptr()
+    a.w_kvb, a.out = w_kvb.data_ptr(), out.data_ptr()
+    a.lse = None if lse is None else lse.data_ptr()
+    a.B, a.S, a.L, a.H = B, latent_cache.shape[1], latent_cache.shape[2], H
+    a.heads_total, a.head_begin, a.N, a.R, a.V = heads_total, head_begin, N, R, V
+    a.num_splits, a.scale, a.dtype = num_splits, float(scale), _dtype(q)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def mla_latent_decode_workspace_size(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V,
+                                     num_splits, scale) -> int:
+    a = _decode_args(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits, scale,
+                     None, None)
+    return int(load_library().mla_latent_decode_workspace_size(ctypes.byref(a)))
+
+
+def mla_latent_decode_fwd(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits,
+                          scale, lse=None, workspace=None, stream=None):
+    """q [B][H][N+R], latent_cache [B][S][L], rope_cache [B][S][R], w_kvb [L][heads_total*(N+V)] -> out [B][H][V]."""
+    lib = load_library()
+    _dev(q, latent_cache, rope_cache, w_kvb, out, lse, workspace)
+    for t in (q, latent_cache, rope_cache, w_kvb, out):
+        assert t.is_contiguous()
+    if workspace is None:
+        need = mla_latent_decode_workspace_size(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin,
+                                                N, R, V, num_splits, scale)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = _decode_args(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits, scale,
+                     lse, workspace)
+    _check("mla_latent_decode_fwd", lib.mla_latent_decode_fwd(ctypes.byref(a), _stream(stream)))
+    return out

@@ -1,0 +1,66 @@
+// Device helpers shared by the gfx950 kernels: bf16 vector types, the bf16
+// MFMA wrappers, and fp32 <-> bf16 conversion.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// D[32x32] += A[32x16] * B[16x32] in fp32. Lane l holds A row (l%32), k = 8*(l/32)..+7
+// and B column (l%32), k = 8*(l/32)..+7; D[i][j] sits in lane j + 32*((i/4)%2),
+// register 4*(i/8) + i%4.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D[16x16] += A[16x32] * B[32x16]. Lane l holds A row (l%16), k = 8*(l/16)..+7 and
+// B column (l%16), k = 8*(l/16)..+7; D[i][j] sits in lane j + 16*(i/4), register i%4.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(const bf16x8 &v) { return __builtin_bit_cast(u32x4, v); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two fp32 -> two bf16 packed in one dword (low = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Interleave the 16-bit halves of two dwords: lo16(a)|lo16(b)<<16 and hi16(a)|hi16(b)<<16.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ float load_f32<float>(const float *p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_f32<uint16_t>(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T>
+__device__ __forceinline__ void store_f32(T *p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_f32<float>(float *p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void store_f32<uint16_t>(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+}  // namespace mla

@@ -1,0 +1,291 @@
+// Host front end of libmla.so: argument validation, error reporting and
+// dispatch to the HIP launchers. Every check runs before anything is launched,
+// so a bad call changes no output (the one-GPU analogue of validating on every
+// rank before the first collective, DeepSpeed PR #8316 review thread).
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MLA_OK;
+}
+
+int launched(int hip_err, const char *what) {
+  if (hip_err != 0) return fail(MLA_ELAUNCH, "%s: HIP launch failed: %s", what, mla::hip_error_name(hip_err));
+  return ok();
+}
+
+bool valid_dtype(int dt) { return dt == MLA_BF16 || dt == MLA_F32; }
+int64_t elem_bytes(int dt) { return dt == MLA_BF16 ? 2 : 4; }
+
+// head offsets from a host shard list; checks every entry
+int shard_offsets(const int *sizes, int sp, int heads_total, int *off, const char *who) {
+  if (sizes == nullptr) return fail(MLA_EINVAL, "%s: sizes is NULL", who);
+  if (sp < 1 || sp > mla::kMaxRanks) return fail(MLA_EINVAL, "%s: sp=%d outside [1, %d]", who, sp, mla::kMaxRanks);
+  int64_t acc = 0;
+  for (int r = 0; r < sp; ++r) {
+    if (sizes[r] < 1) return fail(MLA_EINVAL, "%s: sizes[%d]=%d must be positive", who, r, sizes[r]);
+    off[r] = static_cast<int>(acc);
+    acc += sizes[r];
+  }
+  if (acc != heads_total)
+    return fail(MLA_EINVAL, "%s: shard sizes sum to %lld, heads_total is %d", who, static_cast<long long>(acc),
+                heads_total);
+  off[sp] = heads_total;
+  return MLA_OK;
+}
+
+int pack_common(const void *src, void *dst, int64_t tokens, int heads_total, int feat, const int *sizes, int sp,
+                int dtype, void *stream, int to_slabs, const char *who) {
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (tokens < 0 || heads_total < 1 || feat < 1)
+    return fail(MLA_EINVAL, "%s: need tokens >= 0, heads_total >= 1, feat >= 1 (got %lld, %d, %d)", who,
+                static_cast<long long>(tokens), heads_total, feat);
+  mla::PackPlan p;
+  const int rc = shard_offsets(sizes, sp, heads_total, p.off, who);
+  if (rc != MLA_OK) return rc;
+  if (tokens == 0) return ok();
+  if (src == nullptr || dst == nullptr) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const int64_t eb = elem_bytes(dtype);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uint64_t bytes = static_cast<uint64_t>(tokens) * heads_total * feat * eb;
+  if (a % eb || b % eb) return fail(MLA_EINVAL, "%s: buffers must be aligned to the element size", who);
+  if (a < b + bytes && b < a + bytes) return fail(MLA_EINVAL, "%s: source and destination overlap", who);
+  p.src = src;
+  p.dst = dst;
+  p.tokens = tokens;
+  p.heads_total = heads_total;
+  p.row_bytes = feat * eb;
+  p.sp = sp;
+  p.to_slabs = to_slabs;
+  return launched(mla::launch_pack(p, stream), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_last_error(void) { return g_err.c_str(); }
+
+const char *mla_version(void) { return "mla 0.1 gfx950"; }
+
+int mla_head_shard_sizes(int q_heads, int kv_heads, int sp, int *sizes_out) {
+  const char *who = "mla_head_shard_sizes";
+  if (sizes_out == nullptr) return fail(MLA_EINVAL, "%s: sizes_out is NULL", who);
+  if (sp < 1 || q_heads < 1 || kv_heads < 1)
+    return fail(MLA_EINVAL, "%s: q_heads, kv_heads and sp must be positive (got %d, %d, %d)", who, q_heads,
+                kv_heads, sp);
+  if (q_heads % kv_heads != 0)
+    return fail(MLA_EINVAL, "%s: q_heads (%d) is not a multiple of kv_heads (%d)", who, q_heads, kv_heads);
+  if (kv_heads < sp)
+    return fail(MLA_EINVAL, "%s: kv_heads (%d) < sp (%d): some rank would own no KV head", who, kv_heads, sp);
+  const int group = q_heads / kv_heads;
+  const int base = kv_heads / sp, extra = kv_heads % sp;
+  for (int r = 0; r < sp; ++r) sizes_out[r] = (base + (r < extra ? 1 : 0)) * group;
+  return ok();
+}
+
+int mla_pack_heads(const void *x, void *send, int64_t tokens, int heads_total, int feat, const int *sizes, int sp,
+                   int dtype, void *stream) {
+  return pack_common(x, send, tokens, heads_total, feat, sizes, sp, dtype, stream, 1, "mla_pack_heads");
+}
+
+int mla_unpack_heads(const void *recv, void *x, int64_t tokens, int heads_total, int feat, const int *sizes,
+                     int sp, int dtype, void *stream) {
+  return pack_common(recv, x, tokens, heads_total, feat, sizes, sp, dtype, stream, 0, "mla_unpack_heads");
+}
+
+int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int64_t T, int L, int heads_total,
+                       int head_begin, int heads, int N, int V, int dtype, void *stream) {
+  const char *who = "mla_latent_up_proj";
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (T < 0 || L < 1 || N < 1 || V < 1 || heads < 1 || heads_total < 1)
+    return fail(MLA_EINVAL, "%s: need T >= 0 and L, N, V, heads, heads_total >= 1", who);
+  if (head_begin < 0 || head_begin + heads > heads_total)
+    return fail(MLA_EINVAL, "%s: head range [%d, %d) outside the %d heads of the weight", who, head_begin,
+                head_begin + heads, heads_total);
+  if (T == 0) return ok();
+  if (latent == nullptr || w_kvb == nullptr || kv_out == nullptr) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const int64_t P = static_cast<int64_t>(N) + V;
+  const int64_t eb = elem_bytes(dtype);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w_kvb) |
+                       reinterpret_cast<uintptr_t>(kv_out);
+  if (al % eb) return fail(MLA_EINVAL, "%s: buffers must be aligned to the element size", who);
+  if (dtype == MLA_BF16 && (L % 8 || P % 8 || (heads_total * P) % 8 || al % 16))
+    return fail(MLA_EUNSUPPORTED, "%s: bf16 needs L and N+V multiples of 8 and 16-byte aligned buffers", who);
+  mla::UpProjPlan p;
+  p.latent = latent;
+  p.w = w_kvb;
+  p.out = kv_out;
+  p.T = T;
+  p.L = L;
+  p.ldw = heads_total * P;
+  p.col0 = head_begin * P;
+  p.ncols = heads * P;
+  p.bf16 = dtype == MLA_BF16;
+  return launched(mla::launch_up_proj(p, stream), who);
+}
+
+static int attn_validate(const mla_attn_args *a, const char *who) {
+  if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
+  if (!valid_dtype(a->dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, a->dtype);
+  if (a->T < 0 || a->H < 1 || a->N < 1 || a->R < 0 || a->V < 1)
+    return fail(MLA_EINVAL, "%s: need T >= 0, H >= 1, N >= 1, R >= 0, V >= 1", who);
+  if (a->R % 2) return fail(MLA_EINVAL, "%s: the RoPE band width R=%d must be even", who, a->R);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(MLA_EINVAL, "%s: scale must be finite and positive", who);
+  if (a->T > 0x7fffffffLL) return fail(MLA_EUNSUPPORTED, "%s: T above 2^31-1", who);
+  if (a->cu_seqlens != nullptr && a->n_seq < 1)
+    return fail(MLA_EINVAL, "%s: cu_seqlens needs n_seq >= 1", who);
+  const int64_t K = static_cast<int64_t>(a->N) + a->R;
+  if (a->q_stride_h < K || a->q_stride_t < a->H * a->q_stride_h - (a->q_stride_h - K))
+    return fail(MLA_EINVAL, "%s: q strides (%lld, %lld) overlap rows of width %lld", who,
+                static_cast<long long>(a->q_stride_t), static_cast<long long>(a->q_stride_h),
+                static_cast<long long>(K));
+  const int64_t P = static_cast<int64_t>(a->N) + a->V;
+  if (a->kv_stride_h < P || a->kv_stride_t < a->kv_stride_h * (a->H - 1) + P)
+    return fail(MLA_EINVAL, "%s: kv strides overlap rows of width N+V=%lld", who, static_cast<long long>(P));
+  if (a->kr_stride_t < a->R) return fail(MLA_EINVAL, "%s: k_rope stride below R", who);
+  if (a->o_stride_h < a->V || a->o_stride_t < a->o_stride_h * (a->H - 1) + a->V)
+    return fail(MLA_EINVAL, "%s: out strides overlap rows of width V", who);
+  if (a->T == 0) return MLA_OK;
+  if (!a->q || !a->kv || !a->out || (a->R > 0 && !a->k_rope)) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  if (mla::attn_fast_path(a->N, a->R, a->V, a->dtype == MLA_BF16)) {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->kv) |
+                         reinterpret_cast<uintptr_t>(a->k_rope) | reinterpret_cast<uintptr_t>(a->out);
+    const int64_t st = a->q_stride_t | a->q_stride_h | a->kv_stride_t | a->kv_stride_h | a->kr_stride_t |
+                       a->o_stride_t | a->o_stride_h;
+    if (al % 16 || st % 8)
+      return fail(MLA_EUNSUPPORTED, "%s: bf16 tiles need 16-byte aligned buffers and strides multiple of 8", who);
+    const size_t need = mla::attn_workspace_bytes(a->T, a->n_seq, a->cu_seqlens != nullptr, a->N, a->R, a->V, 1);
+    if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need ||
+                     reinterpret_cast<uintptr_t>(a->workspace) % 256))
+      return fail(MLA_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", who, need,
+                  a->workspace_bytes);
+  }
+  return MLA_OK;
+}
+
+size_t mla_attention_workspace_size(const mla_attn_args *a) {
+  if (a == nullptr) return 0;
+  return mla::attn_workspace_bytes(a->T, a->n_seq, a->cu_seqlens != nullptr, a->N, a->R, a->V,
+                                   a->dtype == MLA_BF16);
+}
+
+int mla_attention_fwd(const mla_attn_args *a, void *stream) {
+  const char *who = "mla_attention_fwd";
+  const int rc = attn_validate(a, who);
+  if (rc != MLA_OK) return rc;
+  if (a->T == 0) return ok();
+  mla::AttnPlan p;
+  p.q = a->q;
+  p.q_st = a->q_stride_t;
+  p.q_sh = a->q_stride_h;
+  p.kv = a->kv;
+  p.kv_st = a->kv_stride_t;
+  p.kv_sh = a->kv_stride_h;
+  p.kr = a->k_rope;
+  p.kr_st = a->kr_stride_t;
+  p.out = a->out;
+  p.o_st = a->o_stride_t;
+  p.o_sh = a->o_stride_h;
+  p.lse = a->lse;
+  p.cu = a->cu_seqlens;
+  p.n_seq = a->cu_seqlens ? a->n_seq : 1;
+  p.T = a->T;
+  p.H = a->H;
+  p.N = a->N;
+  p.R = a->R;
+  p.V = a->V;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.bf16 = a->dtype == MLA_BF16;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return launched(mla::launch_attention(p, stream), who);
+}
+
+static int decode_validate(const mla_decode_args *a, const char *who) {
+  if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
+  if (a->dtype != MLA_BF16) return fail(MLA_EUNSUPPORTED, "%s: bf16 only", who);
+  if (a->B < 0 || a->S < 1 || a->L < 1 || a->H < 1 || a->N < 1 || a->R < 0 || a->V < 1 || a->num_splits < 1)
+    return fail(MLA_EINVAL, "%s: need B >= 0, S >= 1 and positive L, H, N, V, num_splits", who);
+  if (a->R % 2) return fail(MLA_EINVAL, "%s: the RoPE band width R=%d must be even", who, a->R);
+  if (a->head_begin < 0 || a->head_begin + a->H > a->heads_total)
+    return fail(MLA_EINVAL, "%s: head range [%d, %d) outside the %d heads of the weight", who, a->head_begin,
+                a->head_begin + a->H, a->heads_total);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(MLA_EINVAL, "%s: scale must be finite and positive", who);
+  if (a->num_splits > a->S) return fail(MLA_EINVAL, "%s: more splits (%d) than cached positions", who, a->num_splits);
+  if (!mla::decode_supported(a->L, a->N, a->R, a->V) || a->H > 16)
+    return fail(MLA_EUNSUPPORTED, "%s: no decode kernel for L=%d N=%d R=%d V=%d H=%d (needs L=512, R=64, H<=16)",
+                who, a->L, a->N, a->R, a->V, a->H);
+  if (a->B == 0) return MLA_OK;
+  if (!a->q || !a->latent_cache || !a->w_kvb || !a->out || (a->R > 0 && !a->rope_cache))
+    return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->latent_cache) |
+                       reinterpret_cast<uintptr_t>(a->rope_cache) | reinterpret_cast<uintptr_t>(a->w_kvb) |
+                       reinterpret_cast<uintptr_t>(a->out);
+  if (al % 16) return fail(MLA_EUNSUPPORTED, "%s: buffers must be 16-byte aligned", who);
+  const size_t need = mla::decode_workspace_bytes(a->B, a->H, a->L, a->N, a->R, a->V, a->num_splits);
+  if (a->workspace == nullptr || a->workspace_bytes < need || reinterpret_cast<uintptr_t>(a->workspace) % 256)
+    return fail(MLA_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", who, need,
+                a->workspace_bytes);
+  return MLA_OK;
+}
+
+size_t mla_latent_decode_workspace_size(const mla_decode_args *a) {
+  if (a == nullptr || a->num_splits < 1) return 0;
+  return mla::decode_workspace_bytes(a->B, a->H, a->L, a->N, a->R, a->V, a->num_splits);
+}
+
+int mla_latent_decode_fwd(const mla_decode_args *a, void *stream) {
+  const char *who = "mla_latent_decode_fwd";
+  const int rc = decode_validate(a, who);
+  if (rc != MLA_OK) return rc;
+  if (a->B == 0) return ok();
+  mla::DecodePlan p;
+  p.q = a->q;
+  p.c = a->latent_cache;
+  p.kr = a->rope_cache;
+  p.w = a->w_kvb;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.B = a->B;
+  p.S = a->S;
+  p.L = a->L;
+  p.H = a->H;
+  p.N = a->N;
+  p.R = a->R;
+  p.V = a->V;
+  p.ldw = static_cast<int64_t>(a->heads_total) * (a->N + a->V);
+  p.col0 = static_cast<int64_t>(a->head_begin) * (a->N + a->V);
+  p.splits = a->num_splits;
+  p.scale = a->scale;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return launched(mla::launch_decode(p, stream), who);
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal interface between the host front end (mla_host.cpp, plain C++) and
+// the HIP launchers (*.hip). Pointers are device pointers; `stream` is a
+// hipStream_t passed as void*. Launchers return 0 or a hipError_t value.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace mla {
+
+constexpr int kMaxRanks = 256;   // largest sequence-parallel degree the pack accepts
+
+// ---- token <-> head pack -------------------------------------------------
+struct PackPlan {
+  const void *src;
+  void *dst;
+  int64_t tokens;
+  int heads_total;
+  int64_t row_bytes;       // feat * element size
+  int sp;
+  int to_slabs;            // 1: x -> slabs (pack), 0: slabs -> x (unpack)
+  int off[kMaxRanks + 1];  // head offset of each rank, off[sp] = heads_total
+};
+int launch_pack(const PackPlan &p, void *stream);
+
+// ---- latent up-projection -------------------------------------------------
+struct UpProjPlan {
+  const void *latent;  // [T][L]
+  const void *w;       // [L][ldw], columns [col0, col0 + ncols)
+  void *out;           // [T][ncols]
+  int64_t T;
+  int L;
+  int64_t ldw, col0, ncols;
+  int bf16;
+};
+int launch_up_proj(const UpProjPlan &p, void *stream);
+
+// ---- attention ------------------------------------------------------------
+struct AttnPlan {
+  const void *q;
+  int64_t q_st, q_sh;
+  const void *kv;
+  int64_t kv_st, kv_sh;
+  const void *kr;
+  int64_t kr_st;
+  void *out;
+  int64_t o_st, o_sh;
+  float *lse;
+  const int32_t *cu;   // device cu_seqlens or nullptr
+  int n_seq;
+  int64_t T;
+  int H, N, R, V;
+  float scale;
+  int causal;
+  int bf16;
+  void *ws;
+  size_t ws_bytes;
+};
+// true when the MFMA kernel covers these head widths (others use the generic kernel)
+bool attn_fast_path(int N, int R, int V, int bf16);
+size_t attn_workspace_bytes(int64_t T, int n_seq, int has_cu, int N, int R, int V, int bf16);
+int launch_attention(const AttnPlan &p, void *stream);
+
+// ---- latent-cache decode ------------------------------------------------
+struct DecodePlan {
+  const void *q;       // [B][H][N+R]
+  const void *c;       // [B][S][L]
+  const void *kr;      // [B][S][R]
+  const void *w;       // [L][ldw]
+  void *out;           // [B][H][V]
+  float *lse;          // [B][H] or nullptr
+  int B;
+  int64_t S;
+  int L, H, N, R, V;
+  int64_t ldw, col0;   // head h uses columns col0 + h*(N+V) ...
+  int splits;
+  float scale;
+  void *ws;
+  size_t ws_bytes;
+};
+bool decode_supported(int L, int N, int R, int V);
+size_t decode_workspace_bytes(int B, int H, int L, int N, int R, int V, int splits);
+int launch_decode(const DecodePlan &p, void *stream);
+
+const char *hip_error_name(int err);
+
+}  // namespace mla

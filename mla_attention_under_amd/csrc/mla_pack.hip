@@ -1,0 +1,109 @@
+// Token <-> head permutation of packed [q | kv] rows (the local send/receive
+// side of the Ulysses exchange; torchtitan "MLA CP optimization", section
+// "Ulysses CP").
+//
+// Every (token, rank) pair moves one contiguous run of sizes[r]*row_bytes
+// bytes between x[t][off_r .. off_r+sizes[r]) and slab r's row t, so the copy
+// is a set of contiguous runs. HBM-bound: each thread moves UNROLL vector
+// chunks of the widest size (16, 8, 4 or 2 bytes) that divides the row, with
+// all loads issued before any store so that every wave keeps UNROLL requests
+// in flight. Indexing is over the slab side, so slab reads/writes are one
+// contiguous stream per rank and the x side is a contiguous run per token.
+#include <hip/hip_runtime.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+struct PackArgs {
+  const unsigned char *src;
+  unsigned char *dst;
+  uint32_t heads_total;
+  uint32_t row_chunks;   // chunks per (token, head) row
+  uint64_t tokens;
+  int to_slabs;
+  int off[kMaxRanks + 1];
+};
+
+// Index is uint32_t when every chunk index of the whole buffer fits 32 bits
+// (the common case: cheap 32-bit division), else uint64_t.
+template <typename Chunk, typename Index>
+__global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
+  const int r = blockIdx.y;
+  const Index q = static_cast<Index>(a.off[r + 1] - a.off[r]);
+  const Index run = q * a.row_chunks;     // chunks per token in slab r
+  const Index total = static_cast<Index>(a.tokens) * run;
+  const Index slab_base = static_cast<Index>(a.tokens) * static_cast<Index>(a.off[r]) * a.row_chunks;
+  const Index x_tok = static_cast<Index>(a.heads_total) * a.row_chunks;
+  const Index x_off = static_cast<Index>(a.off[r]) * a.row_chunks;
+  const Chunk *src = reinterpret_cast<const Chunk *>(a.src);
+  Chunk *dst = reinterpret_cast<Chunk *>(a.dst);
+
+  const Index first = static_cast<Index>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
+  Chunk v[kUnroll];
+  Index didx[kUnroll];
+  bool ok[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const Index c = first + static_cast<Index>(u) * kThreads;
+    ok[u] = c < total;
+    const Index t = ok[u] ? c / run : 0;
+    const Index w = c - t * run;
+    const Index xi = t * x_tok + x_off + w;
+    const Index si = slab_base + c;
+    const Index sidx = a.to_slabs ? xi : si;
+    didx[u] = a.to_slabs ? si : xi;
+    if (ok[u]) v[u] = __builtin_nontemporal_load(src + sidx);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (ok[u]) __builtin_nontemporal_store(v[u], dst + didx[u]);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename Chunk>
+hipError_t run(const PackPlan &p, hipStream_t s) {
+  PackArgs a;
+  a.src = static_cast<const unsigned char *>(p.src);
+  a.dst = static_cast<unsigned char *>(p.dst);
+  a.heads_total = static_cast<uint32_t>(p.heads_total);
+  a.row_chunks = static_cast<uint32_t>(p.row_bytes / sizeof(Chunk));
+  a.tokens = static_cast<uint64_t>(p.tokens);
+  a.to_slabs = p.to_slabs;
+  int maxq = 0;
+  for (int r = 0; r <= p.sp; ++r) a.off[r] = p.off[r];
+  for (int r = 0; r < p.sp; ++r) maxq = maxq > (p.off[r + 1] - p.off[r]) ? maxq : (p.off[r + 1] - p.off[r]);
+  const uint64_t per_rank = a.tokens * static_cast<uint64_t>(maxq) * a.row_chunks;
+  const uint64_t blocks = (per_rank + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffULL) return hipErrorInvalidConfiguration;
+  const uint64_t all = a.tokens * static_cast<uint64_t>(p.heads_total) * a.row_chunks;
+  const dim3 grid(static_cast<unsigned>(blocks), p.sp);
+  if (all + kThreads * kUnroll < 0xffffffffULL)
+    hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((pack_kernel<Chunk, uint64_t>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_pack(const PackPlan &p, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uintptr_t align = reinterpret_cast<uintptr_t>(p.src) | reinterpret_cast<uintptr_t>(p.dst);
+  auto fits = [&](int64_t g) { return p.row_bytes % g == 0 && align % g == 0; };
+  if (fits(16)) return run<u32x4>(p, s);
+  if (fits(8)) return run<u32x2>(p, s);
+  if (fits(4)) return run<unsigned int>(p, s);
+  return run<unsigned short>(p, s);
+}
+
+const char *hip_error_name(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+}  // namespace mla

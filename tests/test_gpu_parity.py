@@ -1,0 +1,309 @@
+"""GPU parity: every C-ABI call against the fp64 oracle on the same seeded inputs.
+
+Permutations (pack/unpack) must match bit for bit. bf16 outputs must satisfy
+max|diff| <= 2e-2 and relative L2 <= 1e-2; the fp32 tiny workload 1e-5.
+Workloads: tiny fp32, the DeepSeek-V3-shaped rank shard (T=2048, H=16), the
+uneven 22-head shard (T=4096), packed documents (T=16384) and latent-cache
+decode (32 x 8192), plus ragged sizes that leave partial tiles.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import oracle
+from gpu_helpers import bits, check_close, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+mla = pytest.importorskip("mla_attention_under_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------- pack / unpack
+
+PACK_CASES = [
+    # (name, tokens, sizes, feat, elem_bytes)
+    ("tiny_fp32", 64, [3, 1], 56, 4),
+    ("dsv3_rank_pack", 256, [16] * 8, 448, 2),
+    ("dsv3_rank_out_restore", 256, [16] * 8, 128, 2),
+    ("uneven22_pack", 4096, [22, 22, 21, 21, 21, 21], 448, 2),
+    ("ragged_2byte_rows", 7, [5, 3, 2], 9, 2),
+    ("ragged_4byte_rows", 3, [2, 1], 6, 2),
+    ("ragged_8byte_rows", 5, [3], 4, 2),
+    ("one_token_one_head", 1, [1], 8, 2),
+    ("gqa_q6_kv3", 33, [4, 2], 448, 2),
+]
+
+
+@pytest.mark.parametrize("name,tokens,sizes,feat,eb", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_pack_unpack_bit_exact(name, tokens, sizes, feat, eb):
+    Ht = sum(sizes)
+    x = mi.pack_payload(tokens, Ht, feat, cfg=7, elem_bytes=eb)
+    tdt = torch.int16 if eb == 2 else torch.int32
+    npdt = np.int16 if eb == 2 else np.int32
+    xd = torch.from_numpy(x.view(npdt)).cuda()
+    send = torch.empty(x.size, dtype=tdt, device="cuda")
+    send.fill_(-1)
+    mla.mla_pack_heads(xd, send, sizes)
+    back = torch.empty_like(xd)
+    back.fill_(-1)
+    mla.mla_unpack_heads(send, back, sizes)
+    _sync()
+    ref = oracle.pack_heads(x, sizes)
+    assert np.array_equal(bits(send), ref), name
+    assert np.array_equal(bits(back), x), name
+
+
+def test_pack_zero_tokens_is_a_no_op():
+    x = torch.zeros((0, 4, 8), dtype=torch.int16, device="cuda")
+    send = torch.zeros(0, dtype=torch.int16, device="cuda")
+    mla.mla_pack_heads(x, send, [2, 2])
+    _sync()
+
+
+def test_pack_shard_list_from_the_library():
+    sizes = mla.mla_head_shard_sizes(6, 3, 2)          # GQA: [4, 2]
+    x = mi.pack_payload(9, 6, 12, cfg=8)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    send = torch.empty(x.size, dtype=torch.int16, device="cuda")
+    mla.mla_pack_heads(xd, send, sizes)
+    _sync()
+    assert np.array_equal(bits(send), oracle.pack_heads(x, oracle.head_shard_sizes(6, 3, 2)))
+
+
+# ------------------------------------------------------------------------- up-projection
+
+def _up_proj_case(w, T, head_begin, heads, seed_cfg=None):
+    d = mi.shard_inputs(w, T=T, seed_cfg=seed_cfg)
+    lat, W = dev(d["latent"]), dev(d["w_kvb"])
+    out = torch.empty((T, heads, w.P), dtype=lat.dtype, device="cuda")
+    mla.mla_latent_up_proj(lat, W, out, w.heads_total, head_begin, heads, w.N, w.V)
+    _sync()
+    ref = oracle.latent_up_proj(d["latent"], d["w_kvb"], head_begin, heads, w.N, w.V)
+    return host64(out), ref
+
+
+@pytest.mark.parametrize("wname,T,hb,heads", [
+    ("tiny", 64, 0, 4), ("tiny", 37, 1, 2),
+    ("dsv3_rank", 2048, 0, 16),
+    ("uneven22", 4096, 0, 22), ("uneven22", 300, 22, 22),
+    ("dsv3_rank", 1, 3, 2), ("dsv3_rank", 129, 0, 16), ("dsv3_rank", 1000, 5, 3),
+])
+def test_up_proj_matches_oracle(wname, T, hb, heads):
+    w = mi.WORKLOADS[wname]
+    got, ref = _up_proj_case(w, T, hb, heads)
+    check_close(got, ref, bf16=w.bf16, name=f"{wname} T={T} heads[{hb},{hb + heads})")
+
+
+def test_up_proj_generic_widths():
+    # N+V = 64: the column count is not a multiple of the 128-wide tile
+    w = mi.Workload("odd", 11, T=200, H=3, L=40, N=40, R=8, V=24, heads_total=5)
+    got, ref = _up_proj_case(w, 200, 1, 3)
+    check_close(got, ref, name="N=40 V=24 L=40")
+
+
+# ------------------------------------------------------------------------- attention
+
+def _attn_inputs(w, T, seed_cfg=None, kv_direct=True):
+    """q, k_rope and kv as bf16 bits (kv drawn directly, isolating the attention kernel)."""
+    d = mi.shard_inputs(w, T=T, seed_cfg=seed_cfg)
+    if kv_direct:
+        d["kv"] = mi.draw((T, w.H, w.P), w.cfg if seed_cfg is None else seed_cfg, 9, bf16=w.bf16)
+    return d
+
+
+def _run_attn(w, d, T, causal=True, cu=None, want_lse=False):
+    q, kv, kr = dev(d["q"]), dev(d["kv"]), dev(d["k_rope"])
+    out = torch.full((T, w.H, w.V), float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((w.H, T), float("nan"), dtype=torch.float32, device="cuda") if want_lse else None
+    cud = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K), causal=causal, lse=lse, cu_seqlens=cud)
+    _sync()
+    return host64(out), (None if lse is None else lse.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("T", [64, 1, 37])
+def test_attention_tiny_fp32(T):
+    w = mi.WORKLOADS["tiny"]
+    d = _attn_inputs(w, T)
+    got, lse = _run_attn(w, d, T, want_lse=True)
+    ref, rlse = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K))
+    check_close(got, ref, bf16=False, name=f"tiny T={T}")
+    check_close(lse, rlse, bf16=False, name=f"tiny lse T={T}")
+
+
+@pytest.mark.parametrize("T,H", [(2048, 16), (1, 2), (63, 2), (200, 3), (1000, 2), (4097, 1)])
+def test_attention_dense_causal(T, H):
+    w = mi.WORKLOADS["dsv3_rank"]
+    w = mi.Workload(w.name, w.cfg, T=T, H=H, L=w.L, N=w.N, R=w.R, V=w.V, heads_total=H)
+    d = _attn_inputs(w, T)
+    got, lse = _run_attn(w, d, T, want_lse=True)
+    ref, rlse = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K))
+    check_close(got, ref, name=f"dense T={T} H={H}")
+    check_close(lse, rlse, name=f"lse T={T} H={H}")
+
+
+def test_attention_non_causal():
+    w = mi.WORKLOADS["dsv3_rank"]
+    w = mi.Workload(w.name, w.cfg, T=333, H=2, L=w.L, N=w.N, R=w.R, V=w.V, heads_total=2)
+    d = _attn_inputs(w, 333)
+    got, _ = _run_attn(w, d, 333, causal=False)
+    ref, _ = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K), causal=False)
+    check_close(got, ref, name="non-causal T=333")
+
+
+def test_attention_composed_with_up_projection_dsv3():
+    """Rank shard end to end: GPU up-projection feeds the GPU attention (T=2048, H=16)."""
+    w = mi.WORKLOADS["dsv3_rank"]
+    d = mi.shard_inputs(w)
+    lat, W, q, kr = dev(d["latent"]), dev(d["w_kvb"]), dev(d["q"]), dev(d["k_rope"])
+    kv = torch.empty((w.T, w.H, w.P), dtype=torch.bfloat16, device="cuda")
+    mla.mla_latent_up_proj(lat, W, kv, w.heads_total, 0, w.H, w.N, w.V)
+    out = torch.empty((w.T, w.H, w.V), dtype=torch.bfloat16, device="cuda")
+    mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K))
+    _sync()
+    kv_ref = oracle.latent_up_proj(d["latent"], d["w_kvb"], 0, w.H, w.N, w.V)
+    ref, _ = oracle.attention(d["q"], kv_ref, d["k_rope"], w.N, 1 / math.sqrt(w.K))
+    check_close(host64(out), ref, name="dsv3 composed")
+
+
+def test_attention_uneven22_sampled_rows():
+    """22 heads at T=4096 with the weight's head range [0, 22) of 128; sampled query rows."""
+    w = mi.WORKLOADS["uneven22"]
+    d = mi.shard_inputs(w)
+    lat, W, q, kr = dev(d["latent"]), dev(d["w_kvb"]), dev(d["q"]), dev(d["k_rope"])
+    kv = torch.empty((w.T, w.H, w.P), dtype=torch.bfloat16, device="cuda")
+    mla.mla_latent_up_proj(lat, W, kv, w.heads_total, 0, w.H, w.N, w.V)
+    out = torch.empty((w.T, w.H, w.V), dtype=torch.bfloat16, device="cuda")
+    mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K))
+    _sync()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4095], np.random.default_rng(3).integers(0, 4096, 40)]))
+    kv_ref = oracle.latent_up_proj(d["latent"], d["w_kvb"], 0, w.H, w.N, w.V)
+    ref, _ = oracle.attention(d["q"], kv_ref, d["k_rope"], w.N, 1 / math.sqrt(w.K), rows=rows)
+    check_close(host64(out)[rows], ref[rows], name="uneven22 sampled")
+
+
+@pytest.mark.parametrize("cu", [
+    [0, 100, 101, 101, 400, 531],          # empty and one-token documents, ragged tiles
+    [0, 128, 256, 640],
+    [0, 1, 2, 3],
+])
+def test_attention_varlen_small(cu):
+    T = cu[-1]
+    w = mi.WORKLOADS["varlen16k"]
+    w = mi.Workload(w.name, w.cfg, T=T, H=2, L=w.L, N=w.N, R=w.R, V=w.V, heads_total=2)
+    d = _attn_inputs(w, T)
+    got, lse = _run_attn(w, d, T, cu=cu, want_lse=True)
+    ref, rlse = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K), cu_seqlens=cu)
+    check_close(got, ref, name=f"varlen {cu}")
+    check_close(lse, rlse, name=f"varlen lse {cu}")
+
+
+def test_attention_varlen16k_sampled_rows():
+    w = mi.WORKLOADS["varlen16k"]
+    cu = [int(x) for x in w.cu_seqlens]
+    d = _attn_inputs(w, w.T)
+    got, _ = _run_attn(w, d, w.T, cu=cu)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([np.array(cu[:-1]), np.array(cu[1:]) - 1, [8192 + 127, 8192 + 128],
+                                     rng.integers(0, w.T, 48)]))
+    ref, _ = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K), cu_seqlens=cu, rows=rows)
+    check_close(got[rows], ref[rows], name="varlen16k sampled")
+    # a document's first token returns its own value row
+    for a in cu[:-1]:
+        np.testing.assert_allclose(got[a], oracle.widen(d["kv"])[a, :, w.N:], atol=1e-2, rtol=0)
+
+
+def test_attention_reads_packed_rows_in_place():
+    """torchtitan 'Ulysses CP' order on one rank: every simulated rank projects its own
+    tokens for all heads and packs [q | kv] rows by the shard list; rank r's slab of
+    every peer forms its receive buffer, which the attention reads in place."""
+    Htot, sp, Tl = 16, 4, 96
+    base = mi.WORKLOADS["dsv3_rank"]
+    w = mi.Workload("pipe", 12, T=sp * Tl, H=Htot, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=Htot)
+    d = mi.shard_inputs(w)
+    sizes = mla.mla_head_shard_sizes(Htot, Htot, sp)
+    offs = oracle.head_offsets(sizes)
+    lat, W, q, kr = dev(d["latent"]), dev(d["w_kvb"]), dev(d["q"]), dev(d["k_rope"])
+    sends = []
+    for s in range(sp):
+        kv_s = torch.empty((Tl, Htot, w.P), dtype=torch.bfloat16, device="cuda")
+        mla.mla_latent_up_proj(lat[s * Tl:(s + 1) * Tl].contiguous(), W, kv_s, Htot, 0, Htot, w.N, w.V)
+        rows = torch.cat([q[s * Tl:(s + 1) * Tl], kv_s], dim=2).contiguous()       # [Tl][Htot][F]
+        send = torch.empty(rows.numel(), dtype=torch.bfloat16, device="cuda")
+        mla.mla_pack_heads(rows, send, sizes)
+        sends.append(send)
+    refs = oracle.ulysses_materialise_k_first(d["latent"], d["w_kvb"], d["q"], d["k_rope"], sizes, w.N, w.V,
+                                               1 / math.sqrt(w.K))
+    for r in range(sp):
+        n = Tl * sizes[r] * w.F
+        recv = torch.cat([snd[Tl * offs[r] * w.F:Tl * offs[r] * w.F + n] for snd in sends]).view(sp * Tl, sizes[r], w.F)
+        out = torch.empty((sp * Tl, sizes[r], w.V), dtype=torch.bfloat16, device="cuda")
+        mla.mla_attention_fwd(recv[:, :, :w.K], recv[:, :, w.K:], kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K))
+        _sync()
+        check_close(host64(out), refs[r], name=f"packed rank {r}")
+    # and the latent-first order gives the same answer on the GPU as well
+    latent_first = oracle.ulysses_latent_first(d["latent"], d["w_kvb"], d["q"], d["k_rope"], sizes, w.N, w.V,
+                                               1 / math.sqrt(w.K))
+    for r in range(sp):
+        kv = torch.empty((w.T, sizes[r], w.P), dtype=torch.bfloat16, device="cuda")
+        mla.mla_latent_up_proj(lat, W, kv, Htot, offs[r], sizes[r], w.N, w.V)
+        out = torch.empty((w.T, sizes[r], w.V), dtype=torch.bfloat16, device="cuda")
+        mla.mla_attention_fwd(q[:, offs[r]:offs[r] + sizes[r]], kv, kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K))
+        _sync()
+        check_close(host64(out), latent_first[r], name=f"latent-first rank {r}")
+
+
+def test_attention_is_deterministic():
+    w = mi.WORKLOADS["dsv3_rank"]
+    d = _attn_inputs(w, 1024)
+    q, kv, kr = dev(d["q"][:1024]), dev(d["kv"]), dev(d["k_rope"][:1024])
+    outs = []
+    for _ in range(2):
+        o = torch.empty((1024, w.H, w.V), dtype=torch.bfloat16, device="cuda")
+        mla.mla_attention_fwd(q, kv, kr, o, w.N, w.R, w.V, 1 / math.sqrt(w.K))
+        outs.append(bits(o))
+    assert np.array_equal(outs[0], outs[1])
+
+
+# ------------------------------------------------------------------------- decode
+
+def _decode_case(w, B, S, splits, seqs):
+    d = mi.decode_inputs(w, batch=B, kv_len=S)
+    q, c, kr, W = dev(d["q"]), dev(d["latent"]), dev(d["k_rope"]), dev(d["w_kvb"])
+    out = torch.full((B, w.H, w.V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mla.mla_latent_decode_fwd(q, c, kr, W, out, w.heads_total, 0, w.N, w.R, w.V, splits, 1 / math.sqrt(w.K))
+    _sync()
+    ref, _ = oracle.decode_split_kv(d["q"], d["latent"], d["k_rope"], d["w_kvb"], w.N, w.V, 1 / math.sqrt(w.K),
+                                    splits, seqs=seqs)
+    return host64(out), ref
+
+
+@pytest.mark.parametrize("B,S,splits", [(3, 1000, 8), (2, 64, 1), (1, 130, 3), (2, 9, 4)])
+def test_decode_small(B, S, splits):
+    w = mi.WORKLOADS["decode32"]
+    got, ref = _decode_case(w, B, S, splits, seqs=range(B))
+    check_close(got, ref, name=f"decode B={B} S={S} splits={splits}")
+
+
+def test_decode32_sampled_sequences():
+    w = mi.WORKLOADS["decode32"]
+    seqs = [0, 17, 31]
+    got, ref = _decode_case(w, w.batch, w.kv_len, w.kv_splits, seqs=seqs)
+    check_close(got[seqs], ref[seqs], name="decode32 sampled")
+    assert np.all(np.isfinite(got))

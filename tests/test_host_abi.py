@@ -1,0 +1,200 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, computes shard lists bit-exactly like the oracle, and rejects bad
+arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from golden_io import shard_cases
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("mla_attention_under_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.fail("libmla.so is not built (python -m mla_attention_under_amd.build)")
+    return mla.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_path_calls():
+    fns = declared_functions()
+    for name in ("mla_pack_heads", "mla_latent_up_proj", "mla_attention_fwd", "mla_unpack_heads"):
+        assert name in fns
+    assert set(fns) == set(mla.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (mla_\w+)$", out, flags=re.M))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        getattr(lib, f)
+
+
+def test_struct_layouts_match_the_header():
+    # offsets computed by the C compiler from the header itself
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "mla.h"
+#define P(s, f) printf(#s "." #f " %zu\n", offsetof(s, f));
+int main(void) {
+  P(mla_attn_args, q) P(mla_attn_args, kv_stride_h) P(mla_attn_args, out) P(mla_attn_args, lse)
+  P(mla_attn_args, cu_seqlens) P(mla_attn_args, n_seq) P(mla_attn_args, T) P(mla_attn_args, V)
+  P(mla_attn_args, scale) P(mla_attn_args, dtype) P(mla_attn_args, workspace) P(mla_attn_args, workspace_bytes)
+  P(mla_decode_args, lse) P(mla_decode_args, B) P(mla_decode_args, S) P(mla_decode_args, num_splits)
+  P(mla_decode_args, scale) P(mla_decode_args, workspace) P(mla_decode_args, workspace_bytes)
+  printf("sizeof.attn %zu\nsizeof.decode %zu\n", sizeof(mla_attn_args), sizeof(mla_decode_args));
+  return 0;
+}'''
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "off.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "off")
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    got = dict(zip(lines[0::2], (int(x) for x in lines[1::2])))
+    from mla_attention_under_amd._binding import mla_attn_args, mla_decode_args
+    for key, off in got.items():
+        s, f = key.split(".")
+        if s == "sizeof":
+            assert ctypes.sizeof({"attn": mla_attn_args, "decode": mla_decode_args}[f]) == off
+        else:
+            cls = {"mla_attn_args": mla_attn_args, "mla_decode_args": mla_decode_args}[s]
+            assert getattr(cls, f).offset == off, key
+
+
+@pytest.mark.parametrize("q,kv,sp,exp,src", shard_cases() + shard_cases("workload_shards.txt"))
+def test_shard_lists_match_pages_and_oracle(lib, q, kv, sp, exp, src):
+    if exp is None:
+        with pytest.raises(mla.MlaError) as e:
+            mla.mla_head_shard_sizes(q, kv, sp)
+        assert e.value.code == mla.MLA_EINVAL
+    else:
+        assert mla.mla_head_shard_sizes(q, kv, sp) == exp == oracle.head_shard_sizes(q, kv, sp)
+
+
+def test_shard_lists_bit_exact_against_oracle_exhaustive(lib):
+    for kv in range(1, 33):
+        for g in (1, 2, 3, 8):
+            for sp in range(1, 40):
+                q = kv * g
+                try:
+                    ref = oracle.head_shard_sizes(q, kv, sp)
+                except ValueError:
+                    with pytest.raises(mla.MlaError):
+                        mla.mla_head_shard_sizes(q, kv, sp)
+                    continue
+                assert mla.mla_head_shard_sizes(q, kv, sp) == ref
+
+
+def test_shard_list_error_leaves_output_untouched(lib):
+    out = (ctypes.c_int * 2)(-7, -7)
+    assert lib.mla_head_shard_sizes(2, 1, 2, out) == mla.MLA_EINVAL
+    assert list(out) == [-7, -7]
+    assert b"sp" in lib.mla_last_error()
+    assert lib.mla_head_shard_sizes(6, 3, 2, out) == mla.MLA_OK and list(out) == [4, 2]
+    assert lib.mla_last_error() == b""
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000000)
+
+
+def _pack(lib, tokens, Ht, F, sizes, dtype=mla.MLA_BF16, src=FAKE, dst=FAKE2):
+    arr = (ctypes.c_int * len(sizes))(*sizes)
+    return lib.mla_pack_heads(src, dst, tokens, Ht, F, arr, len(sizes), dtype, None)
+
+
+def test_pack_validation_before_launch(lib):
+    assert _pack(lib, 4, 5, 8, [3, 1]) == mla.MLA_EINVAL           # sizes do not sum to heads_total
+    assert _pack(lib, 4, 4, 8, [4, 0]) == mla.MLA_EINVAL           # a rank with no heads
+    assert _pack(lib, -1, 4, 8, [2, 2]) == mla.MLA_EINVAL
+    assert _pack(lib, 4, 4, 0, [2, 2]) == mla.MLA_EINVAL
+    assert _pack(lib, 4, 4, 8, [2, 2], dtype=7) == mla.MLA_EINVAL
+    assert _pack(lib, 4, 4, 8, [2, 2], dst=FAKE) == mla.MLA_EINVAL  # overlapping buffers
+    assert _pack(lib, 4, 4, 8, [2, 2], src=ctypes.c_void_p(0x10001)) == mla.MLA_EINVAL   # misaligned
+    assert _pack(lib, 0, 4, 8, [2, 2]) == mla.MLA_OK                 # empty: nothing to do
+    assert lib.mla_pack_heads(FAKE, FAKE2, 4, 4, 8, None, 2, 0, None) == mla.MLA_EINVAL
+    assert lib.mla_pack_heads(FAKE, FAKE2, 4, 300, 8, (ctypes.c_int * 300)(*([1] * 300)), 300, 0,
+                              None) == mla.MLA_EINVAL               # sp above the supported maximum
+
+
+def test_up_proj_validation_before_launch(lib):
+    f = lib.mla_latent_up_proj
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, 3, 2, 16, 16, 0, None) == mla.MLA_EINVAL    # head range past W
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, -1, 2, 16, 16, 0, None) == mla.MLA_EINVAL
+    assert f(FAKE, FAKE, FAKE2, 16, 0, 4, 0, 2, 16, 16, 0, None) == mla.MLA_EINVAL
+    assert f(FAKE, FAKE, FAKE2, 16, 30, 4, 0, 2, 16, 16, 0, None) == mla.MLA_EUNSUPPORTED   # bf16 needs L%8
+    assert f(FAKE, FAKE, FAKE2, 0, 32, 4, 0, 2, 16, 16, 0, None) == mla.MLA_OK            # T = 0
+
+
+def _attn(**kw):
+    from mla_attention_under_amd._binding import mla_attn_args
+    a = mla_attn_args()
+    a.q, a.kv, a.k_rope, a.out = 0x10000, 0x20000, 0x30000, 0x40000
+    a.T, a.H, a.N, a.R, a.V = 256, 2, 128, 64, 128
+    a.q_stride_h, a.q_stride_t = 192, 384
+    a.kv_stride_h, a.kv_stride_t = 256, 512
+    a.kr_stride_t = 64
+    a.o_stride_h, a.o_stride_t = 128, 256
+    a.scale, a.causal, a.dtype = 0.07, 1, mla.MLA_BF16
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_attention_validation_before_launch(lib):
+    f = lambda **kw: lib.mla_attention_fwd(ctypes.byref(_attn(**kw)), None)  # noqa: E731
+    assert f(R=63) == mla.MLA_EINVAL                       # odd rope band
+    assert f(scale=0.0) == mla.MLA_EINVAL
+    assert f(scale=float("nan")) == mla.MLA_EINVAL
+    assert f(q_stride_h=100) == mla.MLA_EINVAL             # rows overlap
+    assert f(kv_stride_t=300) == mla.MLA_EINVAL
+    assert f(o_stride_h=64) == mla.MLA_EINVAL
+    assert f(q=0x10002) == mla.MLA_EUNSUPPORTED            # misaligned for the tiled path
+    assert f(cu_seqlens=0x50000, n_seq=2) == mla.MLA_EINVAL   # missing workspace
+    assert f(cu_seqlens=0x50000, n_seq=0) == mla.MLA_EINVAL
+    assert f(T=0) == mla.MLA_OK
+    assert lib.mla_attention_fwd(None, None) == mla.MLA_EINVAL
+    a = _attn(cu_seqlens=0x50000, n_seq=4, T=16384)
+    need = lib.mla_attention_workspace_size(ctypes.byref(a))
+    assert need > 0 and lib.mla_attention_workspace_size(ctypes.byref(_attn())) == 0
+
+
+def test_decode_validation_before_launch(lib):
+    from mla_attention_under_amd._binding import mla_decode_args
+
+    def args(**kw):
+        a = mla_decode_args()
+        a.q, a.latent_cache, a.rope_cache, a.w_kvb, a.out = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+        a.B, a.S, a.L, a.H, a.heads_total, a.head_begin = 32, 8192, 512, 16, 16, 0
+        a.N, a.R, a.V, a.num_splits, a.scale, a.dtype = 128, 64, 128, 8, 0.07, mla.MLA_BF16
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    f = lambda **kw: lib.mla_latent_decode_fwd(ctypes.byref(args(**kw)), None)  # noqa: E731
+    assert f() == mla.MLA_EINVAL                            # no workspace
+    assert f(head_begin=1) == mla.MLA_EINVAL                # head range past W
+    assert f(num_splits=0) == mla.MLA_EINVAL
+    assert f(S=4, num_splits=8) == mla.MLA_EINVAL
+    assert f(dtype=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
+    assert f(L=256) == mla.MLA_EUNSUPPORTED
+    assert f(B=0) == mla.MLA_OK
+    assert lib.mla_latent_decode_workspace_size(ctypes.byref(args())) > 0
