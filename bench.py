@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the uneven22 pack/unpack HBM measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain contiguous copy of 1 GiB (the pack kernel with one rank) 3 times, "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -119,6 +122,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     mla.load_library()
+
+    if args.copy_calibration:
+        n = 1 << 29                                   # 2-byte elements: 1 GiB read + 1 GiB written
+        src = torch.randint(-32768, 32767, (n // 512, 1, 512), dtype=torch.int16, device="cuda")
+        dst = torch.empty(n, dtype=torch.int16, device="cuda")
+        for _ in range(3):
+            mla.mla_pack_heads(src, dst, [1])
+        torch.cuda.synchronize()
+        assert torch.equal(dst.view_as(src), src)
+        print(json.dumps({"copy_calibration_bytes_each_way": 2 * n, "launches": 3}), flush=True)
+        return
 
     w = mi.WORKLOADS["dsv3_rank"]
     T, H, L, N, R, V, P, K = w.T, w.H, w.L, w.N, w.R, w.V, w.P, w.K

@@ -5,31 +5,33 @@
 // with no look-ahead for causal, `_causal_partition` for document-local keys).
 //
 // gfx950 design (bf16 in, fp32 accumulate):
-//  * One workgroup = 4 waves = one (head, 128-query tile); each wave owns 32
-//    queries for the whole key loop, its Q fragment resident in VGPRs.
-//  * Keys stream in 64-key tiles through double-buffered LDS with
-//    global->register prefetch of the next tile. The K tile is assembled from
-//    two sources per key: k_nope from the projected kv rows (per head) and the
-//    shared k_rope row (the same row for every head), so the expanded key is
-//    never materialised in HBM.
+//  * One workgroup = 4 waves = 64 queries of one head: 2 query blocks of 32 x
+//    2 key halves. A 64-key tile is split between the halves (32 keys each);
+//    the two partial softmax states of a query block are merged through LDS
+//    at the end. Two workgroups fit a CU (80 KB LDS, <= 256 registers), so
+//    every SIMD runs two waves and one wave's softmax overlaps the other's MFMAs.
+//  * Tiles move global->LDS with buffer_load ... lds (no staging registers),
+//    double-buffered, one barrier per tile. The key tile is assembled from two
+//    sources: k_nope from this head's projected kv rows and the shared k_rope
+//    row (one copy for all heads), so the expanded key never exists in HBM.
+//    Loads past the visible keys fall outside the buffer range and read zero.
+//  * LDS rows are unpadded and XOR-swizzled per row, so MFMA operand reads and
+//    the transposing reads do not conflict on banks.
 //  * Scores are computed transposed, S^T = K Q^T (32x32x16 MFMA), so lane l
-//    holds 16 keys of query (l % 32) and lane l^32 the other 16: the row max
-//    and row sum need one cross-lane step. P^T leaves the accumulator already
-//    in the B-operand layout of O^T = V^T P^T (the MFMA k order is permuted to
-//    match), so P never goes through LDS; V is written to LDS transposed
-//    (V^T[d][key], keys permuted to the same k order) by a 4x8 register
-//    transpose in the loader.
-//  * Online softmax in the exp2 domain (scale*log2(e) folded into one multiply),
-//    with the running output rescaled only when a row max grows by more than
-//    2^8 (exact: any reference max gives the same quotient).
-//  * Causal tiles past a wave's last query are skipped per wave; masks are
-//    applied only on tiles that cross the diagonal or the document end.
-//  * Work order: heaviest query tiles first (dense: from the end of the
-//    sequence; packed documents: a device-built schedule sorted by key-tile
-//    count, held in the caller's workspace).
+//    holds 16 keys of query (l % 32) and lane l^32 the other 16: row max and
+//    sum take one cross-lane step. P^T stays in registers as the B operand of
+//    O^T = V^T P^T (MFMA k order permuted to match); V^T comes straight from
+//    the row-major V tile with ds_read_b64_tr_b16.
+//  * Online softmax in the exp2 domain (one fma + one exp per score); the
+//    running output is rescaled only when a row max grows by more than 2^8
+//    (exact: any reference max gives the same quotient).
+//  * Work order: dense causal tiles are dealt heaviest-first, then lightest-
+//    first, so co-resident workgroups carry complementary causal work; packed
+//    documents use a device-built schedule sorted by key-tile count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "mla_common.cuh"
 #include "mla_internal.h"
@@ -37,8 +39,8 @@
 namespace mla {
 namespace {
 
-constexpr int BM = 128;      // queries per workgroup
-constexpr int BN = 64;       // keys per tile
+constexpr int BM = 64;       // queries per workgroup (2 blocks of 32)
+constexpr int BN = 64;       // keys per tile (2 halves of 32)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;   // log2 growth of a row max that forces a rescale
 constexpr float kNegBig = -1.0e30f;
@@ -53,44 +55,73 @@ struct AttnArgs {
   const int32_t *cu;      // nullptr: one document [0, T)
   const int2 *tasks;      // packed documents: (query start, document) per task, sorted
   const int *task_count;
-  int n_qtiles;           // dense: query tiles
+  int n_qtiles;           // dense: query tiles per head
+  int order;              // dense tile order: 0 heaviest first, 1 heavy half then light half
   int T, H;
   float scale_log2;       // scale * log2(e)
   int causal;
 };
 
-// Position of key (kq*4 .. kq*4+3) inside its 16-key group in the permuted k order
-// the P^T operand uses: lanes 0-31 hold keys {0-3, 8-11}, lanes 32-63 {4-7, 12-15}.
-__device__ __forceinline__ int vt_pos(int kq) {
-  const int q4 = kq & 3;
-  return 16 * (kq >> 2) + ((q4 & 1) << 3) + ((q4 >> 1) << 2);
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// per-row XOR swizzles of the unpadded LDS tiles (16-byte chunks / 32-byte segments)
+__device__ __forceinline__ int kn_swz(int key) { return key & 15; }
+__device__ __forceinline__ int kr_swz(int key) { return (key ^ (key >> 3)) & 7; }
+__device__ __forceinline__ int v_swz(int key) { return (key & 2) | ((key & 1) * 5); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint16_t *lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds_dst), 16, static_cast<int>(voff), 0, 0, 0);
+}
+
+// 4 bf16 of V^T from a row-major V tile: ds_read_b64_tr_b16 hands lane i of
+// each 16-lane group column i of the 4x16 block whose rows its lanes address.
+__device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
 template <int N, int R, int V>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int KD = N + R;            // score width
-  constexpr int KP = KD + 8;           // LDS pitch of K rows [key][d]
-  constexpr int VP = BN + 8;           // LDS pitch of V^T rows [d][key]
-  constexpr int KCH = KD / 8;          // 16-byte chunks per key row
-  constexpr int NCH = N / 8;
-  constexpr int KLOADS = BN * KCH / 256;
-  constexpr int VGROUPS = (BN / 4) * (V / 8);
-  constexpr int VLOADS = VGROUPS / 256;
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int KD = N + R;          // score width
+  constexpr int NCH = N / 8;         // 16-byte chunks per k_nope row
+  constexpr int RCH = R / 8;         // per k_rope row
+  constexpr int VCH = V / 8;         // per V row
   constexpr int KSTEPS = KD / 16;
+  constexpr int NSTEPS = N / 16;
   constexpr int DBLK = V / 32;
-  constexpr int KT_ELEMS = BN * KP, VT_ELEMS = V * VP;
-  static_assert(KD % 16 == 0 && N % 8 == 0 && V % 32 == 0, "head widths");
-  static_assert((BN * KCH) % 256 == 0 && VGROUPS % 256 == 0, "tile loads must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT_ELEMS + VT_ELEMS)];
+  constexpr int KN_E = BN * N, KR_E = BN * R, V_E = BN * V;   // elements per stage
+  constexpr int KN_I = BN * NCH / 256, KR_I = BN * RCH / 256, V_I = BN * VCH / 256;   // DMA instrs per wave
+  static_assert(N == 128 && R == 64 && V == 128, "swizzles and DMA splits are laid out for 128/64/128");
+  static_assert(KN_I * 256 == BN * NCH && KR_I * 256 == BN * RCH && V_I * 256 == BN * VCH, "tile DMA split");
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[KN_E + KR_E + V_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[KN_E + KR_E + V_E];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = wave & 1, kh = wave >> 1;          // query block, key half
   const int half = lane >> 5, lrow = lane & 31;
+  const int grp = lane >> 4, gl = lane & 15;        // 16-lane groups for the transposing read
 
   // ---- which (head, query tile)
   int h, q0, doc_lo, doc_hi;
   if (a.tasks == nullptr) {
-    h = blockIdx.x % a.H;
-    q0 = (a.n_qtiles - 1 - static_cast<int>(blockIdx.x) / a.H) * BM;
+    const int b = blockIdx.x, H = a.H, n = a.n_qtiles;
+    int qt;
+    if (a.order == 1 && a.causal) {
+      const int heavy = ((n + 1) / 2) * H;
+      if (b < heavy) {
+        h = b % H;
+        qt = n - 1 - b / H;
+      } else {
+        h = (b - heavy) % H;
+        qt = (b - heavy) / H;
+      }
+    } else {
+      h = b % H;
+      qt = n - 1 - b / H;
+    }
+    q0 = qt * BM;
     doc_lo = 0;
     doc_hi = a.T;
   } else {
@@ -102,79 +133,82 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     doc_lo = min(max(a.cu[task.y], 0), a.T);          // the same clamping as the schedule
     doc_hi = min(max(a.cu[task.y + 1], doc_lo), a.T);
   }
+  h = __builtin_amdgcn_readfirstlane(h);
+  q0 = __builtin_amdgcn_readfirstlane(q0);
+  doc_lo = __builtin_amdgcn_readfirstlane(doc_lo);
+  doc_hi = __builtin_amdgcn_readfirstlane(doc_hi);
   const int q_end = min(q0 + BM, doc_hi);
   const int kv_hi = a.causal ? q_end : doc_hi;
   const int n_tiles = (kv_hi - doc_lo + BN - 1) / BN;
+  if (n_tiles <= 0) return;   // uniform: an empty task
 
-  // ---- this lane's query and its Q fragment (B operand of S^T = K Q^T)
-  const int qi = q0 + 32 * wave + lrow;
-  const bool q_ok = qi < q_end;
-  const int wave_q_first = q0 + 32 * wave;
-  const int wave_q_last = min(q0 + 32 * wave + 31, q_end - 1);
-  bf16x8 qf[KSTEPS];
+  // ---- zero both stages once: loads past the buffer range may leave LDS untouched
   {
-    const uint16_t *qp = a.q + static_cast<int64_t>(q_ok ? qi : q0) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 v = q_ok ? *reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
-      qf[ks] = as_bf16x8(v);
+    u32x4 z{0, 0, 0, 0};
+    for (int i = tid; i < (KN_E + KR_E + V_E) / 8; i += 256) {
+      reinterpret_cast<u32x4 *>(st0)[i] = z;
+      reinterpret_cast<u32x4 *>(st1)[i] = z;
     }
   }
 
-  // ---- tile loaders
-  u32x4 rk[KLOADS];
-  u32x4 rv[VLOADS][4];
+  // ---- this lane's query and its Q fragment (B operand of S^T = K Q^T)
+  const int qi = q0 + 32 * qb + lrow;
+  const bool q_ok = qi < q_end;
+  const int wq_first = q0 + 32 * qb;
+  const int wq_last = min(q0 + 32 * qb + 31, q_end - 1);
+  const bool wave_has_q = wq_first < q_end;
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t *qp = a.q + static_cast<int64_t>(min(qi, q_end - 1)) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half));
+  }
+
+  // ---- DMA plan: every wave issues KN_I + KR_I + V_I 1 KB transfers per tile.
+  // Transfer i of wave w fills LDS chunks [64*(w*I + i), +64); lane l loads the
+  // global chunk that the swizzle places at chunk 64*(w*I + i) + l.
   const uint16_t *kv_h = a.kv + static_cast<int64_t>(h) * a.kv_sh;
-  auto load = [&](int j0) {
+  uint32_t kn_off[KN_I], kr_off[KR_I], v_off[V_I];
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int c = tid + 256 * u;
-      const int key = c / KCH, part = c % KCH;
-      const int j = j0 + key;
-      u32x4 v{0, 0, 0, 0};
-      if (j < kv_hi) {
-        const uint16_t *src = part < NCH ? kv_h + static_cast<int64_t>(j) * a.kv_st + 8 * part
-                                         : a.kr + static_cast<int64_t>(j) * a.kr_st + 8 * (part - NCH);
-        v = *reinterpret_cast<const u32x4 *>(src);
-      }
-      rk[u] = v;
-    }
+  for (int i = 0; i < KN_I; ++i) {
+    const int p = 64 * (wave * KN_I + i) + lane;
+    const int key = p / NCH, c = (p % NCH) ^ kn_swz(key);
+    kn_off[i] = static_cast<uint32_t>((key * a.kv_st + 8 * c) * 2);
+  }
 #pragma unroll
-    for (int u = 0; u < VLOADS; ++u) {
-      const int g = tid + 256 * u;
-      const int kq = g % (BN / 4), dq = g / (BN / 4);
+  for (int i = 0; i < KR_I; ++i) {
+    const int p = 64 * (wave * KR_I + i) + lane;
+    const int key = p / RCH, c = (p % RCH) ^ kr_swz(key);
+    kr_off[i] = static_cast<uint32_t>((key * a.kr_st + 8 * c) * 2);
+  }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * kq + r;
-        rv[u][r] = j < kv_hi ? *reinterpret_cast<const u32x4 *>(kv_h + static_cast<int64_t>(j) * a.kv_st + N + 8 * dq)
-                             : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store = [&](int buf) {
-    uint16_t *Ks = smem + buf * (KT_ELEMS + VT_ELEMS);
-    uint16_t *Vt = Ks + KT_ELEMS;
+  for (int i = 0; i < V_I; ++i) {
+    const int p = 64 * (wave * V_I + i) + lane;
+    const int key = p / VCH, cp = p % VCH;
+    const int c = 2 * ((cp >> 1) ^ v_swz(key)) + (cp & 1);
+    v_off[i] = static_cast<uint32_t>((key * a.kv_st + N + 8 * c) * 2);
+  }
+  auto issue = [&](uint16_t *st, int j0) {
+    const int rows = min(kv_hi - j0, BN);
+    const __amdgpu_buffer_rsrc_t rkv =
+        make_rsrc(kv_h + static_cast<int64_t>(j0) * a.kv_st, static_cast<uint32_t>(rows * a.kv_st * 2));
+    const __amdgpu_buffer_rsrc_t rkr =
+        make_rsrc(a.kr + static_cast<int64_t>(j0) * a.kr_st, static_cast<uint32_t>(rows * a.kr_st * 2));
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int c = tid + 256 * u;
-      *reinterpret_cast<u32x4 *>(Ks + (c / KCH) * KP + 8 * (c % KCH)) = rk[u];
-    }
+    for (int i = 0; i < KN_I; ++i) dma16(rkv, st + 512 * (wave * KN_I + i), kn_off[i]);
 #pragma unroll
-    for (int u = 0; u < VLOADS; ++u) {
-      const int g = tid + 256 * u;
-      const int kq = g % (BN / 4), dq = g / (BN / 4);
-      const int pos = vt_pos(kq);
+    for (int i = 0; i < KR_I; ++i) dma16(rkr, st + KN_E + 512 * (wave * KR_I + i), kr_off[i]);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const u32x2 lo{lo_halves(rv[u][0][m], rv[u][1][m]), lo_halves(rv[u][2][m], rv[u][3][m])};
-        const u32x2 hi{hi_halves(rv[u][0][m], rv[u][1][m]), hi_halves(rv[u][2][m], rv[u][3][m])};
-        *reinterpret_cast<u32x2 *>(Vt + (8 * dq + 2 * m) * VP + pos) = lo;
-        *reinterpret_cast<u32x2 *>(Vt + (8 * dq + 2 * m + 1) * VP + pos) = hi;
-      }
-    }
+    for (int i = 0; i < V_I; ++i) dma16(rkv, st + KN_E + KR_E + 512 * (wave * V_I + i), v_off[i]);
   };
 
-  // ---- running state (per lane: one query, partial row sum over its keys)
+  // ---- LDS read addresses (elements), loop-invariant
+  // K: key 32*kh + lrow, chunk 2*ks + half
+  const int kkey = 32 * kh + lrow;
+  // V^T: for 16-key step b and read r, rows 32kh + 16b + 8r + 4*(grp>>1) + (gl>>2), d = 32db + 16*(grp&1) + 4*(gl&3)
+  const int vrow0 = 32 * kh + 4 * (grp >> 1) + (gl >> 2);
+
+  // ---- running state (per lane: one query; m in log2 units, partial row sum)
   f32x16 o[DBLK];
 #pragma unroll
   for (int d = 0; d < DBLK; ++d)
@@ -183,88 +217,135 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   float m_run = kNegBig, l_run = 0.f;
   const float c = a.scale_log2;
 
-  if (n_tiles > 0) {
-    load(doc_lo);
-    store(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int j0 = doc_lo + kt * BN;
-    if (kt + 1 < n_tiles) load(j0 + BN);
-    const uint16_t *Ks = smem + (kt & 1) * (KT_ELEMS + VT_ELEMS);
-    const uint16_t *Vt = Ks + KT_ELEMS;
-    const bool wave_active = !(a.causal && j0 > wave_q_last) && wave_q_first < q_end;
-    if (wave_active) {
-      // S^T = K Q^T : two 32-key blocks
-      f32x16 s[2];
+  // V^T operand fragments of this wave's 32-key half: [16-key step b][d block]
+  auto active_for = [&](int j0) {
+    const int jh = j0 + 32 * kh;
+    return wave_has_q && jh < kv_hi && !(a.causal && jh > wq_last);
+  };
+  auto read_v = [&](const uint16_t *st, bf16x8 (&vf)[2][DBLK]) {
+    const uint16_t *Vs = st + KN_E + KR_E;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (32 * jb + lrow) * KP + 16 * ks + 8 * half);
-          s[jb] = mfma32(kf, qf[ks], s[jb]);
-        }
+      for (int d = 0; d < DBLK; ++d) {
+        const int dcol = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+        const int r0 = vrow0 + 16 * b, r1 = r0 + 8;
+        const s16x4 lo = read_tr(Vs + r0 * V + 16 * ((dcol >> 4) ^ v_swz(r0)) + (dcol & 15));
+        const s16x4 hi = read_tr(Vs + r1 * V + 16 * ((dcol >> 4) ^ v_swz(r1)) + (dcol & 15));
+        vf[b][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      // scale into the log2 domain and mask
-      const bool need_mask = (j0 + BN > kv_hi) || (a.causal && j0 + BN - 1 > wave_q_first);
-      float mt = kNegBig;
+  };
+  auto compute = [&](const uint16_t *st, int j0, const bf16x8 (&vf)[2][DBLK]) {
+    const uint16_t *Kn = st, *Kr = st + KN_E;
+    const int jh = j0 + 32 * kh;                     // first key of this wave's half
+    f32x16 s;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[jb][r] * c;
-          if (need_mask) {
-            const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (j >= kv_hi || (a.causal && j > qi)) x = -INFINITY;
-          }
-          s[jb][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__any(mt > m_run + kRescale)) {
-        const float mn = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        m_run = mn;
-        l_run *= alpha;
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int cidx = 2 * ks + half;
+      const uint16_t *src = ks < NSTEPS ? Kn + kkey * N + 8 * (cidx ^ kn_swz(kkey))
+                                        : Kr + kkey * R + 8 * ((cidx - 2 * NSTEPS) ^ kr_swz(kkey));
+      s = mfma32(*reinterpret_cast<const bf16x8 *>(src), qf[ks], s);
+    }
+    // mask keys past the diagonal / the visible end (uniform test)
+    if (jh + 31 >= kv_hi || (a.causal && jh + 31 > wq_first)) {
+      const int lim = a.causal ? min(qi, kv_hi - 1) : kv_hi - 1;
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const int j = jh + 8 * (r >> 2) + 4 * half + (r & 3);
+        s[r] = j > lim ? -INFINITY : s[r];
       }
-      // P^T in the B-operand layout of the PV MFMA: 16-key step b = registers 8*(b%2).. of block b/2
-      bf16x8 pf[BN / 16];
-      float lsum = 0.f;
+    }
+    float mt = s[0];
 #pragma unroll
-      for (int b = 0; b < BN / 16; ++b) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(s[b >> 1][8 * (b & 1) + 2 * e] - m_run);
-          const float p1 = __builtin_amdgcn_exp2f(s[b >> 1][8 * (b & 1) + 2 * e + 1] - m_run);
-          lsum += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
-        }
-        pf[b] = as_bf16x8(w);
-      }
-      l_run += lsum;
-      // O^T += V^T P^T
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+    if (__any(mt > m_run + kRescale)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-        for (int b = 0; b < BN / 16; ++b) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + (32 * d + lrow) * VP + 16 * b + 8 * half);
-          o[d] = mfma32(vf, pf[b], o[d]);
-        }
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
     }
-    if (kt + 1 < n_tiles) store((kt + 1) & 1);
-    __syncthreads();
+    bf16x8 pf[2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * b + 2 * e], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * b + 2 * e + 1], c, -m_run));
+        lsum += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pf[b] = as_bf16x8(w);
+    }
+    l_run += lsum;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) o[d] = mfma32(vf[b][d], pf[b], o[d]);
+  };
+
+  // One barrier per tile. A tile's V^T fragments are read into registers
+  // before the next tile's transfers are issued, so no LDS read of the tile
+  // being computed waits on the transfers in flight into the other stage.
+  __syncthreads();                 // stages zeroed before the first transfer lands
+  issue(st0, doc_lo);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's transfers have landed
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    const int j0 = doc_lo + kt * BN;
+    {
+      const bool act = active_for(j0);
+      bf16x8 vf[2][DBLK];
+      if (act) read_v(st0, vf);
+      if (kt + 1 < n_tiles) issue(st1, j0 + BN);
+      if (act) compute(st0, j0, vf);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+    if (kt + 1 < n_tiles) {
+      const bool act = active_for(j0 + BN);
+      bf16x8 vf[2][DBLK];
+      if (act) read_v(st1, vf);
+      if (kt + 2 < n_tiles) issue(st0, j0 + 2 * BN);
+      if (act) compute(st1, j0 + BN, vf);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
   }
 
-  // ---- finish: full row sum, normalise, store
+  // ---- merge the two key halves of each query block through LDS (stage 0 is free)
+  float *xo = reinterpret_cast<float *>(st0) + qb * (DBLK * 16 + 2) * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(d * 16 + r) * 64 + lane] = o[d][r];
+    xo[(DBLK * 16) * 64 + lane] = m_run;
+    xo[(DBLK * 16 + 1) * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1 || !wave_has_q) return;
+  {
+    const float m1 = xo[(DBLK * 16) * 64 + lane];
+    const float l1 = xo[(DBLK * 16 + 1) * 64 + lane];
+    const float mn = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+    l_run = l_run * a0 + l1 * a1;
+    m_run = mn;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + xo[(d * 16 + r) * 64 + lane] * a1;
+  }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!q_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -413,6 +494,18 @@ WsLayout ws_layout(int64_t T, int n_seq) {
   return w;
 }
 
+// Dense causal work order. 1 (default): the heavier half of the query tiles
+// heaviest-first, then the lighter half lightest-first, so the workgroups that
+// share a CU carry complementary causal work. 0: heaviest-first throughout.
+// MLA_ATTN_ORDER overrides it (for measurement).
+int attn_order() {
+  static const int order = [] {
+    const char *e = getenv("MLA_ATTN_ORDER");
+    return e ? atoi(e) : 1;
+  }();
+  return order;
+}
+
 }  // namespace
 
 bool attn_fast_path(int N, int R, int V, int bf16) { return bf16 && N == 128 && R == 64 && V == 128; }
@@ -457,6 +550,7 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.tasks = nullptr;
     a.task_count = nullptr;
     a.n_qtiles = static_cast<int>((p.T + BM - 1) / BM);
+    a.order = attn_order();
     tasks = a.n_qtiles;
   } else {
     const WsLayout w = ws_layout(p.T, p.n_seq);
@@ -472,6 +566,7 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.tasks = task_arr;
     a.task_count = count;
     a.n_qtiles = 0;
+    a.order = 0;
     tasks = (p.T + BM - 1) / BM + p.n_seq;
   }
   const int64_t blocks = tasks * p.H;

@@ -49,6 +49,16 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// (hardware range check), so tile loaders need no clamps or branches.
+constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit data format (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kBufferDword3);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
+}
+
 template <typename T>
 __device__ __forceinline__ float load_f32(const T *p, int64_t i);
 template <>
