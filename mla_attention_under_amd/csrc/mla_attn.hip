@@ -308,6 +308,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       if (act) read_v(st0, vf);
       if (kt + 1 < n_tiles) issue(st1, j0 + BN);
       if (act) compute(st0, j0, vf);
+      __builtin_amdgcn_sched_barrier(0);   // keep the tile's MFMAs ahead of the wait
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
@@ -317,6 +318,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       if (act) read_v(st1, vf);
       if (kt + 2 < n_tiles) issue(st0, j0 + 2 * BN);
       if (act) compute(st1, j0 + BN, vf);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
