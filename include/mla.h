@@ -73,7 +73,7 @@ int mla_head_shard_sizes(int q_heads, int kv_heads, int sp, int *sizes_out);
  * sizes: HOST array of sp positive ints summing to heads_total (e.g. from
  * mla_head_shard_sizes). The copy is bit-exact; dtype only fixes the element
  * size (MLA_BF16: 2 bytes, MLA_F32: 4 bytes). x and send must not overlap.
- * tokens == 0 is a valid no-op. sp <= 1024.
+ * tokens == 0 is a valid no-op. sp <= 256.
  */
 int mla_pack_heads(const void *x, void *send, int64_t tokens, int heads_total, int feat,
                    const int *sizes, int sp, int dtype, void *stream);
@@ -129,7 +129,11 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
  * The packed q+kv rows of mla_pack_heads can be read in place with
  * q_stride_h = kv_stride_h = F and kv = q + K.
  * Workspace: mla_attention_workspace_size() bytes of device memory, 256-byte
- * aligned (0 when cu_seqlens is NULL); contents need not be initialised.
+ * aligned (0 when none is needed); scratch whose contents need not be
+ * initialised and are left arbitrary. Dense causal calls keep there the
+ * partial softmax states of the query tiles they split between two
+ * workgroups; packed-document calls keep the device-built tile schedule.
+ * Calls that may run concurrently need separate workspaces.
  */
 typedef struct mla_attn_args {
   const void *q;

@@ -92,6 +92,24 @@ def _check(fn, rc):
         raise MlaError(fn, rc, load_library().mla_last_error().decode())
 
 
+_ws_cache = {}
+
+
+def _workspace(nbytes: int, device) -> "torch.Tensor | None":
+    """Device scratch of at least nbytes, reused by every call on that device.
+
+    Calls that may overlap on different streams must pass their own workspace.
+    """
+    if nbytes == 0:
+        return None
+    key = torch.device(device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
+        _ws_cache[key] = ws
+    return ws
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -199,9 +217,8 @@ def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None,
     if cu_seqlens is not None:
         assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
     if workspace is None:
-        need = mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens),
+                               q.device)
     a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace)
     _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
     return out
@@ -237,9 +254,8 @@ def mla_latent_decode_fwd(q, latent_cache, rope_cache, w_kvb, out, heads_total, 
     for t in (q, latent_cache, rope_cache, w_kvb, out):
         assert t.is_contiguous()
     if workspace is None:
-        need = mla_latent_decode_workspace_size(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin,
-                                                N, R, V, num_splits, scale)
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(mla_latent_decode_workspace_size(q, latent_cache, rope_cache, w_kvb, out, heads_total,
+                                                                head_begin, N, R, V, num_splits, scale), q.device)
     a = _decode_args(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits, scale,
                      lse, workspace)
     _check("mla_latent_decode_fwd", lib.mla_latent_decode_fwd(ctypes.byref(a), _stream(stream)))

@@ -5,11 +5,12 @@
 // with no look-ahead for causal, `_causal_partition` for document-local keys).
 //
 // gfx950 design (bf16 in, fp32 accumulate):
-//  * One workgroup = 4 waves = 64 queries of one head: 2 query blocks of 32 x
+//  * One workgroup = 8 waves = 128 queries of one head: 4 query blocks of 32 x
 //    2 key halves. A 64-key tile is split between the halves (32 keys each);
 //    the two partial softmax states of a query block are merged through LDS
-//    at the end. Two workgroups fit a CU (80 KB LDS, <= 256 registers), so
-//    every SIMD runs two waves and one wave's softmax overlaps the other's MFMAs.
+//    at the end. Every SIMD runs two waves (<= 256 registers each), so one
+//    wave's softmax overlaps the other's MFMAs, and each K/V tile brought into
+//    LDS (80 KB, double-buffered) serves 128 queries.
 //  * Tiles move global->LDS with buffer_load ... lds (no staging registers),
 //    double-buffered, one barrier per tile. The key tile is assembled from two
 //    sources: k_nope from this head's projected kv rows and the shared k_rope
@@ -25,9 +26,10 @@
 //  * Online softmax in the exp2 domain (one fma + one exp per score); the
 //    running output is rescaled only when a row max grows by more than 2^8
 //    (exact: any reference max gives the same quotient).
-//  * Work order: dense causal tiles are dealt heaviest-first, then lightest-
-//    first, so co-resident workgroups carry complementary causal work; packed
-//    documents use a device-built schedule sorted by key-tile count.
+//  * Work order: dense causal query tiles are paired (i, n-1-i) and every pair
+//    is split into two workgroups of equal key-tile count; the tile that
+//    straddles both is merged by a second kernel (see pair_plan).
+//    Packed documents use a device-built schedule sorted by key-tile count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,11 +41,12 @@
 namespace mla {
 namespace {
 
-constexpr int BM = 64;       // queries per workgroup (2 blocks of 32)
+constexpr int BM = 128;      // queries per workgroup (4 blocks of 32)
 constexpr int BN = 64;       // keys per tile (2 halves of 32)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;   // log2 growth of a row max that forces a rescale
 constexpr float kNegBig = -1.0e30f;
+__device__ constexpr bf16x2_t kOnesBf16x2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
 struct AttnArgs {
   const uint16_t *q;
@@ -56,7 +59,8 @@ struct AttnArgs {
   const int2 *tasks;      // packed documents: (query start, document) per task, sorted
   const int *task_count;
   int n_qtiles;           // dense: query tiles per head
-  int order;              // dense tile order: 0 heaviest first, 1 heavy half then light half
+  int order;              // dense causal: 1 pairs tiles and splits the work evenly, 0 heaviest first
+  float *part;            // dense causal pairing: two softmax-state records per pair
   int T, H;
   float scale_log2;       // scale * log2(e)
   int causal;
@@ -81,8 +85,122 @@ __device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
+// Causal pairing of query tiles (dense, one sequence). Query tiles i and
+// n-1-i of a head together hold U = u(i) + u(n-1-i) key tiles, nearly the
+// same for every i; two workgroups share the pair, U/2 key tiles each. The
+// first takes the first x key tiles of the heavier tile j = n-1-i and then all
+// of tile i; the second takes the remaining key tiles of tile j. Both write
+// their partial softmax state of tile j to the workspace and a second, small
+// kernel merges them. (Merging inside the kernel would need agent-scope
+// fences, which on this chip write back and invalidate the XCD's L2 and throw
+// away the K/V tiles the other workgroups are reusing.) With an odd tile
+// count the middle tile is one workgroup alone.
+struct PairPlan {
+  int qt;        // query tile of the first segment
+  int t0, t1;    // its key-tile range
+  int part;      // 1: the first segment is a partial of a split tile
+  int qt2;       // second segment (full tile), -1 if none
+  int slot;      // split-tile slot in the workspace, -1 if none
+};
+
+__device__ __forceinline__ int key_tiles_of(int qt, int T) { return (min((qt + 1) * BM, T) + BN - 1) / BN; }
+
+__device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T) {
+  PairPlan pp;
+  const int pairs = n / 2;
+  pp.qt2 = -1;
+  pp.slot = -1;
+  pp.part = 0;
+  if (k >= 2 * pairs) {                      // middle tile
+    pp.qt = pairs;
+    pp.t0 = 0;
+    pp.t1 = key_tiles_of(pairs, T);
+    return pp;
+  }
+  const int i = k >> 1, j = n - 1 - i;
+  const int ui = key_tiles_of(i, T), uj = key_tiles_of(j, T);
+  const int x = max(0, (ui + uj + 1) / 2 - ui);   // key tiles of j done by the first workgroup
+  if ((k & 1) == 0) {
+    if (x > 0) {
+      pp.qt = j;
+      pp.t0 = 0;
+      pp.t1 = x;
+      pp.part = 1;
+      pp.qt2 = i;
+    } else {
+      pp.qt = i;
+      pp.t0 = 0;
+      pp.t1 = ui;
+    }
+  } else {
+    pp.qt = j;
+    pp.t0 = x;
+    pp.t1 = uj;
+    pp.part = x > 0;
+  }
+  if (pp.part) pp.slot = h * pairs + i;
+  return pp;
+}
+
+// Softmax state of one query block as a wave holds it after the key halves
+// are merged: o[d] is the 32x32 block d of O^T (dims x queries, MFMA output
+// layout), m is the running max (log2 domain, equal on lanes l and l^32) and
+// l the partial denominator of this lane's keys.
+constexpr int kRecFloats = 4 * (4 * 16 + 2) * 64;   // 4 query blocks x (64 O + m + l) x 64 lanes
+
+// normalise the state of query block qb of the tile starting at q0 and store it
+template <int DBLK>
+__device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[DBLK], float m_run, float l_run,
+                                           int h, int q0, int q_end, int qb, int lane) {
+  const int half = lane >> 5;
+  const int qi = q0 + 32 * qb + (lane & 31);
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qi >= q_end) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t *op = a.out + static_cast<int64_t>(qi) * a.o_st + static_cast<int64_t>(h) * a.o_sh;
+#pragma unroll
+  for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 v{pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
+                    pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
+      *reinterpret_cast<u32x2 *>(op + 32 * d + 8 * g + 4 * half) = v;
+    }
+  if (a.lse != nullptr && half == 0)
+    a.lse[static_cast<int64_t>(h) * a.T + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+}
+
+// Second pass of the causal pairing: one workgroup (4 waves, one per query
+// block) per pair; if the pair's heavier tile was split, combine its two
+// partial states, m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m),
+// o = o0 2^(m0-m) + o1 2^(m1-m), then normalise and store.
+template <int DBLK>
+__global__ __launch_bounds__(256) void attn_pair_merge_kernel(AttnArgs a) {
+  constexpr int REC = DBLK * 16 + 2;
+  const int pairs = a.n_qtiles / 2;
+  const int h = blockIdx.x % a.H, i = blockIdx.x / a.H;
+  const PairPlan pp = pair_plan(2 * i + 1, h, a.n_qtiles, a.T);
+  if (!pp.part) return;
+  const int qb = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float *r0 = a.part + static_cast<int64_t>(h * pairs + i) * (2 * kRecFloats) + qb * REC * 64 + lane;
+  const float *r1 = r0 + kRecFloats;
+  const float m0 = __builtin_nontemporal_load(r0 + DBLK * 16 * 64), m1 = __builtin_nontemporal_load(r1 + DBLK * 16 * 64);
+  const float l0 = __builtin_nontemporal_load(r0 + (DBLK * 16 + 1) * 64);
+  const float l1 = __builtin_nontemporal_load(r1 + (DBLK * 16 + 1) * 64);
+  const float mn = fmaxf(m0, m1);
+  const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+  f32x16 o[DBLK];
+#pragma unroll
+  for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      o[d][r] = __builtin_nontemporal_load(r0 + (d * 16 + r) * 64) * a0 +
+                __builtin_nontemporal_load(r1 + (d * 16 + r) * 64) * a1;
+  store_rows<DBLK>(a, o, mn, l0 * a0 + l1 * a1, h, pp.qt * BM, a.T, qb, lane);
+}
+
 template <int N, int R, int V>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KD = N + R;          // score width
   constexpr int NCH = N / 8;         // 16-byte chunks per k_nope row
   constexpr int RCH = R / 8;         // per k_rope row
@@ -91,77 +209,65 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NSTEPS = N / 16;
   constexpr int DBLK = V / 32;
   constexpr int KN_E = BN * N, KR_E = BN * R, V_E = BN * V;   // elements per stage
-  constexpr int KN_I = BN * NCH / 256, KR_I = BN * RCH / 256, V_I = BN * VCH / 256;   // DMA instrs per wave
+  constexpr int NW = 8;              // waves per workgroup
+  constexpr int KN_I = BN * NCH / (64 * NW), KR_I = BN * RCH / (64 * NW), V_I = BN * VCH / (64 * NW);   // DMA instrs per wave
+  constexpr int REC = DBLK * 16 + 2; // floats per lane of a wave's softmax state: O, m, l
   static_assert(N == 128 && R == 64 && V == 128, "swizzles and DMA splits are laid out for 128/64/128");
-  static_assert(KN_I * 256 == BN * NCH && KR_I * 256 == BN * RCH && V_I * 256 == BN * VCH, "tile DMA split");
+  static_assert(4 * REC * 64 == kRecFloats, "workspace record size");
+  static_assert(KN_I * 64 * NW == BN * NCH && KR_I * 64 * NW == BN * RCH && V_I * 64 * NW == BN * VCH, "tile DMA split");
   __shared__ __attribute__((aligned(1024))) uint16_t st0[KN_E + KR_E + V_E];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[KN_E + KR_E + V_E];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = wave & 1, kh = wave >> 1;          // query block, key half
+  const int qb = wave & 3, kh = wave >> 2;          // query block, key half
   const int half = lane >> 5, lrow = lane & 31;
   const int grp = lane >> 4, gl = lane & 15;        // 16-lane groups for the transposing read
 
-  // ---- which (head, query tile)
-  int h, q0, doc_lo, doc_hi;
+  // ---- which head, document and segments
+  int h, doc_lo, doc_hi;
+  PairPlan pp;
   if (a.tasks == nullptr) {
     const int b = blockIdx.x, H = a.H, n = a.n_qtiles;
-    int qt;
-    if (a.order == 1 && a.causal) {
-      const int heavy = ((n + 1) / 2) * H;
-      if (b < heavy) {
-        h = b % H;
-        qt = n - 1 - b / H;
-      } else {
-        h = (b - heavy) % H;
-        qt = (b - heavy) / H;
-      }
-    } else {
-      h = b % H;
-      qt = n - 1 - b / H;
-    }
-    q0 = qt * BM;
+    h = b % H;
     doc_lo = 0;
     doc_hi = a.T;
+    if (a.causal && a.order == 1) {
+      pp = pair_plan(b / H, h, n, a.T);
+    } else {                                  // heaviest first
+      pp.qt = n - 1 - b / H;
+      pp.t0 = 0;
+      pp.t1 = a.causal ? key_tiles_of(pp.qt, a.T) : (a.T + BN - 1) / BN;
+      pp.part = 0;
+      pp.qt2 = -1;
+      pp.slot = -1;
+    }
   } else {
     const int t = static_cast<int>(blockIdx.x) / a.H;
     if (t >= *a.task_count) return;
     h = blockIdx.x % a.H;
     const int2 task = a.tasks[t];
-    q0 = task.x;
     doc_lo = min(max(a.cu[task.y], 0), a.T);          // the same clamping as the schedule
     doc_hi = min(max(a.cu[task.y + 1], doc_lo), a.T);
+    pp.qt = (task.x - doc_lo) / BM;
+    const int q_end = min(task.x + BM, doc_hi);
+    pp.t0 = 0;
+    pp.t1 = ((a.causal ? q_end : doc_hi) - doc_lo + BN - 1) / BN;
+    pp.part = 0;
+    pp.qt2 = -1;
+    pp.slot = -1;
   }
   h = __builtin_amdgcn_readfirstlane(h);
-  q0 = __builtin_amdgcn_readfirstlane(q0);
   doc_lo = __builtin_amdgcn_readfirstlane(doc_lo);
   doc_hi = __builtin_amdgcn_readfirstlane(doc_hi);
-  const int q_end = min(q0 + BM, doc_hi);
-  const int kv_hi = a.causal ? q_end : doc_hi;
-  const int n_tiles = (kv_hi - doc_lo + BN - 1) / BN;
-  if (n_tiles <= 0) return;   // uniform: an empty task
 
   // ---- zero both stages once: loads past the buffer range may leave LDS untouched
   {
     u32x4 z{0, 0, 0, 0};
-    for (int i = tid; i < (KN_E + KR_E + V_E) / 8; i += 256) {
+    for (int i = tid; i < (KN_E + KR_E + V_E) / 8; i += 64 * NW) {
       reinterpret_cast<u32x4 *>(st0)[i] = z;
       reinterpret_cast<u32x4 *>(st1)[i] = z;
     }
-  }
-
-  // ---- this lane's query and its Q fragment (B operand of S^T = K Q^T)
-  const int qi = q0 + 32 * qb + lrow;
-  const bool q_ok = qi < q_end;
-  const int wq_first = q0 + 32 * qb;
-  const int wq_last = min(q0 + 32 * qb + 31, q_end - 1);
-  const bool wave_has_q = wq_first < q_end;
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t *qp = a.q + static_cast<int64_t>(min(qi, q_end - 1)) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half));
   }
 
   // ---- DMA plan: every wave issues KN_I + KR_I + V_I 1 KB transfers per tile.
@@ -188,180 +294,221 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const int c = 2 * ((cp >> 1) ^ v_swz(key)) + (cp & 1);
     v_off[i] = static_cast<uint32_t>((key * a.kv_st + N + 8 * c) * 2);
   }
-  auto issue = [&](uint16_t *st, int j0) {
-    const int rows = min(kv_hi - j0, BN);
-    const __amdgpu_buffer_rsrc_t rkv =
-        make_rsrc(kv_h + static_cast<int64_t>(j0) * a.kv_st, static_cast<uint32_t>(rows * a.kv_st * 2));
-    const __amdgpu_buffer_rsrc_t rkr =
-        make_rsrc(a.kr + static_cast<int64_t>(j0) * a.kr_st, static_cast<uint32_t>(rows * a.kr_st * 2));
-#pragma unroll
-    for (int i = 0; i < KN_I; ++i) dma16(rkv, st + 512 * (wave * KN_I + i), kn_off[i]);
-#pragma unroll
-    for (int i = 0; i < KR_I; ++i) dma16(rkr, st + KN_E + 512 * (wave * KR_I + i), kr_off[i]);
-#pragma unroll
-    for (int i = 0; i < V_I; ++i) dma16(rkv, st + KN_E + KR_E + 512 * (wave * V_I + i), v_off[i]);
-  };
-
-  // ---- LDS read addresses (elements), loop-invariant
-  // K: key 32*kh + lrow, chunk 2*ks + half
-  const int kkey = 32 * kh + lrow;
-  // V^T: for 16-key step b and read r, rows 32kh + 16b + 8r + 4*(grp>>1) + (gl>>2), d = 32db + 16*(grp&1) + 4*(gl&3)
-  const int vrow0 = 32 * kh + 4 * (grp >> 1) + (gl >> 2);
-
-  // ---- running state (per lane: one query; m in log2 units, partial row sum)
-  f32x16 o[DBLK];
-#pragma unroll
-  for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-  float m_run = kNegBig, l_run = 0.f;
+  const int kkey = 32 * kh + lrow;                      // K rows this lane reads
+  const int vrow0 = 32 * kh + 4 * (grp >> 1) + (gl >> 2);   // first V row of the transposing reads
   const float c = a.scale_log2;
 
-  // V^T operand fragments of this wave's 32-key half: [16-key step b][d block]
-  auto active_for = [&](int j0) {
-    const int jh = j0 + 32 * kh;
-    return wave_has_q && jh < kv_hi && !(a.causal && jh > wq_last);
-  };
-  auto read_v = [&](const uint16_t *st, bf16x8 (&vf)[2][DBLK]) {
-    const uint16_t *Vs = st + KN_E + KR_E;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d) {
-        const int dcol = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
-        const int r0 = vrow0 + 16 * b, r1 = r0 + 8;
-        const s16x4 lo = read_tr(Vs + r0 * V + 16 * ((dcol >> 4) ^ v_swz(r0)) + (dcol & 15));
-        const s16x4 hi = read_tr(Vs + r1 * V + 16 * ((dcol >> 4) ^ v_swz(r1)) + (dcol & 15));
-        vf[b][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-  };
-  auto compute = [&](const uint16_t *st, int j0, const bf16x8 (&vf)[2][DBLK]) {
-    const uint16_t *Kn = st, *Kr = st + KN_E;
-    const int jh = j0 + 32 * kh;                     // first key of this wave's half
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int cidx = 2 * ks + half;
-      const uint16_t *src = ks < NSTEPS ? Kn + kkey * N + 8 * (cidx ^ kn_swz(kkey))
-                                        : Kr + kkey * R + 8 * ((cidx - 2 * NSTEPS) ^ kr_swz(kkey));
-      s = mfma32(*reinterpret_cast<const bf16x8 *>(src), qf[ks], s);
-    }
-    // mask keys past the diagonal / the visible end (uniform test)
-    if (jh + 31 >= kv_hi || (a.causal && jh + 31 > wq_first)) {
-      const int lim = a.causal ? min(qi, kv_hi - 1) : kv_hi - 1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jh + 8 * (r >> 2) + 4 * half + (r & 3);
-        s[r] = j > lim ? -INFINITY : s[r];
-      }
-    }
-    float mt = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
-    if (__any(mt > m_run + kRescale)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      m_run = mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-    }
-    bf16x8 pf[2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * b + 2 * e], c, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * b + 2 * e + 1], c, -m_run));
-        lsum += p0 + p1;
-        w[e] = pack_bf16x2(p0, p1);
-      }
-      pf[b] = as_bf16x8(w);
-    }
-    l_run += lsum;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d) o[d] = mfma32(vf[b][d], pf[b], o[d]);
-  };
+  f32x16 o[DBLK];
+  float m_run, l_run;
 
-  // One barrier per tile. A tile's V^T fragments are read into registers
-  // before the next tile's transfers are issued, so no LDS read of the tile
-  // being computed waits on the transfers in flight into the other stage.
-  __syncthreads();                 // stages zeroed before the first transfer lands
-  issue(st0, doc_lo);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's transfers have landed
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; kt += 2) {
-    const int j0 = doc_lo + kt * BN;
+  // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
+  // (both key halves) softmax state in the waves with kh == 0
+  auto segment = [&](int qt, int t0, int t1) {
+    const int q0 = doc_lo + qt * BM;
+    const int q_end = min(q0 + BM, doc_hi);
+    const int kv_hi = a.causal ? q_end : doc_hi;
+    const int qi = q0 + 32 * qb + lrow;
+    const int wq_first = q0 + 32 * qb;
+    const int wq_last = min(q0 + 32 * qb + 31, q_end - 1);
+    const bool wave_has_q = wq_first < q_end;
+    bf16x8 qf[KSTEPS];
     {
-      const bool act = active_for(j0);
-      bf16x8 vf[2][DBLK];
-      if (act) read_v(st0, vf);
-      if (kt + 1 < n_tiles) issue(st1, j0 + BN);
-      if (act) compute(st0, j0, vf);
-      __builtin_amdgcn_sched_barrier(0);   // keep the tile's MFMAs ahead of the wait
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
+      const uint16_t *qp =
+          a.q + static_cast<int64_t>(min(qi, q_end - 1)) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half));
     }
-    if (kt + 1 < n_tiles) {
-      const bool act = active_for(j0 + BN);
-      bf16x8 vf[2][DBLK];
-      if (act) read_v(st1, vf);
-      if (kt + 2 < n_tiles) issue(st0, j0 + 2 * BN);
-      if (act) compute(st1, j0 + BN, vf);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-    }
-  }
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    m_run = kNegBig;
+    l_run = 0.f;
 
-  // ---- merge the two key halves of each query block through LDS (stage 0 is free)
-  float *xo = reinterpret_cast<float *>(st0) + qb * (DBLK * 16 + 2) * 64;
-  if (kh == 1) {
+    auto issue = [&](uint16_t *st, int j0) {
+      const int rows = min(kv_hi - j0, BN);
+      const __amdgpu_buffer_rsrc_t rkv =
+          make_rsrc(kv_h + static_cast<int64_t>(j0) * a.kv_st, static_cast<uint32_t>(rows * a.kv_st * 2));
+      const __amdgpu_buffer_rsrc_t rkr =
+          make_rsrc(a.kr + static_cast<int64_t>(j0) * a.kr_st, static_cast<uint32_t>(rows * a.kr_st * 2));
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+      for (int i = 0; i < KN_I; ++i) dma16(rkv, st + 512 * (wave * KN_I + i), kn_off[i]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(d * 16 + r) * 64 + lane] = o[d][r];
-    xo[(DBLK * 16) * 64 + lane] = m_run;
-    xo[(DBLK * 16 + 1) * 64 + lane] = l_run;
-  }
-  __syncthreads();
-  if (kh == 1 || !wave_has_q) return;
-  {
-    const float m1 = xo[(DBLK * 16) * 64 + lane];
-    const float l1 = xo[(DBLK * 16 + 1) * 64 + lane];
-    const float mn = fmaxf(m_run, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-    l_run = l_run * a0 + l1 * a1;
-    m_run = mn;
+      for (int i = 0; i < KR_I; ++i) dma16(rkr, st + KN_E + 512 * (wave * KR_I + i), kr_off[i]);
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+      for (int i = 0; i < V_I; ++i) dma16(rkv, st + KN_E + KR_E + 512 * (wave * V_I + i), v_off[i]);
+    };
+    auto active_for = [&](int j0) {
+      const int jh = j0 + 32 * kh;
+      return wave_has_q && jh < kv_hi && !(a.causal && jh > wq_last);
+    };
+    auto read_v = [&](const uint16_t *st, bf16x8 (&vf)[2][DBLK]) {
+      const uint16_t *Vs = st + KN_E + KR_E;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + xo[(d * 16 + r) * 64 + lane] * a1;
-  }
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!q_ok) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t *op = a.out + static_cast<int64_t>(qi) * a.o_st + static_cast<int64_t>(h) * a.o_sh;
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-  for (int d = 0; d < DBLK; ++d)
+        for (int d = 0; d < DBLK; ++d) {
+          const int dcol = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+          const int r0 = vrow0 + 16 * b, r1 = r0 + 8;
+          const s16x4 lo = read_tr(Vs + r0 * V + 16 * ((dcol >> 4) ^ v_swz(r0)) + (dcol & 15));
+          const s16x4 hi = read_tr(Vs + r1 * V + 16 * ((dcol >> 4) ^ v_swz(r1)) + (dcol & 15));
+          vf[b][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    auto compute = [&](const uint16_t *st, int j0, const bf16x8 (&vf)[2][DBLK]) {
+      const uint16_t *Kn = st, *Kr = st + KN_E;
+      const int jh = j0 + 32 * kh;                     // first key of this wave's half
+      f32x16 sc;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const u32x2 v{pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
-                    pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2 *>(op + 32 * d + 8 * g + 4 * half) = v;
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int cidx = 2 * ks + half;
+        const uint16_t *src = ks < NSTEPS ? Kn + kkey * N + 8 * (cidx ^ kn_swz(kkey))
+                                          : Kr + kkey * R + 8 * ((cidx - 2 * NSTEPS) ^ kr_swz(kkey));
+        sc = mfma32(*reinterpret_cast<const bf16x8 *>(src), qf[ks], sc);
+      }
+      // mask keys past the diagonal / the visible end (uniform test)
+      if (jh + 31 >= kv_hi || (a.causal && jh + 31 > wq_first)) {
+        const int lim = a.causal ? min(qi, kv_hi - 1) : kv_hi - 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jh + 8 * (r >> 2) + 4 * half + (r & 3);
+          sc[r] = j > lim ? -INFINITY : sc[r];
+        }
+      }
+      float mt = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      {
+        // lanes l and l^32 hold the two key halves of one query row. (The swap's
+        // results are copied to scalars first: bit-casting a vector element in
+        // place reads element 0.)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt),
+                                                         __builtin_bit_cast(unsigned, mt), false, false);
+        const unsigned own = sw[0], other = sw[1];
+        mt = fmaxf(__uint_as_float(own), __uint_as_float(other)) * c;
+      }
+      if (__any(mt > m_run + kRescale)) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      // P^T in bf16; the row sum is taken over the same rounded weights the
+      // PV product uses (one bf16 dot2 with (1, 1) per packed pair)
+      bf16x8 pf[2];
+      float lsum = l_run;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * e], c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * e + 1], c, -m_run));
+          const uint32_t pp = pack_bf16x2(p0, p1);
+          w[e] = pp;
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), kOnesBf16x2, lsum, false);
+        }
+        pf[b] = as_bf16x8(w);
+      }
+      l_run = lsum;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) o[d] = mfma32(vf[b][d], pf[b], o[d]);
+    };
+
+    // One barrier per tile. A tile's V^T fragments are read into registers
+    // before the next tile's transfers are issued, so no LDS read of the tile
+    // being computed waits on the transfers in flight into the other stage.
+    __syncthreads();               // the previous segment's readers are done with the stages
+    issue(st0, doc_lo + t0 * BN);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's transfers have landed
+    __syncthreads();
+    for (int kt = t0; kt < t1; kt += 2) {
+      const int j0 = doc_lo + kt * BN;
+      {
+        const bool act = active_for(j0);
+        bf16x8 vf[2][DBLK];
+        if (act) read_v(st0, vf);
+        if (kt + 1 < t1) issue(st1, j0 + BN);
+        if (act) compute(st0, j0, vf);
+        __builtin_amdgcn_sched_barrier(0);   // keep the tile's MFMAs ahead of the wait
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
+      if (kt + 1 < t1) {
+        const bool act = active_for(j0 + BN);
+        bf16x8 vf[2][DBLK];
+        if (act) read_v(st1, vf);
+        if (kt + 2 < t1) issue(st0, j0 + 2 * BN);
+        if (act) compute(st1, j0 + BN, vf);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
     }
-  if (a.lse != nullptr && half == 0)
-    a.lse[static_cast<int64_t>(h) * a.T + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+
+    // merge the two key halves of each query block through LDS (stage 0 is
+    // free), two query blocks per round so a round fits one stage
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      float *xo = reinterpret_cast<float *>(st0) + (qb & 1) * REC * 64;
+      const bool mine = (qb >> 1) == round;
+      if (kh == 1 && mine) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xo[(d * 16 + r) * 64 + lane] = o[d][r];
+        xo[(DBLK * 16) * 64 + lane] = m_run;
+        xo[(DBLK * 16 + 1) * 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (kh == 0 && mine) {
+        const float m1 = xo[(DBLK * 16) * 64 + lane];
+        const float l1 = xo[(DBLK * 16 + 1) * 64 + lane];
+        const float mn = fmaxf(m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+        l_run = l_run * a0 + l1 * a1;
+        m_run = mn;
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + xo[(d * 16 + r) * 64 + lane] * a1;
+      }
+      __syncthreads();
+    }
+  };
+
+  // ---- a split tile's partial: the merge kernel combines the two records
+  auto publish = [&](int slot, int role) {
+    if (kh != 0) return;
+    float *rec = a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) + role * kRecFloats + qb * REC * 64;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rec[(d * 16 + r) * 64 + lane] = o[d][r];
+    rec[(DBLK * 16) * 64 + lane] = m_run;
+    rec[(DBLK * 16 + 1) * 64 + lane] = l_run;
+  };
+
+  const int qt1 = __builtin_amdgcn_readfirstlane(pp.qt);
+  segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1));
+  if (pp.part)
+    publish(pp.slot, pp.qt2 >= 0 ? 0 : 1);
+  else if (kh == 0)
+    store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane);
+  if (pp.qt2 >= 0) {
+    const int qt2 = __builtin_amdgcn_readfirstlane(pp.qt2);
+    segment(qt2, 0, key_tiles_of(qt2, a.T));
+    if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane);
+  }
 }
 
 // ---- packed-document schedule: all (document, query tile) tasks, heaviest first
@@ -486,6 +633,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnPlan p) {
 struct WsLayout {
   size_t count_off, tasks_off, first_off, bytes;
 };
+// packed documents: task count | task list | first task of each document
 WsLayout ws_layout(int64_t T, int n_seq) {
   WsLayout w;
   const size_t max_tasks = static_cast<size_t>((T + BM - 1) / BM + n_seq);
@@ -496,10 +644,9 @@ WsLayout ws_layout(int64_t T, int n_seq) {
   return w;
 }
 
-// Dense causal work order. 1 (default): the heavier half of the query tiles
-// heaviest-first, then the lighter half lightest-first, so the workgroups that
-// share a CU carry complementary causal work. 0: heaviest-first throughout.
-// MLA_ATTN_ORDER overrides it (for measurement).
+// Dense causal work order. 1 (default): tile pairing with an even split of
+// each pair's key tiles (see pair_plan). 0: one query tile per workgroup,
+// heaviest first (no workspace). MLA_ATTN_ORDER overrides it (for measurement).
 int attn_order() {
   static const int order = [] {
     const char *e = getenv("MLA_ATTN_ORDER");
@@ -508,13 +655,21 @@ int attn_order() {
   return order;
 }
 
+// Dense causal pairing: two softmax-state records per (head, pair), scratch.
+size_t pair_ws_bytes(int64_t T, int H) {
+  const int64_t n = (T + BM - 1) / BM;
+  return static_cast<size_t>(H) * static_cast<size_t>(n / 2) * 2 * kRecFloats * sizeof(float);
+}
+
 }  // namespace
 
 bool attn_fast_path(int N, int R, int V, int bf16) { return bf16 && N == 128 && R == 64 && V == 128; }
 
-size_t attn_workspace_bytes(int64_t T, int n_seq, int has_cu, int N, int R, int V, int bf16) {
-  if (!has_cu || !attn_fast_path(N, R, V, bf16)) return 0;
-  return ws_layout(T, n_seq).bytes;
+size_t attn_workspace_bytes(int64_t T, int H, int n_seq, int has_cu, int causal, int N, int R, int V, int bf16) {
+  if (!attn_fast_path(N, R, V, bf16) || T == 0) return 0;
+  if (has_cu) return ws_layout(T, n_seq).bytes;
+  if (causal && attn_order() == 1) return pair_ws_bytes(T, H);
+  return 0;
 }
 
 int launch_attention(const AttnPlan &p, void *stream) {
@@ -552,7 +707,9 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.tasks = nullptr;
     a.task_count = nullptr;
     a.n_qtiles = static_cast<int>((p.T + BM - 1) / BM);
-    a.order = attn_order();
+    a.order = p.causal ? attn_order() : 0;
+    a.part = nullptr;
+    if (a.order == 1) a.part = static_cast<float *>(p.ws);
     tasks = a.n_qtiles;
   } else {
     const WsLayout w = ws_layout(p.T, p.n_seq);
@@ -569,11 +726,18 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.task_count = count;
     a.n_qtiles = 0;
     a.order = 0;
+    a.part = nullptr;
     tasks = (p.T + BM - 1) / BM + p.n_seq;
   }
   const int64_t blocks = tasks * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_kernel<128, 64, 128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<128, 64, 128>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, a);
+  if (a.part != nullptr && a.n_qtiles >= 2) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_pair_merge_kernel<4>, dim3(static_cast<unsigned>((a.n_qtiles / 2) * p.H)), dim3(256), 0,
+                       s, a);
+  }
   return hipGetLastError();
 }
 

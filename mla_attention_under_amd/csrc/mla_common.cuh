@@ -36,9 +36,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
-// Two fp32 -> two bf16 packed in one dword (low = a).
+// Two fp32 -> two bf16 packed in one dword (low = a), one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // Interleave the 16-bit halves of two dwords: lo16(a)|lo16(b)<<16 and hi16(a)|hi16(b)<<16.

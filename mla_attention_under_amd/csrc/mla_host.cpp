@@ -178,7 +178,8 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
                        a->o_stride_t | a->o_stride_h;
     if (al % 16 || st % 8)
       return fail(MLA_EUNSUPPORTED, "%s: bf16 tiles need 16-byte aligned buffers and strides multiple of 8", who);
-    const size_t need = mla::attn_workspace_bytes(a->T, a->n_seq, a->cu_seqlens != nullptr, a->N, a->R, a->V, 1);
+    const size_t need = mla::attn_workspace_bytes(a->T, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0,
+                                                  a->N, a->R, a->V, 1);
     if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need ||
                      reinterpret_cast<uintptr_t>(a->workspace) % 256))
       return fail(MLA_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", who, need,
@@ -189,7 +190,8 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
 
 size_t mla_attention_workspace_size(const mla_attn_args *a) {
   if (a == nullptr) return 0;
-  return mla::attn_workspace_bytes(a->T, a->n_seq, a->cu_seqlens != nullptr, a->N, a->R, a->V,
+  if (a->T < 0 || a->H < 1) return 0;
+  return mla::attn_workspace_bytes(a->T, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0, a->N, a->R, a->V,
                                    a->dtype == MLA_BF16);
 }
 

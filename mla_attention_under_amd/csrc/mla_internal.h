@@ -57,7 +57,7 @@ struct AttnPlan {
 };
 // true when the MFMA kernel covers these head widths (others use the generic kernel)
 bool attn_fast_path(int N, int R, int V, int bf16);
-size_t attn_workspace_bytes(int64_t T, int n_seq, int has_cu, int N, int R, int V, int bf16);
+size_t attn_workspace_bytes(int64_t T, int H, int n_seq, int has_cu, int causal, int N, int R, int V, int bf16);
 int launch_attention(const AttnPlan &p, void *stream);
 
 // ---- latent-cache decode ------------------------------------------------

@@ -307,3 +307,39 @@ def test_decode32_sampled_sequences():
     got, ref = _decode_case(w, w.batch, w.kv_len, w.kv_splits, seqs=seqs)
     check_close(got[seqs], ref[seqs], name="decode32 sampled")
     assert np.all(np.isfinite(got))
+
+
+def test_dense_causal_workspace_reuse_across_shapes():
+    """The dense causal path splits paired query tiles between workgroups through a
+    reusable workspace; calls of different shapes in a row must each be exact."""
+    base = mi.WORKLOADS["dsv3_rank"]
+    rng = np.random.default_rng(5)
+    for T, H in [(2048, 16), (4097, 1), (200, 3), (1000, 2), (2048, 16), (640, 5)]:
+        w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+        d = _attn_inputs(w, T, seed_cfg=T + H)
+        got, lse = _run_attn(w, d, T, want_lse=True)
+        rows = np.unique(np.concatenate([[0, T - 1, T // 2], rng.integers(0, T, 24)]))
+        ref, rlse = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K), rows=rows)
+        check_close(got[rows], ref[rows], name=f"reuse T={T} H={H}")
+        check_close(lse[:, rows], rlse[:, rows], name=f"reuse lse T={T} H={H}")
+
+
+def test_attention_dominant_keys():
+    """A few keys outscore all others by far more than the fp32 exp2 range (score
+    gaps of ~200 in log2 units), in both halves of the key sub-tiles: the row max
+    must cover every key of a tile or the weights overflow."""
+    base = mi.WORKLOADS["dsv3_rank"]
+    T, H = 300, 2
+    w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    d = _attn_inputs(w, T, seed_cfg=77)
+    q = mi.bf16_bits_to_f32(d["q"]).copy()
+    kv = mi.bf16_bits_to_f32(d["kv"]).copy()
+    q[:, :, : w.N] += 4.0
+    hot = [5, 70, 133, 250, 252]        # offsets 5, 6, 5 (upper lanes) and 2, 4 within 8-key groups
+    kv[hot, :, : w.N] = 4.0
+    d["q"], d["kv"] = mi.f32_to_bf16_bits(q), mi.f32_to_bf16_bits(kv)
+    got, lse = _run_attn(w, d, T, want_lse=True)
+    ref, rlse = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K))
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
+    check_close(got, ref, name="dominant keys")
+    check_close(lse, rlse, name="dominant keys lse")

@@ -169,13 +169,17 @@ def test_attention_validation_before_launch(lib):
     assert f(kv_stride_t=300) == mla.MLA_EINVAL
     assert f(o_stride_h=64) == mla.MLA_EINVAL
     assert f(q=0x10002) == mla.MLA_EUNSUPPORTED            # misaligned for the tiled path
-    assert f(cu_seqlens=0x50000, n_seq=2) == mla.MLA_EINVAL   # missing workspace
+    assert f(cu_seqlens=0x50000, n_seq=2) == mla.MLA_EINVAL   # missing workspace (packed documents)
+    assert f() == mla.MLA_EINVAL                              # missing workspace (dense causal pairing)
+    assert f(workspace=0x60000, workspace_bytes=64) == mla.MLA_EINVAL   # too small
     assert f(cu_seqlens=0x50000, n_seq=0) == mla.MLA_EINVAL
     assert f(T=0) == mla.MLA_OK
     assert lib.mla_attention_fwd(None, None) == mla.MLA_EINVAL
     a = _attn(cu_seqlens=0x50000, n_seq=4, T=16384)
-    need = lib.mla_attention_workspace_size(ctypes.byref(a))
-    assert need > 0 and lib.mla_attention_workspace_size(ctypes.byref(_attn())) == 0
+    assert lib.mla_attention_workspace_size(ctypes.byref(a)) > 0
+    assert lib.mla_attention_workspace_size(ctypes.byref(_attn())) > 0          # dense causal
+    assert lib.mla_attention_workspace_size(ctypes.byref(_attn(causal=0))) == 0  # non-causal needs none
+    assert lib.mla_attention_workspace_size(ctypes.byref(_attn(N=16, R=8, V=16))) == 0   # generic kernel
 
 
 def test_decode_validation_before_launch(lib):
