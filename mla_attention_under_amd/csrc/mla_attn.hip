@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "mla_common.cuh"
 #include "mla_internal.h"
@@ -75,8 +76,29 @@ __device__ __forceinline__ int kn_swz(int key) { return key & 15; }
 __device__ __forceinline__ int kr_swz(int key) { return (key ^ (key >> 3)) & 7; }
 __device__ __forceinline__ int v_swz(int key) { return (key & 2) | ((key & 1) * 5); }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint16_t *lds_dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds_dst), 16, static_cast<int>(voff), 0, 0, 0);
+// Buffer resource (base, byte range) as four scalar dwords for the transfer below.
+__device__ __forceinline__ u32x4 dma_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(b), hi = static_cast<uint32_t>(b >> 32) & 0xffffu;
+  return u32x4{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lo)),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(hi)),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), static_cast<uint32_t>(kBufferDword3)};
+}
+
+// One 1 KB global->LDS transfer of a wave: lane l copies the 16 bytes at byte
+// voff of the buffer (zero outside its range) to lds_dst + 16 l. Written as
+// inline assembly so that the compiler does not track it: completion is
+// awaited explicitly with vmcnt before the barrier that publishes the tile.
+// (Tracked, its alias analysis loses the buffers apart in the unrolled ring
+// and waits for every transfer in flight before reading any tile.)
+__device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds_dst));
+}
+
+// LDS byte address of a shared-memory pointer (uniform)
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+      static_cast<int>(reinterpret_cast<uintptr_t>((lds_void *)(p)))));
 }
 
 // 4 bf16 of V^T from a row-major V tile: ds_read_b64_tr_b16 hands lane i of
@@ -87,7 +109,8 @@ __device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
 
 // Causal pairing of query tiles (dense, one sequence). Query tiles i and
 // n-1-i of a head together hold U = u(i) + u(n-1-i) key tiles, nearly the
-// same for every i; two workgroups share the pair, U/2 key tiles each. The
+// same for every i; two workgroups share the pair, about U/2 key tiles each
+// (the one that runs two segments a few less). The
 // first takes the first x key tiles of the heavier tile j = n-1-i and then all
 // of tile i; the second takes the remaining key tiles of tile j. Both write
 // their partial softmax state of tile j to the workspace and a second, small
@@ -95,6 +118,8 @@ __device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
 // fences, which on this chip write back and invalidate the XCD's L2 and throw
 // away the K/V tiles the other workgroups are reusing.) With an odd tile
 // count the middle tile is one workgroup alone.
+constexpr int kPairShift = 3;
+
 struct PairPlan {
   int qt;        // query tile of the first segment
   int t0, t1;    // its key-tile range
@@ -119,7 +144,10 @@ __device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T) {
   }
   const int i = k >> 1, j = n - 1 - i;
   const int ui = key_tiles_of(i, T), uj = key_tiles_of(j, T);
-  const int x = max(0, (ui + uj + 1) / 2 - ui);   // key tiles of j done by the first workgroup
+  // key tiles of j done by the first workgroup: half the pair's work, less
+  // kPairShift tiles for the second segment's fixed cost (its Q load, first
+  // transfers and final merge, measured at about six key tiles on this chip)
+  const int x = max(0, (ui + uj + 1) / 2 - ui - kPairShift);
   if ((k & 1) == 0) {
     if (x > 0) {
       pp.qt = j;
@@ -170,33 +198,52 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
     a.lse[static_cast<int64_t>(h) * a.T + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
 }
 
-// Second pass of the causal pairing: one workgroup (4 waves, one per query
-// block) per pair; if the pair's heavier tile was split, combine its two
-// partial states, m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m),
-// o = o0 2^(m0-m) + o1 2^(m1-m), then normalise and store.
+// Second pass of the causal pairing. If a pair's heavier tile was split,
+// combine its two partial states, m = max(m0, m1), l = l0 2^(m0-m) +
+// l1 2^(m1-m), o = o0 2^(m0-m) + o1 2^(m1-m), then normalise and store. One
+// 64-lane workgroup per (pair, head, query block, 32-wide output block):
+// every lane has all of its loads in flight at once.
 template <int DBLK>
-__global__ __launch_bounds__(256) void attn_pair_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void attn_pair_merge_kernel(AttnArgs a) {
   constexpr int REC = DBLK * 16 + 2;
   const int pairs = a.n_qtiles / 2;
-  const int h = blockIdx.x % a.H, i = blockIdx.x / a.H;
+  int b = blockIdx.x;
+  const int d = b % DBLK;
+  b /= DBLK;
+  const int qb = b % 4;
+  b /= 4;
+  const int h = b % a.H, i = b / a.H;
   const PairPlan pp = pair_plan(2 * i + 1, h, a.n_qtiles, a.T);
   if (!pp.part) return;
-  const int qb = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
   const float *r0 = a.part + static_cast<int64_t>(h * pairs + i) * (2 * kRecFloats) + qb * REC * 64 + lane;
   const float *r1 = r0 + kRecFloats;
+  float v0[16], v1[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    v0[r] = __builtin_nontemporal_load(r0 + (d * 16 + r) * 64);
+    v1[r] = __builtin_nontemporal_load(r1 + (d * 16 + r) * 64);
+  }
   const float m0 = __builtin_nontemporal_load(r0 + DBLK * 16 * 64), m1 = __builtin_nontemporal_load(r1 + DBLK * 16 * 64);
   const float l0 = __builtin_nontemporal_load(r0 + (DBLK * 16 + 1) * 64);
   const float l1 = __builtin_nontemporal_load(r1 + (DBLK * 16 + 1) * 64);
   const float mn = fmaxf(m0, m1);
   const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-  f32x16 o[DBLK];
+  const float l = l0 * a0 + l1 * a1;
+  const float l_tot = l + __shfl_xor(l, 32);
+  const int half = lane >> 5;
+  const int qi = pp.qt * BM + 32 * qb + (lane & 31);
+  if (qi >= a.T) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t *op = a.out + static_cast<int64_t>(qi) * a.o_st + static_cast<int64_t>(h) * a.o_sh + 32 * d + 4 * half;
 #pragma unroll
-  for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      o[d][r] = __builtin_nontemporal_load(r0 + (d * 16 + r) * 64) * a0 +
-                __builtin_nontemporal_load(r1 + (d * 16 + r) * 64) * a1;
-  store_rows<DBLK>(a, o, mn, l0 * a0 + l1 * a1, h, pp.qt * BM, a.T, qb, lane);
+  for (int g = 0; g < 4; ++g) {
+    const float o0 = (v0[4 * g] * a0 + v1[4 * g] * a1) * inv, o1 = (v0[4 * g + 1] * a0 + v1[4 * g + 1] * a1) * inv;
+    const float o2 = (v0[4 * g + 2] * a0 + v1[4 * g + 2] * a1) * inv, o3 = (v0[4 * g + 3] * a0 + v1[4 * g + 3] * a1) * inv;
+    *reinterpret_cast<u32x2 *>(op + 8 * g) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+  }
+  if (d == 0 && a.lse != nullptr && half == 0)
+    a.lse[static_cast<int64_t>(h) * a.T + qi] = (mn + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
 }
 
 template <int N, int R, int V>
@@ -214,9 +261,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   constexpr int REC = DBLK * 16 + 2; // floats per lane of a wave's softmax state: O, m, l
   static_assert(N == 128 && R == 64 && V == 128, "swizzles and DMA splits are laid out for 128/64/128");
   static_assert(4 * REC * 64 == kRecFloats, "workspace record size");
+  static_assert(REC * 64 * 4 <= (KN_E + KR_E) * 2, "a query block's state fits one K buffer");
   static_assert(KN_I * 64 * NW == BN * NCH && KR_I * 64 * NW == BN * RCH && V_I * 64 * NW == BN * VCH, "tile DMA split");
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[KN_E + KR_E + V_E];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[KN_E + KR_E + V_E];
+  // K (k_nope | k_rope) and V tiles in rings of three buffers each. Separate
+  // arrays let the compiler tell transfers in flight from tiles being read.
+  __shared__ __attribute__((aligned(1024))) uint16_t kb0[KN_E + KR_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb1[KN_E + KR_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb2[KN_E + KR_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb0[V_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb1[V_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t vb2[V_E];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -261,12 +315,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   doc_lo = __builtin_amdgcn_readfirstlane(doc_lo);
   doc_hi = __builtin_amdgcn_readfirstlane(doc_hi);
 
-  // ---- zero both stages once: loads past the buffer range may leave LDS untouched
+  // ---- zero the stages once: loads past the buffer range may leave LDS untouched
   {
     u32x4 z{0, 0, 0, 0};
-    for (int i = tid; i < (KN_E + KR_E + V_E) / 8; i += 64 * NW) {
-      reinterpret_cast<u32x4 *>(st0)[i] = z;
-      reinterpret_cast<u32x4 *>(st1)[i] = z;
+    for (int i = tid; i < (KN_E + KR_E) / 8; i += 64 * NW) {
+      reinterpret_cast<u32x4 *>(kb0)[i] = z;
+      reinterpret_cast<u32x4 *>(kb1)[i] = z;
+      reinterpret_cast<u32x4 *>(kb2)[i] = z;
+    }
+    for (int i = tid; i < V_E / 8; i += 64 * NW) {
+      reinterpret_cast<u32x4 *>(vb0)[i] = z;
+      reinterpret_cast<u32x4 *>(vb1)[i] = z;
+      reinterpret_cast<u32x4 *>(vb2)[i] = z;
     }
   }
 
@@ -294,7 +354,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const int c = 2 * ((cp >> 1) ^ v_swz(key)) + (cp & 1);
     v_off[i] = static_cast<uint32_t>((key * a.kv_st + N + 8 * c) * 2);
   }
+  const uint32_t kv_row_bytes = static_cast<uint32_t>(a.kv_st) * 2, kr_row_bytes = static_cast<uint32_t>(a.kr_st) * 2;
   const int kkey = 32 * kh + lrow;                      // K rows this lane reads
+  // byte offset, within a K buffer, of the 16 bytes this lane feeds to score step ks
+  uint32_t koff[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int cidx = 2 * ks + half;
+    koff[ks] = static_cast<uint32_t>(ks < NSTEPS ? 2 * (kkey * N + 8 * (cidx ^ kn_swz(kkey)))
+                                                 : 2 * (KN_E + kkey * R + 8 * ((cidx - 2 * NSTEPS) ^ kr_swz(kkey))));
+  }
   const int vrow0 = 32 * kh + 4 * (grp >> 1) + (gl >> 2);   // first V row of the transposing reads
   const float c = a.scale_log2;
 
@@ -302,15 +371,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   float m_run, l_run;
 
   // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
-  // (both key halves) softmax state in the waves with kh == 0
-  auto segment = [&](int qt, int t0, int t1) {
+  // (both key halves) softmax state in the waves with kh == 0.
+  //
+  // Per tile t a wave does M_t = {O += V_{t-1}^T P_{t-1}^T, S_t = K_t Q^T} on
+  // the matrix cores and then X_t = softmax(S_t) -> P_t on the vector ALUs.
+  // The two waves of a SIMD (same query block, key halves 0 and 1) run these
+  // half a tile apart, so while one does M the other does X:
+  //     step t, first half:   kh 0: M_t   kh 1: X_{t-1}
+  //     step t, second half:  kh 0: X_t   kh 1: M_t
+  // During its M_t every wave also starts its share of the transfers of
+  // K_{t+2} and V_{t+1} (five 1 KB transfers spread between its MFMAs, so the
+  // address path never backs up), into the buffers that held K_{t-1} and
+  // V_{t-2}. A step ends with each wave waiting only for its transfers of the
+  // previous step, then a barrier.
+  auto segment = [&](int qt, int t0, int t1) __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
     const int kv_hi = a.causal ? q_end : doc_hi;
     const int qi = q0 + 32 * qb + lrow;
     const int wq_first = q0 + 32 * qb;
-    const int wq_last = min(q0 + 32 * qb + 31, q_end - 1);
-    const bool wave_has_q = wq_first < q_end;
+    const int nt = t1 - t0;
     bf16x8 qf[KSTEPS];
     {
       const uint16_t *qp =
@@ -325,49 +405,127 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     m_run = kNegBig;
     l_run = 0.f;
 
-    auto issue = [&](uint16_t *st, int j0) {
-      const int rows = min(kv_hi - j0, BN);
-      const __amdgpu_buffer_rsrc_t rkv =
-          make_rsrc(kv_h + static_cast<int64_t>(j0) * a.kv_st, static_cast<uint32_t>(rows * a.kv_st * 2));
-      const __amdgpu_buffer_rsrc_t rkr =
-          make_rsrc(a.kr + static_cast<int64_t>(j0) * a.kr_st, static_cast<uint32_t>(rows * a.kr_st * 2));
-#pragma unroll
-      for (int i = 0; i < KN_I; ++i) dma16(rkv, st + 512 * (wave * KN_I + i), kn_off[i]);
-#pragma unroll
-      for (int i = 0; i < KR_I; ++i) dma16(rkr, st + KN_E + 512 * (wave * KR_I + i), kr_off[i]);
-#pragma unroll
-      for (int i = 0; i < V_I; ++i) dma16(rkv, st + KN_E + KR_E + 512 * (wave * V_I + i), v_off[i]);
+    auto j0_of = [&](int t) { return doc_lo + (t0 + t) * BN; };
+    // rows past the visible keys (a whole tile past the end included) lie
+    // outside the buffer range: nothing is read for them
+    // rows of the tile at key j0 that are visible, 0..BN (uniform)
+    // visible rows of tile t (uniform): BN before the last tile, the remainder
+    // in it, none past it
+    const int last_rows = __builtin_amdgcn_readfirstlane(kv_hi - j0_of(nt - 1));
+    auto tile_rows = [&](int t) {
+      return static_cast<uint32_t>(t < nt - 1 ? BN : t == nt - 1 ? last_rows : 0);
     };
-    auto active_for = [&](int j0) {
-      const int jh = j0 + 32 * kh;
-      return wave_has_q && jh < kv_hi && !(a.causal && jh > wq_last);
-    };
-    auto read_v = [&](const uint16_t *st, bf16x8 (&vf)[2][DBLK]) {
-      const uint16_t *Vs = st + KN_E + KR_E;
+    auto issue_k = [&](uint16_t *kb, int t) {
+      const int j0 = j0_of(t);
+      const uint32_t rows = tile_rows(t);
+      const u32x4 rkv = dma_rsrc(kv_h + static_cast<int64_t>(j0) * a.kv_st, rows * kv_row_bytes);
+      const u32x4 rkr = dma_rsrc(a.kr + static_cast<int64_t>(j0) * a.kr_st, rows * kr_row_bytes);
+      const uint32_t base = lds_addr(kb);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int i = 0; i < KN_I; ++i) dma16(rkv, base + 1024 * (wave * KN_I + i), kn_off[i]);
+#pragma unroll
+      for (int i = 0; i < KR_I; ++i) dma16(rkr, base + 2 * KN_E + 1024 * (wave * KR_I + i), kr_off[i]);
+    };
+    auto issue_v = [&](uint16_t *vb, int t) {
+      const int j0 = j0_of(t);
+      const uint32_t rows = tile_rows(t);
+      const u32x4 rkv = dma_rsrc(kv_h + static_cast<int64_t>(j0) * a.kv_st, rows * kv_row_bytes);
+      const uint32_t base = lds_addr(vb);
+#pragma unroll
+      for (int i = 0; i < V_I; ++i) dma16(rkv, base + 1024 * (wave * V_I + i), v_off[i]);
+    };
+    f32x16 sc;           // S_t awaiting its softmax
+    bf16x8 pf[2];        // P_t awaiting its PV product
+
+    // Matrix half-phase: PV of the previous tile (from vprev and pf) and/or
+    // S = K Q^T of this tile (from kb). Straight-line code: every LDS read is
+    // issued well ahead of the MFMA that consumes it, since no other wave's
+    // MFMAs cover the LDS latency while this one runs.
+    constexpr int KAHEAD = 4;   // K fragment reads in flight during the S chain
+    // dma: also start this wave's share of the transfers of K tile jk into
+    // kdst and V tile jv into vdst
+    auto M = [&](auto pv, auto sv, auto dma, const uint16_t *kb, const uint16_t *vprev, uint16_t *kdst,
+                 uint16_t *vdst, int jk, int jv) __attribute__((always_inline)) {
+      constexpr bool DO_PV = decltype(pv)::value, DO_S = decltype(sv)::value, DO_DMA = decltype(dma)::value;
+      auto kread = [&](int ks) {
+        return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(kb) + koff[ks]);
+      };
+      auto vread = [&](int b, int d) {
+        const int dcol = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+        const int r0 = vrow0 + 16 * b, r1 = r0 + 8;
+        const s16x4 lo = read_tr(vprev + r0 * V + 16 * ((dcol >> 4) ^ v_swz(r0)) + (dcol & 15));
+        const s16x4 hi = read_tr(vprev + r1 * V + 16 * ((dcol >> 4) ^ v_swz(r1)) + (dcol & 15));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vf[2][DBLK];
+      bf16x8 kf[KAHEAD];
+      if constexpr (DO_PV) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) vf[0][d] = vread(0, d);
+      }
+      if constexpr (DO_S) {
+#pragma unroll
+        for (int i = 0; i < KAHEAD; ++i) kf[i] = kread(i);
+      }
+      if constexpr (DO_PV) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) vf[1][d] = vread(1, d);
+        // O^T += V^T P^T
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int d = 0; d < DBLK; ++d) o[d] = mfma32(vf[b][d], pf[b], o[d]);
+      }
+      if constexpr (DO_DMA) {
+        issue_k(kdst, jk);
+        issue_v(vdst, jv);
+      }
+      if constexpr (DO_S) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          sc = mfma32(kf[ks % KAHEAD], qf[ks], sc);
+          if (ks + KAHEAD < KSTEPS) kf[ks % KAHEAD] = kread(ks + KAHEAD);
+        }
+      }
+      // Pin the issue order (the scheduler would otherwise sink each read next
+      // to its MFMA): first reads up front, then one MFMA per read, with the
+      // tile transfers placed one after each MFMA from the PV tail on.
+      constexpr int kMfma = 0x008, kDsRead = 0x100, kVmem = 0x060;
+      int vm = DO_DMA ? KN_I + KR_I + V_I : 0;
+      auto mfma_then_dma = [&]() {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        if (vm > 0) {
+          __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
+          --vm;
+        }
+      };
+      if constexpr (DO_PV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * DBLK, 0);
+      if constexpr (DO_S) __builtin_amdgcn_sched_group_barrier(kDsRead, KAHEAD, 0);
+      if constexpr (DO_PV) {
 #pragma unroll
         for (int d = 0; d < DBLK; ++d) {
-          const int dcol = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
-          const int r0 = vrow0 + 16 * b, r1 = r0 + 8;
-          const s16x4 lo = read_tr(Vs + r0 * V + 16 * ((dcol >> 4) ^ v_swz(r0)) + (dcol & 15));
-          const s16x4 hi = read_tr(Vs + r1 * V + 16 * ((dcol >> 4) ^ v_swz(r1)) + (dcol & 15));
-          vf[b][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
         }
-    };
-    auto compute = [&](const uint16_t *st, int j0, const bf16x8 (&vf)[2][DBLK]) {
-      const uint16_t *Kn = st, *Kr = st + KN_E;
-      const int jh = j0 + 32 * kh;                     // first key of this wave's half
-      f32x16 sc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int cidx = 2 * ks + half;
-        const uint16_t *src = ks < NSTEPS ? Kn + kkey * N + 8 * (cidx ^ kn_swz(kkey))
-                                          : Kr + kkey * R + 8 * ((cidx - 2 * NSTEPS) ^ kr_swz(kkey));
-        sc = mfma32(*reinterpret_cast<const bf16x8 *>(src), qf[ks], sc);
+        for (int d = 0; d < DBLK; ++d) mfma_then_dma();
       }
+      if constexpr (DO_S) {
+#pragma unroll
+        for (int ks = 0; ks + KAHEAD < KSTEPS; ++ks) {
+          mfma_then_dma();
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < KAHEAD; ++i) mfma_then_dma();
+      }
+      for (; vm > 0; --vm) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
+    };
+
+    auto X = [&](int t) __attribute__((always_inline)) {
+      const int jh = j0_of(t) + 32 * kh;               // first key of this wave's half
       // mask keys past the diagonal / the visible end (uniform test)
       if (jh + 31 >= kv_hi || (a.causal && jh + 31 > wq_first)) {
         const int lim = a.causal ? min(qi, kv_hi - 1) : kv_hi - 1;
@@ -399,67 +557,88 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
-      // P^T in bf16; the row sum is taken over the same rounded weights the
-      // PV product uses (one bf16 dot2 with (1, 1) per packed pair)
-      bf16x8 pf[2];
-      float lsum = l_run;
+      // P^T in bf16 (the row sum stays in fp32 adds: the bf16 dot instructions
+      // share the matrix pipe and would stall behind the other wave's MFMAs)
+      float ps[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ps[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -m_run));
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * e], c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * e + 1], c, -m_run));
-          const uint32_t pp = pack_bf16x2(p0, p1);
-          w[e] = pp;
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), kOnesBf16x2, lsum, false);
-        }
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(ps[8 * b + 2 * e], ps[8 * b + 2 * e + 1]);
         pf[b] = as_bf16x8(w);
       }
-      l_run = lsum;
-      // O^T += V^T P^T
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int r = 0; r < 8; ++r) ps[r] += ps[r + 8];
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d) o[d] = mfma32(vf[b][d], pf[b], o[d]);
+      for (int r = 0; r < 4; ++r) ps[r] += ps[r + 4];
+      l_run += (ps[0] + ps[2]) + (ps[1] + ps[3]);
     };
 
-    // One barrier per tile. A tile's V^T fragments are read into registers
-    // before the next tile's transfers are issued, so no LDS read of the tile
-    // being computed waits on the transfers in flight into the other stage.
-    __syncthreads();               // the previous segment's readers are done with the stages
-    issue(st0, doc_lo + t0 * BN);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's transfers have landed
-    __syncthreads();
-    for (int kt = t0; kt < t1; kt += 2) {
-      const int j0 = doc_lo + kt * BN;
-      {
-        const bool act = active_for(j0);
-        bf16x8 vf[2][DBLK];
-        if (act) read_v(st0, vf);
-        if (kt + 1 < t1) issue(st1, j0 + BN);
-        if (act) compute(st0, j0, vf);
-        __builtin_amdgcn_sched_barrier(0);   // keep the tile's MFMAs ahead of the wait
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+    // Step t (0 <= t <= nt): K_t in kcur, V_{t-1} in vprev; K_{t+2} goes to
+    // kdst and V_{t+1} to vdst. pv / sv / dma: whether the matrix half-phase
+    // has a PV product (t >= 1), a score product (t < nt) and transfers.
+    constexpr int kDmaPerStep = KN_I + KR_I + V_I;
+    static_assert(kDmaPerStep < 16, "vmcnt field");
+    auto step = [&](auto pv, auto sv, auto dma, int t, const uint16_t *kcur, const uint16_t *vprev,
+                    uint16_t *kdst, uint16_t *vdst) __attribute__((always_inline)) {
+      const int jk = t + 2, jv = t + 1;
+      if (kh == 0) M(pv, sv, dma, kcur, vprev, kdst, vdst, jk, jv);
+      if (kh == 1 && t >= 1) X(t - 1);
+      // Phase alignment only: both half-phases read buffers that landed before
+      // this step, so no memory fence (which would wait for the transfers just
+      // started) is needed at either barrier. Each wave waits for its own
+      // transfers of the previous step before the second one, which makes
+      // them visible to all waves after it.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kh == 1) M(pv, sv, dma, kcur, vprev, kdst, vdst, jk, jv);
+      if (kh == 0 && t < nt) X(t);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(dma)::value)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerStep);   // vmcnt(5): this step's transfers may stay in flight
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const std::true_type yes;
+    const std::false_type no;
+
+    __syncthreads();               // the previous segment's readers are done with the buffers
+    if (nt > 0) {
+      // K_t lives in kb[t % 3], V_t in vb[t % 3]
+      issue_k(kb0, 0);
+      issue_v(vb0, 0);
+      issue_k(kb1, 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      step(no, yes, yes, 0, kb0, vb2, kb2, vb1);
+      int t = 1;
+      for (; t + 2 < nt; t += 3) {                    // whole rounds of the ring
+        step(yes, yes, yes, t, kb1, vb0, kb0, vb2);
+        step(yes, yes, yes, t + 1, kb2, vb1, kb1, vb0);
+        step(yes, yes, yes, t + 2, kb0, vb2, kb2, vb1);
       }
-      if (kt + 1 < t1) {
-        const bool act = active_for(j0 + BN);
-        bf16x8 vf[2][DBLK];
-        if (act) read_v(st1, vf);
-        if (kt + 2 < t1) issue(st0, j0 + 2 * BN);
-        if (act) compute(st1, j0 + BN, vf);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+      if (t < nt) {
+        step(yes, yes, yes, t, kb1, vb0, kb0, vb2);
+        ++t;
       }
+      if (t < nt) {
+        step(yes, yes, yes, t, kb2, vb1, kb1, vb0);
+        ++t;
+      }
+      const int rl = (nt - 1) % 3;                     // t == nt: the last PV product
+      step(yes, no, no, nt, kb0, rl == 0 ? vb0 : rl == 1 ? vb1 : vb2, kb0, vb0);
     }
 
-    // merge the two key halves of each query block through LDS (stage 0 is
-    // free), two query blocks per round so a round fits one stage
+    // merge the two key halves of each query block through LDS (the K buffers
+    // are free), two query blocks per round, one per buffer
 #pragma unroll
     for (int round = 0; round < 2; ++round) {
-      float *xo = reinterpret_cast<float *>(st0) + (qb & 1) * REC * 64;
+      float *xo = reinterpret_cast<float *>((qb & 1) ? kb1 : kb0);
       const bool mine = (qb >> 1) == round;
       if (kh == 1 && mine) {
 #pragma unroll
@@ -735,8 +914,8 @@ int launch_attention(const AttnPlan &p, void *stream) {
   if (a.part != nullptr && a.n_qtiles >= 2) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_pair_merge_kernel<4>, dim3(static_cast<unsigned>((a.n_qtiles / 2) * p.H)), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL(attn_pair_merge_kernel<4>, dim3(static_cast<unsigned>((a.n_qtiles / 2) * p.H * 4 * 4)), dim3(64),
+                       0, s, a);
   }
   return hipGetLastError();
 }
