@@ -4,15 +4,17 @@
 // hyper-parallel `_head_projection_request` selects the rows of the head range,
 // here the column block [col0, col0 + ncols) of the [L][heads_total*(N+V)] weight).
 //
-// bf16 path: one 128x128 output tile per 256-thread workgroup (4 waves of
-// 64x64, two workgroups per CU), K streamed in 64-wide slices. Tiles move global->LDS with
-// buffer_load ... lds into double-buffered, XOR-swizzled LDS (no staging
-// registers; rows past the matrix read zero through the buffer range check).
-// The latent is k-contiguous and feeds the MFMA straight from LDS; the weight
-// is n-contiguous, and ds_read_b64_tr_b16 delivers its k-contiguous operand
-// from the row-major tile. Each wave computes out^T = W^T latent^T with
-// 32x32x16 MFMAs, so a lane owns one output row and 4-wide column runs; the
-// tile leaves through LDS as 16-byte row-contiguous stores.
+// bf16 path: one 256x128 output tile per 512-thread workgroup (8 waves of
+// 64x64, one workgroup per CU), K streamed in 64-wide slices through rings of
+// three LDS buffers per operand. Tiles move global->LDS with buffer_load ...
+// lds (no staging registers; rows past the matrix read zero through the
+// buffer range check), two slices ahead of the one being multiplied, so a
+// transfer has two slices of MFMA work to land in. The latent is
+// k-contiguous and feeds the MFMA straight from LDS; the weight is
+// n-contiguous, and ds_read_b64_tr_b16 delivers its k-contiguous operand from
+// the row-major tile. Each wave computes out^T = W^T latent^T with 32x32x16
+// MFMAs, so a lane owns one output row and 4-wide column runs; the tile leaves
+// through XOR-swizzled LDS as 16-byte row-contiguous stores.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -23,10 +25,15 @@
 namespace mla {
 namespace {
 
-constexpr int GM = 128, GN = 128, GK = 64;
-constexpr int A_E = GM * GK, B_E = GK * GN;       // elements per stage
-constexpr int CP = GN + 8;                        // LDS pitch of the output tile [m][n]
-constexpr int SMEM_E = 2 * (A_E + B_E) > GM * CP ? 2 * (A_E + B_E) : GM * CP;
+constexpr int GM = 256, GN = 128, GK = 64;
+constexpr int NWAVES = 8;
+constexpr int A_E = GM * GK, B_E = GK * GN;       // elements per buffer
+constexpr int A_I = A_E / 8 / (64 * NWAVES);      // 1 KB transfers per wave per slice (A)
+constexpr int B_I = B_E / 8 / (64 * NWAVES);      // (B)
+constexpr int kDmaPerSlice = A_I + B_I;
+static_assert(A_I * 64 * NWAVES * 8 == A_E && B_I * 64 * NWAVES * 8 == B_E, "transfer split");
+static_assert(kDmaPerSlice < 16, "vmcnt field");
+static_assert(GM / 2 * GN <= A_E, "half the output tile fits one A buffer");
 constexpr uint32_t kOob = 0x80000000u;            // a byte offset past every buffer range
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -36,57 +43,78 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ int a_swz(int m) { return (m ^ (m >> 3)) & 7; }            // 8 chunks per row
 __device__ __forceinline__ int b_swz(int k) { return (k & 2) | ((k & 1) * 5); }       // 8 segments per row
 
-__global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
+// Buffer resource as four scalar dwords.
+__device__ __forceinline__ u32x4 dma_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(b), hi = static_cast<uint32_t>(b >> 32) & 0xffffu;
+  return u32x4{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lo)),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(hi)),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), static_cast<uint32_t>(kBufferDword3)};
+}
+// One 1 KB global->LDS transfer of a wave (lane l: 16 bytes at byte voff of
+// the buffer, zero outside its range, to lds_dst + 16 l). Inline assembly so
+// the compiler does not track it: completion is awaited explicitly with
+// vmcnt before the barrier that publishes the slice.
+__device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds_dst));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+      static_cast<int>(reinterpret_cast<uintptr_t>((lds_void *)(p)))));
+}
+
+__global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
     int M, int K, int64_t ldw, int64_t col0, int ncols, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM_E];
-  uint16_t *const st0 = smem, *const st1 = smem + (A_E + B_E);
+  __shared__ __attribute__((aligned(1024))) uint16_t a0[A_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t a1[A_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t a2[A_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t b0[B_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t b1[B_E];
+  __shared__ __attribute__((aligned(1024))) uint16_t b2[B_E];
 
   // Consecutive workgroups land on different XCDs (round robin over 8); give
   // each XCD a contiguous run of tiles so tiles sharing weight columns share an L2.
   const int nt = tiles_m * tiles_n;
-  const int b = blockIdx.x;
+  const int bid = blockIdx.x;
   const int base = nt / 8 * 8;
-  const int tile = b < base ? (b % 8) * (nt / 8) + b / 8 : b;
+  const int tile = bid < base ? (bid % 8) * (nt / 8) + bid / 8 : bid;
   const int m0 = __builtin_amdgcn_readfirstlane((tile % tiles_m) * GM);
   const int n0 = __builtin_amdgcn_readfirstlane((tile / tiles_m) * GN);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int half = lane >> 5, lrow = lane & 31, grp = lane >> 4, gl = lane & 15;
 
-  // DMA plan: wave w fills A chunks [64*(4w+i), +64) and B chunks [64*(4w+i), +64)
-  uint32_t a_off[4], b_off[4];
-  int a_k[4];
+  // Transfer plan: wave w fills A chunks [64*(A_I w + i), +64) and B chunks
+  // [64*(B_I w + i), +64); lane l loads the global chunk the swizzle puts there.
+  uint32_t a_off[A_I], b_off[B_I];
+  int a_k[A_I];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = 64 * (4 * wave + i) + lane;
+  for (int i = 0; i < A_I; ++i) {
+    const int p = 64 * (A_I * wave + i) + lane;
     const int m = p >> 3, c = (p & 7) ^ a_swz(m);
     a_k[i] = 8 * c;
     a_off[i] = static_cast<uint32_t>((m * K + 8 * c) * 2);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = 64 * (4 * wave + i) + lane;
+  for (int i = 0; i < B_I; ++i) {
+    const int p = 64 * (B_I * wave + i) + lane;
     const int k = p >> 4, cp = p & 15;
     const int c = 2 * ((cp >> 1) ^ b_swz(k)) + (cp & 1);
     b_off[i] = static_cast<uint32_t>((k * ldw + 8 * c) * 2);
   }
-  const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(A + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(M - m0, GM) * K * 2));
-  auto issue = [&](uint16_t *st, int k0) {
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + static_cast<int64_t>(k0) * ldw + col0 + n0,
-                                                static_cast<uint32_t>(min(K - k0, GK) * ldw * 2));
+  const u32x4 ra = dma_rsrc(A + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(M - m0, GM) * K * 2));
+  auto issue = [&](uint16_t *as, uint16_t *bs, int k0) {
+    const u32x4 rb = dma_rsrc(W + static_cast<int64_t>(k0) * ldw + col0 + n0,
+                              static_cast<uint32_t>(min(K - k0, GK) * ldw * 2));
+    const uint32_t la = lds_addr(as), lb = lds_addr(bs);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + 512 * (4 * wave + i)), 16,
-                                               static_cast<int>(k0 + a_k[i] < K ? a_off[i] + 2 * k0 : kOob),
-                                               0, 0, 0);
+    for (int i = 0; i < A_I; ++i)
+      dma16(ra, la + 1024 * (A_I * wave + i), k0 + a_k[i] < K ? a_off[i] + 2 * k0 : kOob);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + A_E + 512 * (4 * wave + i)), 16,
-                                               static_cast<int>(b_off[i]), 0, 0, 0);
+    for (int i = 0; i < B_I; ++i) dma16(rb, lb + 1024 * (B_I * wave + i), b_off[i]);
   };
 
   f32x16 acc[2][2];
@@ -97,12 +125,10 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Operand fragments of one 64-wide k slice: weight^T via transposing reads,
-  // latent^T direct. All of a slice's fragments are read before the next
-  // slice's transfers are issued, so no LDS read waits on transfers in flight.
-  bf16x8 wf[GK / 16][2], lf[GK / 16][2];
-  auto read = [&](const uint16_t *st) {
-    const uint16_t *As = st, *Bs = st + A_E;
+  // one 64-wide k slice from buffers (as, bs): weight^T via transposing
+  // reads, latent^T direct
+  auto slice = [&](const uint16_t *As, const uint16_t *Bs) __attribute__((always_inline)) {
+    bf16x8 wf[GK / 16][2], lf[GK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
 #pragma unroll
@@ -122,8 +148,6 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
         lf[ks][j] = *reinterpret_cast<const bf16x8 *>(As + m * GK + 8 * ((2 * ks + half) ^ a_swz(m)));
       }
     }
-  };
-  auto mma = [&]() {
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks)
 #pragma unroll
@@ -132,50 +156,62 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wf[ks][i], lf[ks][j], acc[i][j]);
   };
 
+  // slice s lives in buffer s % 3; during slice s the transfers of slice s+2
+  // go into the buffer slice s-1 used. Each wave then waits only for its own
+  // transfers of slice s+1 (vmcnt leaves this slice's in flight) and the
+  // barrier makes every wave's visible.
   const int nk = (K + GK - 1) / GK;
-  issue(st0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    read(st0);
-    if (kt + 1 < nk) issue(st1, (kt + 1) * GK);
-    mma();
-    __builtin_amdgcn_sched_barrier(0);   // keep the MFMAs ahead of the wait
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      read(st1);
-      if (kt + 2 < nk) issue(st0, (kt + 2) * GK);
-      mma();
-      __builtin_amdgcn_sched_barrier(0);
+  auto step = [&](int s, const uint16_t *as, const uint16_t *bs, uint16_t *an, uint16_t *bn)
+      __attribute__((always_inline)) {
+    const bool more = s + 2 < nk;
+    if (more) issue(an, bn, (s + 2) * GK);
+    slice(as, bs);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerSlice);
+    else
       __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue(a0, b0, 0);
+  if (nk > 1) issue(a1, b1, GK);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 < nk; s += 3) {
+    step(s, a0, b0, a2, b2);
+    step(s + 1, a1, b1, a0, b0);
+    step(s + 2, a2, b2, a1, b1);
   }
+  if (s < nk) step(s, a0, b0, a2, b2);
+  if (s + 1 < nk) step(s + 1, a1, b1, a0, b0);
 
-  // epilogue: registers -> LDS tile [m][n] (bf16) -> 16-byte row stores
-  uint16_t *Cs = smem;
+  // epilogue: registers -> LDS (rows [0,128) in a0, [128,256) in a1, each
+  // [128][128] bf16 with 16-byte chunks XOR-swizzled by row) -> 16-byte row stores
+  __syncthreads();
+  uint16_t *Cs = wm < 2 ? a0 : a1;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int m = 64 * wm + 32 * j + lrow;
+        const int m = 64 * (wm & 1) + 32 * j + lrow;
         const int n = 64 * wn + 32 * i + 8 * g + 4 * half;
         const u32x2 v{pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
                       pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
-        *reinterpret_cast<u32x2 *>(Cs + m * CP + n) = v;
+        *reinterpret_cast<u32x2 *>(Cs + m * GN + 8 * ((n >> 3) ^ (m & 15)) + (n & 7)) = v;
       }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < GM * GN / 8 / 256; ++u) {
-    const int c = tid + 256 * u;
+  for (int u = 0; u < GM * GN / 8 / 512; ++u) {
+    const int c = tid + 512 * u;
     const int row = c >> 4, nc = c & 15;
     const int m = m0 + row, n = n0 + 8 * nc;
+    const uint16_t *src = (row < GM / 2 ? a0 : a1) + (row & (GM / 2 - 1)) * GN + 8 * (nc ^ (row & 15));
     if (m < M && n < ncols)
-      *reinterpret_cast<u32x4 *>(C + static_cast<int64_t>(m) * ncols + n) =
-          *reinterpret_cast<const u32x4 *>(Cs + row * CP + 8 * nc);
+      *reinterpret_cast<u32x4 *>(C + static_cast<int64_t>(m) * ncols + n) = *reinterpret_cast<const u32x4 *>(src);
   }
 }
 
@@ -206,7 +242,7 @@ int launch_up_proj(const UpProjPlan &p, void *stream) {
   if (tiled) {
     const int tm = static_cast<int>((p.T + GM - 1) / GM);
     const int tn = static_cast<int>((p.ncols + GN - 1) / GN);
-    hipLaunchKernelGGL(up_proj_bf16_kernel, dim3(tm * tn), dim3(256), 0, s,
+    hipLaunchKernelGGL(up_proj_bf16_kernel, dim3(tm * tn), dim3(512), 0, s,
                        static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w),
                        static_cast<uint16_t *>(p.out), static_cast<int>(p.T), p.L, p.ldw, p.col0,
                        static_cast<int>(p.ncols), tm, tn);
