@@ -174,8 +174,9 @@ int mla_attention_fwd(const mla_attn_args *a, void *stream);
  *   w_kvb        : [L][heads_total*(N+V)], heads [head_begin, head_begin+H)
  *   out          : [B][H][V]
  *   lse          : optional fp32 [B][H]
- * MLA_BF16 only. Workspace: mla_latent_decode_workspace_size() bytes, 256-byte
- * aligned; contents need not be initialised.
+ * MLA_BF16 only; 1 <= num_splits <= min(S, 256) (more than 256: MLA_EUNSUPPORTED).
+ * Workspace: mla_latent_decode_workspace_size() bytes, 256-byte aligned;
+ * contents need not be initialised.
  */
 typedef struct mla_decode_args {
   const void *q;

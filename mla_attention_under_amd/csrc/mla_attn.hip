@@ -47,7 +47,6 @@ constexpr int BN = 64;       // keys per tile (2 halves of 32)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;   // log2 growth of a row max that forces a rescale
 constexpr float kNegBig = -1.0e30f;
-__device__ constexpr bf16x2_t kOnesBf16x2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
 struct AttnArgs {
   const uint16_t *q;

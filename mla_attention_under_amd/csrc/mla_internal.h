@@ -77,6 +77,7 @@ struct DecodePlan {
   void *ws;
   size_t ws_bytes;
 };
+constexpr int kDecodeMaxSplits = 256;   // KV chunks one decode call may reduce
 bool decode_supported(int L, int N, int R, int V);
 size_t decode_workspace_bytes(int B, int H, int L, int N, int R, int V, int splits);
 int launch_decode(const DecodePlan &p, void *stream);

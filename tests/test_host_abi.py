@@ -200,5 +200,6 @@ def test_decode_validation_before_launch(lib):
     assert f(S=4, num_splits=8) == mla.MLA_EINVAL
     assert f(dtype=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
     assert f(L=256) == mla.MLA_EUNSUPPORTED
+    assert f(num_splits=257) == mla.MLA_EUNSUPPORTED
     assert f(B=0) == mla.MLA_OK
     assert lib.mla_latent_decode_workspace_size(ctypes.byref(args())) > 0
