@@ -242,7 +242,7 @@ static int decode_validate(const mla_decode_args *a, const char *who) {
   if (a->num_splits > a->S) return fail(MLA_EINVAL, "%s: more splits (%d) than cached positions", who, a->num_splits);
   if (a->num_splits > mla::kDecodeMaxSplits)
     return fail(MLA_EUNSUPPORTED, "%s: at most %d splits", who, mla::kDecodeMaxSplits);
-  if (a->S * static_cast<int64_t>(a->L) * 2 >= (1LL << 32))
+  if ((a->S + 64) * static_cast<int64_t>(a->L) * 2 >= (1LL << 32))
     return fail(MLA_EUNSUPPORTED, "%s: a sequence's latent cache must stay below 4 GiB", who);
   if (!mla::decode_supported(a->L, a->N, a->R, a->V) || a->H > 16)
     return fail(MLA_EUNSUPPORTED, "%s: no decode kernel for L=%d N=%d R=%d V=%d H=%d (needs L=512, R=64, H<=16)",

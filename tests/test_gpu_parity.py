@@ -6,6 +6,7 @@ Workloads: tiny fp32, the DeepSeek-V3-shaped rank shard (T=2048, H=16), the
 uneven 22-head shard (T=4096), packed documents (T=16384) and latent-cache
 decode (32 x 8192), plus ragged sizes that leave partial tiles.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -294,11 +295,25 @@ def _decode_case(w, B, S, splits, seqs):
     return host64(out), ref
 
 
-@pytest.mark.parametrize("B,S,splits", [(3, 1000, 8), (2, 64, 1), (1, 130, 3), (2, 9, 4)])
+@pytest.mark.parametrize("B,S,splits", [(3, 1000, 8), (2, 64, 1), (1, 130, 3), (2, 9, 4), (2, 333, 2)])
 def test_decode_small(B, S, splits):
     w = mi.WORKLOADS["decode32"]
     got, ref = _decode_case(w, B, S, splits, seqs=range(B))
     check_close(got, ref, name=f"decode B={B} S={S} splits={splits}")
+
+
+def test_decode_head_subset():
+    """Five heads starting at head 3 of a 16-head weight: the rank's column block."""
+    w = dataclasses.replace(mi.WORKLOADS["decode32"], H=5)
+    B, S, splits, hb = 3, 300, 2, 3
+    d = mi.decode_inputs(w, batch=B, kv_len=S)
+    q, c, kr, W = dev(d["q"]), dev(d["latent"]), dev(d["k_rope"]), dev(d["w_kvb"])
+    out = torch.full((B, w.H, w.V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mla.mla_latent_decode_fwd(q, c, kr, W, out, w.heads_total, hb, w.N, w.R, w.V, splits, 1 / math.sqrt(w.K))
+    _sync()
+    w_cols = d["w_kvb"][:, hb * w.P:(hb + w.H) * w.P]
+    ref, _ = oracle.decode_split_kv(d["q"], d["latent"], d["k_rope"], w_cols, w.N, w.V, 1 / math.sqrt(w.K), splits)
+    check_close(host64(out), ref, name="decode head subset")
 
 
 def test_decode32_sampled_sequences():
