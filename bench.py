@@ -16,6 +16,9 @@ attention 2*H*T(T+1)/2*(N+R+V), unmasked pairs only) / measured step time.
 The timed region is K steps launched back to back on one stream, with the
 inputs resident in HBM, bracketed by HIP events after a synchronize.
 A second pass times every kernel on its own with events for the roofline.
+Extra fields, outside value: the uneven 22-head pack/unpack beyond the
+Infinity Cache, packed-document attention (T=16384) and latent-cache decode
+(32 x 8192 positions, cache swept before each call).
 """
 from __future__ import annotations
 
@@ -96,13 +99,76 @@ def cpu_baseline(w, d, x_pack, sizes, flops_step):
                       f"{w.H} heads, unpack) in float64 NumPy, {el:.1f} s"}
 
 
+def _median_us(torch, fn, reps, before=None):
+    """Median of reps event-timed calls on the current stream; before() runs untimed ahead of each."""
+    ts = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _varlen(torch, mla, mi, dev):
+    """Packed documents 8192/4096/2048/2048 (T=16384, H=16): block-diagonal causal attention."""
+    w = mi.WORKLOADS["varlen16k"]
+    d = mi.shard_inputs(w)
+    latent, W, q, kr = dev(d["latent"]), dev(d["w_kvb"]), dev(d["q"]), dev(d["k_rope"])
+    kv = torch.empty((w.T, w.H, w.P), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((w.T, w.H, w.V), dtype=torch.bfloat16, device="cuda")
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    mla.mla_latent_up_proj(latent, W, kv, w.heads_total, 0, w.H, w.N, w.V)
+    fn = lambda: mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K), cu_seqlens=cu)  # noqa: E731
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    us = _median_us(torch, fn, 10)
+    pairs = sum(n * (n + 1) // 2 for n in w.doc_lens)
+    flops = 2.0 * w.H * pairs * (w.K + w.V)
+    return {"varlen16k_attention_us": round(us, 2), "varlen16k_attention_tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "varlen16k_mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _decode(torch, mla, mi, dev):
+    """Latent-cache decode: 32 sequences, one query each over 8192 cached positions, 8 KV chunks.
+
+    The 302 MB cache exceeds the 256 MB Infinity Cache only slightly, so every timed call
+    follows a read-only sweep of 512 MB (a sweep that writes would leave dirty lines whose
+    write-back competes with the measured call)."""
+    w = mi.WORKLOADS["decode32"]
+    d = mi.decode_inputs(w)
+    q, c, kr, W = dev(d["q"]), dev(d["latent"]), dev(d["k_rope"]), dev(d["w_kvb"])
+    out = torch.empty((w.batch, w.H, w.V), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: mla.mla_latent_decode_fwd(q, c, kr, W, out, w.heads_total, 0, w.N, w.R, w.V,  # noqa: E731
+                                           w.kv_splits, 1 / math.sqrt(w.K))
+    sweep = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    us = _median_us(torch, fn, 20, before=sweep.sum)
+    cache_bytes = 2.0 * (c.numel() + kr.numel())
+    gbps = (cache_bytes + 2.0 * W.numel()) / (us * 1e-6) / 1e9
+    del sweep
+    return {"decode32_us": round(us, 2), "decode32_cache_gbps": round(gbps, 1),
+            "decode32_hbm_frac": round(gbps / PEAK_HBM_GBS, 4),
+            "decode32_note": "whole mla_latent_decode_fwd call (absorb, split, merge, project) after a 512 MB "
+                             "read-only sweep; bytes = latent + rope cache + weight"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the uneven22 pack/unpack HBM measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the uneven22 pack/unpack, varlen16k and decode32 measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain contiguous copy of 1 GiB (the pack kernel with one rank) 3 times, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -241,6 +307,8 @@ def main():
         extra["uneven22_pack_us"] = round(pk * 1e3, 2)
         assert torch.equal(big_back, big), "uneven22 pack/unpack round trip failed"
         del big, big_send, big_back
+        extra.update(_varlen(torch, mla, mi, dev))
+        extra.update(_decode(torch, mla, mi, dev))
 
     value = flops_step / (ms_step * 1e-3) / 1e12
     traffic = _traffic("attention", "dsv3_rank")
