@@ -368,6 +368,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
 
   f32x16 o[DBLK];
   float m_run, l_run;
+  bf16x8 qf[KSTEPS];   // Q^T fragments of the current segment's query block
+  auto load_q = [&](int qt) __attribute__((always_inline)) {
+    const int q0 = doc_lo + qt * BM;
+    const int q_end = min(q0 + BM, doc_hi);
+    const uint16_t *qp = a.q + static_cast<int64_t>(min(q0 + 32 * qb + lrow, q_end - 1)) * a.q_st +
+                         static_cast<int64_t>(h) * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half));
+  };
 
   // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
   // (both key halves) softmax state in the waves with kh == 0.
@@ -383,20 +392,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // address path never backs up), into the buffers that held K_{t-1} and
   // V_{t-2}. A step ends with each wave waiting only for its transfers of the
   // previous step, then a barrier.
-  auto segment = [&](int qt, int t0, int t1) __attribute__((always_inline)) {
+  // q_ready: qf already holds this tile's Q (prefetched by the previous
+  // segment); next_qt >= 0: prefetch that tile's Q once this one's scores are done
+  auto segment = [&](int qt, int t0, int t1, bool q_ready, int next_qt) __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
     const int kv_hi = a.causal ? q_end : doc_hi;
     const int qi = q0 + 32 * qb + lrow;
     const int wq_first = q0 + 32 * qb;
     const int nt = t1 - t0;
-    bf16x8 qf[KSTEPS];
-    {
-      const uint16_t *qp =
-          a.q + static_cast<int64_t>(min(qi, q_end - 1)) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half));
-    }
+    if (!q_ready) load_q(qt);
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
@@ -606,7 +611,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const std::true_type yes;
     const std::false_type no;
 
-    __syncthreads();               // the previous segment's readers are done with the buffers
+    // the previous segment's LDS readers (and the stage zeroing) are done with
+    // the buffers; its global stores may stay in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
     if (nt > 0) {
       // K_t lives in kb[t % 3], V_t in vb[t % 3]
       issue_k(kb0, 0);
@@ -632,25 +640,28 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       const int rl = (nt - 1) % 3;                     // t == nt: the last PV product
       step(yes, no, no, nt, kb0, rl == 0 ? vb0 : rl == 1 ? vb1 : vb2, kb0, vb0);
     }
+    if (next_qt >= 0) load_q(next_qt);   // in flight through the merge and the stores
 
-    // merge the two key halves of each query block through LDS (the K buffers
-    // are free), two query blocks per round, one per buffer
-#pragma unroll
-    for (int round = 0; round < 2; ++round) {
-      float *xo = reinterpret_cast<float *>((qb & 1) ? kb1 : kb0);
-      const bool mine = (qb >> 1) == round;
-      if (kh == 1 && mine) {
+    // merge the two key halves of each query block through LDS in one round
+    // (every stage buffer is free): query block b's O^T in 16-byte pieces in
+    // kb0 / kb1 / kb2 / vb0, the (m, l) pairs in vb1. The next segment's first
+    // barrier keeps its transfers off these buffers until the reads are done.
+    {
+      f32x4 *xo = reinterpret_cast<f32x4 *>(qb == 0 ? kb0 : qb == 1 ? kb1 : qb == 2 ? kb2 : vb0);
+      f32x2_t *xml = reinterpret_cast<f32x2_t *>(vb1) + 64 * qb;
+      if (kh == 1) {
 #pragma unroll
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) xo[(d * 16 + r) * 64 + lane] = o[d][r];
-        xo[(DBLK * 16) * 64 + lane] = m_run;
-        xo[(DBLK * 16 + 1) * 64 + lane] = l_run;
+          for (int g = 0; g < 4; ++g)
+            xo[(4 * d + g) * 64 + lane] = f32x4{o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2], o[d][4 * g + 3]};
+        xml[lane] = f32x2_t{m_run, l_run};
       }
-      __syncthreads();
-      if (kh == 0 && mine) {
-        const float m1 = xo[(DBLK * 16) * 64 + lane];
-        const float l1 = xo[(DBLK * 16 + 1) * 64 + lane];
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      if (kh == 0) {
+        const f32x2_t ml = xml[lane];
+        const float m1 = ml.x, l1 = ml.y;
         const float mn = fmaxf(m_run, m1);
         const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
         l_run = l_run * a0 + l1 * a1;
@@ -658,9 +669,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + xo[(d * 16 + r) * 64 + lane] * a1;
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = xo[(4 * d + g) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[d][4 * g + e] = o[d][4 * g + e] * a0 + v[e] * a1;
+          }
       }
-      __syncthreads();
     }
   };
 
@@ -677,14 +691,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   };
 
   const int qt1 = __builtin_amdgcn_readfirstlane(pp.qt);
-  segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1));
+  const int qt2 = __builtin_amdgcn_readfirstlane(pp.qt2);
+  segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1), false, qt2);
   if (pp.part)
     publish(pp.slot, pp.qt2 >= 0 ? 0 : 1);
   else if (kh == 0)
     store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane);
-  if (pp.qt2 >= 0) {
-    const int qt2 = __builtin_amdgcn_readfirstlane(pp.qt2);
-    segment(qt2, 0, key_tiles_of(qt2, a.T));
+  if (qt2 >= 0) {
+    segment(qt2, 0, key_tiles_of(qt2, a.T), true, -1);
     if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane);
   }
 }
