@@ -26,14 +26,19 @@ struct PackArgs {
   uint32_t row_chunks;   // chunks per (token, head) row
   uint64_t tokens;
   int to_slabs;
+  int sp;
   int off[kMaxRanks + 1];
 };
 
 // Index is uint32_t when every chunk index of the whole buffer fits 32 bits
 // (the common case: cheap 32-bit division), else uint64_t.
+// Ranks are interleaved in the block order (block b serves rank b % sp), so the
+// workgroups in flight at any moment cover whole x rows of a few tokens and
+// one stretch of every slab, rather than one rank's column of every x row.
 template <typename Chunk, typename Index>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
-  const int r = blockIdx.y;
+  const int r = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.sp));
+  const Index cb = static_cast<Index>(blockIdx.x / static_cast<unsigned>(a.sp));
   const Index q = static_cast<Index>(a.off[r + 1] - a.off[r]);
   const Index run = q * a.row_chunks;     // chunks per token in slab r
   const Index total = static_cast<Index>(a.tokens) * run;
@@ -43,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   const Chunk *src = reinterpret_cast<const Chunk *>(a.src);
   Chunk *dst = reinterpret_cast<Chunk *>(a.dst);
 
-  const Index first = static_cast<Index>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
+  const Index first = cb * (kThreads * kUnroll) + threadIdx.x;
   Chunk v[kUnroll];
   Index didx[kUnroll];
   bool ok[kUnroll];
@@ -76,15 +81,16 @@ hipError_t run(const PackPlan &p, hipStream_t s) {
   a.row_chunks = static_cast<uint32_t>(p.row_bytes / sizeof(Chunk));
   a.tokens = static_cast<uint64_t>(p.tokens);
   a.to_slabs = p.to_slabs;
+  a.sp = p.sp;
   int maxq = 0;
   for (int r = 0; r <= p.sp; ++r) a.off[r] = p.off[r];
   for (int r = 0; r < p.sp; ++r) maxq = maxq > (p.off[r + 1] - p.off[r]) ? maxq : (p.off[r + 1] - p.off[r]);
   const uint64_t per_rank = a.tokens * static_cast<uint64_t>(maxq) * a.row_chunks;
   const uint64_t blocks = (per_rank + kThreads * kUnroll - 1) / (kThreads * kUnroll);
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffULL) return hipErrorInvalidConfiguration;
+  if (blocks * static_cast<uint64_t>(p.sp) > 0x7fffffffULL) return hipErrorInvalidConfiguration;
   const uint64_t all = a.tokens * static_cast<uint64_t>(p.heads_total) * a.row_chunks;
-  const dim3 grid(static_cast<unsigned>(blocks), p.sp);
+  const dim3 grid(static_cast<unsigned>(blocks * static_cast<uint64_t>(p.sp)));
   if (all + kThreads * kUnroll < 0xffffffffULL)
     hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t>), grid, dim3(kThreads), 0, s, a);
   else
