@@ -132,8 +132,10 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
  * aligned (0 when none is needed); scratch whose contents need not be
  * initialised and are left arbitrary. Dense causal calls keep there the
  * partial softmax states of the query tiles they split between two
- * workgroups; packed-document calls keep the device-built tile schedule.
- * Calls that may run concurrently need separate workspaces.
+ * workgroups and one arrival flag per split tile (tagged with a per-call
+ * value, so no clearing is needed); packed-document calls keep the
+ * device-built tile schedule. Calls that may run concurrently need separate
+ * workspaces.
  */
 typedef struct mla_attn_args {
   const void *q;

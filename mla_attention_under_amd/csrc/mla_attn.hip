@@ -28,12 +28,15 @@
 //    (exact: any reference max gives the same quotient).
 //  * Work order: dense causal query tiles are paired (i, n-1-i) and every pair
 //    is split into two workgroups of equal key-tile count; the tile that
-//    straddles both is merged by a second kernel (see pair_plan).
+//    straddles both is merged by whichever finishes second (see arrive).
 //    Packed documents use a device-built schedule sorted by key-tile count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstdlib>
+#include <random>
 #include <type_traits>
 
 #include "mla_common.cuh"
@@ -61,6 +64,8 @@ struct AttnArgs {
   int n_qtiles;           // dense: query tiles per head
   int order;              // dense causal: 1 pairs tiles and splits the work evenly, 0 heaviest first
   float *part;            // dense causal pairing: two softmax-state records per pair
+  unsigned long long *flags;   // dense causal pairing: one arrival flag per pair
+  unsigned long long epoch;    // this call's flag tag (see arrive)
   int T, H;
   float scale_log2;       // scale * log2(e)
   int causal;
@@ -112,11 +117,9 @@ __device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
 // (the one that runs two segments a few less). The
 // first takes the first x key tiles of the heavier tile j = n-1-i and then all
 // of tile i; the second takes the remaining key tiles of tile j. Both write
-// their partial softmax state of tile j to the workspace and a second, small
-// kernel merges them. (Merging inside the kernel would need agent-scope
-// fences, which on this chip write back and invalidate the XCD's L2 and throw
-// away the K/V tiles the other workgroups are reusing.) With an odd tile
-// count the middle tile is one workgroup alone.
+// their partial softmax state of tile j to the workspace and the later of the
+// two merges them (see arrive). With an odd tile count the middle tile is one
+// workgroup alone.
 constexpr int kPairShift = 3;
 
 struct PairPlan {
@@ -197,52 +200,30 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
     a.lse[static_cast<int64_t>(h) * a.T + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
 }
 
-// Second pass of the causal pairing. If a pair's heavier tile was split,
-// combine its two partial states, m = max(m0, m1), l = l0 2^(m0-m) +
-// l1 2^(m1-m), o = o0 2^(m0-m) + o1 2^(m1-m), then normalise and store. One
-// 64-lane workgroup per (pair, head, query block, 32-wide output block):
-// every lane has all of its loads in flight at once.
-template <int DBLK>
-__global__ __launch_bounds__(64) void attn_pair_merge_kernel(AttnArgs a) {
-  constexpr int REC = DBLK * 16 + 2;
-  const int pairs = a.n_qtiles / 2;
-  int b = blockIdx.x;
-  const int d = b % DBLK;
-  b /= DBLK;
-  const int qb = b % 4;
-  b /= 4;
-  const int h = b % a.H, i = b / a.H;
-  const PairPlan pp = pair_plan(2 * i + 1, h, a.n_qtiles, a.T);
-  if (!pp.part) return;
-  const int lane = threadIdx.x;
-  const float *r0 = a.part + static_cast<int64_t>(h * pairs + i) * (2 * kRecFloats) + qb * REC * 64 + lane;
-  const float *r1 = r0 + kRecFloats;
-  float v0[16], v1[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    v0[r] = __builtin_nontemporal_load(r0 + (d * 16 + r) * 64);
-    v1[r] = __builtin_nontemporal_load(r1 + (d * 16 + r) * 64);
-  }
-  const float m0 = __builtin_nontemporal_load(r0 + DBLK * 16 * 64), m1 = __builtin_nontemporal_load(r1 + DBLK * 16 * 64);
-  const float l0 = __builtin_nontemporal_load(r0 + (DBLK * 16 + 1) * 64);
-  const float l1 = __builtin_nontemporal_load(r1 + (DBLK * 16 + 1) * 64);
-  const float mn = fmaxf(m0, m1);
-  const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-  const float l = l0 * a0 + l1 * a1;
-  const float l_tot = l + __shfl_xor(l, 32);
-  const int half = lane >> 5;
-  const int qi = pp.qt * BM + 32 * qb + (lane & 31);
-  if (qi >= a.T) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t *op = a.out + static_cast<int64_t>(qi) * a.o_st + static_cast<int64_t>(h) * a.o_sh + 32 * d + 4 * half;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const float o0 = (v0[4 * g] * a0 + v1[4 * g] * a1) * inv, o1 = (v0[4 * g + 1] * a0 + v1[4 * g + 1] * a1) * inv;
-    const float o2 = (v0[4 * g + 2] * a0 + v1[4 * g + 2] * a1) * inv, o3 = (v0[4 * g + 3] * a0 + v1[4 * g + 3] * a1) * inv;
-    *reinterpret_cast<u32x2 *>(op + 8 * g) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-  }
-  if (d == 0 && a.lse != nullptr && half == 0)
-    a.lse[static_cast<int64_t>(h) * a.T + qi] = (mn + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+// Split tiles of the causal pairing: each of the two workgroups that share
+// tile j stores its partial softmax state (O^T, m, l per lane, fp32) with
+// agent-scope stores, waits for them to complete and then arrives at the
+// pair's flag; the one that arrives second reads both records with
+// agent-scope loads, combines them, m = max(m0, m1), l = l0 2^(m0-m) +
+// l1 2^(m1-m), o = o0 2^(m0-m) + o1 2^(m1-m), and stores the rows. Nothing
+// ever waits for the other workgroup, and no cache maintenance is needed (an
+// agent-scope fence would write back and invalidate the L2 that the other
+// workgroups of the XCD are reading their K/V tiles from).
+//
+// The flag holds (epoch << 1) | 1 after a first arrival of this call and
+// epoch << 1 after the second; any other value (an earlier call, or memory
+// never used) reads as "nobody yet". The epoch is a 62-bit per-call tag from
+// a process-wide counter with a random start, so the workspace needs no
+// clearing.
+__device__ __forceinline__ bool arrive(unsigned long long *flag, unsigned long long epoch) {
+  const unsigned long long one = (epoch << 1) | 1ull, done = epoch << 1;
+  unsigned long long cur = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool second;
+  do {   // lock-free: a failed exchange means the other workgroup's succeeded
+    second = cur == one;
+  } while (!__hip_atomic_compare_exchange_strong(flag, &cur, second ? done : one, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return second;
 }
 
 template <int N, int R, int V>
@@ -678,16 +659,48 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // ---- a split tile's partial: the merge kernel combines the two records
+  // ---- a split tile's partial state, stored past this XCD's L2
   auto publish = [&](int slot, int role) {
     if (kh != 0) return;
-    float *rec = a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) + role * kRecFloats + qb * REC * 64;
+    float *rec = a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) + role * kRecFloats + qb * REC * 64 + lane;
+    auto put = [&](int i, float v) { __hip_atomic_store(rec + i * 64, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rec[(d * 16 + r) * 64 + lane] = o[d][r];
-    rec[(DBLK * 16) * 64 + lane] = m_run;
-    rec[(DBLK * 16 + 1) * 64 + lane] = l_run;
+      for (int r = 0; r < 16; ++r) put(d * 16 + r, o[d][r]);
+    put(DBLK * 16, m_run);
+    put(DBLK * 16 + 1, l_run);
+  };
+  // ---- after publishing: arrive at the pair's flag; the second arrival
+  // combines both records of split tile qt and stores its rows
+  __shared__ int second_arrival;
+  auto arrive_and_merge = [&](int slot, int qt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's record stores are complete
+    __syncthreads();
+    if (tid == 0) second_arrival = arrive(a.flags + slot, a.epoch);
+    __syncthreads();
+    if (!second_arrival || kh != 0) return;
+    const float *r0 = a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) + qb * REC * 64 + lane;
+    const float *r1 = r0 + kRecFloats;
+    auto get = [&](const float *r, int i) { return __hip_atomic_load(r + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    const float m0 = get(r0, DBLK * 16), m1 = get(r1, DBLK * 16);
+    const float l0 = get(r0, DBLK * 16 + 1), l1 = get(r1, DBLK * 16 + 1);
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = get(r0, d * 16 + r);
+    f32x16 o1[DBLK];
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o1[d][r] = get(r1, d * 16 + r);
+    const float mn = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + o1[d][r] * a1;
+    store_rows<DBLK>(a, o, mn, l0 * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane);
   };
 
   const int qt1 = __builtin_amdgcn_readfirstlane(pp.qt);
@@ -701,6 +714,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     segment(qt2, 0, key_tiles_of(qt2, a.T), true, -1);
     if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane);
   }
+  if (pp.part) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
 }
 
 // ---- packed-document schedule: all (document, query tile) tasks, heaviest first
@@ -847,10 +861,26 @@ int attn_order() {
   return order;
 }
 
-// Dense causal pairing: two softmax-state records per (head, pair), scratch.
-size_t pair_ws_bytes(int64_t T, int H) {
+// Dense causal pairing: two softmax-state records and one arrival flag per
+// (head, pair); the flags follow the records.
+size_t pair_records_bytes(int64_t T, int H) {
   const int64_t n = (T + BM - 1) / BM;
   return static_cast<size_t>(H) * static_cast<size_t>(n / 2) * 2 * kRecFloats * sizeof(float);
+}
+size_t pair_ws_bytes(int64_t T, int H) {
+  const int64_t n = (T + BM - 1) / BM;
+  return pair_records_bytes(T, H) + static_cast<size_t>(H) * static_cast<size_t>(n / 2) * sizeof(unsigned long long);
+}
+
+// Per-call tag of the pairing flags: 62 bits from a process-wide counter that
+// starts at a random value.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    return (static_cast<unsigned long long>(rd()) << 32) ^ rd() ^
+           static_cast<unsigned long long>(std::chrono::steady_clock::now().time_since_epoch().count());
+  }()};
+  return counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << 62) - 1);
 }
 
 }  // namespace
@@ -901,7 +931,13 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.n_qtiles = static_cast<int>((p.T + BM - 1) / BM);
     a.order = p.causal ? attn_order() : 0;
     a.part = nullptr;
-    if (a.order == 1) a.part = static_cast<float *>(p.ws);
+    a.flags = nullptr;
+    a.epoch = 0;
+    if (a.order == 1) {
+      a.part = static_cast<float *>(p.ws);
+      a.flags = reinterpret_cast<unsigned long long *>(static_cast<char *>(p.ws) + pair_records_bytes(p.T, p.H));
+      a.epoch = next_epoch();
+    }
     tasks = a.n_qtiles;
   } else {
     const WsLayout w = ws_layout(p.T, p.n_seq);
@@ -919,17 +955,13 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.n_qtiles = 0;
     a.order = 0;
     a.part = nullptr;
+    a.flags = nullptr;
+    a.epoch = 0;
     tasks = (p.T + BM - 1) / BM + p.n_seq;
   }
   const int64_t blocks = tasks * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_fwd_kernel<128, 64, 128>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, a);
-  if (a.part != nullptr && a.n_qtiles >= 2) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_pair_merge_kernel<4>, dim3(static_cast<unsigned>((a.n_qtiles / 2) * p.H * 4 * 4)), dim3(64),
-                       0, s, a);
-  }
   return hipGetLastError();
 }
 
