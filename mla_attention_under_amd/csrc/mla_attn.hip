@@ -33,10 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
-#include <chrono>
 #include <cstdlib>
-#include <random>
 #include <type_traits>
 
 #include "mla_common.cuh"
@@ -212,9 +209,8 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
 //
 // The flag holds (epoch << 1) | 1 after a first arrival of this call and
 // epoch << 1 after the second; any other value (an earlier call, or memory
-// never used) reads as "nobody yet". The epoch is a 62-bit per-call tag from
-// a process-wide counter with a random start, so the workspace needs no
-// clearing.
+// never used) reads as "nobody yet". The epoch is a 62-bit per-call tag
+// (next_call_tag), so the workspace needs no clearing.
 __device__ __forceinline__ bool arrive(unsigned long long *flag, unsigned long long epoch) {
   const unsigned long long one = (epoch << 1) | 1ull, done = epoch << 1;
   unsigned long long cur = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -872,17 +868,6 @@ size_t pair_ws_bytes(int64_t T, int H) {
   return pair_records_bytes(T, H) + static_cast<size_t>(H) * static_cast<size_t>(n / 2) * sizeof(unsigned long long);
 }
 
-// Per-call tag of the pairing flags: 62 bits from a process-wide counter that
-// starts at a random value.
-unsigned long long next_epoch() {
-  static std::atomic<unsigned long long> counter{[] {
-    std::random_device rd;
-    return (static_cast<unsigned long long>(rd()) << 32) ^ rd() ^
-           static_cast<unsigned long long>(std::chrono::steady_clock::now().time_since_epoch().count());
-  }()};
-  return counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << 62) - 1);
-}
-
 }  // namespace
 
 bool attn_fast_path(int N, int R, int V, int bf16) { return bf16 && N == 128 && R == 64 && V == 128; }
@@ -936,7 +921,7 @@ int launch_attention(const AttnPlan &p, void *stream) {
     if (a.order == 1) {
       a.part = static_cast<float *>(p.ws);
       a.flags = reinterpret_cast<unsigned long long *>(static_cast<char *>(p.ws) + pair_records_bytes(p.T, p.H));
-      a.epoch = next_epoch();
+      a.epoch = next_call_tag() & ((1ull << 62) - 1);
     }
     tasks = a.n_qtiles;
   } else {

@@ -2,11 +2,14 @@
 // dispatch to the HIP launchers. Every check runs before anything is launched,
 // so a bad call changes no output (the one-GPU analogue of validating on every
 // rank before the first collective, DeepSpeed PR #8316 review thread).
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <random>
 #include <string>
 
 #include "../../include/mla.h"
@@ -83,6 +86,18 @@ int pack_common(const void *src, void *dst, int64_t tokens, int heads_total, int
 }
 
 }  // namespace
+
+namespace mla {
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    return (static_cast<unsigned long long>(rd()) << 32) ^ rd() ^
+           static_cast<unsigned long long>(std::chrono::steady_clock::now().time_since_epoch().count());
+  }()};
+  return counter.fetch_add(1, std::memory_order_relaxed);
+}
+
+}  // namespace mla
 
 extern "C" {
 

@@ -84,4 +84,9 @@ int launch_decode(const DecodePlan &p, void *stream);
 
 const char *hip_error_name(int err);
 
+// Per-call tag for the arrival flags that kernels keep in a caller's
+// workspace: a process-wide counter that starts at a random 64-bit value, so
+// a flag left by another call (or never written) does not match.
+unsigned long long next_call_tag();
+
 }  // namespace mla
