@@ -359,35 +359,43 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void decode_split_kernel(SplitArg
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
                                                            const float *__restrict__ o, uint16_t *__restrict__ olat,
                                                            float *__restrict__ lse, int splits, int L) {
-  __shared__ float wt[kDecodeMaxSplits];
   const int64_t bh = blockIdx.x;
-  const float *mp = m + bh * splits, *lp = l + bh * splits;
-  float mx = -INFINITY;
-  for (int c = 0; c < splits; ++c) mx = fmaxf(mx, mp[c]);
-  float den = 0.f;
-  for (int c = 0; c < splits; ++c) den += lp[c] * __builtin_amdgcn_exp2f(mp[c] - mx);
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  for (int c = threadIdx.x; c < splits; c += blockDim.x) wt[c] = lp[c] * __builtin_amdgcn_exp2f(mp[c] - mx) * inv;
-  __syncthreads();
-  const float *ob = o + bh * splits * L;
+  const float *mp = m + bh * splits, *lp = l + bh * splits, *ob = o + bh * splits * L;
   for (int d = 2 * threadIdx.x; d < L; d += 2 * blockDim.x) {
-    float a0 = 0.f, a1 = 0.f;
-    for (int c0 = 0; c0 < splits; c0 += 8) {   // eight partial rows in flight at a time
+    // the splits combine online, eight at a time with all their loads in
+    // flight together: running max mx (finite start, so empty splits with
+    // m_c = -inf weigh zero), denominator den and the two output sums
+    float mx = -1.0e30f, den = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int c0 = 0; c0 < splits; c0 += 8) {
       f32x2_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = c0 + u < splits ? *reinterpret_cast<const f32x2_t *>(ob + static_cast<int64_t>(c0 + u) * L + d)
-                               : f32x2_t{0.f, 0.f};
+      float mc[8], lc[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float wu = c0 + u < splits ? wt[c0 + u] : 0.f;
+        const bool in = c0 + u < splits;
+        v[u] = in ? *reinterpret_cast<const f32x2_t *>(ob + static_cast<int64_t>(c0 + u) * L + d) : f32x2_t{0.f, 0.f};
+        mc[u] = in ? mp[c0 + u] : -INFINITY;
+        lc[u] = in ? lp[c0 + u] : 0.f;
+      }
+      float cm = mx;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cm = fmaxf(cm, mc[u]);
+      const float sc = __builtin_amdgcn_exp2f(mx - cm);
+      den *= sc;
+      a0 *= sc;
+      a1 *= sc;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = lc[u] * __builtin_amdgcn_exp2f(mc[u] - cm);
+        den += wu;
         a0 += wu * v[u].x;
         a1 += wu * v[u].y;
       }
+      mx = cm;
     }
-    *reinterpret_cast<uint32_t *>(olat + bh * L + d) = pack_bf16x2(a0, a1);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    *reinterpret_cast<uint32_t *>(olat + bh * L + d) = pack_bf16x2(a0 * inv, a1 * inv);
+    if (lse != nullptr && d == 0) lse[bh] = (mx + __builtin_amdgcn_logf(den)) * 0.6931471805599453f;
   }
-  if (lse != nullptr && threadIdx.x == 0) lse[bh] = (mx + __builtin_amdgcn_logf(den)) * 0.6931471805599453f;
 }
 
 // ---- 3b. out[b][h][v] = sum_d o_lat[b][h][d] W[d][v-col(h) + v]. One
