@@ -175,25 +175,39 @@ __device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T) {
 // l the partial denominator of this lane's keys.
 constexpr int kRecFloats = 4 * (4 * 16 + 2) * 64;   // 4 query blocks x (64 O + m + l) x 64 lanes
 
-// normalise the state of query block qb of the tile starting at q0 and store it
+// normalise the state of query block qb of the tile starting at q0 and store
+// it. The lane layout (a lane holds 8-byte pieces of one query row) goes
+// through the wave's own free stage buffer xs, so every query row leaves as
+// 16 whole 16-byte chunks, streamed past L2 with nontemporal stores (no dirty
+// lines left for the end-of-kernel write-back).
 template <int DBLK>
 __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[DBLK], float m_run, float l_run,
-                                           int h, int q0, int q_end, int qb, int lane) {
-  const int half = lane >> 5;
-  const int qi = q0 + 32 * qb + (lane & 31);
+                                           int h, int q0, int q_end, int qb, int lane, uint16_t *xs) {
+  constexpr int XLD = 32 * DBLK + 8;   // padded row of xs (bf16)
+  const int half = lane >> 5, row = lane & 31;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qi >= q_end) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t *op = a.out + static_cast<int64_t>(qi) * a.o_st + static_cast<int64_t>(h) * a.o_sh;
 #pragma unroll
   for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const u32x2 v{pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
-                    pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2 *>(op + 32 * d + 8 * g + 4 * half) = v;
-    }
-  if (a.lse != nullptr && half == 0)
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<u32x2 *>(xs + row * XLD + 32 * d + 8 * g + 4 * half) =
+          u32x2{pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
+                pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
+  // one wave writes and reads xs, and its LDS accesses complete in order
+  constexpr int CPR = 32 * DBLK / 8;   // 16-byte chunks per output row
+  const int rsub = lane / CPR, c = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int rr = rsub + (64 / CPR) * i;
+    const int qi = q0 + 32 * qb + rr;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + rr * XLD + 8 * c);
+    if (qi < q_end)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(a.out + static_cast<int64_t>(qi) * a.o_st +
+                                                               static_cast<int64_t>(h) * a.o_sh + 8 * c));
+  }
+  const int qi = q0 + 32 * qb + row;
+  if (a.lse != nullptr && half == 0 && qi < q_end)
     a.lse[static_cast<int64_t>(h) * a.T + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
 }
 
@@ -253,6 +267,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   const int qb = wave & 3, kh = wave >> 2;          // query block, key half
   const int half = lane >> 5, lrow = lane & 31;
   const int grp = lane >> 4, gl = lane & 15;        // 16-lane groups for the transposing read
+  // the stage buffer this query block's waves use for the key-half merge and the output transpose
+  uint16_t *const xs_own = qb == 0 ? kb0 : qb == 1 ? kb1 : qb == 2 ? kb2 : vb0;
 
   // ---- which head, document and segments
   int h, doc_lo, doc_hi;
@@ -624,7 +640,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     // kb0 / kb1 / kb2 / vb0, the (m, l) pairs in vb1. The next segment's first
     // barrier keeps its transfers off these buffers until the reads are done.
     {
-      f32x4 *xo = reinterpret_cast<f32x4 *>(qb == 0 ? kb0 : qb == 1 ? kb1 : qb == 2 ? kb2 : vb0);
+      f32x4 *xo = reinterpret_cast<f32x4 *>(xs_own);
       f32x2_t *xml = reinterpret_cast<f32x2_t *>(vb1) + 64 * qb;
       if (kh == 1) {
 #pragma unroll
@@ -696,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + o1[d][r] * a1;
-    store_rows<DBLK>(a, o, mn, l0 * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane);
+    store_rows<DBLK>(a, o, mn, l0 * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_own);
   };
 
   const int qt1 = __builtin_amdgcn_readfirstlane(pp.qt);
@@ -705,10 +721,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   if (pp.part)
     publish(pp.slot, pp.qt2 >= 0 ? 0 : 1);
   else if (kh == 0)
-    store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane);
+    store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_own);
   if (qt2 >= 0) {
     segment(qt2, 0, key_tiles_of(qt2, a.T), true, -1);
-    if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane);
+    if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_own);
   }
   if (pp.part) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
 }
