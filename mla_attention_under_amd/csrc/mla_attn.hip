@@ -380,10 +380,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // half a tile apart, so while one does M the other does X:
   //     step t, first half:   kh 0: M_t   kh 1: X_{t-1}
   //     step t, second half:  kh 0: X_t   kh 1: M_t
-  // During its M_t every wave also starts its share of the transfers of
-  // K_{t+2} and V_{t+1} (five 1 KB transfers spread between its MFMAs, so the
-  // address path never backs up), into the buffers that held K_{t-1} and
-  // V_{t-2}. A step ends with each wave waiting only for its transfers of the
+  // In its vector half-phase of step t every wave also starts its share of
+  // the transfers of K_{t+2} and V_{t+1} (five 1 KB transfers) into the
+  // buffers that held K_{t-1} and V_{t-2}, which no wave reads after step
+  // t-1. A step ends with each wave waiting only for its transfers of the
   // previous step, then a barrier.
   // q_ready: qf already holds this tile's Q (prefetched by the previous
   // segment); next_qt >= 0: prefetch that tile's Q once this one's scores are done
@@ -439,11 +439,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     // issued well ahead of the MFMA that consumes it, since no other wave's
     // MFMAs cover the LDS latency while this one runs.
     constexpr int KAHEAD = 4;   // K fragment reads in flight during the S chain
-    // dma: also start this wave's share of the transfers of K tile jk into
-    // kdst and V tile jv into vdst
-    auto M = [&](auto pv, auto sv, auto dma, const uint16_t *kb, const uint16_t *vprev, uint16_t *kdst,
-                 uint16_t *vdst, int jk, int jv) __attribute__((always_inline)) {
-      constexpr bool DO_PV = decltype(pv)::value, DO_S = decltype(sv)::value, DO_DMA = decltype(dma)::value;
+    auto M = [&](auto pv, auto sv, const uint16_t *kb, const uint16_t *vprev) __attribute__((always_inline)) {
+      constexpr bool DO_PV = decltype(pv)::value, DO_S = decltype(sv)::value;
       auto kread = [&](int ks) {
         return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(kb) + koff[ks]);
       };
@@ -473,10 +470,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
           for (int d = 0; d < DBLK; ++d) o[d] = mfma32(vf[b][d], pf[b], o[d]);
       }
-      if constexpr (DO_DMA) {
-        issue_k(kdst, jk);
-        issue_v(vdst, jv);
-      }
       if constexpr (DO_S) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -487,17 +480,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         }
       }
       // Pin the issue order (the scheduler would otherwise sink each read next
-      // to its MFMA): first reads up front, then one MFMA per read, with the
-      // tile transfers placed one after each MFMA from the PV tail on.
-      constexpr int kMfma = 0x008, kDsRead = 0x100, kVmem = 0x060;
-      int vm = DO_DMA ? KN_I + KR_I + V_I : 0;
-      auto mfma_then_dma = [&]() {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        if (vm > 0) {
-          __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
-          --vm;
-        }
-      };
+      // to its MFMA): first reads up front, then one MFMA per read.
+      constexpr int kMfma = 0x008, kDsRead = 0x100;
+      auto mfma_one = [&]() { __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0); };
       if constexpr (DO_PV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * DBLK, 0);
       if constexpr (DO_S) __builtin_amdgcn_sched_group_barrier(kDsRead, KAHEAD, 0);
       if constexpr (DO_PV) {
@@ -507,18 +492,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
         }
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d) mfma_then_dma();
+        for (int d = 0; d < DBLK; ++d) mfma_one();
       }
       if constexpr (DO_S) {
 #pragma unroll
         for (int ks = 0; ks + KAHEAD < KSTEPS; ++ks) {
-          mfma_then_dma();
+          mfma_one();
           __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
         }
 #pragma unroll
-        for (int i = 0; i < KAHEAD; ++i) mfma_then_dma();
+        for (int i = 0; i < KAHEAD; ++i) mfma_one();
       }
-      for (; vm > 0; --vm) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
     };
 
     auto X = [&](int t) __attribute__((always_inline)) {
@@ -581,8 +565,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     auto step = [&](auto pv, auto sv, auto dma, int t, const uint16_t *kcur, const uint16_t *vprev,
                     uint16_t *kdst, uint16_t *vdst) __attribute__((always_inline)) {
       const int jk = t + 2, jv = t + 1;
-      if (kh == 0) M(pv, sv, dma, kcur, vprev, kdst, vdst, jk, jv);
-      if (kh == 1 && t >= 1) X(t - 1);
+      // the vector half-phase also starts this wave's share of the transfers:
+      // its wave is latency-bound with issue slots to spare, the matrix wave is not
+      auto transfers = [&]() __attribute__((always_inline)) {
+        if constexpr (decltype(dma)::value) {
+          issue_k(kdst, jk);
+          issue_v(vdst, jv);
+        }
+      };
+      if (kh == 0) M(pv, sv, kcur, vprev);
+      if (kh == 1) {
+        transfers();
+        if (t >= 1) X(t - 1);
+      }
       // Phase alignment only: both half-phases read buffers that landed before
       // this step, so no memory fence (which would wait for the transfers just
       // started) is needed at either barrier. Each wave waits for its own
@@ -591,8 +586,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (kh == 1) M(pv, sv, dma, kcur, vprev, kdst, vdst, jk, jv);
-      if (kh == 0 && t < nt) X(t);
+      if (kh == 1) M(pv, sv, kcur, vprev);
+      if (kh == 0) {
+        transfers();
+        if (t < nt) X(t);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(dma)::value)
         __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerStep);   // vmcnt(5): this step's transfers may stay in flight
