@@ -339,6 +339,58 @@ def test_dense_causal_workspace_reuse_across_shapes():
         check_close(lse[:, rows], rlse[:, rows], name=f"reuse lse T={T} H={H}")
 
 
+def test_dense_causal_arbitrary_workspace():
+    """The workspace needs no clearing: split-tile flags left by other calls, or
+    arbitrary bytes, must not be taken for this call's arrivals."""
+    base = mi.WORKLOADS["dsv3_rank"]
+    T, H = 2048, 16
+    w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    d = _attn_inputs(w, T)
+    q, kv, kr = dev(d["q"]), dev(d["kv"]), dev(d["k_rope"])
+    out = torch.empty((T, H, w.V), dtype=torch.bfloat16, device="cuda")
+    scale = 1 / math.sqrt(w.K)
+    nbytes = mla.mla_attention_workspace_size(q, kv, kr, out, w.N, w.R, w.V, scale)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ref, _ = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, scale)
+    for fill in ("random", "ones", "zeros"):
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda"))
+        else:
+            ws.fill_(255 if fill == "ones" else 0)
+        out.fill_(float("nan"))
+        mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, scale, workspace=ws)
+        _sync()
+        check_close(host64(out), ref, name=f"workspace {fill}")
+
+
+def test_dense_causal_graph_replays():
+    """A captured dense causal call (the split-tile flags keep one tag for every
+    replay) gives the eager result on every replay, with eager work between."""
+    base = mi.WORKLOADS["dsv3_rank"]
+    T, H = 2048, 16
+    w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    d = _attn_inputs(w, T)
+    q, kv, kr = dev(d["q"]), dev(d["kv"]), dev(d["k_rope"])
+    scale = 1 / math.sqrt(w.K)
+    eager = torch.empty((T, H, w.V), dtype=torch.bfloat16, device="cuda")
+    mla.mla_attention_fwd(q, kv, kr, eager, w.N, w.R, w.V, scale)   # also allocates the cached workspace
+    _sync()
+    out = torch.full((T, H, w.V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, scale)
+    for i in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        _sync()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+        mla.mla_attention_fwd(q, kv, kr, eager, w.N, w.R, w.V, scale)   # eager work between replays
+        _sync()
+
+
 def test_attention_dominant_keys():
     """A few keys outscore all others by far more than the fp32 exp2 range (score
     gaps of ~200 in log2 units), in both halves of the key sub-tiles: the row max
