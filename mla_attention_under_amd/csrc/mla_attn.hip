@@ -394,7 +394,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const int qi = q0 + 32 * qb + lrow;
     const int wq_first = q0 + 32 * qb;
     const int nt = t1 - t0;
-    if (!q_ready) load_q(qt);
+    // a segment without a prefetched Q takes it with its first transfers:
+    // query block b's 32 rows go to a stage buffer the first step does not
+    // read (kb2: blocks 0 and 1, vb1: block 2, vb2: block 3), one 1 KB
+    // region per 16-wide k step, lane-major, so each lane reads back exactly
+    // its own MFMA fragment; the two waves of a block fetch six steps each
+    uint16_t *const qbuf = qb == 0 ? kb2 : qb == 1 ? kb2 + 32 * KD : qb == 2 ? vb1 : vb2;
+    auto issue_q = [&]() __attribute__((always_inline)) {
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, q_end - (q0 + 32 * qb))));
+      const u32x4 rq = dma_rsrc(a.q + static_cast<int64_t>(q0 + 32 * qb) * a.q_st + static_cast<int64_t>(h) * a.q_sh,
+                                static_cast<uint32_t>(rows * a.q_st * 2));
+      const uint32_t base = lds_addr(qbuf);
+#pragma unroll
+      for (int i = 0; i < KSTEPS / 2; ++i) {
+        const int ks = (KSTEPS / 2) * kh + i;
+        dma16(rq, base + 1024 * ks, static_cast<uint32_t>((lrow * a.q_st + 16 * ks + 8 * half) * 2));
+      }
+    };
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
@@ -608,11 +624,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     if (nt > 0) {
       // K_t lives in kb[t % 3], V_t in vb[t % 3]
+      if (!q_ready) issue_q();
       issue_k(kb0, 0);
       issue_v(vb0, 0);
       issue_k(kb1, 1);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
+      if (!q_ready) {
+        // Q and K_0 have landed once only the five newest transfers (V_0, K_1)
+        // are left; they land during step 0, whose closing wait covers them
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (KN_I + KR_I + V_I));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qbuf + 512 * ks + 8 * lane);
+        // every wave holds its Q before step 0's transfers reuse kb2 and vb1
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
       step(no, yes, yes, 0, kb0, vb2, kb2, vb1);
       int t = 1;
       for (; t + 2 < nt; t += 3) {                    // whole rounds of the ring
