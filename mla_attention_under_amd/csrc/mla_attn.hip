@@ -117,7 +117,11 @@ __device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
 // their partial softmax state of tile j to the workspace and the later of the
 // two merges them (see arrive). With an odd tile count the middle tile is one
 // workgroup alone.
-constexpr int kPairShift = 3;
+//
+// Key tiles the two-segment workgroup gives up to the other: its second
+// segment's first transfers cost about three key tiles, while the other
+// workgroup usually arrives second and pays for the merge (about two).
+constexpr int kPairShift = 2;
 
 struct PairPlan {
   int qt;        // query tile of the first segment
@@ -129,7 +133,7 @@ struct PairPlan {
 
 __device__ __forceinline__ int key_tiles_of(int qt, int T) { return (min((qt + 1) * BM, T) + BN - 1) / BN; }
 
-__device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T) {
+__device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T, int shift) {
   PairPlan pp;
   const int pairs = n / 2;
   pp.qt2 = -1;
@@ -144,9 +148,8 @@ __device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T) {
   const int i = k >> 1, j = n - 1 - i;
   const int ui = key_tiles_of(i, T), uj = key_tiles_of(j, T);
   // key tiles of j done by the first workgroup: half the pair's work, less
-  // kPairShift tiles for the second segment's fixed cost (its Q load, first
-  // transfers and final merge, measured at about six key tiles on this chip)
-  const int x = max(0, (ui + uj + 1) / 2 - ui - kPairShift);
+  // the shift for the second segment's fixed cost
+  const int x = max(0, (ui + uj + 1) / 2 - ui - shift);
   if ((k & 1) == 0) {
     if (x > 0) {
       pp.qt = j;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     doc_lo = 0;
     doc_hi = a.T;
     if (a.causal && a.order == 1) {
-      pp = pair_plan(b / H, h, n, a.T);
+      pp = pair_plan(b / H, h, n, a.T, kPairShift);
     } else {                                  // heaviest first
       pp.qt = n - 1 - b / H;
       pp.t0 = 0;
@@ -362,15 +365,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   f32x16 o[DBLK];
   float m_run, l_run;
   bf16x8 qf[KSTEPS];   // Q^T fragments of the current segment's query block
-  auto load_q = [&](int qt) __attribute__((always_inline)) {
-    const int q0 = doc_lo + qt * BM;
-    const int q_end = min(q0 + BM, doc_hi);
-    const uint16_t *qp = a.q + static_cast<int64_t>(min(q0 + 32 * qb + lrow, q_end - 1)) * a.q_st +
-                         static_cast<int64_t>(h) * a.q_sh;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 16 * ks + 8 * half));
-  };
-
   // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
   // (both key halves) softmax state in the waves with kh == 0.
   //
@@ -385,20 +379,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // buffers that held K_{t-1} and V_{t-2}, which no wave reads after step
   // t-1. A step ends with each wave waiting only for its transfers of the
   // previous step, then a barrier.
-  // q_ready: qf already holds this tile's Q (prefetched by the previous
-  // segment); next_qt >= 0: prefetch that tile's Q once this one's scores are done
-  auto segment = [&](int qt, int t0, int t1, bool q_ready, int next_qt) __attribute__((always_inline)) {
+  auto segment = [&](int qt, int t0, int t1) __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
     const int kv_hi = a.causal ? q_end : doc_hi;
     const int qi = q0 + 32 * qb + lrow;
     const int wq_first = q0 + 32 * qb;
     const int nt = t1 - t0;
-    // a segment without a prefetched Q takes it with its first transfers:
-    // query block b's 32 rows go to a stage buffer the first step does not
-    // read (kb2: blocks 0 and 1, vb1: block 2, vb2: block 3), one 1 KB
-    // region per 16-wide k step, lane-major, so each lane reads back exactly
-    // its own MFMA fragment; the two waves of a block fetch six steps each
+    // Q arrives with the segment's first transfers: query block b's 32 rows
+    // go to a stage buffer the first step does not read (kb2: blocks 0 and
+    // 1, vb1: block 2, vb2: block 3), one 1 KB region per 16-wide k step,
+    // lane-major, so each lane reads back exactly its own MFMA fragment; the
+    // two waves of a block fetch six steps each
     uint16_t *const qbuf = qb == 0 ? kb2 : qb == 1 ? kb2 + 32 * KD : qb == 2 ? vb1 : vb2;
     auto issue_q = [&]() __attribute__((always_inline)) {
       const int rows = __builtin_amdgcn_readfirstlane(max(0, min(32, q_end - (q0 + 32 * qb))));
@@ -624,27 +616,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     if (nt > 0) {
       // K_t lives in kb[t % 3], V_t in vb[t % 3]
-      if (!q_ready) issue_q();
+      issue_q();
       issue_k(kb0, 0);
       issue_v(vb0, 0);
       issue_k(kb1, 1);
-      if (!q_ready) {
-        // Q and K_0 have landed once only the five newest transfers (V_0, K_1)
-        // are left; they land during step 0, whose closing wait covers them
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (KN_I + KR_I + V_I));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+      // Q and K_0 have landed once only the five newest transfers (V_0, K_1)
+      // are left; they land during step 0, whose closing wait covers them
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (KN_I + KR_I + V_I));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qbuf + 512 * ks + 8 * lane);
-        // every wave holds its Q before step 0's transfers reuse kb2 and vb1
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-      }
+      for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qbuf + 512 * ks + 8 * lane);
+      // every wave holds its Q before step 0's transfers reuse kb2 and vb1
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
       step(no, yes, yes, 0, kb0, vb2, kb2, vb1);
       int t = 1;
       for (; t + 2 < nt; t += 3) {                    // whole rounds of the ring
@@ -663,7 +650,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       const int rl = (nt - 1) % 3;                     // t == nt: the last PV product
       step(yes, no, no, nt, kb0, rl == 0 ? vb0 : rl == 1 ? vb1 : vb2, kb0, vb0);
     }
-    if (next_qt >= 0) load_q(next_qt);   // in flight through the merge and the stores
 
     // merge the two key halves of each query block through LDS in one round
     // (every stage buffer is free): query block b's O^T in 16-byte pieces in
@@ -701,62 +687,75 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // ---- a split tile's partial state, stored past this XCD's L2
+  // ---- a split tile's partial state, stored past this XCD's L2. A lane's
+  // 2*DBLK*8+1 float pairs (O^T pieces, then (m, l)) leave as 8-byte
+  // agent-scope stores; pair i of lane l sits at float 128 i + 2 l of its
+  // query block's record.
+  constexpr int RPAIRS = DBLK * 8 + 1;
+  auto rec_of = [&](int slot, int role) {
+    return reinterpret_cast<unsigned long long *>(a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) +
+                                                  role * kRecFloats + qb * REC * 64) + lane;
+  };
   auto publish = [&](int slot, int role) {
     if (kh != 0) return;
-    float *rec = a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) + role * kRecFloats + qb * REC * 64 + lane;
-    auto put = [&](int i, float v) { __hip_atomic_store(rec + i * 64, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    unsigned long long *rec = rec_of(slot, role);
+    auto put = [&](int i, float x, float y) {
+      __hip_atomic_store(rec + 64 * i, (static_cast<unsigned long long>(__float_as_uint(y)) << 32) | __float_as_uint(x),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) put(d * 16 + r, o[d][r]);
-    put(DBLK * 16, m_run);
-    put(DBLK * 16 + 1, l_run);
+      for (int r = 0; r < 16; r += 2) put(d * 8 + r / 2, o[d][r], o[d][r + 1]);
+    put(DBLK * 8, m_run, l_run);
   };
   // ---- after publishing: arrive at the pair's flag; the second arrival
-  // combines both records of split tile qt and stores its rows
+  // combines its own state (still in registers) with the other workgroup's
+  // record of split tile qt and stores the rows
   __shared__ int second_arrival;
-  auto arrive_and_merge = [&](int slot, int qt) __attribute__((always_inline)) {
+  auto arrive_and_merge = [&](int slot, int role, int qt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's record stores are complete
     __syncthreads();
     if (tid == 0) second_arrival = arrive(a.flags + slot, a.epoch);
     __syncthreads();
     if (!second_arrival || kh != 0) return;
-    const float *r0 = a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) + qb * REC * 64 + lane;
-    const float *r1 = r0 + kRecFloats;
-    auto get = [&](const float *r, int i) { return __hip_atomic_load(r + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    const float m0 = get(r0, DBLK * 16), m1 = get(r1, DBLK * 16);
-    const float l0 = get(r0, DBLK * 16 + 1), l1 = get(r1, DBLK * 16 + 1);
+    const unsigned long long *r1 = rec_of(slot, 1 - role);
+    auto get = [&](int i) { return __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    unsigned long long v[RPAIRS];
+#pragma unroll
+    for (int i = 0; i < RPAIRS; ++i) v[i] = get(i);
+    const float m1 = __uint_as_float(static_cast<unsigned>(v[DBLK * 8]));
+    const float l1 = __uint_as_float(static_cast<unsigned>(v[DBLK * 8] >> 32));
+    const float mn = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
 #pragma unroll
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = get(r0, d * 16 + r);
-    f32x16 o1[DBLK];
-#pragma unroll
-    for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o1[d][r] = get(r1, d * 16 + r);
-    const float mn = fmaxf(m0, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-#pragma unroll
-    for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = o[d][r] * a0 + o1[d][r] * a1;
-    store_rows<DBLK>(a, o, mn, l0 * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_own);
+      for (int r = 0; r < 16; r += 2) {
+        const unsigned long long x = v[d * 8 + r / 2];
+        o[d][r] = o[d][r] * a0 + __uint_as_float(static_cast<unsigned>(x)) * a1;
+        o[d][r + 1] = o[d][r + 1] * a0 + __uint_as_float(static_cast<unsigned>(x >> 32)) * a1;
+      }
+    store_rows<DBLK>(a, o, mn, l_run * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_own);
   };
 
   const int qt1 = __builtin_amdgcn_readfirstlane(pp.qt);
   const int qt2 = __builtin_amdgcn_readfirstlane(pp.qt2);
-  segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1), false, qt2);
+  segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1));
+  const int role = qt2 >= 0 ? 0 : 1;
   if (pp.part)
-    publish(pp.slot, pp.qt2 >= 0 ? 0 : 1);
+    publish(pp.slot, role);
   else if (kh == 0)
     store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_own);
+  // a workgroup with a second segment arrives before running it (its state
+  // of the split tile is still in registers), so that usually the other
+  // workgroup of the pair, which has no second segment, arrives second and
+  // merges the split tile
+  if (pp.part) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1);
   if (qt2 >= 0) {
-    segment(qt2, 0, key_tiles_of(qt2, a.T), true, -1);
+    segment(qt2, 0, key_tiles_of(qt2, a.T));
     if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_own);
   }
-  if (pp.part) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
 }
 
 // ---- packed-document schedule: all (document, query tile) tasks, heaviest first
