@@ -119,9 +119,10 @@ __device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
 // workgroup alone.
 //
 // Key tiles the two-segment workgroup gives up to the other: its second
-// segment's first transfers cost about three key tiles, while the other
-// workgroup usually arrives second and pays for the merge (about two).
-constexpr int kPairShift = 2;
+// segment's first transfers, its publish and its arrival cost about four key
+// tiles more than the other workgroup's tail (which usually finds the pair
+// already arrived and merges without publishing; measured best at 4).
+constexpr int kPairShift = 4;
 
 struct PairPlan {
   int qt;        // query tile of the first segment
@@ -365,6 +366,25 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   f32x16 o[DBLK];
   float m_run, l_run;
   bf16x8 qf[KSTEPS];   // Q^T fragments of the current segment's query block
+  // ---- a split tile's partial state, stored past this XCD's L2. A lane's
+  // 2*DBLK*8+1 float pairs (O^T pieces, then (m, l)) leave as 8-byte
+  // agent-scope stores; pair i of lane l sits at float 128 i + 2 l of its
+  // query block's record.
+  constexpr int RPAIRS = DBLK * 8 + 1;
+  auto rec_of = [&](int slot, int role) {
+    return reinterpret_cast<unsigned long long *>(a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) +
+                                                  role * kRecFloats + qb * REC * 64) + lane;
+  };
+  // The workgroup without a second segment usually finishes the split tile
+  // long after the other one has arrived. It reads the pair's flag during
+  // its last key step; if the other workgroup has arrived (flag = first
+  // arrival of this call), it is certainly second: it skips publishing and
+  // arriving, and its merging waves load the other record while the key
+  // halves merge.
+  __shared__ int early_second;
+  unsigned long long other[RPAIRS];
+  bool early = false;
+
   // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
   // (both key halves) softmax state in the waves with kh == 0.
   //
@@ -379,13 +399,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // buffers that held K_{t-1} and V_{t-2}, which no wave reads after step
   // t-1. A step ends with each wave waiting only for its transfers of the
   // previous step, then a barrier.
-  auto segment = [&](int qt, int t0, int t1) __attribute__((always_inline)) {
+  // probe: the pair flag to read for an early second arrival (nullptr: none);
+  // its record is other_rec.
+  auto segment = [&](int qt, int t0, int t1, const unsigned long long *probe, const unsigned long long *other_rec)
+                     __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
     const int kv_hi = a.causal ? q_end : doc_hi;
     const int qi = q0 + 32 * qb + lrow;
     const int wq_first = q0 + 32 * qb;
     const int nt = t1 - t0;
+    unsigned long long flag_seen = 0;
     // Q arrives with the segment's first transfers: query block b's 32 rows
     // go to a stage buffer the first step does not read (kb2: blocks 0 and
     // 1, vb1: block 2, vb2: block 3), one 1 KB region per 16-wide k step,
@@ -647,6 +671,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         step(yes, yes, yes, t, kb2, vb1, kb1, vb0);
         ++t;
       }
+      if (probe != nullptr && tid == 0) flag_seen = __hip_atomic_load(probe, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int rl = (nt - 1) % 3;                     // t == nt: the last PV product
       step(yes, no, no, nt, kb0, rl == 0 ? vb0 : rl == 1 ? vb1 : vb2, kb0, vb0);
     }
@@ -666,8 +691,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
             xo[(4 * d + g) * 64 + lane] = f32x4{o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2], o[d][4 * g + 3]};
         xml[lane] = f32x2_t{m_run, l_run};
       }
+      if (probe != nullptr && tid == 0) early_second = flag_seen == ((a.epoch << 1) | 1ull);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();
+      if (probe != nullptr) early = __builtin_amdgcn_readfirstlane(early_second) != 0;
+      if (early && kh == 0) {
+#pragma unroll
+        for (int i = 0; i < RPAIRS; ++i)
+          other[i] = __hip_atomic_load(other_rec + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if (kh == 0) {
         const f32x2_t ml = xml[lane];
         const float m1 = ml.x, l1 = ml.y;
@@ -687,15 +719,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // ---- a split tile's partial state, stored past this XCD's L2. A lane's
-  // 2*DBLK*8+1 float pairs (O^T pieces, then (m, l)) leave as 8-byte
-  // agent-scope stores; pair i of lane l sits at float 128 i + 2 l of its
-  // query block's record.
-  constexpr int RPAIRS = DBLK * 8 + 1;
-  auto rec_of = [&](int slot, int role) {
-    return reinterpret_cast<unsigned long long *>(a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) +
-                                                  role * kRecFloats + qb * REC * 64) + lane;
-  };
   auto publish = [&](int slot, int role) {
     if (kh != 0) return;
     unsigned long long *rec = rec_of(slot, role);
@@ -709,21 +732,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; r += 2) put(d * 8 + r / 2, o[d][r], o[d][r + 1]);
     put(DBLK * 8, m_run, l_run);
   };
-  // ---- after publishing: arrive at the pair's flag; the second arrival
-  // combines its own state (still in registers) with the other workgroup's
-  // record of split tile qt and stores the rows
-  __shared__ int second_arrival;
-  auto arrive_and_merge = [&](int slot, int role, int qt) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's record stores are complete
-    __syncthreads();
-    if (tid == 0) second_arrival = arrive(a.flags + slot, a.epoch);
-    __syncthreads();
-    if (!second_arrival || kh != 0) return;
-    const unsigned long long *r1 = rec_of(slot, 1 - role);
-    auto get = [&](int i) { return __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    unsigned long long v[RPAIRS];
-#pragma unroll
-    for (int i = 0; i < RPAIRS; ++i) v[i] = get(i);
+  // ---- the merging waves combine their own state with the other record
+  // (RPAIRS pairs in v) and store the rows of split tile qt
+  auto combine_store = [&](const unsigned long long (&v)[RPAIRS], int qt) __attribute__((always_inline)) {
     const float m1 = __uint_as_float(static_cast<unsigned>(v[DBLK * 8]));
     const float l1 = __uint_as_float(static_cast<unsigned>(v[DBLK * 8] >> 32));
     const float mn = fmaxf(m_run, m1);
@@ -738,12 +749,34 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       }
     store_rows<DBLK>(a, o, mn, l_run * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_own);
   };
+  // ---- after publishing: arrive at the pair's flag; the second arrival
+  // combines its own state (still in registers) with the other workgroup's
+  // record of split tile qt and stores the rows
+  __shared__ int second_arrival;
+  auto arrive_and_merge = [&](int slot, int role, int qt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's record stores are complete
+    __syncthreads();
+    if (tid == 0) second_arrival = arrive(a.flags + slot, a.epoch);
+    __syncthreads();
+    if (!second_arrival || kh != 0) return;
+    const unsigned long long *r1 = rec_of(slot, 1 - role);
+#pragma unroll
+    for (int i = 0; i < RPAIRS; ++i) other[i] = __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    combine_store(other, qt);
+  };
 
   const int qt1 = __builtin_amdgcn_readfirstlane(pp.qt);
   const int qt2 = __builtin_amdgcn_readfirstlane(pp.qt2);
-  segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1));
+  {
+    const bool probe = pp.part && qt2 < 0;
+    const int slot = __builtin_amdgcn_readfirstlane(pp.slot);
+    segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1),
+            probe ? a.flags + slot : nullptr, probe ? rec_of(slot, 0) : nullptr);
+  }
   const int role = qt2 >= 0 ? 0 : 1;
-  if (pp.part)
+  if (early) {
+    if (kh == 0) combine_store(other, qt1);
+  } else if (pp.part)
     publish(pp.slot, role);
   else if (kh == 0)
     store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_own);
@@ -751,9 +784,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // of the split tile is still in registers), so that usually the other
   // workgroup of the pair, which has no second segment, arrives second and
   // merges the split tile
-  if (pp.part) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1);
+  if (pp.part && !early) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1);
   if (qt2 >= 0) {
-    segment(qt2, 0, key_tiles_of(qt2, a.T));
+    segment(qt2, 0, key_tiles_of(qt2, a.T), nullptr, nullptr);
     if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_own);
   }
 }
