@@ -253,6 +253,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = 8;              // waves per workgroup
   constexpr int KN_I = BN * NCH / (64 * NW), KR_I = BN * RCH / (64 * NW), V_I = BN * VCH / (64 * NW);   // DMA instrs per wave
   constexpr int REC = DBLK * 16 + 2; // floats per lane of a wave's softmax state: O, m, l
+  constexpr int kFirstDma = KSTEPS / 2 + 2 * (KN_I + KR_I) + V_I;   // a segment's first transfers per wave
+  static_assert(kFirstDma < 16, "vmcnt field");
   static_assert(N == 128 && R == 64 && V == 128, "swizzles and DMA splits are laid out for 128/64/128");
   static_assert(4 * REC * 64 == kRecFloats, "workspace record size");
   static_assert(REC * 64 * 4 <= (KN_E + KR_E) * 2, "a query block's state fits one K buffer");
@@ -400,9 +402,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // t-1. A step ends with each wave waiting only for its transfers of the
   // previous step, then a barrier.
   // probe: the pair flag to read for an early second arrival (nullptr: none);
-  // its record is other_rec.
-  auto segment = [&](int qt, int t0, int t1, const unsigned long long *probe, const unsigned long long *other_rec)
-                     __attribute__((always_inline)) {
+  // its record is other_rec. mode 0 runs the whole segment; mode 1 only
+  // starts its first transfers (Q, K_0, V_0, K_1) and leaves the softmax
+  // state alone; mode 2 runs a segment whose first transfers mode 1 started.
+  auto segment = [&](int qt, int t0, int t1, const unsigned long long *probe, const unsigned long long *other_rec,
+                     int mode) __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
     const int kv_hi = a.causal ? q_end : doc_hi;
@@ -427,12 +431,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         dma16(rq, base + 1024 * ks, static_cast<uint32_t>((lrow * a.q_st + 16 * ks + 8 * half) * 2));
       }
     };
+    if (mode != 1) {
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+      for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-    m_run = kNegBig;
-    l_run = 0.f;
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+      m_run = kNegBig;
+      l_run = 0.f;
+    }
 
     auto j0_of = [&](int t) { return doc_lo + (t0 + t) * BN; };
     // rows past the visible keys (a whole tile past the end included) lie
@@ -634,16 +640,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const std::true_type yes;
     const std::false_type no;
 
-    // the previous segment's LDS readers (and the stage zeroing) are done with
-    // the buffers; its global stores may stay in flight
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    if (mode != 2) {
+      // the previous segment's LDS readers (and the stage zeroing) are done
+      // with the buffers; its global stores may stay in flight
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      if (nt > 0) {
+        // K_t lives in kb[t % 3], V_t in vb[t % 3]
+        issue_q();
+        issue_k(kb0, 0);
+        issue_v(vb0, 0);
+        issue_k(kb1, 1);
+      }
+      if (mode == 1) return;
+    }
     if (nt > 0) {
-      // K_t lives in kb[t % 3], V_t in vb[t % 3]
-      issue_q();
-      issue_k(kb0, 0);
-      issue_v(vb0, 0);
-      issue_k(kb1, 1);
       // Q and K_0 have landed once only the five newest transfers (V_0, K_1)
       // are left; they land during step 0, whose closing wait covers them
       __builtin_amdgcn_sched_barrier(0);
@@ -752,16 +763,48 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // ---- after publishing: arrive at the pair's flag; the second arrival
   // combines its own state (still in registers) with the other workgroup's
   // record of split tile qt and stores the rows
+  // (defer: the stage buffers already hold the next segment's first tiles, so
+  // a second arrival only returns true and merges after that segment, see
+  // merge_records)
   __shared__ int second_arrival;
-  auto arrive_and_merge = [&](int slot, int role, int qt) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's record stores are complete
+  auto arrive_and_merge = [&](int slot, int role, int qt, bool defer) __attribute__((always_inline)) {
+    // this wave's record stores are complete: vmcnt(0), or, after the next
+    // segment's first transfers (issued after the stores; the counter
+    // retires in issue order), all but those
+    if (defer)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kFirstDma);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (tid == 0) second_arrival = arrive(a.flags + slot, a.epoch);
     __syncthreads();
-    if (!second_arrival || kh != 0) return;
+    const bool second = __builtin_amdgcn_readfirstlane(second_arrival) != 0;
+    if (defer) return second;
+    if (!second || kh != 0) return false;
     const unsigned long long *r1 = rec_of(slot, 1 - role);
 #pragma unroll
     for (int i = 0; i < RPAIRS; ++i) other[i] = __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    combine_store(other, qt);
+    return false;
+  };
+  // ---- a deferred second arrival: both records of split tile qt (this
+  // workgroup's own is role 0) are combined and stored
+  auto merge_records = [&](int slot, int qt) __attribute__((always_inline)) {
+    if (kh != 0) return;
+    const unsigned long long *r0 = rec_of(slot, 0), *r1 = rec_of(slot, 1);
+#pragma unroll
+    for (int i = 0; i < RPAIRS; ++i) other[i] = __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const unsigned long long x = __hip_atomic_load(r0 + 64 * (d * 8 + r / 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        o[d][r] = __uint_as_float(static_cast<unsigned>(x));
+        o[d][r + 1] = __uint_as_float(static_cast<unsigned>(x >> 32));
+      }
+    const unsigned long long ml = __hip_atomic_load(r0 + 64 * (DBLK * 8), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    m_run = __uint_as_float(static_cast<unsigned>(ml));
+    l_run = __uint_as_float(static_cast<unsigned>(ml >> 32));
     combine_store(other, qt);
   };
 
@@ -771,24 +814,33 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const bool probe = pp.part && qt2 < 0;
     const int slot = __builtin_amdgcn_readfirstlane(pp.slot);
     segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1),
-            probe ? a.flags + slot : nullptr, probe ? rec_of(slot, 0) : nullptr);
+            probe ? a.flags + slot : nullptr, probe ? rec_of(slot, 0) : nullptr, 0);
   }
   const int role = qt2 >= 0 ? 0 : 1;
+  // a workgroup with a split tile and a second segment starts the second
+  // segment's first transfers right after its record stores, so that they
+  // land while it arrives (the arrival waits for the stores only)
+  const bool pre = pp.part && qt2 >= 0;
+  const int tiles2 = qt2 >= 0 ? key_tiles_of(qt2, a.T) : 0;
   if (early) {
     if (kh == 0) combine_store(other, qt1);
-  } else if (pp.part)
+  } else if (pp.part) {
     publish(pp.slot, role);
-  else if (kh == 0)
+    if (pre) segment(qt2, 0, tiles2, nullptr, nullptr, 1);
+  } else if (kh == 0) {
     store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_own);
+  }
   // a workgroup with a second segment arrives before running it (its state
   // of the split tile is still in registers), so that usually the other
   // workgroup of the pair, which has no second segment, arrives second and
   // merges the split tile
-  if (pp.part && !early) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1);
+  bool deferred = false;
+  if (pp.part && !early) deferred = arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1, pre);
   if (qt2 >= 0) {
-    segment(qt2, 0, key_tiles_of(qt2, a.T), nullptr, nullptr);
+    segment(qt2, 0, tiles2, nullptr, nullptr, pre ? 2 : 0);
     if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_own);
   }
+  if (deferred) merge_records(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
 }
 
 // ---- packed-document schedule: all (document, query tile) tasks, heaviest first
