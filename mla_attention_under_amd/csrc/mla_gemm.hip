@@ -176,8 +176,15 @@ __global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
   };
   issue(a0, b0, 0);
   if (nk > 1) issue(a1, b1, GK);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  // slice 0 has landed once only slice 1's transfers are left (the counter
+  // retires in issue order); slice 1 lands during slice 0's products
+  __builtin_amdgcn_sched_barrier(0);
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerSlice);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   int s = 0;
   for (; s + 2 < nk; s += 3) {
     step(s, a0, b0, a2, b2);

@@ -4,11 +4,14 @@
 //
 // Every (token, rank) pair moves one contiguous run of sizes[r]*row_bytes
 // bytes between x[t][off_r .. off_r+sizes[r]) and slab r's row t, so the copy
-// is a set of contiguous runs. HBM-bound: each thread moves UNROLL vector
-// chunks of the widest size (16, 8, 4 or 2 bytes) that divides the row, with
-// all loads issued before any store so that every wave keeps UNROLL requests
-// in flight. Indexing is over the slab side, so slab reads/writes are one
-// contiguous stream per rank and the x side is a contiguous run per token.
+// is a set of contiguous runs. HBM-bound: each thread moves kUnroll vector
+// chunks of the widest size (16, 8, 4 or 2 bytes) that divides the row, all
+// loads issued before any store. Workgroups of 1024 threads moving one
+// 16-byte chunk each (16 KB) measured best on both the cache-resident rank
+// shard and the 940 MB uneven shard (256 threads x 4 chunks: 10-30 % slower
+// for the small unpack, 2-4 % for the large copies). Indexing is over the
+// slab side, so slab reads/writes are one contiguous stream per rank and the
+// x side is a contiguous run per token.
 #include <hip/hip_runtime.h>
 
 #include "mla_internal.h"
@@ -16,8 +19,8 @@
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kThreads = 1024;
+constexpr int kUnroll = 1;
 
 struct PackArgs {
   const unsigned char *src;
@@ -37,9 +40,14 @@ struct PackArgs {
 // one stretch of every slab, rather than one rank's column of every x row.
 // Streaming (nontemporal) stores for large outputs; small outputs (up to
 // kCachedStoreBytes) stay in the caches, which measured faster for them
-// (an 8.4 MB unpack: 5.3 -> 4.1 us) and slower for large ones.
+// (an 8.4 MB unpack: 5.3 -> 4.1 us) and slower for large ones. Likewise
+// streaming loads only for sources beyond kCachedLoadBytes: a source that
+// fits the 256 MB Infinity Cache is read through it (the 29.4 MB rank-shard
+// pack: 10.5 -> 7.7 us back to back), a larger one streams past it (the
+// 470 MB uneven shard pack is 5 % slower with ordinary loads).
 constexpr uint64_t kCachedStoreBytes = 16ull << 20;
-template <typename Chunk, typename Index, bool kStream>
+constexpr uint64_t kCachedLoadBytes = 64ull << 20;
+template <typename Chunk, typename Index, bool kStream, bool kStreamLoad>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   const int r = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.sp));
   const Index cb = static_cast<Index>(blockIdx.x / static_cast<unsigned>(a.sp));
@@ -66,7 +74,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     const Index si = slab_base + c;
     const Index sidx = a.to_slabs ? xi : si;
     didx[u] = a.to_slabs ? si : xi;
-    if (ok[u]) v[u] = __builtin_nontemporal_load(src + sidx);
+    if (ok[u]) {
+      if constexpr (kStreamLoad)
+        v[u] = __builtin_nontemporal_load(src + sidx);
+      else
+        v[u] = src[sidx];
+    }
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u)
@@ -101,13 +114,16 @@ hipError_t run(const PackPlan &p, hipStream_t s) {
   const uint64_t all = a.tokens * static_cast<uint64_t>(p.heads_total) * a.row_chunks;
   const dim3 grid(static_cast<unsigned>(blocks * static_cast<uint64_t>(p.sp)));
   const bool stream = all * sizeof(Chunk) > kCachedStoreBytes;
+  const bool stream_load = all * sizeof(Chunk) > kCachedLoadBytes;
   const bool narrow = all + kThreads * kUnroll < 0xffffffffULL;
-  if (narrow && stream)
-    hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t, true>), grid, dim3(kThreads), 0, s, a);
+  if (narrow && stream_load)
+    hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t, true, true>), grid, dim3(kThreads), 0, s, a);
+  else if (narrow && stream)
+    hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t, true, false>), grid, dim3(kThreads), 0, s, a);
   else if (narrow)
-    hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((pack_kernel<Chunk, uint32_t, false, false>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((pack_kernel<Chunk, uint64_t, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((pack_kernel<Chunk, uint64_t, true, true>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
