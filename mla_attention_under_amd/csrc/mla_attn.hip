@@ -313,8 +313,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   doc_lo = __builtin_amdgcn_readfirstlane(doc_lo);
   doc_hi = __builtin_amdgcn_readfirstlane(doc_hi);
 
-  // ---- zero the stages once: loads past the buffer range may leave LDS untouched
-  {
+  // ---- zero the stages once: loads past the buffer range may leave LDS
+  // untouched, and a masked key's zero probability must not meet a stale
+  // NaN. Only a partial key tile reads past the range: with dense tiles and
+  // T a multiple of the key tile every tile is whole (a query tile's causal
+  // key range ends at a multiple of BM or at T).
+  if (a.tasks != nullptr || a.T % BN != 0) {
     u32x4 z{0, 0, 0, 0};
     for (int i = tid; i < (KN_E + KR_E) / 8; i += 64 * NW) {
       reinterpret_cast<u32x4 *>(kb0)[i] = z;

@@ -148,7 +148,7 @@ def test_attention_tiny_fp32(T):
     check_close(lse, rlse, bf16=False, name=f"tiny lse T={T}")
 
 
-@pytest.mark.parametrize("T,H", [(2048, 16), (1, 2), (63, 2), (200, 3), (1000, 2), (4097, 1)])
+@pytest.mark.parametrize("T,H", [(2048, 16), (1, 2), (63, 2), (192, 2), (200, 3), (1000, 2), (2112, 3), (4097, 1)])
 def test_attention_dense_causal(T, H):
     w = mi.WORKLOADS["dsv3_rank"]
     w = mi.Workload(w.name, w.cfg, T=T, H=H, L=w.L, N=w.N, R=w.R, V=w.V, heads_total=H)
