@@ -28,6 +28,14 @@ NumPy float64, with no blocking or fusion beyond what that definition states:
                            (documents as cumulative ends).
 * split-KV decode       -- DeepSpeed PR #8602, "Components" table (decode
                            attention with KV split-K and an online softmax).
+* expanded pack         -- hyper-parallel ``_expanded`` (one sequence-to-head
+                           exchange of concat(q, k, v) with unequal widths, the
+                           key assembled by ``_assemble_key_value``).
+* query partition and   -- hyper-parallel ``_causal_partition`` and
+  KV exchange ranges       ``_kv_exchange_ranges`` (document-local causal
+                           prefixes of a rank's contiguous query range; the key
+                           interval each rank sends to and receives from every
+                           peer).
 
 Readings where the pages are silent (each also listed in the design doc):
 the scale is an explicit argument; key j is visible to query t iff j <= t in the
@@ -48,6 +56,7 @@ __all__ = [
     "pack_heads", "unpack_heads", "latent_up_proj", "attention_probs",
     "attention", "decode_split_kv", "decode_reference", "doc_bounds",
     "ulysses_materialise_k_first", "ulysses_latent_first",
+    "pack_expanded", "causal_partition", "kv_exchange_ranges",
 ]
 
 
@@ -339,3 +348,94 @@ def ulysses_latent_first(latent, w_kvb, q, k_rope, sizes, N, V, scale):
         out, _ = attention(q[:, o:o + qr, :], kv, k_rope, N, scale, causal=True)
         outs.append(out)
     return outs
+
+
+# --------------------------------------------------------------------------
+# Expanded pack (hyper-parallel _expanded, key from _assemble_key_value)
+# --------------------------------------------------------------------------
+
+def pack_expanded(q: np.ndarray, kv: np.ndarray, k_rope: np.ndarray, N: int, sizes) -> np.ndarray:
+    """Send side of the expanded exchange: one payload row per (token, head),
+    [q (N+R) | k_nope (N) | k_rope (R) | v (V)], the shared RoPE key copied into
+    every head's key, then split into per-rank head slabs exactly as
+    ``pack_heads``.
+
+    q [T][H][N+R], kv [T][H][N+V] ([k_nope | v]), k_rope [T][R] -> flat send.
+    A pure permutation-with-copies of elements: dtypes are kept.
+    """
+    T, H, K = q.shape
+    assert kv.shape[:2] == (T, H) and k_rope.shape[0] == T
+    R = k_rope.shape[1]
+    assert K == N + R
+    key = np.concatenate([kv[:, :, :N], np.broadcast_to(k_rope[:, None, :], (T, H, R))], axis=2)
+    payload = np.concatenate([q, key, kv[:, :, N:]], axis=2)
+    return pack_heads(payload, sizes)
+
+
+# --------------------------------------------------------------------------
+# Query partition and KV exchange ranges (hyper-parallel _causal_partition,
+# _kv_exchange_ranges)
+# --------------------------------------------------------------------------
+
+def causal_partition(ends, query_length: int, query_rank: int, batch: int = 1) -> dict:
+    """The documents' causal prefixes needed by one rank's contiguous queries.
+
+    Documents are given by their cumulative ends. The rank owns global query
+    positions [query_rank*query_length, (query_rank+1)*query_length). For every
+    document [a, b) that overlaps that range in [s, e), the rank holds e-s
+    queries of the document, and those queries see the document's keys [a, e)
+    (causal, no look-ahead, document-local). The selected prefixes are
+    adjacent, so the keys form one range [key_begin, key_end) with key_end the
+    end of the query range. query_ends / key_ends are the cumulative per-
+    document query and key counts (variable-length offsets without the leading
+    0), repeated for each of ``batch`` sequences with the per-sequence totals
+    as strides. Raises ValueError when the documents do not cover the range.
+    """
+    q0, q1 = query_rank * query_length, (query_rank + 1) * query_length
+    parts = []
+    for a, b in doc_bounds(ends=ends):
+        s, e = max(a, q0), min(b, q1)
+        if s < e:
+            parts.append((a, s, e))
+    if sum(e - s for _, s, e in parts) != query_length:
+        raise ValueError("documents do not cover the query partition")
+    q_lens = [e - s for _, s, e in parts]
+    k_lens = [e - a for a, _, e in parts]
+    q_ends = list(np.cumsum(q_lens, dtype=np.int64))
+    k_ends = list(np.cumsum(k_lens, dtype=np.int64))
+    nq, nk = int(sum(q_lens)), int(sum(k_lens))
+    return {
+        "key_begin": int(parts[0][0]),
+        "key_end": int(q1),
+        "query_ends": [int(x) + i * nq for i in range(batch) for x in q_ends],
+        "key_ends": [int(x) + i * nk for i in range(batch) for x in k_ends],
+        "documents": tuple(int(x) for x in ends),
+    }
+
+
+def kv_exchange_ranges(ends, source_length: int, query_length: int, head_copies: int, degree: int, rank: int):
+    """Which key tokens rank ``rank`` sends to and receives from every peer.
+
+    Rank p holds the source tokens [p*source_length, (p+1)*source_length) and
+    owns the queries of query partition p // head_copies (head_copies ranks
+    share one query range). A rank sends to peer p the part of its source
+    range inside p's key range (as (offset in its source range, count)), and
+    receives from peer p the part of p's source range inside its own key
+    range (a count). local_only: every rank's key range lies inside its own
+    source range, so nothing needs to move.
+    """
+    dest = [causal_partition(ends, query_length, p // head_copies, 1) for p in range(degree)]
+
+    def overlap(a0, a1, b0, b1):
+        return max(a0, b0), min(a1, b1)
+
+    s0, s1 = rank * source_length, (rank + 1) * source_length
+    sends, receives = [], []
+    for p in range(degree):
+        b, e = overlap(s0, s1, dest[p]["key_begin"], dest[p]["key_end"])
+        sends.append((b - s0, e - b) if b < e else (0, 0))
+        b, e = overlap(p * source_length, (p + 1) * source_length, dest[rank]["key_begin"], dest[rank]["key_end"])
+        receives.append(max(0, e - b))
+    local_only = all(p * source_length <= d["key_begin"] and d["key_end"] <= (p + 1) * source_length
+                     for p, d in enumerate(dest))
+    return tuple(sends), tuple(receives), local_only

@@ -147,3 +147,47 @@ def test_split_combine_without_rescale_is_caught(monkeypatch):
         return out, (m, l, o)
     _patch(monkeypatch, "decode_split_kv", bad)
     assert _fails(tn.test_split_kv_equals_direct_softmax, 3)
+
+
+# ---- query partition, exchange ranges and the expanded pack
+
+import test_oracle_partition as tp  # noqa: E402
+
+
+def _partition_pins_fail():
+    pins = [lambda: tp.test_causal_partition_matches_brute_force(s) for s in range(4)]
+    pins.append(tp.test_causal_partition_packed_workload)
+    return any(_fails(p) for p in pins)
+
+
+def test_partition_counting_keys_from_the_query_start_is_caught(monkeypatch):
+    # keys counted from the first owned query instead of the document start
+    real = om.causal_partition
+
+    def bad(ends, query_length, query_rank, batch=1):
+        out = real(ends, query_length, query_rank, batch)
+        out["key_ends"] = list(out["query_ends"])
+        return out
+    _patch(monkeypatch, "causal_partition", bad)
+    assert _partition_pins_fail()
+
+
+def test_exchange_receiving_against_the_peer_range_is_caught(monkeypatch):
+    # receives measured against the peer's key range instead of this rank's
+    real = om.kv_exchange_ranges
+
+    def bad(ends, source_length, query_length, head_copies, degree, rank):
+        sends, _, local = real(ends, source_length, query_length, head_copies, degree, rank)
+        return sends, tuple(c for _, c in sends), local
+    _patch(monkeypatch, "kv_exchange_ranges", bad)
+    assert any(_fails(lambda: tp.test_kv_exchange_ranges_match_brute_force_and_pair_up(s)) for s in range(6))
+
+
+def test_expanded_pack_with_rope_before_nope_is_caught(monkeypatch):
+    def bad(q, kv, k_rope, N, sizes):
+        T, H, _ = q.shape
+        R = k_rope.shape[1]
+        key = np.concatenate([np.broadcast_to(k_rope[:, None, :], (T, H, R)), kv[:, :, :N]], axis=2)
+        return om.pack_heads(np.concatenate([q, key, kv[:, :, N:]], axis=2), sizes)
+    _patch(monkeypatch, "pack_expanded", bad)
+    assert _fails(tp.test_pack_expanded_index_loops) and _fails(tp.test_pack_expanded_key_band_is_the_attention_key)
