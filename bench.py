@@ -115,6 +115,40 @@ def _median_us(torch, fn, reps, before=None):
     return ts[len(ts) // 2]
 
 
+def _expanded(torch, mla):
+    """Expanded pack ([q | k_nope | k_rope | v] per head -> head slabs), back-to-back event timing.
+    Bytes = q + kv + one k_rope row per token read, payload written."""
+    out = {}
+    for name, tokens, sizes in (("uneven22", 4096, [22, 22, 21, 21, 21, 21]), ("dsv3_rank", 256, [16] * 8)):
+        Ht, N, R, V = sum(sizes), 128, 64, 128
+        g = torch.Generator(device="cuda").manual_seed(5)
+        q = torch.randint(-32768, 32767, (tokens, Ht, N + R), dtype=torch.int16, device="cuda", generator=g)
+        kv = torch.randint(-32768, 32767, (tokens, Ht, N + V), dtype=torch.int16, device="cuda", generator=g)
+        kr = torch.randint(-32768, 32767, (tokens, R), dtype=torch.int16, device="cuda", generator=g)
+        send = torch.empty(tokens * Ht * (2 * (N + R) + V), dtype=torch.int16, device="cuda")
+        reps = 20 if tokens > 1024 else 200
+        for _ in range(3):
+            mla.mla_pack_expanded(q, kv, kr, send, sizes, N)
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        _busy(torch, 10)
+        st.record()
+        for _ in range(reps):
+            mla.mla_pack_expanded(q, kv, kr, send, sizes, N)
+        en.record()
+        torch.cuda.synchronize()
+        us = st.elapsed_time(en) * 1e3 / reps
+        nbytes = 2.0 * (q.numel() + kv.numel() + kr.numel() + send.numel())
+        out[f"{name}_expanded_pack_us"] = round(us, 2)
+        out[f"{name}_expanded_pack_gbps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        if tokens > 1024:
+            out[f"{name}_expanded_pack_hbm_frac"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        del q, kv, kr, send
+    out["expanded_pack_note"] = ("payload [q | k_nope | k_rope | v] = 512 per head; uneven22 beyond the Infinity "
+                                 "Cache, dsv3_rank cache-resident")
+    return out
+
+
 def _varlen(torch, mla, mi, dev):
     """Packed documents 8192/4096/2048/2048 (T=16384, H=16): block-diagonal causal attention."""
     w = mi.WORKLOADS["varlen16k"]
@@ -307,6 +341,7 @@ def main():
         extra["uneven22_pack_us"] = round(pk * 1e3, 2)
         assert torch.equal(big_back, big), "uneven22 pack/unpack round trip failed"
         del big, big_send, big_back
+        extra.update(_expanded(torch, mla))
         extra.update(_varlen(torch, mla, mi, dev))
         extra.update(_decode(torch, mla, mi, dev))
 

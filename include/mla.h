@@ -79,6 +79,63 @@ int mla_pack_heads(const void *x, void *send, int64_t tokens, int heads_total, i
                    const int *sizes, int sp, int dtype, void *stream);
 
 /*
+ * Expanded token->head pack: the send side of one sequence-to-head exchange of
+ * unequal-width (q, k, v) per head (hyper-parallel mla_context_parallel.py,
+ * `_expanded`; the key is assembled as in `_assemble_key_value`, the shared
+ * RoPE key copied into every head). Per (token t, head h) the payload row is
+ *     [ q[t][h][0:N+R] | kv[t][h][0:N] | k_rope[t][0:R] | kv[t][h][N:N+V] ]
+ * of width W = 2(N+R)+V, split into per-rank head slabs as mla_pack_heads does:
+ *   q      : [tokens][heads_total][N+R]
+ *   kv     : [tokens][heads_total][N+V]   (row [k_nope | v])
+ *   k_rope : [tokens][R]                  (one row per token, all heads)
+ *   send   : concat_r [tokens][sizes[r]][W]
+ * All contiguous. sizes: HOST array of sp positive ints summing to heads_total.
+ * Bit-exact copy (dtype fixes the element size only); N, R, V >= 1; send must
+ * not overlap any source. tokens == 0 is a valid no-op. sp <= 256.
+ */
+int mla_pack_expanded(const void *q, const void *kv, const void *k_rope, void *send, int64_t tokens,
+                      int heads_total, int N, int R, int V, const int *sizes, int sp, int dtype, void *stream);
+
+/*
+ * Query partition (host only, no GPU use): hyper-parallel `_causal_partition`.
+ * Documents are given by their cumulative ends doc_ends[0..n_docs) (non-
+ * negative, non-decreasing; empty documents allowed). The rank owns the query
+ * positions [query_rank*query_length, (query_rank+1)*query_length). Each
+ * document [a, b) overlapping that range in [s, e) contributes e-s queries,
+ * which see the document's keys [a, e) (causal, document-local). The selected
+ * key prefixes are adjacent:
+ *   *key_begin = start of the first overlapping document, *key_end = end of the
+ *   query range;
+ *   query_ends / key_ends = cumulative per-document query / key counts (no
+ *   leading 0), repeated for each of `batch` sequences with the per-sequence
+ *   totals as strides; *n_out = batch * (number of overlapping documents).
+ * cap: capacity of query_ends and key_ends, in entries. Fails with MLA_EINVAL,
+ * writing nothing, if the documents do not cover the query range or cap is
+ * too small (the message gives the count needed).
+ */
+int mla_causal_partition(const int64_t *doc_ends, int n_docs, int64_t query_length, int query_rank, int batch,
+                         int64_t *key_begin, int64_t *key_end, int64_t *query_ends, int64_t *key_ends, int cap,
+                         int *n_out);
+
+/*
+ * KV exchange ranges (host only): hyper-parallel `_kv_exchange_ranges`. Rank p
+ * holds the source tokens [p*source_length, (p+1)*source_length) and owns the
+ * queries of partition p / head_copies (mla_causal_partition with batch 1).
+ * For every peer p of the `degree` ranks, rank `rank`
+ *   sends send_count[p] tokens starting at offset send_offset[p] of its source
+ *   range: the part of its source range inside p's key range (0, 0 if none);
+ *   receives recv_count[p] tokens: the part of p's source range inside its own
+ *   key range.
+ * *local_only = 1 when every rank's key range lies inside its own source
+ * range (nothing needs to move), else 0. Output arrays hold `degree` entries.
+ * Fails with MLA_EINVAL (nothing written) on an invalid argument or when some
+ * rank's queries are not covered by the documents.
+ */
+int mla_kv_exchange_ranges(const int64_t *doc_ends, int n_docs, int64_t source_length, int64_t query_length,
+                           int head_copies, int degree, int rank, int64_t *send_offset, int64_t *send_count,
+                           int64_t *recv_count, int *local_only);
+
+/*
  * Head->token unpack: the exact inverse of mla_pack_heads (the receive side of
  * the head->token exchange of the attention output, torchtitan "Ulysses CP"
  * `all_to_all_head_to_token(out_THV)`; hyper-parallel `restore_output`).

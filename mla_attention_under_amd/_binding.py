@@ -23,6 +23,7 @@ EXPORTS = (
     "mla_last_error", "mla_version", "mla_head_shard_sizes", "mla_pack_heads", "mla_unpack_heads",
     "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
+    "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges",
 )
 
 
@@ -75,6 +76,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in (lib.mla_pack_heads, lib.mla_unpack_heads):
         fn.argtypes = [vp, vp, i64, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
     lib.mla_latent_up_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.mla_pack_expanded.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
+    p64 = ctypes.POINTER(i64)
+    lib.mla_causal_partition.argtypes = [p64, i32, i64, i32, i32, p64, p64, p64, p64, i32, ctypes.POINTER(i32)]
+    lib.mla_kv_exchange_ranges.argtypes = [p64, i32, i64, i64, i32, i32, i32, p64, p64, p64, ctypes.POINTER(i32)]
     lib.mla_attention_workspace_size.argtypes = [ctypes.POINTER(mla_attn_args)]
     lib.mla_attention_workspace_size.restype = sz
     lib.mla_attention_fwd.argtypes = [ctypes.POINTER(mla_attn_args), vp]
@@ -165,6 +170,53 @@ def mla_unpack_heads(recv, x, sizes, stream=None):
     assert x.is_contiguous() and recv.is_contiguous() and x.dim() == 3 and recv.numel() == x.numel()
     T, Ht, F = x.shape
     return _pack("mla_unpack_heads", recv, x, sizes, T, Ht, F, stream)
+
+
+def mla_pack_expanded(q, kv, k_rope, send, sizes, N, stream=None):
+    """q [T][Ht][N+R], kv [T][Ht][N+V], k_rope [T][R] -> send (flat, concat_r [T][sizes[r]][2(N+R)+V])."""
+    lib = load_library()
+    _dev(q, kv, k_rope, send)
+    assert all(t.is_contiguous() for t in (q, kv, k_rope, send))
+    T, Ht, K = q.shape
+    R = k_rope.shape[1]
+    V = kv.shape[2] - N
+    assert kv.shape[:2] == (T, Ht) and k_rope.shape[0] == T and K == N + R
+    assert send.numel() == T * Ht * (2 * K + V)
+    if len({t.element_size() for t in (q, kv, k_rope, send)}) != 1:
+        raise ValueError("all buffers must have one element size")
+    dt = {2: MLA_BF16, 4: MLA_F32}[q.element_size()]
+    arr = (ctypes.c_int * len(sizes))(*sizes)
+    _check("mla_pack_expanded", lib.mla_pack_expanded(_ptr(q), _ptr(kv), _ptr(k_rope), _ptr(send), T, Ht, N, R, V,
+                                                       arr, len(sizes), dt, _stream(stream)))
+    return send
+
+
+def _i64s(xs):
+    return (ctypes.c_int64 * max(len(xs), 1))(*[int(x) for x in xs])
+
+
+def mla_causal_partition(doc_ends, query_length, query_rank, batch=1):
+    """Host interval algebra: dict(key_begin, key_end, query_ends, key_ends)."""
+    lib = load_library()
+    cap = batch * len(doc_ends)
+    kb, ke, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    qe, kend = (ctypes.c_int64 * max(cap, 1))(), (ctypes.c_int64 * max(cap, 1))()
+    _check("mla_causal_partition", lib.mla_causal_partition(
+        _i64s(doc_ends), len(doc_ends), query_length, query_rank, batch, ctypes.byref(kb), ctypes.byref(ke), qe, kend,
+        cap, ctypes.byref(n)))
+    return {"key_begin": kb.value, "key_end": ke.value, "query_ends": list(qe)[:n.value],
+            "key_ends": list(kend)[:n.value]}
+
+
+def mla_kv_exchange_ranges(doc_ends, source_length, query_length, head_copies, degree, rank):
+    """Host interval algebra: (((offset, count) sent to each peer), (count received from each peer), local_only)."""
+    lib = load_library()
+    so, sc, rc = (ctypes.c_int64 * degree)(), (ctypes.c_int64 * degree)(), (ctypes.c_int64 * degree)()
+    local = ctypes.c_int()
+    _check("mla_kv_exchange_ranges", lib.mla_kv_exchange_ranges(
+        _i64s(doc_ends), len(doc_ends), source_length, query_length, head_copies, degree, rank, so, sc, rc,
+        ctypes.byref(local)))
+    return tuple(zip(list(so), list(sc))), tuple(rc), bool(local.value)
 
 
 def mla_latent_up_proj(latent, w_kvb, kv_out, heads_total, head_begin, heads, N, V, stream=None):

@@ -10,7 +10,10 @@
 #include <cstdio>
 #include <cstring>
 #include <random>
+#include <algorithm>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/mla.h"
 #include "mla_internal.h"
@@ -129,6 +132,150 @@ int mla_pack_heads(const void *x, void *send, int64_t tokens, int heads_total, i
 int mla_unpack_heads(const void *recv, void *x, int64_t tokens, int heads_total, int feat, const int *sizes,
                      int sp, int dtype, void *stream) {
   return pack_common(recv, x, tokens, heads_total, feat, sizes, sp, dtype, stream, 0, "mla_unpack_heads");
+}
+
+int mla_pack_expanded(const void *q, const void *kv, const void *k_rope, void *send, int64_t tokens, int heads_total,
+                      int N, int R, int V, const int *sizes, int sp, int dtype, void *stream) {
+  const char *who = "mla_pack_expanded";
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (tokens < 0 || heads_total < 1 || N < 1 || R < 1 || V < 1)
+    return fail(MLA_EINVAL, "%s: need tokens >= 0, heads_total, N, R, V >= 1 (got %lld, %d, %d, %d, %d)", who,
+                static_cast<long long>(tokens), heads_total, N, R, V);
+  mla::PackExpandedPlan p;
+  const int rc = shard_offsets(sizes, sp, heads_total, p.off, who);
+  if (rc != MLA_OK) return rc;
+  if (tokens == 0) return ok();
+  if (q == nullptr || kv == nullptr || k_rope == nullptr || send == nullptr)
+    return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const int64_t eb = elem_bytes(dtype);
+  const uint64_t th = static_cast<uint64_t>(tokens) * heads_total;
+  const uint64_t q_bytes = th * (N + R) * eb, kv_bytes = th * (N + V) * eb;
+  const uint64_t kr_bytes = static_cast<uint64_t>(tokens) * R * eb, out_bytes = th * (2 * (N + R) + V) * eb;
+  const uintptr_t pq = reinterpret_cast<uintptr_t>(q), pkv = reinterpret_cast<uintptr_t>(kv),
+                  pkr = reinterpret_cast<uintptr_t>(k_rope), po = reinterpret_cast<uintptr_t>(send);
+  if ((pq | pkv | pkr | po) % eb) return fail(MLA_EINVAL, "%s: buffers must be aligned to the element size", who);
+  auto overlaps = [&](uintptr_t a, uint64_t na) { return a < po + out_bytes && po < a + na; };
+  if (overlaps(pq, q_bytes) || overlaps(pkv, kv_bytes) || overlaps(pkr, kr_bytes))
+    return fail(MLA_EINVAL, "%s: send overlaps a source", who);
+  p.q = q;
+  p.kv = kv;
+  p.kr = k_rope;
+  p.dst = send;
+  p.tokens = tokens;
+  p.heads_total = heads_total;
+  p.n_bytes = N * eb;
+  p.r_bytes = R * eb;
+  p.v_bytes = V * eb;
+  p.sp = sp;
+  return launched(mla::launch_pack_expanded(p, stream), who);
+}
+
+namespace {
+// documents as [start, end) from cumulative ends; checks them
+int doc_ranges(const int64_t *ends, int n, std::vector<std::pair<int64_t, int64_t>> &docs, const char *who) {
+  if (ends == nullptr || n < 1) return fail(MLA_EINVAL, "%s: need at least one document end", who);
+  int64_t prev = 0;
+  docs.clear();
+  for (int i = 0; i < n; ++i) {
+    if (ends[i] < prev) return fail(MLA_EINVAL, "%s: document ends must be non-negative and non-decreasing", who);
+    docs.emplace_back(prev, ends[i]);
+    prev = ends[i];
+  }
+  return MLA_OK;
+}
+
+struct Partition {
+  int64_t key_begin = 0, key_end = 0;
+  std::vector<int64_t> q_ends, k_ends;   // one sequence, cumulative
+};
+
+// the documents' causal prefixes seen by the queries [rank*len, (rank+1)*len)
+int partition_of(const std::vector<std::pair<int64_t, int64_t>> &docs, int64_t len, int64_t rank, Partition &out,
+                 const char *who) {
+  const int64_t q0 = rank * len, q1 = q0 + len;
+  int64_t nq = 0, nk = 0;
+  bool first = true;
+  out.q_ends.clear();
+  out.k_ends.clear();
+  for (const auto &d : docs) {
+    const int64_t s = std::max(d.first, q0), e = std::min(d.second, q1);
+    if (s >= e) continue;
+    if (first) out.key_begin = d.first;
+    first = false;
+    nq += e - s;
+    nk += e - d.first;
+    out.q_ends.push_back(nq);
+    out.k_ends.push_back(nk);
+  }
+  if (nq != len)
+    return fail(MLA_EINVAL, "%s: the documents do not cover the queries [%lld, %lld)", who,
+                static_cast<long long>(q0), static_cast<long long>(q1));
+  out.key_end = q1;
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_causal_partition(const int64_t *doc_ends, int n_docs, int64_t query_length, int query_rank, int batch,
+                         int64_t *key_begin, int64_t *key_end, int64_t *query_ends, int64_t *key_ends, int cap,
+                         int *n_out) {
+  const char *who = "mla_causal_partition";
+  if (query_length < 1 || query_rank < 0 || batch < 1)
+    return fail(MLA_EINVAL, "%s: need query_length >= 1, query_rank >= 0, batch >= 1", who);
+  if (query_rank > INT64_MAX / query_length - 1) return fail(MLA_EINVAL, "%s: query range overflows", who);
+  if (key_begin == nullptr || key_end == nullptr || query_ends == nullptr || key_ends == nullptr || n_out == nullptr)
+    return fail(MLA_EINVAL, "%s: NULL output", who);
+  std::vector<std::pair<int64_t, int64_t>> docs;
+  int rc = doc_ranges(doc_ends, n_docs, docs, who);
+  if (rc != MLA_OK) return rc;
+  Partition p;
+  rc = partition_of(docs, query_length, query_rank, p, who);
+  if (rc != MLA_OK) return rc;
+  const int64_t m = static_cast<int64_t>(p.q_ends.size());
+  if (m * batch > cap)
+    return fail(MLA_EINVAL, "%s: %lld output entries needed, capacity %d", who, static_cast<long long>(m * batch),
+                cap);
+  for (int i = 0; i < batch; ++i)
+    for (int64_t j = 0; j < m; ++j) {
+      query_ends[i * m + j] = p.q_ends[j] + i * p.q_ends.back();
+      key_ends[i * m + j] = p.k_ends[j] + i * p.k_ends.back();
+    }
+  *key_begin = p.key_begin;
+  *key_end = p.key_end;
+  *n_out = static_cast<int>(m * batch);
+  return ok();
+}
+
+int mla_kv_exchange_ranges(const int64_t *doc_ends, int n_docs, int64_t source_length, int64_t query_length,
+                           int head_copies, int degree, int rank, int64_t *send_offset, int64_t *send_count,
+                           int64_t *recv_count, int *local_only) {
+  const char *who = "mla_kv_exchange_ranges";
+  if (source_length < 0 || query_length < 1 || head_copies < 1 || degree < 1 || rank < 0 || rank >= degree)
+    return fail(MLA_EINVAL, "%s: need source_length >= 0, query_length >= 1, head_copies >= 1, 0 <= rank < degree",
+                who);
+  if (source_length > 0 && degree > INT64_MAX / source_length) return fail(MLA_EINVAL, "%s: ranges overflow", who);
+  if (send_offset == nullptr || send_count == nullptr || recv_count == nullptr || local_only == nullptr)
+    return fail(MLA_EINVAL, "%s: NULL output", who);
+  std::vector<std::pair<int64_t, int64_t>> docs;
+  int rc = doc_ranges(doc_ends, n_docs, docs, who);
+  if (rc != MLA_OK) return rc;
+  std::vector<Partition> dest(degree);
+  for (int p = 0; p < degree; ++p) {
+    rc = partition_of(docs, query_length, p / head_copies, dest[p], who);
+    if (rc != MLA_OK) return rc;
+  }
+  const int64_t s0 = rank * source_length, s1 = s0 + source_length;
+  bool local = true;
+  for (int p = 0; p < degree; ++p) {
+    const int64_t b = std::max(s0, dest[p].key_begin), e = std::min(s1, dest[p].key_end);
+    send_offset[p] = b < e ? b - s0 : 0;
+    send_count[p] = b < e ? e - b : 0;
+    const int64_t rb = std::max(p * source_length, dest[rank].key_begin);
+    const int64_t re = std::min((p + 1) * source_length, dest[rank].key_end);
+    recv_count[p] = std::max<int64_t>(0, re - rb);
+    local = local && p * source_length <= dest[p].key_begin && dest[p].key_end <= (p + 1) * source_length;
+  }
+  *local_only = local ? 1 : 0;
+  return ok();
 }
 
 int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int64_t T, int L, int heads_total,

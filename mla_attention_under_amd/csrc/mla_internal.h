@@ -22,6 +22,20 @@ struct PackPlan {
 };
 int launch_pack(const PackPlan &p, void *stream);
 
+// ---- expanded pack: per (token, head) row [q | k_nope | k_rope | v] -> head slabs
+struct PackExpandedPlan {
+  const void *q;        // [tokens][heads_total][N+R]
+  const void *kv;       // [tokens][heads_total][N+V]
+  const void *kr;       // [tokens][R]
+  void *dst;            // concat_r [tokens][sizes[r]][2(N+R)+V]
+  int64_t tokens;
+  int heads_total;
+  int64_t n_bytes, r_bytes, v_bytes;   // N, R, V in bytes
+  int sp;
+  int off[kMaxRanks + 1];
+};
+int launch_pack_expanded(const PackExpandedPlan &p, void *stream);
+
 // ---- latent up-projection -------------------------------------------------
 struct UpProjPlan {
   const void *latent;  // [T][L]

@@ -127,6 +127,93 @@ hipError_t run(const PackPlan &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- expanded pack (hyper-parallel `_expanded`): payload row per (token,
+// head) [q (K) | k_nope (N) | k_rope (R) | v (V)], K = N + R, the shared RoPE
+// key copied into every head. Indexing is over the slab side, one chunk per
+// thread; every chunk comes from exactly one source segment (the chunk width
+// divides every segment's width). q and kv stream like the plain pack; the
+// k_rope row of a token is read once per head and stays in the caches.
+struct PackExpArgs {
+  const unsigned char *q, *kv, *kr;
+  unsigned char *dst;
+  uint32_t heads_total;
+  uint32_t nc, rc, vc;   // N, R, V in chunks
+  uint64_t tokens;
+  int sp;
+  int off[kMaxRanks + 1];
+};
+
+template <typename Chunk, typename Index, bool kStream>
+__global__ __launch_bounds__(kThreads) void pack_expanded_kernel(PackExpArgs a) {
+  const int r = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.sp));
+  const Index cb = static_cast<Index>(blockIdx.x / static_cast<unsigned>(a.sp));
+  const Index kc = a.nc + a.rc, pc = a.nc + a.vc, wc = 2 * kc + a.vc;   // chunks per q / kv / payload row
+  const Index qr = static_cast<Index>(a.off[r + 1] - a.off[r]);
+  const Index per_tok = qr * wc;
+  const Index total = static_cast<Index>(a.tokens) * per_tok;
+  const Index c = cb * kThreads + threadIdx.x;
+  if (c >= total) return;
+  const Index t = c / per_tok;
+  const Index rem = c - t * per_tok;
+  const Index hh = rem / wc;
+  const Index f = rem - hh * wc;
+  const Index row = t * static_cast<Index>(a.heads_total) + static_cast<Index>(a.off[r]) + hh;
+  const Chunk *q = reinterpret_cast<const Chunk *>(a.q);
+  const Chunk *kv = reinterpret_cast<const Chunk *>(a.kv);
+  const Chunk *kr = reinterpret_cast<const Chunk *>(a.kr);
+  Chunk v;
+  if (f < kc) {
+    v = kStream ? __builtin_nontemporal_load(q + row * kc + f) : q[row * kc + f];
+  } else if (f < kc + a.nc) {
+    const Index i = row * pc + (f - kc);
+    v = kStream ? __builtin_nontemporal_load(kv + i) : kv[i];
+  } else if (f < 2 * kc) {
+    v = kr[t * a.rc + (f - kc - a.nc)];
+  } else {
+    const Index i = row * pc + a.nc + (f - 2 * kc);
+    v = kStream ? __builtin_nontemporal_load(kv + i) : kv[i];
+  }
+  Chunk *dst = reinterpret_cast<Chunk *>(a.dst) + static_cast<Index>(a.tokens) * static_cast<Index>(a.off[r]) * wc + c;
+  if constexpr (kStream)
+    __builtin_nontemporal_store(v, dst);
+  else
+    *dst = v;
+}
+
+template <typename Chunk>
+hipError_t run_expanded(const PackExpandedPlan &p, hipStream_t s) {
+  PackExpArgs a;
+  a.q = static_cast<const unsigned char *>(p.q);
+  a.kv = static_cast<const unsigned char *>(p.kv);
+  a.kr = static_cast<const unsigned char *>(p.kr);
+  a.dst = static_cast<unsigned char *>(p.dst);
+  a.heads_total = static_cast<uint32_t>(p.heads_total);
+  a.nc = static_cast<uint32_t>(p.n_bytes / sizeof(Chunk));
+  a.rc = static_cast<uint32_t>(p.r_bytes / sizeof(Chunk));
+  a.vc = static_cast<uint32_t>(p.v_bytes / sizeof(Chunk));
+  a.tokens = static_cast<uint64_t>(p.tokens);
+  a.sp = p.sp;
+  int maxq = 0;
+  for (int r = 0; r <= p.sp; ++r) a.off[r] = p.off[r];
+  for (int r = 0; r < p.sp; ++r) maxq = maxq > (p.off[r + 1] - p.off[r]) ? maxq : (p.off[r + 1] - p.off[r]);
+  const uint64_t wc = 2ull * (a.nc + a.rc) + a.vc;
+  const uint64_t per_rank = a.tokens * static_cast<uint64_t>(maxq) * wc;
+  const uint64_t blocks = (per_rank + kThreads - 1) / kThreads;
+  if (blocks == 0) return hipSuccess;
+  if (blocks * static_cast<uint64_t>(p.sp) > 0x7fffffffULL) return hipErrorInvalidConfiguration;
+  const uint64_t all = a.tokens * static_cast<uint64_t>(p.heads_total) * wc;   // output chunks
+  const bool stream = all * sizeof(Chunk) > kCachedStoreBytes;
+  const bool narrow = all + kThreads < 0xffffffffULL;
+  const dim3 grid(static_cast<unsigned>(blocks * static_cast<uint64_t>(p.sp)));
+  if (narrow && stream)
+    hipLaunchKernelGGL((pack_expanded_kernel<Chunk, uint32_t, true>), grid, dim3(kThreads), 0, s, a);
+  else if (narrow)
+    hipLaunchKernelGGL((pack_expanded_kernel<Chunk, uint32_t, false>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((pack_expanded_kernel<Chunk, uint64_t, true>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int launch_pack(const PackPlan &p, void *stream) {
@@ -137,6 +224,17 @@ int launch_pack(const PackPlan &p, void *stream) {
   if (fits(8)) return run<u32x2>(p, s);
   if (fits(4)) return run<unsigned int>(p, s);
   return run<unsigned short>(p, s);
+}
+
+int launch_pack_expanded(const PackExpandedPlan &p, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uintptr_t align = reinterpret_cast<uintptr_t>(p.q) | reinterpret_cast<uintptr_t>(p.kv) |
+                          reinterpret_cast<uintptr_t>(p.kr) | reinterpret_cast<uintptr_t>(p.dst);
+  auto fits = [&](int64_t g) { return p.n_bytes % g == 0 && p.r_bytes % g == 0 && p.v_bytes % g == 0 && align % g == 0; };
+  if (fits(16)) return run_expanded<u32x4>(p, s);
+  if (fits(8)) return run_expanded<u32x2>(p, s);
+  if (fits(4)) return run_expanded<unsigned int>(p, s);
+  return run_expanded<unsigned short>(p, s);
 }
 
 const char *hip_error_name(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }

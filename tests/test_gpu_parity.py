@@ -70,6 +70,36 @@ def test_pack_unpack_bit_exact(name, tokens, sizes, feat, eb):
     assert np.array_equal(bits(back), x), name
 
 
+EXP_CASES = [
+    # (name, tokens, sizes, N, R, V, elem_bytes)
+    ("dsv3_rank_expanded", 256, [16] * 8, 128, 64, 128, 2),
+    ("uneven22_expanded", 4096, [22, 22, 21, 21, 21, 21], 128, 64, 128, 2),
+    ("tiny_fp32_expanded", 64, [3, 1], 16, 8, 16, 4),
+    ("ragged_2byte_widths", 7, [2, 3], 5, 3, 7, 2),
+    ("ragged_4byte_widths", 5, [1, 2], 2, 2, 4, 2),
+    ("one_token_one_head", 1, [1], 8, 8, 8, 2),
+]
+
+
+@pytest.mark.parametrize("name,tokens,sizes,N,R,V,eb", EXP_CASES, ids=[c[0] for c in EXP_CASES])
+def test_pack_expanded_bit_exact(name, tokens, sizes, N, R, V, eb):
+    Ht = sum(sizes)
+    rng = np.random.default_rng(17)
+    npdt = np.uint16 if eb == 2 else np.uint32
+    tdt = torch.int16 if eb == 2 else torch.int32
+    sdt = np.int16 if eb == 2 else np.int32
+    q = rng.integers(0, 1 << (8 * eb), size=(tokens, Ht, N + R), dtype=np.uint64).astype(npdt)
+    kv = rng.integers(0, 1 << (8 * eb), size=(tokens, Ht, N + V), dtype=np.uint64).astype(npdt)
+    kr = rng.integers(0, 1 << (8 * eb), size=(tokens, R), dtype=np.uint64).astype(npdt)
+    to = lambda a: torch.from_numpy(a.view(sdt)).cuda()
+    send = torch.empty(tokens * Ht * (2 * (N + R) + V), dtype=tdt, device="cuda")
+    mla.mla_pack_expanded(to(q), to(kv), to(kr), send, sizes, N)
+    _sync()
+    got = send.cpu().numpy().view(npdt)
+    exp = oracle.pack_expanded(q, kv, kr, N, sizes)
+    assert np.array_equal(got, exp), name
+
+
 def test_pack_zero_tokens_is_a_no_op():
     x = torch.zeros((0, 4, 8), dtype=torch.int16, device="cuda")
     send = torch.zeros(0, dtype=torch.int16, device="cuda")

@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -203,3 +204,76 @@ def test_decode_validation_before_launch(lib):
     assert f(num_splits=257) == mla.MLA_EUNSUPPORTED
     assert f(B=0) == mla.MLA_OK
     assert lib.mla_latent_decode_workspace_size(ctypes.byref(args())) > 0
+
+
+# ---- expanded pack validation, and the host interval algebra against the oracle
+
+def _pack_exp(lib, tokens, Ht, N, R, V, sizes, dtype=mla.MLA_BF16, q=FAKE, kv=FAKE2, kr=FAKE2, send=None):
+    arr = (ctypes.c_int * len(sizes))(*sizes) if sizes is not None else None
+    send = send if send is not None else ctypes.c_void_p(0x7f0000000000)
+    return lib.mla_pack_expanded(q, kv, kr, send, tokens, Ht, N, R, V, arr, len(sizes or [1]), dtype, None)
+
+
+def test_pack_expanded_validation_before_launch(lib):
+    assert _pack_exp(lib, 4, 5, 8, 4, 8, [3, 1]) == mla.MLA_EINVAL      # sizes do not sum to heads_total
+    assert _pack_exp(lib, 4, 4, 0, 4, 8, [2, 2]) == mla.MLA_EINVAL      # N < 1
+    assert _pack_exp(lib, 4, 4, 8, 0, 8, [2, 2]) == mla.MLA_EINVAL      # R < 1
+    assert _pack_exp(lib, 4, 4, 8, 4, 0, [2, 2]) == mla.MLA_EINVAL      # V < 1
+    assert _pack_exp(lib, 4, 4, 8, 4, 8, [2, 2], dtype=9) == mla.MLA_EINVAL
+    assert _pack_exp(lib, 4, 4, 8, 4, 8, [2, 2], send=FAKE) == mla.MLA_EINVAL        # send overlaps q
+    assert _pack_exp(lib, 4, 4, 8, 4, 8, [2, 2], kr=ctypes.c_void_p(0x10001)) == mla.MLA_EINVAL   # misaligned
+    assert _pack_exp(lib, 4, 4, 8, 4, 8, None) == mla.MLA_EINVAL
+    assert _pack_exp(lib, 0, 4, 8, 4, 8, [2, 2]) == mla.MLA_OK          # empty: nothing to do
+
+
+def _random_layout(rng):
+    copies = int(rng.integers(1, 4))
+    qparts = int(rng.integers(1, 5))
+    degree = copies * qparts
+    Lq = degree * int(rng.integers(1, 8))
+    total = qparts * Lq
+    n = int(rng.integers(1, min(total, 6) + 1))
+    cuts = sorted(int(x) for x in rng.choice(np.arange(1, total), size=n - 1, replace=False)) if n > 1 else []
+    return cuts + [total], Lq, copies, degree, total // degree
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_causal_partition_matches_oracle(seed):
+    rng = np.random.default_rng(300 + seed)
+    ends, Lq, _, _, _ = _random_layout(rng)
+    batch = int(rng.integers(1, 4))
+    for r in range(ends[-1] // Lq):
+        got = mla.mla_causal_partition(ends, Lq, r, batch)
+        exp = oracle.causal_partition(ends, Lq, r, batch)
+        assert got == {k: exp[k] for k in ("key_begin", "key_end", "query_ends", "key_ends")}, (ends, Lq, r)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_kv_exchange_ranges_match_oracle(seed):
+    rng = np.random.default_rng(400 + seed)
+    ends, Lq, copies, degree, S = _random_layout(rng)
+    for r in range(degree):
+        got = mla.mla_kv_exchange_ranges(ends, S, Lq, copies, degree, r)
+        assert got == oracle.kv_exchange_ranges(tuple(ends), S, Lq, copies, degree, r), (ends, S, Lq, copies, r)
+
+
+def test_interval_algebra_errors_leave_outputs_untouched(lib):
+    ends = (ctypes.c_int64 * 2)(10, 20)
+    kb, ke, n = ctypes.c_int64(-5), ctypes.c_int64(-5), ctypes.c_int(-5)
+    qe, kend = (ctypes.c_int64 * 4)(*[-5] * 4), (ctypes.c_int64 * 4)(*[-5] * 4)
+    # queries [16, 24) are not covered by documents ending at 20
+    assert lib.mla_causal_partition(ends, 2, 8, 2, 1, ctypes.byref(kb), ctypes.byref(ke), qe, kend, 4,
+                                    ctypes.byref(n)) == mla.MLA_EINVAL
+    assert "cover" in lib.mla_last_error().decode()
+    # capacity too small: queries [0, 16) touch two documents, batch 3 needs 6 entries
+    assert lib.mla_causal_partition(ends, 2, 16, 0, 3, ctypes.byref(kb), ctypes.byref(ke), qe, kend, 4,
+                                    ctypes.byref(n)) == mla.MLA_EINVAL
+    assert (kb.value, ke.value, n.value, list(qe), list(kend)) == (-5, -5, -5, [-5] * 4, [-5] * 4)
+    bad = (ctypes.c_int64 * 2)(10, 5)                       # decreasing ends
+    assert lib.mla_causal_partition(bad, 2, 5, 0, 1, ctypes.byref(kb), ctypes.byref(ke), qe, kend, 4,
+                                    ctypes.byref(n)) == mla.MLA_EINVAL
+    so, sc, rc = (ctypes.c_int64 * 2)(-5, -5), (ctypes.c_int64 * 2)(-5, -5), (ctypes.c_int64 * 2)(-5, -5)
+    loc = ctypes.c_int(-5)
+    assert lib.mla_kv_exchange_ranges(ends, 2, 10, 10, 1, 2, 2, so, sc, rc, ctypes.byref(loc)) == mla.MLA_EINVAL
+    assert lib.mla_kv_exchange_ranges(ends, 2, 10, 12, 1, 2, 0, so, sc, rc, ctypes.byref(loc)) == mla.MLA_EINVAL
+    assert (list(so), list(sc), list(rc), loc.value) == ([-5, -5], [-5, -5], [-5, -5], -5)
