@@ -31,6 +31,10 @@ NumPy float64, with no blocking or fusion beyond what that definition states:
 * expanded pack         -- hyper-parallel ``_expanded`` (one sequence-to-head
                            exchange of concat(q, k, v) with unequal widths, the
                            key assembled by ``_assemble_key_value``).
+* rotary embedding      -- hyper-parallel ``apply_mla_rope`` (position tables
+                           given by the caller in the tensor's dtype; half-band
+                           rotation, or adjacent pairs rotated and returned as
+                           real then imaginary half-bands).
 * query partition and   -- hyper-parallel ``_causal_partition`` and
   KV exchange ranges       ``_kv_exchange_ranges`` (document-local causal
                            prefixes of a rank's contiguous query range; the key
@@ -56,7 +60,7 @@ __all__ = [
     "pack_heads", "unpack_heads", "latent_up_proj", "attention_probs",
     "attention", "decode_split_kv", "decode_reference", "doc_bounds",
     "ulysses_materialise_k_first", "ulysses_latent_first",
-    "pack_expanded", "causal_partition", "kv_exchange_ranges",
+    "pack_expanded", "causal_partition", "kv_exchange_ranges", "rope",
 ]
 
 
@@ -439,3 +443,34 @@ def kv_exchange_ranges(ends, source_length: int, query_length: int, head_copies:
     local_only = all(p * source_length <= d["key_begin"] and d["key_end"] <= (p + 1) * source_length
                      for p, d in enumerate(dest))
     return tuple(sends), tuple(receives), local_only
+
+
+# --------------------------------------------------------------------------
+# Rotary embedding of the RoPE band (hyper-parallel apply_mla_rope)
+# --------------------------------------------------------------------------
+
+def rope(x, cos, sin, interleaved: bool = False) -> np.ndarray:
+    """Rotate the RoPE band x [T][...][R] by per-token tables cos, sin [T][R].
+
+    The tables are the caller's position embeddings in the tensor's dtype (the
+    pages cast them to it), one angle per pair: for the half-band form entry i
+    and i + R/2 carry the same angle. Half-band (interleaved=False): with
+    x = [a | b] (halves of R/2), out = [a cos - b sin | b cos + a sin], i.e. the
+    complex number a + i b times e^{i angle}. Interleaved: the pairs are
+    adjacent, (x[2i], x[2i+1]) times e^{i angle_i} with angle_i from the first
+    R/2 table entries, and the result is returned as the real parts followed by
+    the imaginary parts (half-band order). float64 result.
+    """
+    x = widen(x)
+    c, sn = widen(cos), widen(sin)
+    T, R = c.shape
+    assert x.shape[0] == T and x.shape[-1] == R and R % 2 == 0
+    h = R // 2
+    shape = (T,) + (1,) * (x.ndim - 2) + (R,)
+    c, sn = c.reshape(shape), sn.reshape(shape)
+    if not interleaved:
+        a, b = x[..., :h], x[..., h:]
+        return np.concatenate([a * c[..., :h] - b * sn[..., :h], b * c[..., h:] + a * sn[..., h:]], axis=-1)
+    re_in, im_in = x[..., 0::2], x[..., 1::2]
+    ci, si = c[..., :h], sn[..., :h]
+    return np.concatenate([re_in * ci - im_in * si, im_in * ci + re_in * si], axis=-1)

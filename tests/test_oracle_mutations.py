@@ -191,3 +191,18 @@ def test_expanded_pack_with_rope_before_nope_is_caught(monkeypatch):
         return om.pack_heads(np.concatenate([q, key, kv[:, :, N:]], axis=2), sizes)
     _patch(monkeypatch, "pack_expanded", bad)
     assert _fails(tp.test_pack_expanded_index_loops) and _fails(tp.test_pack_expanded_key_band_is_the_attention_key)
+
+
+def test_rope_with_a_flipped_rotation_is_caught(monkeypatch):
+    def bad(x, cos, sin, interleaved=False):
+        x = om.widen(x)
+        c, sn = om.widen(cos), om.widen(sin)
+        R = c.shape[1]
+        h = R // 2
+        shape = (c.shape[0],) + (1,) * (x.ndim - 2) + (R,)
+        c, sn = c.reshape(shape), sn.reshape(shape)
+        a, b = (x[..., 0::2], x[..., 1::2]) if interleaved else (x[..., :h], x[..., h:])
+        return np.concatenate([a * c[..., :h] + b * sn[..., :h], b * c[..., :h] - a * sn[..., :h]], axis=-1)
+    _patch(monkeypatch, "rope", bad)
+    assert _fails(lambda: tp.test_rope_is_complex_multiplication(False))
+    assert _fails(lambda: tp.test_rope_is_complex_multiplication(True))

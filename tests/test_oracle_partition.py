@@ -164,3 +164,54 @@ def test_pack_expanded_key_band_is_the_attention_key():
         torch.from_numpy(ve).transpose(0, 1), is_causal=True, scale=scale).transpose(0, 1).numpy()
     ref, _ = oracle.attention(q, kv, kr, N, scale)
     assert np.max(np.abs(sdpa - ref)) < 1e-12
+
+
+# ---- rotary embedding
+
+def _tables(T, R, base=10000.0, offset=0):
+    inv = base ** (-np.arange(0, R, 2) / R)
+    ang = np.outer(np.arange(offset, offset + T), inv)          # [T][R/2]
+    ang = np.concatenate([ang, ang], axis=1)                     # half-band table layout
+    return np.cos(ang), np.sin(ang), ang[:, :R // 2]
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rope_is_complex_multiplication(interleaved):
+    T, H, R = 7, 3, 16
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((T, H, R))
+    c, s, ang = _tables(T, R)
+    got = oracle.rope(x, c, s, interleaved)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) if interleaved else (x[..., :R // 2] + 1j * x[..., R // 2:])
+    w = z * np.exp(1j * ang)[:, None, :]
+    assert np.max(np.abs(got - np.concatenate([w.real, w.imag], axis=-1))) < 1e-12
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rope_scores_depend_on_relative_position_only(interleaved):
+    R = 32
+    rng = np.random.default_rng(22)
+    q, k = rng.standard_normal((1, R)), rng.standard_normal((1, R))
+    dots = []
+    for shift in (0, 5, 1000):
+        cq, sq, _ = _tables(1, R, offset=37 + shift)
+        ck, sk, _ = _tables(1, R, offset=11 + shift)
+        dots.append((oracle.rope(q, cq, sq, interleaved) @ oracle.rope(k, ck, sk, interleaved).T).item())
+    assert max(dots) - min(dots) < 1e-9
+
+
+def test_rope_at_position_zero():
+    R = 8
+    x = np.arange(3 * R, dtype=np.float64).reshape(3, R)
+    c, s = np.ones((3, R)), np.zeros((3, R))
+    assert np.array_equal(oracle.rope(x, c, s, False), x)
+    assert np.array_equal(oracle.rope(x, c, s, True), np.concatenate([x[:, 0::2], x[:, 1::2]], axis=1))
+
+
+def test_rope_interleaved_is_half_band_of_deinterleaved_input():
+    T, R = 5, 12
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((T, 2, R))
+    c, s, _ = _tables(T, R)
+    de = np.concatenate([x[..., 0::2], x[..., 1::2]], axis=-1)
+    assert np.max(np.abs(oracle.rope(x, c, s, True) - oracle.rope(de, c, s, False))) < 1e-15
