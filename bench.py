@@ -149,6 +149,39 @@ def _expanded(torch, mla):
     return out
 
 
+def _rope(torch, mla):
+    """In-place RoPE of q's band for all 128 heads of 4096 tokens (the pack side), both conventions.
+    Bytes = band read + band written + the two [T][R] tables."""
+    T, H, N, R = 4096, 128, 128, 64
+    g = torch.Generator(device="cuda").manual_seed(6)
+    q = torch.randn((T, H, N + R), device="cuda", generator=g).bfloat16()
+    ang = torch.arange(T, device="cuda", dtype=torch.float32)[:, None] * (
+        10000.0 ** (-torch.arange(0, R, 2, device="cuda", dtype=torch.float32) / R))[None, :]
+    ang = torch.cat([ang, ang], dim=1)
+    c, s = ang.cos().bfloat16(), ang.sin().bfloat16()
+    out = {}
+    for inter in (False, True):
+        reps = 50
+        for _ in range(3):
+            mla.mla_apply_rope(q[..., N:], c, s, interleaved=inter)
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        _busy(torch, 10)
+        st.record()
+        for _ in range(reps):
+            mla.mla_apply_rope(q[..., N:], c, s, interleaved=inter)
+        en.record()
+        torch.cuda.synchronize()
+        us = st.elapsed_time(en) * 1e3 / reps
+        nbytes = 2.0 * (2 * T * H * R + 2 * T * R)
+        key = "rope_interleaved" if inter else "rope_half_band"
+        out[f"{key}_us"] = round(us, 2)
+        out[f"{key}_gbps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    out["rope_note"] = "q band of 128 heads x 4096 tokens in place (67 MB each way), beyond the Infinity Cache"
+    del q, c, s
+    return out
+
+
 def _varlen(torch, mla, mi, dev):
     """Packed documents 8192/4096/2048/2048 (T=16384, H=16): block-diagonal causal attention."""
     w = mi.WORKLOADS["varlen16k"]
@@ -342,6 +375,7 @@ def main():
         assert torch.equal(big_back, big), "uneven22 pack/unpack round trip failed"
         del big, big_send, big_back
         extra.update(_expanded(torch, mla))
+        extra.update(_rope(torch, mla))
         extra.update(_varlen(torch, mla, mi, dev))
         extra.update(_decode(torch, mla, mi, dev))
 

@@ -97,6 +97,24 @@ int mla_pack_expanded(const void *q, const void *kv, const void *k_rope, void *s
                       int heads_total, int N, int R, int V, const int *sizes, int sp, int dtype, void *stream);
 
 /*
+ * Rotary embedding of a RoPE band, in place (hyper-parallel mla_context_parallel.py,
+ * `apply_mla_rope`; used on q's band of every head and on the shared k_rope).
+ *   x   : row (t, h) of the band is the R contiguous elements at
+ *         x + t*stride_t + h*stride_h (elements), t < tokens, h < heads;
+ *   cos, sin : [tokens][R] tables with row stride cs_stride, in x's element type
+ *         (the pages cast the position tables to the tensor's dtype).
+ * interleaved == 0 (half-band): with the row [a | b] (halves of R/2),
+ *     out = [a*cos[:R/2] - b*sin[:R/2] | b*cos[R/2:] + a*sin[R/2:]].
+ * interleaved == 1: the pairs (x[2i], x[2i+1]) are rotated by cos[i], sin[i]
+ *     (i < R/2) and stored as real parts then imaginary parts (half-band order).
+ * fp32 arithmetic; bf16 results rounded to nearest even. R even, 2 <= R <= 256.
+ * Rows must not overlap each other (stride_h >= R when heads > 1, stride_t >=
+ * (heads-1)*stride_h + R when tokens > 1) nor the tables. tokens == 0 is a no-op.
+ */
+int mla_apply_rope(void *x, int64_t tokens, int heads, int64_t stride_t, int64_t stride_h, int R, const void *cos,
+                   const void *sin, int64_t cs_stride, int interleaved, int dtype, void *stream);
+
+/*
  * Query partition (host only, no GPU use): hyper-parallel `_causal_partition`.
  * Documents are given by their cumulative ends doc_ends[0..n_docs) (non-
  * negative, non-decreasing; empty documents allowed). The rank owns the query

@@ -23,7 +23,7 @@ EXPORTS = (
     "mla_last_error", "mla_version", "mla_head_shard_sizes", "mla_pack_heads", "mla_unpack_heads",
     "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
-    "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges",
+    "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope",
 )
 
 
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [vp, vp, i64, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
     lib.mla_latent_up_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.mla_pack_expanded.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
+    lib.mla_apply_rope.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp, i64, i32, i32, vp]
     p64 = ctypes.POINTER(i64)
     lib.mla_causal_partition.argtypes = [p64, i32, i64, i32, i32, p64, p64, p64, p64, i32, ctypes.POINTER(i32)]
     lib.mla_kv_exchange_ranges.argtypes = [p64, i32, i64, i64, i32, i32, i32, p64, p64, p64, ctypes.POINTER(i32)]
@@ -189,6 +190,24 @@ def mla_pack_expanded(q, kv, k_rope, send, sizes, N, stream=None):
     _check("mla_pack_expanded", lib.mla_pack_expanded(_ptr(q), _ptr(kv), _ptr(k_rope), _ptr(send), T, Ht, N, R, V,
                                                        arr, len(sizes), dt, _stream(stream)))
     return send
+
+
+def mla_apply_rope(band, cos, sin, interleaved=False, stream=None):
+    """Rotate a RoPE band in place: band is a view [T][H][R] (e.g. q[..., N:]) or [T][R] with unit last
+    stride; cos, sin are [T][R] tables of the band's dtype."""
+    lib = load_library()
+    _dev(band, cos, sin)
+    if band.dim() == 2:
+        T, R = band.shape
+        H, st, sh = 1, band.stride(0), R
+    else:
+        T, H, R = band.shape
+        st, sh = band.stride(0), band.stride(1)
+    assert band.stride(-1) == 1 and cos.shape == (T, R) and sin.shape == (T, R)
+    assert cos.stride(-1) == 1 and sin.stride() == cos.stride() and cos.dtype == sin.dtype == band.dtype
+    _check("mla_apply_rope", lib.mla_apply_rope(_ptr(band), T, H, st, sh, R, _ptr(cos), _ptr(sin), cos.stride(0),
+                                                 int(bool(interleaved)), _dtype(band), _stream(stream)))
+    return band
 
 
 def _i64s(xs):

@@ -170,6 +170,42 @@ int mla_pack_expanded(const void *q, const void *kv, const void *k_rope, void *s
   return launched(mla::launch_pack_expanded(p, stream), who);
 }
 
+int mla_apply_rope(void *x, int64_t tokens, int heads, int64_t stride_t, int64_t stride_h, int R, const void *cos,
+                   const void *sin, int64_t cs_stride, int interleaved, int dtype, void *stream) {
+  const char *who = "mla_apply_rope";
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (tokens < 0 || heads < 1 || R < 2 || R > 256 || R % 2 || (interleaved != 0 && interleaved != 1))
+    return fail(MLA_EINVAL, "%s: need tokens >= 0, heads >= 1, even 2 <= R <= 256, interleaved 0/1 (got %lld, %d, %d, %d)",
+                who, static_cast<long long>(tokens), heads, R, interleaved);
+  if (tokens == 0) return ok();
+  if (x == nullptr || cos == nullptr || sin == nullptr) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  if ((heads > 1 && stride_h < R) || (tokens > 1 && stride_t < (heads - 1) * stride_h + R) ||
+      (tokens > 1 && cs_stride < R) || stride_h < 0 || stride_t < 0 || cs_stride < 0)
+    return fail(MLA_EINVAL, "%s: strides let band rows overlap (stride_t %lld, stride_h %lld, cs_stride %lld)", who,
+                static_cast<long long>(stride_t), static_cast<long long>(stride_h), static_cast<long long>(cs_stride));
+  const int64_t eb = elem_bytes(dtype);
+  const uintptr_t px = reinterpret_cast<uintptr_t>(x), pc = reinterpret_cast<uintptr_t>(cos),
+                  ps = reinterpret_cast<uintptr_t>(sin);
+  if ((px | pc | ps) % eb) return fail(MLA_EINVAL, "%s: buffers must be aligned to the element size", who);
+  const uint64_t xb = static_cast<uint64_t>((tokens - 1) * stride_t + (heads - 1) * stride_h + R) * eb;
+  const uint64_t tb = static_cast<uint64_t>((tokens - 1) * cs_stride + R) * eb;
+  if ((px < pc + tb && pc < px + xb) || (px < ps + tb && ps < px + xb))
+    return fail(MLA_EINVAL, "%s: the band overlaps a table", who);
+  mla::RopePlan p;
+  p.x = x;
+  p.cos = cos;
+  p.sin = sin;
+  p.tokens = tokens;
+  p.stride_t = stride_t;
+  p.stride_h = stride_h;
+  p.cs_stride = cs_stride;
+  p.heads = heads;
+  p.R = R;
+  p.interleaved = interleaved;
+  p.bf16 = dtype == MLA_BF16;
+  return launched(mla::launch_rope(p, stream), who);
+}
+
 namespace {
 // documents as [start, end) from cumulative ends; checks them
 int doc_ranges(const int64_t *ends, int n, std::vector<std::pair<int64_t, int64_t>> &docs, const char *who) {

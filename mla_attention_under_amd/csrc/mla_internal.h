@@ -36,6 +36,15 @@ struct PackExpandedPlan {
 };
 int launch_pack_expanded(const PackExpandedPlan &p, void *stream);
 
+// ---- rotary embedding of a band, in place
+struct RopePlan {
+  void *x;
+  const void *cos, *sin;
+  int64_t tokens, stride_t, stride_h, cs_stride;
+  int heads, R, interleaved, bf16;
+};
+int launch_rope(const RopePlan &p, void *stream);
+
 // ---- latent up-projection -------------------------------------------------
 struct UpProjPlan {
   const void *latent;  // [T][L]

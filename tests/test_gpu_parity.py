@@ -100,6 +100,43 @@ def test_pack_expanded_bit_exact(name, tokens, sizes, N, R, V, eb):
     assert np.array_equal(got, exp), name
 
 
+def _rope_tables(T, R, dtype_bf16, offset=0, base=10000.0):
+    """Position tables [T][R] (half-band layout, one angle per pair) in the band's dtype."""
+    inv = base ** (-np.arange(0, R, 2) / R)
+    ang = np.outer(np.arange(offset, offset + T), inv)
+    ang = np.concatenate([ang, ang], axis=1)
+    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    return (mi.f32_to_bf16_bits(c), mi.f32_to_bf16_bits(s)) if dtype_bf16 else (c, s)
+
+
+ROPE_CASES = [
+    # (name, T, H, N, R, bf16)
+    ("dsv3_rank_q", 2048, 16, 128, 64, True),
+    ("pack_side_q_all_heads", 4096, 128, 128, 64, True),
+    ("shared_key_band", 2048, 0, 0, 64, True),
+    ("tiny_fp32_q", 64, 4, 16, 8, False),
+    ("odd_band_bf16", 37, 3, 6, 10, True),
+    ("one_token", 1, 1, 128, 64, True),
+]
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("name,T,H,N,R,bf16", ROPE_CASES, ids=[c[0] for c in ROPE_CASES])
+def test_rope_matches_oracle(name, T, H, N, R, bf16, interleaved):
+    shape = (T, R) if H == 0 else (T, H, N + R)
+    x = mi.draw(shape, 31, 1, bf16=bf16)
+    c, s = _rope_tables(T, R, bf16, offset=17)
+    xd, cd, sd = dev(x), dev(c), dev(s)
+    band = xd if H == 0 else xd[..., N:]
+    mla.mla_apply_rope(band, cd, sd, interleaved=interleaved)
+    _sync()
+    got = host64(xd)
+    ref_band = oracle.rope(x if H == 0 else x[..., N:], c, s, interleaved)
+    check_close(got if H == 0 else got[..., N:], ref_band, bf16=bf16, name=f"{name} interleaved={interleaved}")
+    if H:
+        assert np.array_equal(bits(xd)[..., :N], x[..., :N].view(bits(xd).dtype)), "columns outside the band changed"
+
+
 def test_pack_zero_tokens_is_a_no_op():
     x = torch.zeros((0, 4, 8), dtype=torch.int16, device="cuda")
     send = torch.zeros(0, dtype=torch.int16, device="cuda")

@@ -277,3 +277,25 @@ def test_interval_algebra_errors_leave_outputs_untouched(lib):
     assert lib.mla_kv_exchange_ranges(ends, 2, 10, 10, 1, 2, 2, so, sc, rc, ctypes.byref(loc)) == mla.MLA_EINVAL
     assert lib.mla_kv_exchange_ranges(ends, 2, 10, 12, 1, 2, 0, so, sc, rc, ctypes.byref(loc)) == mla.MLA_EINVAL
     assert (list(so), list(sc), list(rc), loc.value) == ([-5, -5], [-5, -5], [-5, -5], -5)
+
+
+def test_rope_validation_before_launch(lib):
+    f = lib.mla_apply_rope
+    X, C, S = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    ok = dict(tokens=4, heads=2, st=384, sh=192, R=64, cs=64, inter=0, dt=mla.MLA_BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(kw.get("x", X), a["tokens"], a["heads"], a["st"], a["sh"], a["R"], kw.get("c", C), S, a["cs"],
+                 a["inter"], a["dt"], None)
+    assert call(R=63) == mla.MLA_EINVAL            # odd band
+    assert call(R=258) == mla.MLA_EINVAL           # wider than supported
+    assert call(heads=0) == mla.MLA_EINVAL
+    assert call(inter=2) == mla.MLA_EINVAL
+    assert call(dt=5) == mla.MLA_EINVAL
+    assert call(sh=32) == mla.MLA_EINVAL           # head rows overlap
+    assert call(st=200) == mla.MLA_EINVAL          # token rows overlap
+    assert call(cs=8) == mla.MLA_EINVAL            # table rows overlap
+    assert call(c=X) == mla.MLA_EINVAL             # band overlaps a table
+    assert call(x=ctypes.c_void_p(0x100001)) == mla.MLA_EINVAL   # misaligned
+    assert call(tokens=0) == mla.MLA_OK
