@@ -1,10 +1,10 @@
 // Rotary embedding of the RoPE band, in place (hyper-parallel
 // mla_context_parallel.py, `apply_mla_rope`): the half-band rotation
 // [a | b] -> [a cos - b sin | b cos + a sin], or adjacent pairs rotated and
-// stored as real then imaginary half-bands. One thread per band row: the
-// interleaved form writes positions other threads would read, so a row is read
-// whole before any of it is written. HBM-bound (the band, the two tables of
-// its token, the band again); rows of 16-byte multiples move as 16-byte chunks.
+// stored as real then imaginary half-bands. A row is read whole (its chunks
+// spread over a group of lanes, or one thread's registers) before any of it is
+// written, since the interleaved form writes positions other chunks are read
+// from. HBM-bound: the band, the two tables of its token, the band again.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -24,62 +24,74 @@ struct RopeArgs {
   int heads, R;
 };
 
-template <bool BF16>
-__device__ __forceinline__ float elem(const u32x4 (&v)[32], int i) {
-  if constexpr (BF16) {
-    const uint32_t w = v[i >> 3][(i >> 1) & 3];
-    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
-  } else {
-    return __uint_as_float(v[i >> 2][i & 3]);
-  }
-}
-
-// R known at compile time, rows and tables 16-byte aligned: registers only
-template <bool BF16, int R, bool INTERLEAVED>
-__global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(RopeArgs a) {
-  constexpr int EB = BF16 ? 2 : 4;
-  constexpr int CH = R * EB / 16;     // 16-byte chunks per row
-  constexpr int H = R / 2;
-  static_assert(CH * 16 == R * EB && CH <= 32, "row of whole 16-byte chunks");
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRopeThreads + threadIdx.x;
-  if (row >= a.rows) return;
+// Rows of CH 16-byte chunks (CH dividing 64), rows and tables 16-byte aligned:
+// a row is handled by CH consecutive lanes, lane c holding chunk c, so every
+// load and store instruction covers whole rows. Half-band: the partner half of
+// chunk c is chunk c ^ CH/2 (one exchange). Interleaved: output chunk c takes
+// the real (c < CH/2) or imaginary parts of the pairs in input chunks
+// 2c mod CH and 2c+1 mod CH (two exchanges); its angles are table chunk
+// c mod CH/2.
+template <bool BF16, bool INTERLEAVED>
+__global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(RopeArgs a, int ch) {
+  constexpr int E = BF16 ? 8 : 4;   // elements per chunk
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kRopeThreads + threadIdx.x;
+  const int64_t row = gid / ch;
+  if (row >= a.rows) return;        // whole rows leave together: ch divides the block
+  const int c = static_cast<int>(gid - row * ch);
+  const int lane = threadIdx.x & 63, base = lane - c;
   const int64_t t = row / a.heads, h = row - t * a.heads;
   u32x4 *xp = reinterpret_cast<u32x4 *>(a.x + t * a.st + h * a.sh);
   const u32x4 *cp = reinterpret_cast<const u32x4 *>(a.cos + t * a.cst);
   const u32x4 *sp = reinterpret_cast<const u32x4 *>(a.sin + t * a.cst);
-  u32x4 xv[32], cv[32], sv[32];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    xv[i] = xp[i];
-    cv[i] = cp[i];
-    sv[i] = sp[i];
-  }
-  float out[R];
-#pragma unroll
-  for (int i = 0; i < H; ++i) {
-    if constexpr (INTERLEAVED) {
-      const float re = elem<BF16>(xv, 2 * i), im = elem<BF16>(xv, 2 * i + 1);
-      const float c = elem<BF16>(cv, i), s = elem<BF16>(sv, i);
-      out[i] = re * c - im * s;
-      out[H + i] = im * c + re * s;
-    } else {
-      const float x0 = elem<BF16>(xv, i), x1 = elem<BF16>(xv, H + i);
-      out[i] = x0 * elem<BF16>(cv, i) - x1 * elem<BF16>(sv, i);
-      out[H + i] = x1 * elem<BF16>(cv, H + i) + x0 * elem<BF16>(sv, H + i);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    u32x4 w;
+  const int half = ch / 2;
+  const bool upper = c >= half;
+  auto get = [&](const u32x4 &v, int e) {
     if constexpr (BF16) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(out[8 * i + 2 * e], out[8 * i + 2 * e + 1]);
+      const uint32_t w = v[e >> 1];
+      return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(out[4 * i + e]);
+      return __uint_as_float(v[e]);
     }
-    xp[i] = w;
+  };
+  auto shfl4 = [&](const u32x4 &v, int src) {
+    return u32x4{static_cast<uint32_t>(__shfl(static_cast<int>(v[0]), src)),
+                 static_cast<uint32_t>(__shfl(static_cast<int>(v[1]), src)),
+                 static_cast<uint32_t>(__shfl(static_cast<int>(v[2]), src)),
+                 static_cast<uint32_t>(__shfl(static_cast<int>(v[3]), src))};
+  };
+  const u32x4 xv = xp[c];
+  float out[E];
+  if constexpr (!INTERLEAVED) {
+    const u32x4 cv = cp[c], sv = sp[c];
+    const u32x4 pv = shfl4(xv, base + (c ^ half));
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float x0 = get(xv, e), xp_ = get(pv, e), cs = get(cv, e), sn = get(sv, e);
+      out[e] = upper ? x0 * cs + xp_ * sn : x0 * cs - xp_ * sn;
+    }
+  } else {
+    const int tc = upper ? c - half : c;   // table chunk of this output chunk's pairs
+    const u32x4 cv = cp[tc], sv = sp[tc];
+    const int src0 = base + ((2 * c) & (ch - 1));
+    const u32x4 in0 = shfl4(xv, src0), in1 = shfl4(xv, src0 + 1);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      // pair tc*E + e: elements 2e, 2e+1 of input chunk 2tc (e < E/2) or 2tc+1
+      const u32x4 &iv = e < E / 2 ? in0 : in1;
+      const int k = 2 * (e % (E / 2));
+      const float re = get(iv, k), im = get(iv, k + 1), cs = get(cv, e), sn = get(sv, e);
+      out[e] = upper ? im * cs + re * sn : re * cs - im * sn;
+    }
   }
+  u32x4 w;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(out[2 * e], out[2 * e + 1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(out[e]);
+  }
+  xp[c] = w;
 }
 
 // any even R <= 256, any element-aligned layout
@@ -119,27 +131,28 @@ __global__ __launch_bounds__(kRopeThreads) void rope_generic_kernel(RopeArgs a, 
   }
 }
 
-template <bool BF16, int R>
-hipError_t launch_vec(const RopeArgs &a, bool inter, dim3 grid, hipStream_t s) {
-  if (inter)
-    hipLaunchKernelGGL((rope_vec_kernel<BF16, R, true>), grid, dim3(kRopeThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((rope_vec_kernel<BF16, R, false>), grid, dim3(kRopeThreads), 0, s, a);
-  return hipGetLastError();
-}
-
 template <bool BF16>
-hipError_t dispatch(const RopeArgs &a, const RopePlan &p, dim3 grid, hipStream_t s) {
+hipError_t dispatch(const RopeArgs &a, const RopePlan &p, hipStream_t s) {
   constexpr int EB = BF16 ? 2 : 4;
   const uintptr_t al = reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.cos) |
                        reinterpret_cast<uintptr_t>(p.sin) | static_cast<uintptr_t>(a.st) |
                        static_cast<uintptr_t>(a.sh) | static_cast<uintptr_t>(a.cst);
-  const bool vec = al % 16 == 0 && (p.R * EB) % 16 == 0;
-  const bool inter = p.interleaved != 0;
-  if (vec && p.R == 64) return launch_vec<BF16, 64>(a, inter, grid, s);
-  if (vec && p.R == 32) return launch_vec<BF16, 32>(a, inter, grid, s);
-  if (vec && p.R == 128) return launch_vec<BF16, 128>(a, inter, grid, s);
-  hipLaunchKernelGGL((rope_generic_kernel<BF16>), grid, dim3(kRopeThreads), 0, s, a, p.interleaved);
+  const int ch = (p.R * EB) % 16 == 0 ? p.R * EB / 16 : 0;
+  const bool vec = al % 16 == 0 && ch >= 2 && ch <= 64 && (ch & (ch - 1)) == 0;
+  if (vec) {
+    const int64_t blocks = (a.rows * ch + kRopeThreads - 1) / kRopeThreads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (p.interleaved)
+      hipLaunchKernelGGL((rope_vec_kernel<BF16, true>), grid, dim3(kRopeThreads), 0, s, a, ch);
+    else
+      hipLaunchKernelGGL((rope_vec_kernel<BF16, false>), grid, dim3(kRopeThreads), 0, s, a, ch);
+    return hipGetLastError();
+  }
+  const int64_t blocks = (a.rows + kRopeThreads - 1) / kRopeThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((rope_generic_kernel<BF16>), dim3(static_cast<unsigned>(blocks)), dim3(kRopeThreads), 0, s, a,
+                     p.interleaved);
   return hipGetLastError();
 }
 
@@ -158,11 +171,8 @@ int launch_rope(const RopePlan &p, void *stream) {
   a.cst = p.cs_stride * eb;
   a.heads = p.heads;
   a.R = p.R;
-  const int64_t blocks = (a.rows + kRopeThreads - 1) / kRopeThreads;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(blocks));
-  return p.bf16 ? dispatch<true>(a, p, grid, s) : dispatch<false>(a, p, grid, s);
+  if (a.rows == 0) return hipSuccess;
+  return p.bf16 ? dispatch<true>(a, p, s) : dispatch<false>(a, p, s);
 }
 
 }  // namespace mla
