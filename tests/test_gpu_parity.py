@@ -178,6 +178,13 @@ def test_up_proj_matches_oracle(wname, T, hb, heads):
     check_close(got, ref, bf16=w.bf16, name=f"{wname} T={T} heads[{hb},{hb + heads})")
 
 
+def test_up_proj_as_the_query_projection():
+    # q_b_proj of the DeepSeek-V3 rank shard: latent width 1536 -> 16 heads of [q_nope 128 | q_rope 64]
+    w = mi.Workload("q_proj", 12, T=2048, H=16, L=1536, N=128, R=64, V=64, heads_total=16)
+    got, ref = _up_proj_case(w, 2048, 0, 16)
+    check_close(got, ref, name="query projection L=1536, 16 x 192")
+
+
 def test_up_proj_generic_widths():
     # N+V = 64: the column count is not a multiple of the 128-wide tile
     w = mi.Workload("odd", 11, T=200, H=3, L=40, N=40, R=8, V=24, heads_total=5)
