@@ -182,6 +182,57 @@ def _rope(torch, mla):
     return out
 
 
+def _project_pack(torch, mla):
+    """The rank's send buffer straight from latents: q_b_proj + RoPE and wkv_b written into the 8 head slabs of
+    [256 tokens][128 heads][448] (DeepSeek-V3 widths: q latent 1536, kv latent 512). Against the separate calls
+    (two projections, the rotation, the pack of an already assembled payload)."""
+    T, Hq, Lq, Lkv, N, R, V, sp = 256, 128, 1536, 512, 128, 64, 128, 8
+    F = 2 * N + R + V
+    g = torch.Generator(device="cuda").manual_seed(7)
+    rnd = lambda *shape, std=1.0: (torch.randn(shape, device="cuda", generator=g) * std).bfloat16()
+    ql, kl = rnd(T, Lq), rnd(T, Lkv)
+    wq, wkv = rnd(Lq, Hq * (N + R), std=Lq ** -0.5), rnd(Lkv, Hq * (N + V), std=Lkv ** -0.5)
+    ang = torch.arange(T, device="cuda", dtype=torch.float32)[:, None] * (
+        10000.0 ** (-torch.arange(0, R, 2, device="cuda", dtype=torch.float32) / R))[None, :]
+    ang = torch.cat([ang, ang], dim=1)
+    c, s = ang.cos().bfloat16(), ang.sin().bfloat16()
+    sizes = [Hq // sp] * sp
+    send = torch.empty(T * Hq * F, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((T, Hq, N + R), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((T, Hq, N + V), dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((T, Hq, F), dtype=torch.bfloat16, device="cuda")
+
+    def fused():
+        mla.mla_project_pack(ql, wq, send, Hq, 0, Hq, N + R, F, 0, sizes, rope_offset=N, cos=c, sin=s)
+        mla.mla_project_pack(kl, wkv, send, Hq, 0, Hq, N + V, F, N + R, sizes)
+
+    def separate():
+        mla.mla_latent_up_proj(ql, wq, q, Hq, 0, Hq, N, R)
+        mla.mla_apply_rope(q[..., N:], c, s)
+        mla.mla_latent_up_proj(kl, wkv, kv, Hq, 0, Hq, N, V)
+        mla.mla_pack_heads(x, send, sizes)
+
+    out = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for _ in range(5):
+            fn()
+        reps = 100
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        _busy(torch, 10)
+        st.record()
+        for _ in range(reps):
+            fn()
+        en.record()
+        torch.cuda.synchronize()
+        out[f"project_pack_{name}_us"] = round(st.elapsed_time(en) * 1e3 / reps, 2)
+    flops = 2.0 * T * (Lq * Hq * (N + R) + Lkv * Hq * (N + V))
+    out["project_pack_fused_tflops"] = round(flops / (out["project_pack_fused_us"] * 1e-6) / 1e12, 1)
+    out["project_pack_note"] = ("send [256][128][448] -> 8 x 16 heads from the q latent (1536, RoPE on 64) and the kv "
+                                "latent (512); separate = two projections + rotation + pack of an assembled payload")
+    return out
+
+
 def _varlen(torch, mla, mi, dev):
     """Packed documents 8192/4096/2048/2048 (T=16384, H=16): block-diagonal causal attention."""
     w = mi.WORKLOADS["varlen16k"]
@@ -376,6 +427,7 @@ def main():
         del big, big_send, big_back
         extra.update(_expanded(torch, mla))
         extra.update(_rope(torch, mla))
+        extra.update(_project_pack(torch, mla))
         extra.update(_varlen(torch, mla, mi, dev))
         extra.update(_decode(torch, mla, mi, dev))
 

@@ -115,6 +115,31 @@ int mla_apply_rope(void *x, int64_t tokens, int heads, int64_t stride_t, int64_t
                    const void *sin, int64_t cs_stride, int interleaved, int dtype, void *stream);
 
 /*
+ * Projection written straight into the token->head pack (torchtitan "MLA CP
+ * optimization", section "Ulysses CP": the pack of concat(q_THK, kv_THP) whose
+ * parts come from q_b_proj with RoPE and from wkv_b; hyper-parallel `_query`,
+ * `apply_mla_rope`). One call writes one part of every payload row:
+ *   out[t][h][j] = sum_l latent[t][l] * w[l][(head_begin+h)*P + j],  h < heads, j < P
+ * rotated like mla_apply_rope on its columns [rope_offset, rope_offset+R) when
+ * R > 0 (cos, sin: [tokens][R] tables, row stride cs_stride), then stored as
+ *   send[T*off_r*F + (t*sizes[r] + h-off_r)*F + col_offset + j]
+ * for the rank r holding head h (sizes: HOST list of sp positive ints summing
+ * to heads). Columns of send outside [col_offset, col_offset+P) are untouched.
+ * The result equals mla_latent_up_proj, then mla_apply_rope on the band, then
+ * mla_pack_heads into those columns, bit for bit (the tile is rounded to bf16
+ * before the rotation, as the separate calls round it).
+ *   latent : [tokens][L] bf16;  w : [L][w_heads*P] bf16;  send: bf16.
+ * Runs bf16 only (MLA_EUNSUPPORTED otherwise) with L, P, F, col_offset,
+ * rope_offset multiples of 8, R a multiple of 16, 16-byte aligned buffers and
+ * tables (cs_stride a multiple of 8), and each head's band inside one 128-column
+ * tile of the projection (true for P = 192, rope_offset = 128, R = 64).
+ * heads <= 256, sp <= 256. tokens == 0 is a no-op.
+ */
+int mla_project_pack(const void *latent, const void *w, void *send, int64_t tokens, int L, int w_heads, int head_begin,
+                     int heads, int P, int F, int col_offset, const int *sizes, int sp, int rope_offset, int R,
+                     const void *cos, const void *sin, int64_t cs_stride, int interleaved, int dtype, void *stream);
+
+/*
  * Query partition (host only, no GPU use): hyper-parallel `_causal_partition`.
  * Documents are given by their cumulative ends doc_ends[0..n_docs) (non-
  * negative, non-decreasing; empty documents allowed). The rank owns the query

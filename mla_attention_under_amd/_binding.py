@@ -23,7 +23,7 @@ EXPORTS = (
     "mla_last_error", "mla_version", "mla_head_shard_sizes", "mla_pack_heads", "mla_unpack_heads",
     "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
-    "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope",
+    "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope", "mla_project_pack",
 )
 
 
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_latent_up_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.mla_pack_expanded.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
     lib.mla_apply_rope.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp, i64, i32, i32, vp]
+    lib.mla_project_pack.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32), i32,
+                                     i32, i32, vp, vp, i64, i32, i32, vp]
     p64 = ctypes.POINTER(i64)
     lib.mla_causal_partition.argtypes = [p64, i32, i64, i32, i32, p64, p64, p64, p64, i32, ctypes.POINTER(i32)]
     lib.mla_kv_exchange_ranges.argtypes = [p64, i32, i64, i64, i32, i32, i32, p64, p64, p64, ctypes.POINTER(i32)]
@@ -208,6 +210,25 @@ def mla_apply_rope(band, cos, sin, interleaved=False, stream=None):
     _check("mla_apply_rope", lib.mla_apply_rope(_ptr(band), T, H, st, sh, R, _ptr(cos), _ptr(sin), cos.stride(0),
                                                  int(bool(interleaved)), _dtype(band), _stream(stream)))
     return band
+
+
+def mla_project_pack(latent, w, send, w_heads, head_begin, heads, P, F, col_offset, sizes, rope_offset=-1,
+                     cos=None, sin=None, interleaved=False, stream=None):
+    """latent [T][L] x w [L][w_heads*P] (heads [head_begin, +heads)) -> columns [col_offset, +P) of every
+    payload row of send (flat, concat_r [T][sizes[r]][F]); RoPE on the block's columns [rope_offset, +R)
+    when cos/sin ([T][R]) are given."""
+    lib = load_library()
+    _dev(latent, w, send, *(t for t in (cos, sin) if t is not None))
+    T, L = latent.shape
+    assert latent.is_contiguous() and w.is_contiguous() and send.is_contiguous()
+    assert w.shape == (L, w_heads * P) and send.numel() == T * heads * F
+    R = 0 if cos is None else cos.shape[1]
+    cs = 0 if cos is None else cos.stride(0)
+    arr = (ctypes.c_int * len(sizes))(*sizes)
+    _check("mla_project_pack", lib.mla_project_pack(
+        _ptr(latent), _ptr(w), _ptr(send), T, L, w_heads, head_begin, heads, P, F, col_offset, arr, len(sizes),
+        rope_offset, R, _ptr(cos), _ptr(sin), cs, int(bool(interleaved)), _dtype(latent), _stream(stream)))
+    return send
 
 
 def _i64s(xs):

@@ -43,6 +43,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
+// One rotated element of a RoPE pair (the real part when `second` is false,
+// the imaginary part when it is true): first*c - second_in*s and
+// second_in*c + first*s, evaluated as one product and one fused multiply-add
+// so that every kernel rotating a band rounds identically.
+__device__ __forceinline__ float rope_re(float re, float im, float c, float s) {
+  return __builtin_fmaf(re, c, -(im * s));
+}
+__device__ __forceinline__ float rope_im(float re, float im, float c, float s) {
+  return __builtin_fmaf(im, c, re * s);
+}
+// bf16 element e of a 16-byte chunk, widened
+__device__ __forceinline__ float bf16_elem(const u32x4 &v, int e) {
+  const uint32_t w = v[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
 // Interleave the 16-bit halves of two dwords: lo16(a)|lo16(b)<<16 and hi16(a)|hi16(b)<<16.
 __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
   return (a & 0xffffu) | (b << 16);

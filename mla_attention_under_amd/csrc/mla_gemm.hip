@@ -63,9 +63,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       static_cast<int>(reinterpret_cast<uintptr_t>((lds_void *)(p)))));
 }
 
+// Slab-layout output (the projection written straight into the token->head
+// pack): column n of the projection is element n % P of head n / P's block;
+// head h (0-based within the projected range) belongs to the rank whose slab
+// starts at head off[h] and holds qr[h] heads. Its row for token m is
+//   send[T*off*F + (m*qr + h - off)*F + col_off + n % P].
+// Columns [rope_off, rope_off + R) of each block are rotated (RoPE) from the
+// bf16-rounded tile before they leave, exactly as the in-place rotation does.
+struct SlabOut {
+  uint16_t *send;
+  const uint16_t *cos, *sin;
+  int64_t tokens, cs_stride;
+  int P, F, col_off, rope_off, R, interleaved;
+  int16_t off[kMaxSlabHeads], qr[kMaxSlabHeads];
+};
+
+template <bool SLAB>
 __global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
-    int M, int K, int64_t ldw, int64_t col0, int ncols, int tiles_m, int tiles_n) {
+    int M, int K, int64_t ldw, int64_t col0, int ncols, int tiles_m, int tiles_n, SlabOut so) {
   __shared__ __attribute__((aligned(1024))) uint16_t a0[A_E];
   __shared__ __attribute__((aligned(1024))) uint16_t a1[A_E];
   __shared__ __attribute__((aligned(1024))) uint16_t a2[A_E];
@@ -211,6 +227,53 @@ __global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
         *reinterpret_cast<u32x2 *>(Cs + m * GN + 8 * ((n >> 3) ^ (m & 15)) + (n & 7)) = v;
       }
   __syncthreads();
+  if constexpr (SLAB) {
+#pragma unroll 4
+    for (int u = 0; u < GM * GN / 8 / 512; ++u) {
+      const int c = tid + 512 * u;
+      const int row = c >> 4, nc = c & 15;
+      const int m = m0 + row, n = n0 + 8 * nc;
+      if (m >= M || n >= ncols) continue;
+      const uint16_t *rowp = (row < GM / 2 ? a0 : a1) + (row & (GM / 2 - 1)) * GN;
+      auto chunk_at = [&](int col) { return *reinterpret_cast<const u32x4 *>(rowp + 8 * ((col >> 3) ^ (row & 15))); };
+      u32x4 v = chunk_at(8 * nc);
+      const int hh = n / so.P, f = n - hh * so.P;
+      if (f >= so.rope_off && f < so.rope_off + so.R) {
+        // the band lies inside this tile (checked on the host)
+        const int b0 = f - so.rope_off, half = so.R / 2, band = 8 * nc - b0;
+        const bool upper = b0 >= half;
+        float o[8];
+        if (!so.interleaved) {
+          const u32x4 pv = chunk_at(band + (upper ? b0 - half : b0 + half));
+          const u32x4 cv = *reinterpret_cast<const u32x4 *>(so.cos + m * so.cs_stride + b0);
+          const u32x4 sv = *reinterpret_cast<const u32x4 *>(so.sin + m * so.cs_stride + b0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x0 = bf16_elem(v, e), xp = bf16_elem(pv, e), cs = bf16_elem(cv, e), sn = bf16_elem(sv, e);
+            o[e] = upper ? rope_im(xp, x0, cs, sn) : rope_re(x0, xp, cs, sn);
+          }
+        } else {
+          const int p0 = upper ? b0 - half : b0;   // first pair of this output chunk
+          const u32x4 in0 = chunk_at(band + 2 * p0), in1 = chunk_at(band + 2 * p0 + 8);
+          const u32x4 cv = *reinterpret_cast<const u32x4 *>(so.cos + m * so.cs_stride + p0);
+          const u32x4 sv = *reinterpret_cast<const u32x4 *>(so.sin + m * so.cs_stride + p0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const u32x4 &iv = e < 4 ? in0 : in1;
+            const float re = bf16_elem(iv, 2 * (e & 3)), im = bf16_elem(iv, 2 * (e & 3) + 1);
+            const float cs = bf16_elem(cv, e), sn = bf16_elem(sv, e);
+            o[e] = upper ? rope_im(re, im, cs, sn) : rope_re(re, im, cs, sn);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+      }
+      const int ro = so.off[hh], qr = so.qr[hh];
+      uint16_t *dst = so.send + (so.tokens * ro + static_cast<int64_t>(m) * qr + (hh - ro)) * so.F + so.col_off + f;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < GM * GN / 8 / 512; ++u) {
     const int c = tid + 512 * u;
@@ -252,10 +315,11 @@ int launch_up_proj(const UpProjPlan &p, void *stream) {
   if (tiled) {
     const int tm = static_cast<int>((p.T + GM - 1) / GM);
     const int tn = static_cast<int>((p.ncols + GN - 1) / GN);
-    hipLaunchKernelGGL(up_proj_bf16_kernel, dim3(tm * tn), dim3(512), 0, s,
+    SlabOut none{};
+    hipLaunchKernelGGL(up_proj_bf16_kernel<false>, dim3(tm * tn), dim3(512), 0, s,
                        static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w),
                        static_cast<uint16_t *>(p.out), static_cast<int>(p.T), p.L, p.ldw, p.col0,
-                       static_cast<int>(p.ncols), tm, tn);
+                       static_cast<int>(p.ncols), tm, tn, none);
     return hipGetLastError();
   }
   const int64_t total = p.T * p.ncols;
@@ -268,6 +332,34 @@ int launch_up_proj(const UpProjPlan &p, void *stream) {
     hipLaunchKernelGGL(up_proj_generic_kernel<float>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const float *>(p.latent), static_cast<const float *>(p.w),
                        static_cast<float *>(p.out), p.T, p.L, p.ldw, p.col0, p.ncols);
+  return hipGetLastError();
+}
+
+int launch_project_pack(const ProjectPackPlan &p, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.T == 0) return hipSuccess;
+  SlabOut so;
+  so.send = static_cast<uint16_t *>(p.send);
+  so.cos = static_cast<const uint16_t *>(p.cos);
+  so.sin = static_cast<const uint16_t *>(p.sin);
+  so.tokens = p.T;
+  so.cs_stride = p.cs_stride;
+  so.P = p.P;
+  so.F = p.F;
+  so.col_off = p.col_off;
+  so.rope_off = p.R > 0 ? p.rope_off : p.P;   // no band: no column qualifies
+  so.R = p.R;
+  so.interleaved = p.interleaved;
+  for (int h = 0; h < p.heads; ++h) {
+    so.off[h] = static_cast<int16_t>(p.off[h]);
+    so.qr[h] = static_cast<int16_t>(p.qr[h]);
+  }
+  const int64_t ncols = static_cast<int64_t>(p.heads) * p.P;
+  const int tm = static_cast<int>((p.T + GM - 1) / GM);
+  const int tn = static_cast<int>((ncols + GN - 1) / GN);
+  hipLaunchKernelGGL(up_proj_bf16_kernel<true>, dim3(tm * tn), dim3(512), 0, s,
+                     static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w), nullptr,
+                     static_cast<int>(p.T), p.L, p.ldw, p.col0, static_cast<int>(ncols), tm, tn, so);
   return hipGetLastError();
 }
 

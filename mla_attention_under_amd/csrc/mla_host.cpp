@@ -206,6 +206,72 @@ int mla_apply_rope(void *x, int64_t tokens, int heads, int64_t stride_t, int64_t
   return launched(mla::launch_rope(p, stream), who);
 }
 
+int mla_project_pack(const void *latent, const void *w, void *send, int64_t tokens, int L, int w_heads, int head_begin,
+                     int heads, int P, int F, int col_offset, const int *sizes, int sp, int rope_offset, int R,
+                     const void *cos, const void *sin, int64_t cs_stride, int interleaved, int dtype, void *stream) {
+  const char *who = "mla_project_pack";
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (tokens < 0 || L < 1 || w_heads < 1 || heads < 1 || P < 1 || F < 1 || head_begin < 0 ||
+      head_begin + heads > w_heads || col_offset < 0 || col_offset + P > F || R < 0 || (interleaved != 0 && interleaved != 1))
+    return fail(MLA_EINVAL, "%s: inconsistent sizes (tokens %lld, L %d, heads [%d, %d) of %d, P %d, F %d, col_offset %d, R %d)",
+                who, static_cast<long long>(tokens), L, head_begin, head_begin + heads, w_heads, P, F, col_offset, R);
+  if (R > 0 && (rope_offset < 0 || rope_offset + R > P || R % 2))
+    return fail(MLA_EINVAL, "%s: the RoPE band [%d, %d) must be an even-width part of the %d-column block", who, rope_offset,
+                rope_offset + R, P);
+  if (heads > mla::kMaxSlabHeads) return fail(MLA_EUNSUPPORTED, "%s: more than %d heads", who, mla::kMaxSlabHeads);
+  mla::ProjectPackPlan p;
+  int offs[mla::kMaxRanks + 1];
+  const int rc = shard_offsets(sizes, sp, heads, offs, who);
+  if (rc != MLA_OK) return rc;
+  if (dtype != MLA_BF16) return fail(MLA_EUNSUPPORTED, "%s: bf16 only", who);
+  if (L % 8 || P % 8 || F % 8 || col_offset % 8 || (R > 0 && (rope_offset % 8 || R % 16)))
+    return fail(MLA_EUNSUPPORTED, "%s: L, P, F, col_offset, rope_offset must be multiples of 8 and R of 16", who);
+  if (R > 0)
+    for (int h = 0; h < heads; ++h) {
+      const int64_t b = static_cast<int64_t>(h) * P + rope_offset;
+      if (b / 128 != (b + R - 1) / 128)
+        return fail(MLA_EUNSUPPORTED, "%s: head %d's RoPE band crosses a 128-column tile", who, h);
+    }
+  if (tokens == 0) return ok();
+  if (latent == nullptr || w == nullptr || send == nullptr || (R > 0 && (cos == nullptr || sin == nullptr)))
+    return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w) |
+                       reinterpret_cast<uintptr_t>(send) |
+                       (R > 0 ? reinterpret_cast<uintptr_t>(cos) | reinterpret_cast<uintptr_t>(sin) : 0);
+  if (al % 16 || (R > 0 && (cs_stride % 8 || (tokens > 1 && cs_stride < R))))
+    return fail(MLA_EUNSUPPORTED, "%s: buffers must be 16-byte aligned, table rows multiples of 8 elements", who);
+  if (tokens >= (int64_t(1) << 31)) return fail(MLA_EUNSUPPORTED, "%s: too many tokens", who);
+  const uint64_t sb = static_cast<uint64_t>(tokens) * heads * F * 2;
+  const uintptr_t ps = reinterpret_cast<uintptr_t>(send), pl = reinterpret_cast<uintptr_t>(latent),
+                  pw = reinterpret_cast<uintptr_t>(w);
+  const uint64_t lb = static_cast<uint64_t>(tokens) * L * 2, wb = static_cast<uint64_t>(L) * w_heads * P * 2;
+  if ((ps < pl + lb && pl < ps + sb) || (ps < pw + wb && pw < ps + sb))
+    return fail(MLA_EINVAL, "%s: send overlaps an input", who);
+  for (int r = 0; r < sp; ++r)
+    for (int h = offs[r]; h < offs[r + 1]; ++h) {
+      p.off[h] = offs[r];
+      p.qr[h] = sizes[r];
+    }
+  p.latent = latent;
+  p.w = w;
+  p.send = send;
+  p.T = tokens;
+  p.L = L;
+  p.ldw = static_cast<int64_t>(w_heads) * P;
+  p.col0 = static_cast<int64_t>(head_begin) * P;
+  p.heads = heads;
+  p.P = P;
+  p.F = F;
+  p.col_off = col_offset;
+  p.rope_off = rope_offset;
+  p.R = R;
+  p.interleaved = interleaved;
+  p.cos = cos;
+  p.sin = sin;
+  p.cs_stride = cs_stride;
+  return launched(mla::launch_project_pack(p, stream), who);
+}
+
 namespace {
 // documents as [start, end) from cumulative ends; checks them
 int doc_ranges(const int64_t *ends, int n, std::vector<std::pair<int64_t, int64_t>> &docs, const char *who) {

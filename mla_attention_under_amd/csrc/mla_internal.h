@@ -57,6 +57,23 @@ struct UpProjPlan {
 };
 int launch_up_proj(const UpProjPlan &p, void *stream);
 
+// ---- projection written straight into the token->head pack (bf16)
+constexpr int kMaxSlabHeads = 256;
+struct ProjectPackPlan {
+  const void *latent;  // [T][L]
+  const void *w;       // [L][ldw], head blocks of P columns from col0
+  void *send;          // concat_r [T][sizes[r]][F]; columns [col_off, col_off + P) written
+  int64_t T;
+  int L;
+  int64_t ldw, col0;
+  int heads, P, F, col_off;
+  int rope_off, R, interleaved;   // R = 0: no rotation
+  const void *cos, *sin;
+  int64_t cs_stride;
+  int off[kMaxSlabHeads], qr[kMaxSlabHeads];   // per projected head: its rank's first head, that rank's head count
+};
+int launch_project_pack(const ProjectPackPlan &p, void *stream);
+
 // ---- attention ------------------------------------------------------------
 struct AttnPlan {
   const void *q;

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(RopeArgs a, int 
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const float x0 = get(xv, e), xp_ = get(pv, e), cs = get(cv, e), sn = get(sv, e);
-      out[e] = upper ? x0 * cs + xp_ * sn : x0 * cs - xp_ * sn;
+      out[e] = upper ? rope_im(xp_, x0, cs, sn) : rope_re(x0, xp_, cs, sn);
     }
   } else {
     const int tc = upper ? c - half : c;   // table chunk of this output chunk's pairs
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(RopeArgs a, int 
       const u32x4 &iv = e < E / 2 ? in0 : in1;
       const int k = 2 * (e % (E / 2));
       const float re = get(iv, k), im = get(iv, k + 1), cs = get(cv, e), sn = get(sv, e);
-      out[e] = upper ? im * cs + re * sn : re * cs - im * sn;
+      out[e] = upper ? rope_im(re, im, cs, sn) : rope_re(re, im, cs, sn);
     }
   }
   u32x4 w;
@@ -113,12 +113,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_generic_kernel(RopeArgs a, 
   for (int i = 0; i < H; ++i) {
     if (interleaved) {
       const float re = ld(xp, 2 * i), im = ld(xp, 2 * i + 1), c = ld(cp, i), s = ld(sp, i);
-      out[i] = re * c - im * s;
-      out[H + i] = im * c + re * s;
+      out[i] = rope_re(re, im, c, s);
+      out[H + i] = rope_im(re, im, c, s);
     } else {
       const float x0 = ld(xp, i), x1 = ld(xp, H + i);
-      out[i] = x0 * ld(cp, i) - x1 * ld(sp, i);
-      out[H + i] = x1 * ld(cp, H + i) + x0 * ld(sp, H + i);
+      out[i] = rope_re(x0, x1, ld(cp, i), ld(sp, i));
+      out[H + i] = rope_im(x0, x1, ld(cp, H + i), ld(sp, H + i));
     }
   }
   for (int i = 0; i < R; ++i) {

@@ -137,6 +137,45 @@ def test_rope_matches_oracle(name, T, H, N, R, bf16, interleaved):
         assert np.array_equal(bits(xd)[..., :N], x[..., :N].view(bits(xd).dtype)), "columns outside the band changed"
 
 
+PROJ_CASES = [
+    # (name, T, L, w_heads, head_begin, heads, P, F, col_offset, sizes, rope_offset, R)
+    ("q_part_rank_shard", 256, 1536, 128, 0, 128, 192, 448, 0, [16] * 8, 128, 64),
+    ("kv_part_rank_shard", 256, 512, 128, 0, 128, 256, 448, 192, [16] * 8, -1, 0),
+    ("q_part_uneven_ragged", 300, 1536, 128, 0, 128, 192, 448, 0, [22, 22, 21, 21, 21, 21], 128, 64),
+    ("q_part_head_range", 37, 512, 32, 8, 12, 192, 448, 0, [5, 4, 3], 128, 64),
+]
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("name,T,L,w_heads,hb,heads,P,F,col,sizes,ro,R", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_project_pack_equals_separate_calls(name, T, L, w_heads, hb, heads, P, F, col, sizes, ro, R, interleaved):
+    if R == 0 and interleaved:
+        pytest.skip("no band")
+    lat = dev(mi.draw((T, L), 41, 0))
+    W = dev(mi.draw((L, w_heads * P), 41, 1, std=L ** -0.5))
+    fill = dev(mi.draw((T, heads, F), 41, 2))
+    cos = sin = None
+    if R:
+        c, s = _rope_tables(T, R, True, offset=512)
+        cos, sin = dev(c), dev(s)
+    # separate calls: projection, rotation of the band, pack of the payload with that part in place
+    part = torch.empty((T, heads, P), dtype=torch.bfloat16, device="cuda")
+    mla.mla_latent_up_proj(lat, W, part, w_heads, hb, heads, P // 2, P - P // 2)   # any split of the P columns
+    if R:
+        mla.mla_apply_rope(part[..., ro:ro + R], cos, sin, interleaved=interleaved)
+    x = fill.clone()
+    x[..., col:col + P] = part
+    ref = torch.empty(x.numel(), dtype=torch.bfloat16, device="cuda")
+    mla.mla_pack_heads(x, ref, sizes)
+    # fused: the pack of the fill, then the projection written into its columns
+    send = torch.empty_like(ref)
+    mla.mla_pack_heads(fill, send, sizes)
+    mla.mla_project_pack(lat, W, send, w_heads, hb, heads, P, F, col, sizes, rope_offset=ro, cos=cos, sin=sin,
+                         interleaved=interleaved)
+    _sync()
+    assert np.array_equal(bits(send), bits(ref)), name
+
+
 def test_pack_zero_tokens_is_a_no_op():
     x = torch.zeros((0, 4, 8), dtype=torch.int16, device="cuda")
     send = torch.zeros(0, dtype=torch.int16, device="cuda")

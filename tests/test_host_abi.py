@@ -299,3 +299,25 @@ def test_rope_validation_before_launch(lib):
     assert call(c=X) == mla.MLA_EINVAL             # band overlaps a table
     assert call(x=ctypes.c_void_p(0x100001)) == mla.MLA_EINVAL   # misaligned
     assert call(tokens=0) == mla.MLA_OK
+
+
+def test_project_pack_validation_before_launch(lib):
+    f = lib.mla_project_pack
+    A, Wp, S = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x4000000), ctypes.c_void_p(0x8000000)
+    C, Sn = ctypes.c_void_p(0xc000000), ctypes.c_void_p(0xd000000)
+    sizes = (ctypes.c_int * 2)(2, 2)
+    base = dict(T=8, L=512, wh=4, hb=0, heads=4, P=192, F=448, col=0, ro=128, R=64, cs=64, inter=0, dt=mla.MLA_BF16)
+
+    def call(sz=sizes, sp=2, **kw):
+        a = dict(base, **kw)
+        return f(A, Wp, kw.get("send", S), a["T"], a["L"], a["wh"], a["hb"], a["heads"], a["P"], a["F"], a["col"],
+                 sz, sp, a["ro"], a["R"], C, Sn, a["cs"], a["inter"], a["dt"], None)
+    assert call(hb=1) == mla.MLA_EINVAL                 # head range outside the weight
+    assert call(col=300) == mla.MLA_EINVAL              # part wider than the payload row
+    assert call(ro=160) == mla.MLA_EINVAL               # band outside the block
+    assert call(sz=(ctypes.c_int * 2)(3, 2)) == mla.MLA_EINVAL   # sizes do not sum to heads
+    assert call(dt=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
+    assert call(L=500) == mla.MLA_EUNSUPPORTED          # not a multiple of 8
+    assert call(P=184, ro=120) == mla.MLA_EUNSUPPORTED  # a band crosses a 128-column tile
+    assert call(send=A) == mla.MLA_EINVAL               # send overlaps the latent
+    assert call(T=0) == mla.MLA_OK
