@@ -31,6 +31,11 @@ NumPy float64, with no blocking or fusion beyond what that definition states:
 * expanded pack         -- hyper-parallel ``_expanded`` (one sequence-to-head
                            exchange of concat(q, k, v) with unequal widths, the
                            key assembled by ``_assemble_key_value``).
+* backward              -- torchtitan "MLA CP optimization", section
+                           "Numerical comparison" (the two forms' gradients);
+                           hyper-parallel ``_selective_kv_launch`` (SUM
+                           gradients through repeated slices: the shared RoPE
+                           key's gradient is the sum over heads).
 * rotary embedding      -- hyper-parallel ``apply_mla_rope`` (position tables
                            given by the caller in the tensor's dtype; half-band
                            rotation, or adjacent pairs rotated and returned as
@@ -61,6 +66,7 @@ __all__ = [
     "attention", "decode_split_kv", "decode_reference", "doc_bounds",
     "ulysses_materialise_k_first", "ulysses_latent_first",
     "pack_expanded", "causal_partition", "kv_exchange_ranges", "rope",
+    "attention_backward", "latent_up_proj_backward",
 ]
 
 
@@ -474,3 +480,55 @@ def rope(x, cos, sin, interleaved: bool = False) -> np.ndarray:
     re_in, im_in = x[..., 0::2], x[..., 1::2]
     ci, si = c[..., :h], sn[..., :h]
     return np.concatenate([re_in * ci - im_in * si, im_in * ci + re_in * si], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Backward of the shard: attention, then the latent up-projection
+# --------------------------------------------------------------------------
+
+def attention_backward(q, kv, k_rope, dout, N: int, scale: float, causal: bool = True, cu_seqlens=None):
+    """Gradients of ``attention``'s output against dout [T][H][V].
+
+    Per document and head, with p the probabilities, v the values and k the
+    assembled key [k_nope | k_rope]: dv = p^T dout, dp = dout v^T, the row term
+    D_t = sum_j p_tj dp_tj, ds = p (dp - D), dq = scale ds k, dk = scale ds^T q.
+    Returns dq [T][H][N+R], dkv [T][H][N+V] (= [dk_nope | dv]) and dk_rope [T][R]:
+    the shared band receives the SUM over heads of each head's band gradient.
+    float64.
+    """
+    q, kv, k_rope, dout = widen(q), widen(kv), widen(k_rope), widen(dout)
+    T, H, _ = q.shape
+    dq = np.zeros_like(q)
+    dkv = np.zeros_like(kv)
+    dkr = np.zeros_like(k_rope)
+    for a, b in doc_bounds(cu_seqlens, T):
+        if b == a:
+            continue
+        for h in range(H):
+            s = _scores(q, kv, k_rope, h, slice(a, b), slice(a, b), N, scale)
+            if causal:
+                s = np.where(np.tril(np.ones((b - a, b - a), bool)), s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            v, do = kv[a:b, h, N:], dout[a:b, h]
+            dp = do @ v.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            k = np.concatenate([kv[a:b, h, :N], k_rope[a:b]], axis=1)
+            dq[a:b, h] = scale * (ds @ k)
+            dk = scale * (ds.T @ q[a:b, h])
+            dkv[a:b, h, :N] = dk[:, :N]
+            dkv[a:b, h, N:] = p.T @ do
+            dkr[a:b] += dk[:, N:]
+    return dq, dkv, dkr
+
+
+def latent_up_proj_backward(latent, w_kvb, head_begin: int, heads: int, dkv, N: int, V: int):
+    """Gradients of ``latent_up_proj`` against dkv [T][heads][N+V]: d_latent [T][L] =
+    dkv W_cols^T and dW = latent^T dkv on the head range's columns (zero elsewhere). float64."""
+    c, W, g = widen(latent), widen(w_kvb), widen(dkv)
+    P = N + V
+    cols = slice(head_begin * P, (head_begin + heads) * P)
+    g2 = g.reshape(c.shape[0], heads * P)
+    dW = np.zeros_like(W)
+    dW[:, cols] = c.T @ g2
+    return g2 @ W[:, cols].T, dW

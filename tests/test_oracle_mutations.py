@@ -206,3 +206,56 @@ def test_rope_with_a_flipped_rotation_is_caught(monkeypatch):
     _patch(monkeypatch, "rope", bad)
     assert _fails(lambda: tp.test_rope_is_complex_multiplication(False))
     assert _fails(lambda: tp.test_rope_is_complex_multiplication(True))
+
+
+# ---- backward
+
+import test_oracle_backward as tb  # noqa: E402
+
+
+def _backward_pins_fail():
+    pins = [lambda: tb.test_attention_backward_matches_autograd(True, None),
+            tb.test_attention_backward_matches_finite_differences,
+            tb.test_shard_backward_chain_matches_autograd]
+    return any(_fails(p) for p in pins)
+
+
+def _backward_with(mutate):
+    real = om.attention_backward
+
+    def bad(q, kv, k_rope, dout, N, scale, causal=True, cu_seqlens=None):
+        return mutate(real, q, kv, k_rope, dout, N, scale, causal, cu_seqlens)
+    return bad
+
+
+def test_backward_without_the_row_term_is_caught(monkeypatch):
+    # ds = p * dp, the softmax Jacobian's row term D = sum_j p dp forgotten
+    def bad(q, kv, k_rope, dout, N, scale, causal=True, cu_seqlens=None):
+        q, kv, k_rope, dout = (om.widen(x) for x in (q, kv, k_rope, dout))
+        T, H, _ = q.shape
+        dq, dkv, dkr = np.zeros_like(q), np.zeros_like(kv), np.zeros_like(k_rope)
+        for a, b in om.doc_bounds(cu_seqlens, T):
+            for h in range(H):
+                s = om._scores(q, kv, k_rope, h, slice(a, b), slice(a, b), N, scale)
+                if causal:
+                    s = np.where(np.tril(np.ones((b - a, b - a), bool)), s, -np.inf)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                ds = p * (dout[a:b, h] @ kv[a:b, h, N:].T)
+                k = np.concatenate([kv[a:b, h, :N], k_rope[a:b]], axis=1)
+                dq[a:b, h] = scale * ds @ k
+                dk = scale * ds.T @ q[a:b, h]
+                dkv[a:b, h, :N], dkv[a:b, h, N:] = dk[:, :N], p.T @ dout[a:b, h]
+                dkr[a:b] += dk[:, N:]
+        return dq, dkv, dkr
+    _patch(monkeypatch, "attention_backward", bad)
+    assert _backward_pins_fail()
+
+
+def test_backward_shared_band_from_one_head_is_caught(monkeypatch):
+    def mutate(real, q, kv, k_rope, dout, N, scale, causal, cu):
+        dq, dkv, _ = real(q, kv, k_rope, dout, N, scale, causal, cu)
+        one = real(q[:, :1], kv[:, :1], k_rope, dout[:, :1], N, scale, causal, cu)[2]
+        return dq, dkv, one
+    _patch(monkeypatch, "attention_backward", _backward_with(mutate))
+    assert _backward_pins_fail() or _fails(tb.test_shared_band_gradient_is_the_sum_over_heads)
