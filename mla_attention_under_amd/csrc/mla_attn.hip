@@ -899,15 +899,33 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int3
     for (int t = tid; t < nt; t += kSchedThreads) atomicAdd(&hist[work_of(d, t)], 1);
   }
   __syncthreads();
-  // descending-bin exclusive offsets (serial over bins; 4096 bins, one thread)
-  if (tid == 0) {
-    int acc = 0;
-    for (int b = kSchedBins - 1; b >= 0; --b) {
-      const int v = hist[b];
-      hist[b] = acc;
-      acc += v;
+  // descending-bin exclusive offsets: thread i scans bins [kSchedBins-1 - PER*i, -PER) of the
+  // descending order, the per-thread sums meet in a block-wide scan
+  {
+    constexpr int PER = kSchedBins / kSchedThreads;
+    static_assert(PER * kSchedThreads == kSchedBins, "bins per thread");
+    int local[PER];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      local[k] = hist[kSchedBins - 1 - (PER * tid + k)];
+      sum += local[k];
     }
-    *count = min(total, max_tasks);
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kSchedThreads; off <<= 1) {
+      const int add = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    int acc = part[tid] - sum;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      hist[kSchedBins - 1 - (PER * tid + k)] = acc;
+      acc += local[k];
+    }
+    if (tid == 0) *count = min(total, max_tasks);
   }
   __syncthreads();
   for (int d = 0; d < n_seq; ++d) {
