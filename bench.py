@@ -233,6 +233,45 @@ def _project_pack(torch, mla):
     return out
 
 
+def _backward(torch, mla):
+    """Backward of the rank shard's attention (T=2048, H=16, dense causal): the whole mla_attention_bwd call.
+    FLOPs = the five products per visible (query, key) pair of the standard backward (scores, dp, dv, dk, dq):
+    2*(3*(N+R) + 2*V) per pair, H*T(T+1)/2 pairs; the kernels also recompute scores and dp for dq."""
+    T, H, N, R, V = 2048, 16, 128, 64, 128
+    g = torch.Generator(device="cuda").manual_seed(8)
+    q = torch.randn((T, H, N + R), device="cuda", generator=g).bfloat16()
+    kv = torch.randn((T, H, N + V), device="cuda", generator=g).bfloat16()
+    kr = torch.randn((T, R), device="cuda", generator=g).bfloat16()
+    dout = torch.randn((T, H, V), device="cuda", generator=g).bfloat16()
+    out = torch.empty((T, H, V), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    scale = 1 / math.sqrt(N + R)
+    mla.mla_attention_fwd(q, kv, kr, out, N, R, V, scale, causal=True, lse=lse)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq, dkv, dkr = torch.empty((T, H, N + R), **f32), torch.empty((T, H, N + V), **f32), torch.empty((T, R), **f32)
+    ws = torch.empty(mla.mla_attention_bwd_workspace_size(q, kv, kr, out, dout, N, R, V, scale), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: mla.mla_attention_bwd(q, kv, kr, out, dout, lse, N, R, V, scale, causal=True,  # noqa: E731
+                                         dq=dq, dkv=dkv, dk_rope=dkr, workspace=ws)
+    for _ in range(3):
+        call()
+    reps = 20
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(reps):
+        call()
+    en.record()
+    torch.cuda.synchronize()
+    us = st.elapsed_time(en) * 1e3 / reps
+    flops = 2.0 * (3 * (N + R) + 2 * V) * H * T * (T + 1) / 2
+    tf = flops / (us * 1e-6) / 1e12
+    return {"attention_bwd_us": round(us, 2), "attention_bwd_tflops": round(tf, 1),
+            "attention_bwd_mfma_frac": round(tf / 2500.0, 4),
+            "attention_bwd_note": "dsv3_rank shard (T=2048, H=16, causal), row terms + dk/dv + dq + band sum, "
+                                  "fp32 gradients; 5 products per visible pair counted"}
+
+
 def _varlen(torch, mla, mi, dev):
     """Packed documents 8192/4096/2048/2048 (T=16384, H=16): block-diagonal causal attention."""
     w = mi.WORKLOADS["varlen16k"]
@@ -428,6 +467,7 @@ def main():
         extra.update(_expanded(torch, mla))
         extra.update(_rope(torch, mla))
         extra.update(_project_pack(torch, mla))
+        extra.update(_backward(torch, mla))
         extra.update(_varlen(torch, mla, mi, dev))
         extra.update(_decode(torch, mla, mi, dev))
 

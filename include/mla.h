@@ -262,6 +262,59 @@ size_t mla_attention_workspace_size(const mla_attn_args *a);
 int mla_attention_fwd(const mla_attn_args *a, void *stream);
 
 /*
+ * Backward of mla_attention_fwd (torchtitan "MLA CP optimization", section
+ * "Numerical comparison": the method is trained end to end; hyper-parallel
+ * `_assemble_key_value`: the shared band is one tensor repeated over the
+ * heads, so it receives the SUM of the heads' band gradients). With p the
+ * probabilities rebuilt from lse, D_t = dout[t][h] . out[t][h] and the key
+ * k = [k_nope | k_rope]:
+ *   dv = p^T dout, ds = p (dout v^T - D), dq = scale ds k, dk = scale ds^T q,
+ *   dk_rope[j] = sum over h of dk[j][h][N:].
+ * Inputs as in mla_attention_fwd (same strides, documents and causal flag),
+ * plus:
+ *   out    : [T][H][V] the forward's output, rows at out + t*o_stride_t + h*o_stride_h
+ *   dout   : [T][H][V] gradient of out, rows at dout + t*do_stride_t + h*do_stride_h
+ *   lse    : fp32 [H][T], the forward's natural-log softmax denominator
+ * Outputs (fp32, contiguous, every element written):
+ *   dq     : [T][H][N+R]
+ *   dkv    : [T][H][N+V]  (= [dk_nope | dv], the layout of kv)
+ *   dk_rope: [T][R]
+ * Runs bf16 with N=128, R=64, V=128 (MLA_EUNSUPPORTED otherwise), 16-byte
+ * aligned inputs and strides that are multiples of 8 elements.
+ * Workspace: mla_attention_bwd_workspace_size() bytes, 256-byte aligned,
+ * contents need not be initialised (row terms and per-head band gradients).
+ * The result does not depend on scheduling: every sum runs in a fixed order.
+ */
+typedef struct mla_attn_bwd_args {
+  const void *q;
+  int64_t q_stride_t, q_stride_h;
+  const void *kv;
+  int64_t kv_stride_t, kv_stride_h;
+  const void *k_rope;
+  int64_t kr_stride_t;
+  const void *out;
+  int64_t o_stride_t, o_stride_h;
+  const void *dout;
+  int64_t do_stride_t, do_stride_h;
+  const float *lse;
+  float *dq;
+  float *dkv;
+  float *dk_rope;
+  const int32_t *cu_seqlens;
+  int n_seq;
+  int64_t T;
+  int H, N, R, V;
+  float scale;
+  int causal;
+  int dtype;
+  void *workspace;
+  size_t workspace_bytes;
+} mla_attn_bwd_args;
+
+size_t mla_attention_bwd_workspace_size(const mla_attn_bwd_args *a);
+int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream);
+
+/*
  * Latent-cache decode: one new query token per sequence attends over its whole
  * cached latent, reduced in num_splits KV chunks with an online softmax
  * (DeepSpeed PR #8602, "Components": decode attention with KV split-K and an

@@ -24,6 +24,7 @@ EXPORTS = (
     "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
     "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope", "mla_project_pack",
+    "mla_attention_bwd_workspace_size", "mla_attention_bwd",
 )
 
 
@@ -40,6 +41,21 @@ class mla_attn_args(ctypes.Structure):
         ("k_rope", ctypes.c_void_p), ("kr_stride_t", ctypes.c_int64),
         ("out", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
         ("lse", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("n_seq", ctypes.c_int),
+        ("T", ctypes.c_int64), ("H", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int), ("V", ctypes.c_int),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class mla_attn_bwd_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+        ("kv", ctypes.c_void_p), ("kv_stride_t", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
+        ("k_rope", ctypes.c_void_p), ("kr_stride_t", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
+        ("dout", ctypes.c_void_p), ("do_stride_t", ctypes.c_int64), ("do_stride_h", ctypes.c_int64),
+        ("lse", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dkv", ctypes.c_void_p), ("dk_rope", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("n_seq", ctypes.c_int),
         ("T", ctypes.c_int64), ("H", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int), ("V", ctypes.c_int),
         ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
@@ -86,6 +102,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_attention_workspace_size.argtypes = [ctypes.POINTER(mla_attn_args)]
     lib.mla_attention_workspace_size.restype = sz
     lib.mla_attention_fwd.argtypes = [ctypes.POINTER(mla_attn_args), vp]
+    lib.mla_attention_bwd_workspace_size.argtypes = [ctypes.POINTER(mla_attn_bwd_args)]
+    lib.mla_attention_bwd_workspace_size.restype = sz
+    lib.mla_attention_bwd.argtypes = [ctypes.POINTER(mla_attn_bwd_args), vp]
     lib.mla_latent_decode_workspace_size.argtypes = [ctypes.POINTER(mla_decode_args)]
     lib.mla_latent_decode_workspace_size.restype = sz
     lib.mla_latent_decode_fwd.argtypes = [ctypes.POINTER(mla_decode_args), vp]
@@ -314,6 +333,60 @@ def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None,
     a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace)
     _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def _attn_bwd_args(q, kv, k_rope, out, dout, lse, dq, dkv, dk_rope, N, R, V, scale, causal, cu_seqlens,
+                   workspace):
+    T, H = q.shape[0], q.shape[1]
+    a = mla_attn_bwd_args()
+    a.q, a.q_stride_t, a.q_stride_h = q.data_ptr(), q.stride(0), q.stride(1)
+    a.kv, a.kv_stride_t, a.kv_stride_h = kv.data_ptr(), kv.stride(0), kv.stride(1)
+    a.k_rope, a.kr_stride_t = k_rope.data_ptr(), k_rope.stride(0)
+    a.out, a.o_stride_t, a.o_stride_h = out.data_ptr(), out.stride(0), out.stride(1)
+    a.dout, a.do_stride_t, a.do_stride_h = dout.data_ptr(), dout.stride(0), dout.stride(1)
+    a.lse = None if lse is None else lse.data_ptr()
+    a.dq = None if dq is None else dq.data_ptr()
+    a.dkv = None if dkv is None else dkv.data_ptr()
+    a.dk_rope = None if dk_rope is None else dk_rope.data_ptr()
+    a.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    a.n_seq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a.T, a.H, a.N, a.R, a.V = T, H, N, R, V
+    a.scale, a.causal, a.dtype = float(scale), int(bool(causal)), _dtype(q)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def mla_attention_bwd_workspace_size(q, kv, k_rope, out, dout, N, R, V, scale, causal=True, cu_seqlens=None) -> int:
+    a = _attn_bwd_args(q, kv, k_rope, out, dout, None, None, None, None, N, R, V, scale, causal, cu_seqlens, None)
+    return int(load_library().mla_attention_bwd_workspace_size(ctypes.byref(a)))
+
+
+def mla_attention_bwd(q, kv, k_rope, out, dout, lse, N, R, V, scale, causal=True, cu_seqlens=None,
+                      dq=None, dkv=None, dk_rope=None, workspace=None, stream=None):
+    """Gradients of mla_attention_fwd: (dq [T][H][N+R], dkv [T][H][N+V], dk_rope [T][R]), fp32.
+
+    out and lse are the forward's output and log-sum-exp; dout the gradient of
+    out. Missing outputs and the workspace are allocated through PyTorch.
+    """
+    lib = load_library()
+    _dev(q, kv, k_rope, out, dout, lse, cu_seqlens, dq, dkv, dk_rope, workspace)
+    for t in (q, kv, k_rope, out, dout):
+        assert t.stride(-1) == 1
+    T, H = q.shape[0], q.shape[1]
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(T, H, N + R, **f32) if dq is None else dq
+    dkv = torch.empty(T, H, N + V, **f32) if dkv is None else dkv
+    dk_rope = torch.empty(T, R, **f32) if dk_rope is None else dk_rope
+    for t in (dq, dkv, dk_rope, lse):
+        assert t.dtype == torch.float32 and t.is_contiguous()
+    if workspace is None:
+        workspace = _workspace(mla_attention_bwd_workspace_size(q, kv, k_rope, out, dout, N, R, V, scale, causal,
+                                                                cu_seqlens), q.device)
+    a = _attn_bwd_args(q, kv, k_rope, out, dout, lse, dq, dkv, dk_rope, N, R, V, scale, causal, cu_seqlens,
+                       workspace)
+    _check("mla_attention_bwd", lib.mla_attention_bwd(ctypes.byref(a), _stream(stream)))
+    return dq, dkv, dk_rope
 
 
 def _decode_args(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits, scale,

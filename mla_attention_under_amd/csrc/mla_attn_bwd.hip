@@ -1,0 +1,354 @@
+// Backward of the shard's attention with the head-shared RoPE key band
+// (torchtitan "MLA CP optimization", section "Numerical comparison": the
+// method is trained, so the shard is differentiated; hyper-parallel
+// `_assemble_key_value`: the band is one tensor repeated over the heads, so
+// its gradient is the sum of every head's band gradient).
+//
+// Per head, with p the probabilities recomputed from the forward's
+// log-sum-exp, the row term D_t = sum_v dout[t][v] out[t][v], and k the key
+// [k_nope | k_rope]:
+//   dv = p^T dout, dp = dout v^T, ds = p (dp - D), dq = scale ds k,
+//   dk = scale ds^T q; dk_rope = sum over heads of dk[..., N:].
+//
+// Three passes, all on blocks of 32 keys by 32 queries with the score block
+// kept transposed (keys are rows, queries are the lanes' columns, so a lane's
+// log-sum-exp and row term are one register each):
+//   row_term_kernel   D[h][t] from out and dout;
+//   dkdv_kernel       one workgroup per (32 keys, head): dk, dv accumulated
+//                     over the query blocks that see the keys; the band part
+//                     of dk goes to a per-head slice of the workspace;
+//   dq_kernel         one workgroup per (32 queries, head): dq accumulated
+//                     over the key blocks the queries see (scores recomputed
+//                     rather than reduced across workgroups, so no atomics and
+//                     a fixed summation order);
+//   band_sum_kernel   dk_rope[t] = sum over heads of the band slices, in head
+//                     order.
+// The five products per block are bf16 MFMAs (v_mfma_f32_32x32x16_bf16) with
+// fp32 accumulation; p and ds are rounded to bf16 as MFMA operands.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mla_common.cuh"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int BB = 32;          // keys or queries per block
+constexpr int TP = BB + 8;      // pitch of the transposed (column-major) LDS copies, in bf16
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdArgs {
+  const uint16_t *q, *kv, *kr, *out, *dout;
+  int64_t q_st, q_sh, kv_st, kv_sh, kr_st, o_st, o_sh, do_st, do_sh;   // in elements
+  const float *lse;     // [H][T], natural log
+  float *dq, *dkv;      // [T][H][N+R], [T][H][N+V]
+  float *dkr;           // [T][R]
+  float *Dws;           // [H][T] row terms
+  float *band;          // [H][T][R] per-head band gradients
+  const int32_t *cu;
+  int n_seq;
+  int T, H;
+  float scale;
+  int causal;
+};
+
+// document [lo, hi) holding token t (one document of T tokens without cu)
+__device__ __forceinline__ void doc_of(const BwdArgs &a, int t, int &lo, int &hi) {
+  if (a.cu == nullptr) {
+    lo = 0;
+    hi = a.T;
+    return;
+  }
+  int l = 0, r = a.n_seq;   // largest d with cu[d] <= t lies in [l, r)
+  while (r - l > 1) {
+    const int m = (l + r) >> 1;
+    if (a.cu[m] <= t) l = m;
+    else r = m;
+  }
+  lo = a.cu[l];
+  hi = a.cu[l + 1];
+}
+
+// 32 rows [r0, r0+32) of W bf16 columns (row t at src + t*st) into LDS rows of
+// pitch P at column c0; rows at or past lim read as zero. With TR, also the
+// transposed copy dstT[(c0 + c)*TP + row].
+template <int W, int P, bool TR>
+__device__ __forceinline__ void load_rows(const uint16_t *src, int64_t st, int r0, int lim, uint16_t *dst, int c0,
+                                          uint16_t *dstT, int lane) {
+  constexpr int CH = W / 8;
+  static_assert((BB * CH) % 64 == 0, "whole passes of the wave");
+#pragma unroll
+  for (int it = 0; it < BB * CH / 64; ++it) {
+    const int cidx = it * 64 + lane;
+    const int r = cidx / CH, k = (cidx % CH) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + r < lim) v = *reinterpret_cast<const u32x4 *>(src + static_cast<int64_t>(r0 + r) * st + k);
+    *reinterpret_cast<u32x4 *>(dst + r * P + c0 + k) = v;
+    if constexpr (TR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = v[e >> 1];
+        dstT[(c0 + k + e) * TP + r] = static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    }
+  }
+}
+
+// MFMA operand of contraction step s from a row-major LDS block: lane l takes
+// row rbase + l%32, elements 16s + 8*(l/32) .. +7.
+__device__ __forceinline__ bf16x8 frag(const uint16_t *m, int pitch, int rbase, int s, int lane) {
+  return *reinterpret_cast<const bf16x8 *>(m + (rbase + (lane & 31)) * pitch + 16 * s + 8 * (lane >> 5));
+}
+
+// Score block transposed: st[i][j] = k_i . q_j over the K columns (no scale).
+template <int K, int KP>
+__device__ __forceinline__ f32x16 scores_t(const uint16_t *Ks, const uint16_t *Qs, int lane) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < K / 16; ++s) acc = mfma32(frag(Ks, KP, 0, s, lane), frag(Qs, KP, 0, s, lane), acc);
+  return acc;
+}
+
+// row i of the block held in register r of lane l (column l%32)
+__device__ __forceinline__ int row_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// p^T and ds^T of one block, from the transposed scores and dp^T:
+//   p = exp(scale*s - lse_j), ds = p (dp - D_j), zero where key i is not
+// visible to query j (another document, past the diagonal, past T).
+__device__ __forceinline__ void probs_t(const BwdArgs &a, f32x16 &st, f32x16 &dp, int k0, int q, int qlo, int qhi,
+                                        float lse2, float Dq, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = k0 + row_of(r, lane);
+    const bool vis = key >= qlo && key < qhi && (!a.causal || key <= q);
+    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], a.scale * kLog2e, -lse2)) : 0.f;
+    st[r] = p;
+    dp[r] = p * (dp[r] - Dq);
+  }
+}
+
+// block values (C layout) to a row-major bf16 LDS block [i][j], or its transpose
+__device__ __forceinline__ void store_block(const f32x16 &v, uint16_t *m, bool transpose, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = row_of(r, lane), j = lane & 31;
+    m[transpose ? j * TP + i : i * TP + j] = f32_to_bf16(v[r]);
+  }
+}
+
+__global__ __launch_bounds__(256) void row_term_kernel(BwdArgs a, int V) {
+  // 16 lanes per (t, h) row, 8 elements each per pass
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid >> 4;
+  const int c = static_cast<int>(gid & 15);
+  const bool live = row < static_cast<int64_t>(a.T) * a.H;
+  const int t = live ? static_cast<int>(row / a.H) : 0, h = live ? static_cast<int>(row % a.H) : 0;
+  float acc = 0.f;
+  if (live) {
+    const uint16_t *o = a.out + t * a.o_st + h * a.o_sh;
+    const uint16_t *g = a.dout + t * a.do_st + h * a.do_sh;
+    for (int k = 8 * c; k < V; k += 128) {
+      const u32x4 ov = *reinterpret_cast<const u32x4 *>(o + k);
+      const u32x4 gv = *reinterpret_cast<const u32x4 *>(g + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(bf16_elem(ov, e), bf16_elem(gv, e), acc);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (live && c == 0) a.Dws[static_cast<int64_t>(h) * a.T + t] = acc;
+}
+
+template <int N, int R, int V>
+__global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
+  constexpr int K = N + R, KP = K + 8, VP = V + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BB * KP], Vs[BB * VP], Qs[BB * KP], Os[BB * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t QsT[K * TP], OsT[V * TP], Ps[BB * TP], Ss[BB * TP];
+  const int lane = threadIdx.x;
+  const int h = blockIdx.y, k0 = blockIdx.x * BB;
+  const int k1 = min(k0 + BB, a.T) - 1;   // last key of the block
+  int lo0, hi0, lo1, hi1;
+  doc_of(a, k0, lo0, hi0);
+  doc_of(a, k1, lo1, hi1);
+  // queries that see some key of the block
+  const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? k0 : lo0);
+  const int qend = __builtin_amdgcn_readfirstlane(hi1);
+
+  load_rows<N, KP, false>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, Ks, 0, nullptr, lane);
+  if constexpr (R > 0) load_rows<R, KP, false>(a.kr, a.kr_st, k0, a.T, Ks, N, nullptr, lane);
+  load_rows<V, VP, false>(a.kv + h * a.kv_sh + N, a.kv_st, k0, a.T, Vs, 0, nullptr, lane);
+
+  f32x16 dk[K / 32] = {}, dv[V / 32] = {};
+  for (int q0 = qbeg; q0 < qend; q0 += BB) {
+    __syncthreads();   // the previous block's readers are done
+    load_rows<K, KP, true>(a.q + h * a.q_sh, a.q_st, q0, a.T, Qs, 0, QsT, lane);
+    load_rows<V, VP, true>(a.dout + h * a.do_sh, a.do_st, q0, a.T, Os, 0, OsT, lane);
+    const int q = q0 + (lane & 31);
+    int qlo = 1, qhi = 0;   // no key visible to a query past T
+    float lse2 = 0.f, Dq = 0.f;
+    if (q < a.T) {
+      doc_of(a, q, qlo, qhi);
+      lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
+      Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
+    }
+    __syncthreads();
+    f32x16 st = scores_t<K, KP>(Ks, Qs, lane);
+    f32x16 dp = {};
+#pragma unroll
+    for (int s = 0; s < V / 16; ++s) dp = mfma32(frag(Vs, VP, 0, s, lane), frag(Os, VP, 0, s, lane), dp);
+    probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
+    store_block(st, Ps, false, lane);   // p^T [key][query]
+    store_block(dp, Ss, false, lane);   // ds^T [key][query]
+    __syncthreads();
+    // dv[key][v] += p^T[key][q] dout[q][v]; dk[key][c] += ds^T[key][q] q[q][c]
+#pragma unroll
+    for (int s = 0; s < BB / 16; ++s) {
+      const bf16x8 pa = frag(Ps, TP, 0, s, lane), sa = frag(Ss, TP, 0, s, lane);
+#pragma unroll
+      for (int vt = 0; vt < V / 32; ++vt) dv[vt] = mfma32(pa, frag(OsT, TP, 32 * vt, s, lane), dv[vt]);
+#pragma unroll
+      for (int kt = 0; kt < K / 32; ++kt) dk[kt] = mfma32(sa, frag(QsT, TP, 32 * kt, s, lane), dk[kt]);
+    }
+  }
+  // rows past T are not written; dk_nope and dv to dkv, the band to the head's slice
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = k0 + row_of(r, lane);
+    if (key >= a.T) continue;
+    float *row = a.dkv + (static_cast<int64_t>(key) * a.H + h) * (N + V);
+    float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
+#pragma unroll
+    for (int kt = 0; kt < K / 32; ++kt) {
+      const int c = 32 * kt + (lane & 31);
+      const float g = a.scale * dk[kt][r];
+      if (c < N) row[c] = g;
+      else brow[c - N] = g;
+    }
+#pragma unroll
+    for (int vt = 0; vt < V / 32; ++vt) row[N + 32 * vt + (lane & 31)] = dv[vt][r];
+  }
+}
+
+template <int N, int R, int V>
+__global__ __launch_bounds__(64) void dq_kernel(BwdArgs a) {
+  constexpr int K = N + R, KP = K + 8, VP = V + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[BB * KP], Os[BB * VP], Ks[BB * KP], Vs[BB * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t KsT[K * TP], Ss[BB * TP];
+  const int lane = threadIdx.x;
+  const int h = blockIdx.y, q0 = blockIdx.x * BB;
+  const int q1 = min(q0 + BB, a.T) - 1;
+  int lo0, hi0, lo1, hi1;
+  doc_of(a, q0, lo0, hi0);
+  doc_of(a, q1, lo1, hi1);
+  // keys some query of the block sees
+  const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
+  const int kend = __builtin_amdgcn_readfirstlane(a.causal ? q1 + 1 : hi1);
+
+  load_rows<K, KP, false>(a.q + h * a.q_sh, a.q_st, q0, a.T, Qs, 0, nullptr, lane);
+  load_rows<V, VP, false>(a.dout + h * a.do_sh, a.do_st, q0, a.T, Os, 0, nullptr, lane);
+  const int q = q0 + (lane & 31);
+  int qlo = 1, qhi = 0;
+  float lse2 = 0.f, Dq = 0.f;
+  if (q < a.T) {
+    doc_of(a, q, qlo, qhi);
+    lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
+    Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
+  }
+
+  f32x16 dq[K / 32] = {};
+  for (int k0 = kbeg; k0 < kend; k0 += BB) {
+    __syncthreads();
+    load_rows<N, KP, true>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, Ks, 0, KsT, lane);
+    if constexpr (R > 0) load_rows<R, KP, true>(a.kr, a.kr_st, k0, a.T, Ks, N, KsT, lane);
+    load_rows<V, VP, false>(a.kv + h * a.kv_sh + N, a.kv_st, k0, a.T, Vs, 0, nullptr, lane);
+    __syncthreads();
+    f32x16 st = scores_t<K, KP>(Ks, Qs, lane);
+    f32x16 dp = {};
+#pragma unroll
+    for (int s = 0; s < V / 16; ++s) dp = mfma32(frag(Vs, VP, 0, s, lane), frag(Os, VP, 0, s, lane), dp);
+    probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
+    store_block(dp, Ss, true, lane);   // ds [query][key]
+    __syncthreads();
+    // dq[q][c] += ds[q][key] k[key][c]
+#pragma unroll
+    for (int s = 0; s < BB / 16; ++s) {
+      const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+#pragma unroll
+      for (int kt = 0; kt < K / 32; ++kt) dq[kt] = mfma32(sa, frag(KsT, TP, 32 * kt, s, lane), dq[kt]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = q0 + row_of(r, lane);
+    if (t >= a.T) continue;
+    float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K;
+#pragma unroll
+    for (int kt = 0; kt < K / 32; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt][r];
+  }
+}
+
+__global__ __launch_bounds__(256) void band_sum_kernel(BwdArgs a, int R) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(a.T) * R) return;
+  float acc = 0.f;
+  for (int h = 0; h < a.H; ++h) acc += a.band[static_cast<int64_t>(h) * a.T * R + i];
+  a.dkr[i] = acc;
+}
+
+template <int N, int R, int V>
+int run(const BwdArgs &a, hipStream_t s) {
+  const unsigned rows = static_cast<unsigned>((static_cast<int64_t>(a.T) * a.H * 16 + 255) / 256);
+  row_term_kernel<<<rows, 256, 0, s>>>(a, V);
+  const dim3 grid(static_cast<unsigned>((a.T + BB - 1) / BB), static_cast<unsigned>(a.H));
+  dkdv_kernel<N, R, V><<<grid, 64, 0, s>>>(a);
+  dq_kernel<N, R, V><<<grid, 64, 0, s>>>(a);
+  const unsigned sums = static_cast<unsigned>((static_cast<int64_t>(a.T) * R + 255) / 256);
+  if (R > 0) band_sum_kernel<<<sums, 256, 0, s>>>(a, R);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_supported(int N, int R, int V) { return N == 128 && R == 64 && V == 128; }
+
+size_t attn_bwd_workspace_bytes(int64_t T, int H, int R) {
+  const size_t d = (static_cast<size_t>(T) * H * 4 + 255) / 256 * 256;
+  const size_t b = (static_cast<size_t>(T) * H * R * 4 + 255) / 256 * 256;
+  return d + b;
+}
+
+int launch_attention_bwd(const AttnBwdPlan &p, void *stream) {
+  BwdArgs a;
+  a.q = static_cast<const uint16_t *>(p.q);
+  a.kv = static_cast<const uint16_t *>(p.kv);
+  a.kr = static_cast<const uint16_t *>(p.kr);
+  a.out = static_cast<const uint16_t *>(p.out);
+  a.dout = static_cast<const uint16_t *>(p.dout);
+  a.q_st = p.q_st;
+  a.q_sh = p.q_sh;
+  a.kv_st = p.kv_st;
+  a.kv_sh = p.kv_sh;
+  a.kr_st = p.kr_st;
+  a.o_st = p.o_st;
+  a.o_sh = p.o_sh;
+  a.do_st = p.do_st;
+  a.do_sh = p.do_sh;
+  a.lse = p.lse;
+  a.dq = p.dq;
+  a.dkv = p.dkv;
+  a.dkr = p.dkr;
+  a.Dws = static_cast<float *>(p.ws);
+  a.band = reinterpret_cast<float *>(static_cast<char *>(p.ws) + (static_cast<size_t>(p.T) * p.H * 4 + 255) / 256 * 256);
+  a.cu = p.cu;
+  a.n_seq = p.n_seq;
+  a.T = static_cast<int>(p.T);
+  a.H = p.H;
+  a.scale = p.scale;
+  a.causal = p.causal;
+  if (p.T == 0) return hipSuccess;
+  return run<128, 64, 128>(a, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace mla

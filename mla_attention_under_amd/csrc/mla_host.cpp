@@ -492,6 +492,83 @@ int mla_attention_fwd(const mla_attn_args *a, void *stream) {
   return launched(mla::launch_attention(p, stream), who);
 }
 
+static int attn_bwd_validate(const mla_attn_bwd_args *a, const char *who) {
+  if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
+  if (!valid_dtype(a->dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, a->dtype);
+  if (a->T < 0 || a->H < 1 || a->N < 1 || a->R < 0 || a->V < 1)
+    return fail(MLA_EINVAL, "%s: need T >= 0, H >= 1, N >= 1, R >= 0, V >= 1", who);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(MLA_EINVAL, "%s: scale must be finite and positive", who);
+  if (a->cu_seqlens != nullptr && a->n_seq < 1) return fail(MLA_EINVAL, "%s: cu_seqlens needs n_seq >= 1", who);
+  const int64_t K = static_cast<int64_t>(a->N) + a->R, P = static_cast<int64_t>(a->N) + a->V;
+  if (a->q_stride_h < K || a->q_stride_t < a->q_stride_h * (a->H - 1) + K)
+    return fail(MLA_EINVAL, "%s: q strides overlap rows of width N+R", who);
+  if (a->kv_stride_h < P || a->kv_stride_t < a->kv_stride_h * (a->H - 1) + P)
+    return fail(MLA_EINVAL, "%s: kv strides overlap rows of width N+V", who);
+  if (a->kr_stride_t < a->R) return fail(MLA_EINVAL, "%s: k_rope stride below R", who);
+  if (a->o_stride_h < a->V || a->o_stride_t < a->o_stride_h * (a->H - 1) + a->V ||
+      a->do_stride_h < a->V || a->do_stride_t < a->do_stride_h * (a->H - 1) + a->V)
+    return fail(MLA_EINVAL, "%s: out / dout strides overlap rows of width V", who);
+  if (a->dtype != MLA_BF16 || !mla::attn_bwd_supported(a->N, a->R, a->V))
+    return fail(MLA_EUNSUPPORTED, "%s: runs bf16 with N=128, R=64, V=128 (got dtype %d, N=%d R=%d V=%d)", who,
+                a->dtype, a->N, a->R, a->V);
+  if (a->T > (1LL << 30)) return fail(MLA_EUNSUPPORTED, "%s: T above 2^30", who);
+  if (a->T == 0) return MLA_OK;
+  if (!a->q || !a->kv || !a->k_rope || !a->out || !a->dout || !a->lse || !a->dq || !a->dkv || !a->dk_rope)
+    return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->kv) |
+                       reinterpret_cast<uintptr_t>(a->k_rope) | reinterpret_cast<uintptr_t>(a->out) |
+                       reinterpret_cast<uintptr_t>(a->dout);
+  const int64_t st = a->q_stride_t | a->q_stride_h | a->kv_stride_t | a->kv_stride_h | a->kr_stride_t |
+                     a->o_stride_t | a->o_stride_h | a->do_stride_t | a->do_stride_h;
+  if (al % 16 || st % 8)
+    return fail(MLA_EUNSUPPORTED, "%s: needs 16-byte aligned inputs and strides multiple of 8", who);
+  const size_t need = mla::attn_bwd_workspace_bytes(a->T, a->H, a->R);
+  if (a->workspace == nullptr || a->workspace_bytes < need || reinterpret_cast<uintptr_t>(a->workspace) % 256)
+    return fail(MLA_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", who, need,
+                a->workspace_bytes);
+  return MLA_OK;
+}
+
+size_t mla_attention_bwd_workspace_size(const mla_attn_bwd_args *a) {
+  if (a == nullptr || a->T < 0 || a->H < 1 || a->R < 0) return 0;
+  return mla::attn_bwd_workspace_bytes(a->T, a->H, a->R);
+}
+
+int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream) {
+  const char *who = "mla_attention_bwd";
+  const int rc = attn_bwd_validate(a, who);
+  if (rc != MLA_OK) return rc;
+  if (a->T == 0) return ok();
+  mla::AttnBwdPlan p;
+  p.q = a->q;
+  p.kv = a->kv;
+  p.kr = a->k_rope;
+  p.out = a->out;
+  p.dout = a->dout;
+  p.q_st = a->q_stride_t;
+  p.q_sh = a->q_stride_h;
+  p.kv_st = a->kv_stride_t;
+  p.kv_sh = a->kv_stride_h;
+  p.kr_st = a->kr_stride_t;
+  p.o_st = a->o_stride_t;
+  p.o_sh = a->o_stride_h;
+  p.do_st = a->do_stride_t;
+  p.do_sh = a->do_stride_h;
+  p.lse = a->lse;
+  p.dq = a->dq;
+  p.dkv = a->dkv;
+  p.dkr = a->dk_rope;
+  p.cu = a->cu_seqlens;
+  p.n_seq = a->cu_seqlens ? a->n_seq : 1;
+  p.T = a->T;
+  p.H = a->H;
+  p.scale = a->scale;
+  p.causal = a->causal ? 1 : 0;
+  p.ws = a->workspace;
+  return launched(mla::launch_attention_bwd(p, stream), who);
+}
+
 static int decode_validate(const mla_decode_args *a, const char *who) {
   if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
   if (a->dtype != MLA_BF16) return fail(MLA_EUNSUPPORTED, "%s: bf16 only", who);

@@ -100,6 +100,24 @@ bool attn_fast_path(int N, int R, int V, int bf16);
 size_t attn_workspace_bytes(int64_t T, int H, int n_seq, int has_cu, int causal, int N, int R, int V, int bf16);
 int launch_attention(const AttnPlan &p, void *stream);
 
+// ---- attention backward --------------------------------------------------
+struct AttnBwdPlan {
+  const void *q, *kv, *kr, *out, *dout;
+  int64_t q_st, q_sh, kv_st, kv_sh, kr_st, o_st, o_sh, do_st, do_sh;
+  const float *lse;    // [H][T], natural log
+  float *dq, *dkv, *dkr;
+  const int32_t *cu;
+  int n_seq;
+  int64_t T;
+  int H;
+  float scale;
+  int causal;
+  void *ws;            // attn_bwd_workspace_bytes(T, H, R), 256-byte aligned
+};
+bool attn_bwd_supported(int N, int R, int V);
+size_t attn_bwd_workspace_bytes(int64_t T, int H, int R);
+int launch_attention_bwd(const AttnBwdPlan &p, void *stream);
+
 // ---- latent-cache decode ------------------------------------------------
 struct DecodePlan {
   const void *q;       // [B][H][N+R]

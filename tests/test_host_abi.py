@@ -60,7 +60,11 @@ int main(void) {
   P(mla_attn_args, scale) P(mla_attn_args, dtype) P(mla_attn_args, workspace) P(mla_attn_args, workspace_bytes)
   P(mla_decode_args, lse) P(mla_decode_args, B) P(mla_decode_args, S) P(mla_decode_args, num_splits)
   P(mla_decode_args, scale) P(mla_decode_args, workspace) P(mla_decode_args, workspace_bytes)
-  printf("sizeof.attn %zu\nsizeof.decode %zu\n", sizeof(mla_attn_args), sizeof(mla_decode_args));
+  P(mla_attn_bwd_args, dout) P(mla_attn_bwd_args, do_stride_h) P(mla_attn_bwd_args, lse) P(mla_attn_bwd_args, dq)
+  P(mla_attn_bwd_args, dk_rope) P(mla_attn_bwd_args, cu_seqlens) P(mla_attn_bwd_args, T) P(mla_attn_bwd_args, V)
+  P(mla_attn_bwd_args, scale) P(mla_attn_bwd_args, dtype) P(mla_attn_bwd_args, workspace_bytes)
+  printf("sizeof.attn %zu\nsizeof.decode %zu\nsizeof.bwd %zu\n", sizeof(mla_attn_args), sizeof(mla_decode_args),
+         sizeof(mla_attn_bwd_args));
   return 0;
 }'''
     import tempfile
@@ -71,13 +75,14 @@ int main(void) {
         subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
     got = dict(zip(lines[0::2], (int(x) for x in lines[1::2])))
-    from mla_attention_under_amd._binding import mla_attn_args, mla_decode_args
+    from mla_attention_under_amd._binding import mla_attn_args, mla_attn_bwd_args, mla_decode_args
     for key, off in got.items():
         s, f = key.split(".")
         if s == "sizeof":
-            assert ctypes.sizeof({"attn": mla_attn_args, "decode": mla_decode_args}[f]) == off
+            assert ctypes.sizeof({"attn": mla_attn_args, "decode": mla_decode_args, "bwd": mla_attn_bwd_args}[f]) == off
         else:
-            cls = {"mla_attn_args": mla_attn_args, "mla_decode_args": mla_decode_args}[s]
+            cls = {"mla_attn_args": mla_attn_args, "mla_decode_args": mla_decode_args,
+                   "mla_attn_bwd_args": mla_attn_bwd_args}[s]
             assert getattr(cls, f).offset == off, key
 
 
@@ -181,6 +186,49 @@ def test_attention_validation_before_launch(lib):
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn())) > 0          # dense causal
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn(causal=0))) == 0  # non-causal needs none
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn(N=16, R=8, V=16))) == 0   # generic kernel
+
+
+def _attn_bwd(**kw):
+    from mla_attention_under_amd._binding import mla_attn_bwd_args
+    a = mla_attn_bwd_args()
+    a.q, a.kv, a.k_rope, a.out, a.dout = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    a.lse, a.dq, a.dkv, a.dk_rope = 0x60000, 0x70000, 0x80000, 0x90000
+    a.T, a.H, a.N, a.R, a.V = 256, 2, 128, 64, 128
+    a.q_stride_h, a.q_stride_t = 192, 384
+    a.kv_stride_h, a.kv_stride_t = 256, 512
+    a.kr_stride_t = 64
+    a.o_stride_h, a.o_stride_t = 128, 256
+    a.do_stride_h, a.do_stride_t = 128, 256
+    a.scale, a.causal, a.dtype = 0.07, 1, mla.MLA_BF16
+    a.workspace = 0x100000
+    a.workspace_bytes = lib_ws(a) if kw.pop("sized", True) else 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def lib_ws(a):
+    return mla.load_library().mla_attention_bwd_workspace_size(ctypes.byref(a))
+
+
+def test_attention_bwd_validation_before_launch(lib):
+    f = lambda **kw: lib.mla_attention_bwd(ctypes.byref(_attn_bwd(**kw)), None)  # noqa: E731
+    a = _attn_bwd()
+    # row terms [H][T] and per-head band gradients [H][T][R], fp32, each padded to 256 bytes
+    assert lib.mla_attention_bwd_workspace_size(ctypes.byref(a)) == 256 * 2 * 4 + 256 * 2 * 64 * 4
+    assert f(scale=0.0) == mla.MLA_EINVAL
+    assert f(q_stride_h=100) == mla.MLA_EINVAL              # rows overlap
+    assert f(do_stride_t=200) == mla.MLA_EINVAL
+    assert f(N=64) == mla.MLA_EUNSUPPORTED                  # no kernel for these widths
+    assert f(dtype=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
+    assert f(dout=0x50002) == mla.MLA_EUNSUPPORTED          # misaligned
+    assert f(lse=None) == mla.MLA_EINVAL                     # the forward's lse is required
+    assert f(dk_rope=None) == mla.MLA_EINVAL
+    assert f(sized=False) == mla.MLA_EINVAL                  # workspace too small
+    assert f(workspace=0x100010) == mla.MLA_EINVAL           # workspace misaligned
+    assert f(cu_seqlens=0x50000, n_seq=0) == mla.MLA_EINVAL
+    assert f(T=0, sized=False) == mla.MLA_OK
+    assert lib.mla_attention_bwd(None, None) == mla.MLA_EINVAL
 
 
 def test_decode_validation_before_launch(lib):
