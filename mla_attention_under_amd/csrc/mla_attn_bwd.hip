@@ -71,27 +71,43 @@ __device__ __forceinline__ void doc_of(const BwdArgs &a, int t, int &lo, int &hi
   hi = a.cu[l + 1];
 }
 
-// 32 rows [r0, r0+32) of W bf16 columns (row t at src + t*st) into LDS rows of
-// pitch P at column c0; rows at or past lim read as zero. With TR, also the
-// transposed copy dstT[(c0 + c)*TP + row].
-template <int W, int P, bool TR>
-__device__ __forceinline__ void load_rows(const uint16_t *src, int64_t st, int r0, int lim, uint16_t *dst, int c0,
-                                          uint16_t *dstT, int lane) {
-  constexpr int CH = W / 8;
-  static_assert((BB * CH) % 64 == 0, "whole passes of the wave");
+// MFMA operands straight from memory: fragment s of lane l is row r0 + l%32
+// (zero at or past lim), elements 16s + 8*(l/32) .. +7 of that row; the
+// fragments of W columns are one 16-byte load each.
+template <int W>
+__device__ __forceinline__ void load_frags(const uint16_t *src, int64_t st, int r0, int lim, bf16x8 *f, int lane) {
+  const int r = r0 + (lane & 31);
+  const bool ok = r < lim;
+  const uint16_t *row = src + static_cast<int64_t>(ok ? r : 0) * st + 8 * (lane >> 5);
 #pragma unroll
-  for (int it = 0; it < BB * CH / 64; ++it) {
-    const int cidx = it * 64 + lane;
-    const int r = cidx / CH, k = (cidx % CH) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r0 + r < lim) v = *reinterpret_cast<const u32x4 *>(src + static_cast<int64_t>(r0 + r) * st + k);
-    *reinterpret_cast<u32x4 *>(dst + r * P + c0 + k) = v;
-    if constexpr (TR) {
+  for (int s = 0; s < W / 16; ++s)
+    f[s] = ok ? *reinterpret_cast<const bf16x8 *>(row + 16 * s) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+}
+
+__device__ __forceinline__ uint32_t half_of(const u32x4 &v, int e) {
+  return (v[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+}
+
+// Column-major copy of a block held as fragments (see load_frags):
+// dstT[(c0 + c)*TP + row] for the W columns c. Lanes l and l^1 (adjacent rows)
+// swap fragments and each writes four dwords of two rows, so every store is a
+// dword and no two lanes of a store share a bank.
+template <int W>
+__device__ __forceinline__ void store_transposed(const bf16x8 *f, uint16_t *dstT, int c0, int lane) {
+  const bool odd = lane & 1;
+  const int r2 = (lane & 31) & ~1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = v[e >> 1];
-        dstT[(c0 + k + e) * TP + r] = static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu));
-      }
+  for (int s = 0; s < W / 16; ++s) {
+    const u32x4 mine = as_u32x4(f[s]);
+    u32x4 other;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(mine[i], 1);
+    const u32x4 ev = odd ? other : mine, ov = odd ? mine : other;
+    const int cb = c0 + 16 * s + 8 * (lane >> 5) + (odd ? 4 : 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = (odd ? 4 : 0) + j;
+      *reinterpret_cast<uint32_t *>(dstT + (cb + j) * TP + r2) = half_of(ev, e) | (half_of(ov, e) << 16);
     }
   }
 }
@@ -100,15 +116,6 @@ __device__ __forceinline__ void load_rows(const uint16_t *src, int64_t st, int r
 // row rbase + l%32, elements 16s + 8*(l/32) .. +7.
 __device__ __forceinline__ bf16x8 frag(const uint16_t *m, int pitch, int rbase, int s, int lane) {
   return *reinterpret_cast<const bf16x8 *>(m + (rbase + (lane & 31)) * pitch + 16 * s + 8 * (lane >> 5));
-}
-
-// Score block transposed: st[i][j] = k_i . q_j over the K columns (no scale).
-template <int K, int KP>
-__device__ __forceinline__ f32x16 scores_t(const uint16_t *Ks, const uint16_t *Qs, int lane) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < K / 16; ++s) acc = mfma32(frag(Ks, KP, 0, s, lane), frag(Qs, KP, 0, s, lane), acc);
-  return acc;
 }
 
 // row i of the block held in register r of lane l (column l%32)
@@ -161,10 +168,36 @@ __global__ __launch_bounds__(256) void row_term_kernel(BwdArgs a, int V) {
   if (live && c == 0) a.Dws[static_cast<int64_t>(h) * a.T + t] = acc;
 }
 
+// the keys' fragments of one block: [k_nope | k_rope] and v
+template <int N, int R, int V>
+__device__ __forceinline__ void load_keys(const BwdArgs &a, int h, int k0, bf16x8 *kf, bf16x8 *vf, int lane) {
+  load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, kf, lane);
+  if constexpr (R > 0) load_frags<R>(a.kr, a.kr_st, k0, a.T, kf + N / 16, lane);
+  load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, k0, a.T, vf, lane);
+}
+
+// the queries' fragments of one block: q and dout
+template <int K, int V>
+__device__ __forceinline__ void load_queries(const BwdArgs &a, int h, int q0, bf16x8 *qf, bf16x8 *gf, int lane) {
+  load_frags<K>(a.q + h * a.q_sh, a.q_st, q0, a.T, qf, lane);
+  load_frags<V>(a.dout + h * a.do_sh, a.do_st, q0, a.T, gf, lane);
+}
+
+// s^T = k q^T (no scale) and dp^T = v dout^T of one block
+template <int K, int V>
+__device__ __forceinline__ void scores_dp(const bf16x8 *kf, const bf16x8 *vf, const bf16x8 *qf, const bf16x8 *gf,
+                                          f32x16 &st, f32x16 &dp) {
+  st = f32x16{};
+  dp = f32x16{};
+#pragma unroll
+  for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
+#pragma unroll
+  for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
+}
+
 template <int N, int R, int V>
 __global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
-  constexpr int K = N + R, KP = K + 8, VP = V + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BB * KP], Vs[BB * VP], Qs[BB * KP], Os[BB * VP];
+  constexpr int K = N + R;
   __shared__ __attribute__((aligned(16))) uint16_t QsT[K * TP], OsT[V * TP], Ps[BB * TP], Ss[BB * TP];
   const int lane = threadIdx.x;
   const int h = blockIdx.y, k0 = blockIdx.x * BB;
@@ -176,15 +209,12 @@ __global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
   const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? k0 : lo0);
   const int qend = __builtin_amdgcn_readfirstlane(hi1);
 
-  load_rows<N, KP, false>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, Ks, 0, nullptr, lane);
-  if constexpr (R > 0) load_rows<R, KP, false>(a.kr, a.kr_st, k0, a.T, Ks, N, nullptr, lane);
-  load_rows<V, VP, false>(a.kv + h * a.kv_sh + N, a.kv_st, k0, a.T, Vs, 0, nullptr, lane);
+  bf16x8 kf[K / 16], vf[V / 16], qf[K / 16], gf[V / 16];
+  load_keys<N, R, V>(a, h, k0, kf, vf, lane);
+  if (qbeg < qend) load_queries<K, V>(a, h, qbeg, qf, gf, lane);
 
   f32x16 dk[K / 32] = {}, dv[V / 32] = {};
   for (int q0 = qbeg; q0 < qend; q0 += BB) {
-    __syncthreads();   // the previous block's readers are done
-    load_rows<K, KP, true>(a.q + h * a.q_sh, a.q_st, q0, a.T, Qs, 0, QsT, lane);
-    load_rows<V, VP, true>(a.dout + h * a.do_sh, a.do_st, q0, a.T, Os, 0, OsT, lane);
     const int q = q0 + (lane & 31);
     int qlo = 1, qhi = 0;   // no key visible to a query past T
     float lse2 = 0.f, Dq = 0.f;
@@ -193,11 +223,13 @@ __global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
       lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
       Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
     }
-    __syncthreads();
-    f32x16 st = scores_t<K, KP>(Ks, Qs, lane);
-    f32x16 dp = {};
-#pragma unroll
-    for (int s = 0; s < V / 16; ++s) dp = mfma32(frag(Vs, VP, 0, s, lane), frag(Os, VP, 0, s, lane), dp);
+    __syncthreads();   // the previous block's readers are done with the LDS copies
+    store_transposed<K>(qf, QsT, 0, lane);
+    store_transposed<V>(gf, OsT, 0, lane);
+    f32x16 st, dp;
+    scores_dp<K, V>(kf, vf, qf, gf, st, dp);
+    // the next block's queries load while this one finishes
+    if (q0 + BB < qend) load_queries<K, V>(a, h, q0 + BB, qf, gf, lane);
     probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
     store_block(st, Ps, false, lane);   // p^T [key][query]
     store_block(dp, Ss, false, lane);   // ds^T [key][query]
@@ -233,8 +265,7 @@ __global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
 
 template <int N, int R, int V>
 __global__ __launch_bounds__(64) void dq_kernel(BwdArgs a) {
-  constexpr int K = N + R, KP = K + 8, VP = V + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BB * KP], Os[BB * VP], Ks[BB * KP], Vs[BB * VP];
+  constexpr int K = N + R;
   __shared__ __attribute__((aligned(16))) uint16_t KsT[K * TP], Ss[BB * TP];
   const int lane = threadIdx.x;
   const int h = blockIdx.y, q0 = blockIdx.x * BB;
@@ -246,8 +277,9 @@ __global__ __launch_bounds__(64) void dq_kernel(BwdArgs a) {
   const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
   const int kend = __builtin_amdgcn_readfirstlane(a.causal ? q1 + 1 : hi1);
 
-  load_rows<K, KP, false>(a.q + h * a.q_sh, a.q_st, q0, a.T, Qs, 0, nullptr, lane);
-  load_rows<V, VP, false>(a.dout + h * a.do_sh, a.do_st, q0, a.T, Os, 0, nullptr, lane);
+  bf16x8 kf[K / 16], vf[V / 16], qf[K / 16], gf[V / 16];
+  load_queries<K, V>(a, h, q0, qf, gf, lane);
+  if (kbeg < kend) load_keys<N, R, V>(a, h, kbeg, kf, vf, lane);
   const int q = q0 + (lane & 31);
   int qlo = 1, qhi = 0;
   float lse2 = 0.f, Dq = 0.f;
@@ -260,14 +292,10 @@ __global__ __launch_bounds__(64) void dq_kernel(BwdArgs a) {
   f32x16 dq[K / 32] = {};
   for (int k0 = kbeg; k0 < kend; k0 += BB) {
     __syncthreads();
-    load_rows<N, KP, true>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, Ks, 0, KsT, lane);
-    if constexpr (R > 0) load_rows<R, KP, true>(a.kr, a.kr_st, k0, a.T, Ks, N, KsT, lane);
-    load_rows<V, VP, false>(a.kv + h * a.kv_sh + N, a.kv_st, k0, a.T, Vs, 0, nullptr, lane);
-    __syncthreads();
-    f32x16 st = scores_t<K, KP>(Ks, Qs, lane);
-    f32x16 dp = {};
-#pragma unroll
-    for (int s = 0; s < V / 16; ++s) dp = mfma32(frag(Vs, VP, 0, s, lane), frag(Os, VP, 0, s, lane), dp);
+    store_transposed<K>(kf, KsT, 0, lane);
+    f32x16 st, dp;
+    scores_dp<K, V>(kf, vf, qf, gf, st, dp);
+    if (k0 + BB < kend) load_keys<N, R, V>(a, h, k0 + BB, kf, vf, lane);
     probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
     store_block(dp, Ss, true, lane);   // ds [query][key]
     __syncthreads();
