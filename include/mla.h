@@ -315,6 +315,27 @@ size_t mla_attention_bwd_workspace_size(const mla_attn_bwd_args *a);
 int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream);
 
 /*
+ * Backward of mla_latent_up_proj (torchtitan "MLA CP optimization", section
+ * "Ulysses CP": k_nope and v are linear in the KV latent; section "Numerical
+ * comparison": the method is trained): with C = heads*(N+V) and the head
+ * range's weight columns w[:, col0 + c], col0 = head_begin*(N+V),
+ *   d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]
+ *   dw[l][c]       = sum_t latent[t][l] dkv[t][c]
+ *   latent   : bf16 [T][L]
+ *   w_kvb    : bf16 [L][heads_total*(N+V)]
+ *   dkv      : fp32 [T][heads][N+V] (mla_attention_bwd's dkv of these heads)
+ *   d_latent : fp32 [T][L], overwritten
+ *   dw       : fp32 [L][heads*(N+V)], overwritten: the gradient of the head
+ *              range's columns (the other columns get none from these heads)
+ * dkv is rounded to bf16 as an MFMA operand; products accumulate in fp32.
+ * Runs bf16 with L and heads*(N+V) multiples of 32 and 16-byte aligned
+ * latent, w_kvb and dkv (MLA_EUNSUPPORTED otherwise). T = 0 zeroes dw.
+ */
+int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *dkv, float *d_latent, float *dw,
+                           int64_t T, int L, int heads_total, int head_begin, int heads, int N, int V, int dtype,
+                           void *stream);
+
+/*
  * Latent-cache decode: one new query token per sequence attends over its whole
  * cached latent, reduced in num_splits KV chunks with an online softmax
  * (DeepSpeed PR #8602, "Components": decode attention with KV split-K and an

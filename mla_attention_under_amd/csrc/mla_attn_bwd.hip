@@ -23,6 +23,8 @@
 //                     a fixed summation order);
 //   band_sum_kernel   dk_rope[t] = sum over heads of the band slices, in head
 //                     order.
+// Then the latent up-projection's backward (dlatent_kernel, dw_kernel): the
+// gradients of the latent and of the head range's weight columns.
 // The five products per block are bf16 MFMAs (v_mfma_f32_32x32x16_bf16) with
 // fp32 accumulation; p and ds are rounded to bf16 as MFMA operands.
 #include <hip/hip_runtime.h>
@@ -325,6 +327,129 @@ __global__ __launch_bounds__(256) void band_sum_kernel(BwdArgs a, int R) {
   a.dkr[i] = acc;
 }
 
+// ---- backward of the latent up-projection -------------------------------
+// kv[t][c] = sum_l latent[t][l] w[l][col0 + c] over the head range's columns c,
+// so d_latent = dkv w_cols^T and dw_cols = latent^T dkv. dkv arrives in fp32
+// and is rounded to bf16 as an MFMA operand; both products accumulate in fp32.
+
+struct UpBwdArgs {
+  const uint16_t *latent, *w;
+  const float *dkv;
+  float *dl, *dw;
+  int T, L, C;         // C = heads*(N+V)
+  int64_t ldw, col0;   // w row length and the range's first column
+};
+
+// eight fp32 values -> one bf16 operand fragment (round to nearest even)
+__device__ __forceinline__ bf16x8 f32x8_to_bf16(const f32x4 &lo, const f32x4 &hi) {
+  return as_bf16x8(u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                         pack_bf16x2(hi[2], hi[3])});
+}
+
+constexpr int kDlCols = 64;    // d_latent columns per wave
+constexpr int kDwCols = 128;   // dw columns per wave
+
+// d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]: one wave per 32 tokens x 64
+// latent columns; both operands are contiguous along c, so the fragments come
+// straight from memory, four contraction steps in flight.
+__global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
+  const int lane = threadIdx.x;
+  const int l0 = blockIdx.x * kDlCols, t0 = blockIdx.y * BB;
+  const int t = t0 + (lane & 31);
+  const bool tok = t < a.T;
+  const float *arow = a.dkv + static_cast<int64_t>(tok ? t : 0) * a.C + 8 * (lane >> 5);
+  const uint16_t *brow[kDlCols / 32];
+#pragma unroll
+  for (int j = 0; j < kDlCols / 32; ++j) {
+    const int l = min(l0 + 32 * j + (lane & 31), a.L - 1);
+    brow[j] = a.w + static_cast<int64_t>(l) * a.ldw + a.col0 + 8 * (lane >> 5);
+  }
+  f32x16 acc[kDlCols / 32] = {};
+  constexpr int U = 4;
+  for (int k = 0; k < a.C; k += 16 * U) {
+    bf16x8 af[U], bf[U][kDlCols / 32];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + 16 * u;
+      const bool in = kk < a.C;
+      const f32x4 lo = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk) : f32x4{};
+      const f32x4 hi = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk + 4) : f32x4{};
+      af[u] = f32x8_to_bf16(lo, hi);
+#pragma unroll
+      for (int j = 0; j < kDlCols / 32; ++j)
+        bf[u][j] = in ? *reinterpret_cast<const bf16x8 *>(brow[j] + kk) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < kDlCols / 32; ++j) acc[j] = mfma32(af[u], bf[u][j], acc[j]);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tt = t0 + row_of(r, lane);
+    if (tt >= a.T) continue;
+#pragma unroll
+    for (int j = 0; j < kDlCols / 32; ++j) {
+      const int l = l0 + 32 * j + (lane & 31);
+      if (l < a.L) a.dl[static_cast<int64_t>(tt) * a.L + l] = acc[j][r];
+    }
+  }
+}
+
+// dw[l][c] = sum_t latent[t][l] dkv[t][c]: one wave per 32 latent rows x 128
+// columns. The contraction runs over tokens, the row index of both operands,
+// so each 32-token step is loaded as row fragments and written column-major to
+// LDS, the next step's loads in flight meanwhile.
+__global__ __launch_bounds__(64) void dw_kernel(UpBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t LT[BB * TP], GT[kDwCols * TP];
+  const int lane = threadIdx.x;
+  const int l0 = blockIdx.y * BB, c0 = blockIdx.x * kDwCols;
+  bf16x8 lf[BB / 16], gf[kDwCols / 16];
+  auto load = [&](int t0) {
+    load_frags<BB>(a.latent + l0, a.L, t0, a.T, lf, lane);
+    const int t = t0 + (lane & 31);
+    const bool tok = t < a.T;
+    const float *row = a.dkv + static_cast<int64_t>(tok ? t : 0) * a.C + c0 + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < kDwCols / 16; ++s) {
+      const bool in = tok && c0 + 16 * s < a.C;
+      const f32x4 lo = in ? *reinterpret_cast<const f32x4 *>(row + 16 * s) : f32x4{};
+      const f32x4 hi = in ? *reinterpret_cast<const f32x4 *>(row + 16 * s + 4) : f32x4{};
+      gf[s] = f32x8_to_bf16(lo, hi);
+    }
+  };
+  f32x16 acc[kDwCols / 32] = {};
+  if (a.T > 0) load(0);
+  for (int t0 = 0; t0 < a.T; t0 += BB) {
+    __syncthreads();
+    store_transposed<BB>(lf, LT, 0, lane);
+    store_transposed<kDwCols>(gf, GT, 0, lane);
+    __syncthreads();
+    if (t0 + BB < a.T) load(t0 + BB);
+#pragma unroll
+    for (int s = 0; s < BB / 16; ++s) {
+      const bf16x8 la = frag(LT, TP, 0, s, lane);
+#pragma unroll
+      for (int j = 0; j < kDwCols / 32; ++j) acc[j] = mfma32(la, frag(GT, TP, 32 * j, s, lane), acc[j]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int l = l0 + row_of(r, lane);
+    if (l >= a.L) continue;
+#pragma unroll
+    for (int j = 0; j < kDwCols / 32; ++j) {
+      const int c = c0 + 32 * j + (lane & 31);
+      if (c < a.C) a.dw[static_cast<int64_t>(l) * a.C + c] = acc[j][r];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
+
 template <int N, int R, int V>
 int run(const BwdArgs &a, hipStream_t s) {
   const unsigned rows = static_cast<unsigned>((static_cast<int64_t>(a.T) * a.H * 16 + 255) / 256);
@@ -377,6 +502,29 @@ int launch_attention_bwd(const AttnBwdPlan &p, void *stream) {
   a.causal = p.causal;
   if (p.T == 0) return hipSuccess;
   return run<128, 64, 128>(a, static_cast<hipStream_t>(stream));
+}
+
+int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream) {
+  UpBwdArgs a;
+  a.latent = static_cast<const uint16_t *>(p.latent);
+  a.w = static_cast<const uint16_t *>(p.w);
+  a.dkv = p.dkv;
+  a.dl = p.d_latent;
+  a.dw = p.dw;
+  a.T = static_cast<int>(p.T);
+  a.L = p.L;
+  a.C = p.C;
+  a.ldw = p.ldw;
+  a.col0 = p.col0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.T == 0) {   // no tokens: the weight gradient is zero
+    const int64_t n = static_cast<int64_t>(p.L) * p.C;
+    zero_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p.dw, n);
+    return hipGetLastError();
+  }
+  dlatent_kernel<<<dim3((a.L + kDlCols - 1) / kDlCols, (a.T + BB - 1) / BB), 64, 0, s>>>(a);
+  dw_kernel<<<dim3((a.C + kDwCols - 1) / kDwCols, (a.L + BB - 1) / BB), 64, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace mla

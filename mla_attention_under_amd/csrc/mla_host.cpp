@@ -569,6 +569,36 @@ int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream) {
   return launched(mla::launch_attention_bwd(p, stream), who);
 }
 
+int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *dkv, float *d_latent, float *dw,
+                           int64_t T, int L, int heads_total, int head_begin, int heads, int N, int V, int dtype,
+                           void *stream) {
+  const char *who = "mla_latent_up_proj_bwd";
+  if (T < 0 || L < 1 || N < 1 || V < 1 || heads < 1 || head_begin < 0 || head_begin + heads > heads_total)
+    return fail(MLA_EINVAL, "%s: need T >= 0, L, N, V >= 1 and a head range inside the %d heads", who, heads_total);
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  const int64_t P = static_cast<int64_t>(N) + V, C = P * heads;
+  if (dtype != MLA_BF16 || L % 32 || C % 32 || P % 8)
+    return fail(MLA_EUNSUPPORTED, "%s: runs bf16 with L and heads*(N+V) multiples of 32, N+V of 8 (L=%d, C=%lld)",
+                who, L, static_cast<long long>(C));
+  if (T > (1LL << 30) || C > (1LL << 30)) return fail(MLA_EUNSUPPORTED, "%s: T or heads*(N+V) above 2^30", who);
+  if (!dw || (T > 0 && (!latent || !w_kvb || !dkv || !d_latent))) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w_kvb) |
+                       reinterpret_cast<uintptr_t>(dkv);
+  if (al % 16) return fail(MLA_EUNSUPPORTED, "%s: latent, w_kvb and dkv must be 16-byte aligned", who);
+  mla::UpProjBwdPlan p;
+  p.latent = latent;
+  p.w = w_kvb;
+  p.dkv = dkv;
+  p.d_latent = d_latent;
+  p.dw = dw;
+  p.T = T;
+  p.L = L;
+  p.C = static_cast<int>(C);
+  p.ldw = P * heads_total;
+  p.col0 = P * head_begin;
+  return launched(mla::launch_up_proj_bwd(p, stream), who);
+}
+
 static int decode_validate(const mla_decode_args *a, const char *who) {
   if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
   if (a->dtype != MLA_BF16) return fail(MLA_EUNSUPPORTED, "%s: bf16 only", who);

@@ -118,6 +118,18 @@ bool attn_bwd_supported(int N, int R, int V);
 size_t attn_bwd_workspace_bytes(int64_t T, int H, int R);
 int launch_attention_bwd(const AttnBwdPlan &p, void *stream);
 
+struct UpProjBwdPlan {
+  const void *latent;  // bf16 [T][L]
+  const void *w;       // bf16 [L][ldw]
+  const float *dkv;    // [T][C]
+  float *d_latent;     // [T][L]
+  float *dw;           // [L][C]
+  int64_t T;
+  int L, C;
+  int64_t ldw, col0;
+};
+int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream);
+
 // ---- latent-cache decode ------------------------------------------------
 struct DecodePlan {
   const void *q;       // [B][H][N+R]

@@ -174,3 +174,56 @@ def test_attention_bwd_is_deterministic():
     b = _run_bwd(d, out_bits, lse_t, True, None)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ---- backward of the latent up-projection
+
+def _up_bounds(latent, w, dkv, head_begin, heads, P):
+    """Elementwise bounds: dkv rounded to bf16 (relative 2^-9, taken as 2^-8) plus worst-case fp32 accumulation
+    over the contraction length n (n * 2^-24), each times the matching product of absolute values."""
+    c, W, g = oracle.widen(latent), oracle.widen(w), np.asarray(dkv, np.float64)
+    T = c.shape[0]
+    Wc = np.abs(W[:, head_begin * P:(head_begin + heads) * P])
+    g2 = np.abs(g.reshape(T, heads * P))
+    C = heads * P
+    b_dl = (2.0 ** -8 + C * 2.0 ** -24) * (g2 @ Wc.T)
+    b_dw = (2.0 ** -8 + T * 2.0 ** -24) * (np.abs(c).T @ g2)
+    return b_dl, b_dw
+
+
+UP_CASES = [
+    # name, T, L, heads_total, head_begin, heads, N, V
+    ("small_head_range", 64, 64, 3, 1, 2, 32, 32),
+    ("ragged_tokens", 37, 96, 2, 0, 2, 16, 16),
+    ("uneven_columns", 100, 32, 4, 3, 1, 16, 48),
+    ("dsv3_rank", 2048, 512, 128, 16, 16, 128, 128),
+]
+
+
+@pytest.mark.parametrize("name,T,L,ht,hb,heads,Nn,Vv", UP_CASES, ids=[c[0] for c in UP_CASES])
+def test_latent_up_proj_bwd_matches_oracle(name, T, L, ht, hb, heads, Nn, Vv):
+    print(f"[up_bwd] {name} T={T} L={L} heads {hb}..{hb + heads} of {ht}", flush=True)
+    P = Nn + Vv
+    cfg = W.cfg * 1000 + 77
+    latent = mi.draw((T, L), cfg, 3)
+    w = mi.draw((L, ht * P), cfg, 4, std=0.05)
+    dkv = mi.normal_f32((T, heads, P), cfg, 5)
+    dl, dw = mla.mla_latent_up_proj_bwd(dev(latent), dev(w), dev(dkv), ht, hb, heads, Nn, Vv)
+    torch.cuda.synchronize()
+    ref_dl, ref_dw = oracle.latent_up_proj_backward(latent, w, hb, heads, dkv, Nn, Vv)
+    b_dl, b_dw = _up_bounds(latent, w, dkv, hb, heads, P)
+    _check(host64(dl), ref_dl, b_dl, f"{name} d_latent")
+    cols = slice(hb * P, (hb + heads) * P)
+    _check(host64(dw), ref_dw[:, cols], b_dw, f"{name} dw")
+    assert not np.any(ref_dw[:, :hb * P]) and not np.any(ref_dw[:, (hb + heads) * P:])
+
+
+def test_latent_up_proj_bwd_no_tokens_zeroes_dw():
+    L, P, heads = 64, 64, 2
+    latent = torch.empty((0, L), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((L, heads * P), dtype=torch.bfloat16, device="cuda")
+    dkv = torch.empty((0, heads, P), dtype=torch.float32, device="cuda")
+    dw = torch.full((L, heads * P), float("nan"), dtype=torch.float32, device="cuda")
+    dl, dw = mla.mla_latent_up_proj_bwd(latent, w, dkv, heads, 0, heads, 32, 32, dw=dw)
+    torch.cuda.synchronize()
+    assert dl.shape == (0, L) and torch.all(dw == 0)

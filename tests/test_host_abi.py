@@ -231,6 +231,20 @@ def test_attention_bwd_validation_before_launch(lib):
     assert lib.mla_attention_bwd(None, None) == mla.MLA_EINVAL
 
 
+def test_up_proj_bwd_validation_before_launch(lib):
+    f = lambda *a: lib.mla_latent_up_proj_bwd(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, *a, None)  # noqa: E731
+    # T, L, heads_total, head_begin, heads, N, V, dtype
+    assert f(64, 512, 128, 16, 16, 128, 128, mla.MLA_F32) == mla.MLA_EUNSUPPORTED   # bf16 only
+    assert f(64, 500, 128, 16, 16, 128, 128, mla.MLA_BF16) == mla.MLA_EUNSUPPORTED   # L % 32
+    assert f(64, 512, 4, 0, 1, 8, 8, mla.MLA_BF16) == mla.MLA_EUNSUPPORTED          # heads*(N+V) % 32
+    assert f(64, 512, 128, 120, 16, 128, 128, mla.MLA_BF16) == mla.MLA_EINVAL       # head range outside
+    assert f(-1, 512, 128, 16, 16, 128, 128, mla.MLA_BF16) == mla.MLA_EINVAL
+    assert lib.mla_latent_up_proj_bwd(0x10008, 0x20000, 0x30000, 0x40000, 0x50000, 64, 512, 128, 16, 16, 128, 128,
+                                      mla.MLA_BF16, None) == mla.MLA_EUNSUPPORTED     # misaligned latent
+    assert lib.mla_latent_up_proj_bwd(0x10000, 0x20000, 0x30000, 0x40000, None, 64, 512, 128, 16, 16, 128, 128,
+                                      mla.MLA_BF16, None) == mla.MLA_EINVAL           # no dw
+
+
 def test_decode_validation_before_launch(lib):
     from mla_attention_under_amd._binding import mla_decode_args
 
