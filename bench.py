@@ -266,10 +266,29 @@ def _backward(torch, mla):
     us = st.elapsed_time(en) * 1e3 / reps
     flops = 2.0 * (3 * (N + R) + 2 * V) * H * T * (T + 1) / 2
     tf = flops / (us * 1e-6) / 1e12
-    return {"attention_bwd_us": round(us, 2), "attention_bwd_tflops": round(tf, 1),
-            "attention_bwd_mfma_frac": round(tf / 2500.0, 4),
-            "attention_bwd_note": "dsv3_rank shard (T=2048, H=16, causal), row terms + dk/dv + dq + band sum, "
-                                  "fp32 gradients; 5 products per visible pair counted"}
+    res = {"attention_bwd_us": round(us, 2), "attention_bwd_tflops": round(tf, 1),
+           "attention_bwd_mfma_frac": round(tf / 2500.0, 4),
+           "attention_bwd_note": "dsv3_rank shard (T=2048, H=16, causal), row terms + dk/dv + dq + band sum, "
+                                 "fp32 gradients; 5 products per visible pair counted"}
+    # the latent up-projection's backward for the same heads (16 of 128, latent 512): d_latent and dW
+    L, HT, P = 512, 128, N + V
+    latent = torch.randn((T, L), device="cuda", generator=g).bfloat16()
+    w = (torch.randn((L, HT * P), device="cuda", generator=g) * 0.05).bfloat16()
+    dl, dw = torch.empty((T, L), **f32), torch.empty((L, H * P), **f32)
+    up = lambda: mla.mla_latent_up_proj_bwd(latent, w, dkv, HT, 16, H, N, V, d_latent=dl, dw=dw)  # noqa: E731
+    for _ in range(3):
+        up()
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(reps):
+        up()
+    en.record()
+    torch.cuda.synchronize()
+    us = st.elapsed_time(en) * 1e3 / reps
+    tf = 2 * 2.0 * T * L * H * P / (us * 1e-6) / 1e12
+    res.update({"up_proj_bwd_us": round(us, 2), "up_proj_bwd_tflops": round(tf, 1),
+                "up_proj_bwd_note": "d_latent [2048][512] and dW [512][4096] from fp32 dkv, 2 x 8.6 GFLOP"})
+    return res
 
 
 def _varlen(torch, mla, mi, dev):

@@ -10,17 +10,17 @@
 //   dv = p^T dout, dp = dout v^T, ds = p (dp - D), dq = scale ds k,
 //   dk = scale ds^T q; dk_rope = sum over heads of dk[..., N:].
 //
-// Three passes, all on blocks of 32 keys by 32 queries with the score block
+// Three launches, all on blocks of 32 keys by 32 queries with the score block
 // kept transposed (keys are rows, queries are the lanes' columns, so a lane's
 // log-sum-exp and row term are one register each):
 //   row_term_kernel   D[h][t] from out and dout;
-//   dkdv_kernel       one workgroup per (32 keys, head): dk, dv accumulated
-//                     over the query blocks that see the keys; the band part
-//                     of dk goes to a per-head slice of the workspace;
-//   dq_kernel         one workgroup per (32 queries, head): dq accumulated
-//                     over the key blocks the queries see (scores recomputed
-//                     rather than reduced across workgroups, so no atomics and
-//                     a fixed summation order);
+//   attn_bwd_kernel   one workgroup per (block b, head), two phases:
+//                     dk, dv of key block b accumulated over the query blocks
+//                     that see it (the band part of dk goes to a per-head
+//                     slice of the workspace), then dq of query block b
+//                     accumulated over the key blocks it sees (scores
+//                     recomputed rather than reduced across workgroups, so no
+//                     atomics and a fixed summation order);
 //   band_sum_kernel   dk_rope[t] = sum over heads of the band slices, in head
 //                     order.
 // Then the latent up-projection's backward (dlatent_kernel, dw_kernel): the
@@ -197,12 +197,16 @@ __device__ __forceinline__ void scores_dp(const bf16x8 *kf, const bf16x8 *vf, co
   for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
 }
 
+// LDS of one wave: the dk/dv phase's q^T, dout^T, p^T and ds^T blocks, or the
+// dq phase's k^T and ds blocks
+template <int K, int V>
+constexpr int kBwdLds = (K + V + 2 * BB) * TP;
+
 template <int N, int R, int V>
-__global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_block(const BwdArgs &a, int h, int k0, uint16_t *lds) {
   constexpr int K = N + R;
-  __shared__ __attribute__((aligned(16))) uint16_t QsT[K * TP], OsT[V * TP], Ps[BB * TP], Ss[BB * TP];
+  uint16_t *const QsT = lds, *const OsT = QsT + K * TP, *const Ps = OsT + V * TP, *const Ss = Ps + BB * TP;
   const int lane = threadIdx.x;
-  const int h = blockIdx.y, k0 = blockIdx.x * BB;
   const int k1 = min(k0 + BB, a.T) - 1;   // last key of the block
   int lo0, hi0, lo1, hi1;
   doc_of(a, k0, lo0, hi0);
@@ -266,11 +270,10 @@ __global__ __launch_bounds__(64) void dkdv_kernel(BwdArgs a) {
 }
 
 template <int N, int R, int V>
-__global__ __launch_bounds__(64) void dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_block(const BwdArgs &a, int h, int q0, uint16_t *lds) {
   constexpr int K = N + R;
-  __shared__ __attribute__((aligned(16))) uint16_t KsT[K * TP], Ss[BB * TP];
+  uint16_t *const KsT = lds, *const Ss = KsT + K * TP;
   const int lane = threadIdx.x;
-  const int h = blockIdx.y, q0 = blockIdx.x * BB;
   const int q1 = min(q0 + BB, a.T) - 1;
   int lo0, hi0, lo1, hi1;
   doc_of(a, q0, lo0, hi0);
@@ -317,6 +320,19 @@ __global__ __launch_bounds__(64) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < K / 32; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt][r];
   }
+}
+
+// One workgroup (one wave) per (block b, head): dk/dv of key block b, then dq
+// of query block b. Under the causal mask key block b is seen by nb - b query
+// blocks and query block b sees b + 1 key blocks, so every workgroup carries
+// the same nb + 1 block steps and the grid drains evenly.
+template <int N, int R, int V>
+__global__ __launch_bounds__(64) void attn_bwd_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kBwdLds<N + R, V>];
+  const int h = blockIdx.y, b0 = blockIdx.x * BB;
+  dkdv_block<N, R, V>(a, h, b0, lds);
+  __syncthreads();   // the dk/dv phase's readers are done with the LDS
+  dq_block<N, R, V>(a, h, b0, lds);
 }
 
 __global__ __launch_bounds__(256) void band_sum_kernel(BwdArgs a, int R) {
@@ -455,8 +471,7 @@ int run(const BwdArgs &a, hipStream_t s) {
   const unsigned rows = static_cast<unsigned>((static_cast<int64_t>(a.T) * a.H * 16 + 255) / 256);
   row_term_kernel<<<rows, 256, 0, s>>>(a, V);
   const dim3 grid(static_cast<unsigned>((a.T + BB - 1) / BB), static_cast<unsigned>(a.H));
-  dkdv_kernel<N, R, V><<<grid, 64, 0, s>>>(a);
-  dq_kernel<N, R, V><<<grid, 64, 0, s>>>(a);
+  attn_bwd_kernel<N, R, V><<<grid, 64, 0, s>>>(a);
   const unsigned sums = static_cast<unsigned>((static_cast<int64_t>(a.T) * R + 255) / 256);
   if (R > 0) band_sum_kernel<<<sums, 256, 0, s>>>(a, R);
   return hipGetLastError();
