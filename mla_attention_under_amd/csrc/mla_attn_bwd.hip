@@ -216,26 +216,35 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs &a, int h, int k0, uint
   const int qend = __builtin_amdgcn_readfirstlane(hi1);
 
   bf16x8 kf[K / 16], vf[V / 16], qf[K / 16], gf[V / 16];
+  float lse_n = 0.f, D_n = 0.f;   // the next block's log-sum-exp and row term of this lane's query
+  auto load_rows_terms = [&](int q0) {
+    const int q = q0 + (lane & 31);
+    const int64_t i = static_cast<int64_t>(h) * a.T + (q < a.T ? q : 0);
+    lse_n = a.lse[i];
+    D_n = a.Dws[i];
+  };
   load_keys<N, R, V>(a, h, k0, kf, vf, lane);
-  if (qbeg < qend) load_queries<K, V>(a, h, qbeg, qf, gf, lane);
+  if (qbeg < qend) {
+    load_queries<K, V>(a, h, qbeg, qf, gf, lane);
+    load_rows_terms(qbeg);
+  }
 
   f32x16 dk[K / 32] = {}, dv[V / 32] = {};
   for (int q0 = qbeg; q0 < qend; q0 += BB) {
     const int q = q0 + (lane & 31);
     int qlo = 1, qhi = 0;   // no key visible to a query past T
-    float lse2 = 0.f, Dq = 0.f;
-    if (q < a.T) {
-      doc_of(a, q, qlo, qhi);
-      lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
-      Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
-    }
+    if (q < a.T) doc_of(a, q, qlo, qhi);
+    const float lse2 = lse_n * kLog2e, Dq = D_n;
     __syncthreads();   // the previous block's readers are done with the LDS copies
     store_transposed<K>(qf, QsT, 0, lane);
     store_transposed<V>(gf, OsT, 0, lane);
     f32x16 st, dp;
     scores_dp<K, V>(kf, vf, qf, gf, st, dp);
     // the next block's queries load while this one finishes
-    if (q0 + BB < qend) load_queries<K, V>(a, h, q0 + BB, qf, gf, lane);
+    if (q0 + BB < qend) {
+      load_queries<K, V>(a, h, q0 + BB, qf, gf, lane);
+      load_rows_terms(q0 + BB);
+    }
     probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
     store_block(st, Ps, false, lane);   // p^T [key][query]
     store_block(dp, Ss, false, lane);   // ds^T [key][query]
@@ -363,11 +372,12 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16(const f32x4 &lo, const f32x4 &hi
 }
 
 constexpr int kDlCols = 64;    // d_latent columns per wave
-constexpr int kDwCols = 128;   // dw columns per wave
+constexpr int kDwCols = 64;    // dw columns per wave
 
 // d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]: one wave per 32 tokens x 64
 // latent columns; both operands are contiguous along c, so the fragments come
-// straight from memory, four contraction steps in flight.
+// straight from memory, four contraction steps per group and the next group's
+// loads in flight while one group's products run.
 __global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
   const int lane = threadIdx.x;
   const int l0 = blockIdx.x * kDlCols, t0 = blockIdx.y * BB;
@@ -382,23 +392,34 @@ __global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
   }
   f32x16 acc[kDlCols / 32] = {};
   constexpr int U = 4;
-  for (int k = 0; k < a.C; k += 16 * U) {
-    bf16x8 af[U], bf[U][kDlCols / 32];
+  f32x4 alo[U], ahi[U];
+  bf16x8 bf[U][kDlCols / 32];
+  auto load = [&](int k) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = k + 16 * u;
       const bool in = kk < a.C;
-      const f32x4 lo = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk) : f32x4{};
-      const f32x4 hi = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk + 4) : f32x4{};
-      af[u] = f32x8_to_bf16(lo, hi);
+      alo[u] = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk) : f32x4{};
+      ahi[u] = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk + 4) : f32x4{};
 #pragma unroll
       for (int j = 0; j < kDlCols / 32; ++j)
         bf[u][j] = in ? *reinterpret_cast<const bf16x8 *>(brow[j] + kk) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
+  };
+  load(0);
+  for (int k = 0; k < a.C; k += 16 * U) {
+    bf16x8 af[U], bcur[U][kDlCols / 32];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      af[u] = f32x8_to_bf16(alo[u], ahi[u]);
+#pragma unroll
+      for (int j = 0; j < kDlCols / 32; ++j) bcur[u][j] = bf[u][j];
+    }
+    if (k + 16 * U < a.C) load(k + 16 * U);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < kDlCols / 32; ++j) acc[j] = mfma32(af[u], bf[u][j], acc[j]);
+      for (int j = 0; j < kDlCols / 32; ++j) acc[j] = mfma32(af[u], bcur[u][j], acc[j]);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
