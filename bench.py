@@ -348,6 +348,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain contiguous copy of 1 GiB (the pack kernel with one rank) 3 times, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the backward of the rank shard (attention, then the up-projection) and print "
+                         "its figures as one JSON line (for profiling the backward kernels on their own)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -364,6 +367,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     mla.load_library()
+
+    if args.backward_only:
+        print(json.dumps(_backward(torch, mla)))
+        return
 
     if args.copy_calibration:
         n = 1 << 29                                   # 2-byte elements: 1 GiB read + 1 GiB written

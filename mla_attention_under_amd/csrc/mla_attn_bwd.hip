@@ -335,10 +335,17 @@ __device__ __forceinline__ void dq_block(const BwdArgs &a, int h, int q0, uint16
 // of query block b. Under the causal mask key block b is seen by nb - b query
 // blocks and query block b sees b + 1 key blocks, so every workgroup carries
 // the same nb + 1 block steps and the grid drains evenly.
+// Workgroups are dealt to the 8 XCDs round robin by launch order; when the
+// grid divides evenly, launch slot i is remapped so that each XCD runs a
+// contiguous run of (head, block) pairs, i.e. whole heads, whose q, k, v and
+// dout then stay in that XCD's L2 instead of every XCD streaming every head.
 template <int N, int R, int V>
 __global__ __launch_bounds__(64) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kBwdLds<N + R, V>];
-  const int h = blockIdx.y, b0 = blockIdx.x * BB;
+  const int nb = gridDim.x, G = nb * gridDim.y;
+  int lin = blockIdx.x + nb * blockIdx.y;
+  if (G % 8 == 0) lin = (lin % 8) * (G / 8) + lin / 8;
+  const int h = lin / nb, b0 = (lin % nb) * BB;
   dkdv_block<N, R, V>(a, h, b0, lds);
   __syncthreads();   // the dk/dv phase's readers are done with the LDS
   dq_block<N, R, V>(a, h, b0, lds);
@@ -380,7 +387,7 @@ constexpr int kDwCols = 64;    // dw columns per wave
 // loads in flight while one group's products run.
 __global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
   const int lane = threadIdx.x;
-  const int l0 = blockIdx.x * kDlCols, t0 = blockIdx.y * BB;
+  const int t0 = blockIdx.x * BB, l0 = blockIdx.y * kDlCols;
   const int t = t0 + (lane & 31);
   const bool tok = t < a.T;
   const float *arow = a.dkv + static_cast<int64_t>(tok ? t : 0) * a.C + 8 * (lane >> 5);
@@ -558,7 +565,9 @@ int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream) {
     zero_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p.dw, n);
     return hipGetLastError();
   }
-  dlatent_kernel<<<dim3((a.L + kDlCols - 1) / kDlCols, (a.T + BB - 1) / BB), 64, 0, s>>>(a);
+  // token blocks run fastest: the column tiles of one token block are 8k
+  // launch slots apart and so share an XCD (and its L2 copy of their dkv rows)
+  dlatent_kernel<<<dim3((a.T + BB - 1) / BB, (a.L + kDlCols - 1) / kDlCols), 64, 0, s>>>(a);
   dw_kernel<<<dim3((a.C + kDwCols - 1) / kDwCols, (a.L + BB - 1) / BB), 64, 0, s>>>(a);
   return hipGetLastError();
 }
