@@ -14,13 +14,16 @@
 // kept transposed (keys are rows, queries are the lanes' columns, so a lane's
 // log-sum-exp and row term are one register each):
 //   row_term_kernel   D[h][t] from out and dout;
-//   attn_bwd_kernel   one workgroup per (block b, head), two phases:
-//                     dk, dv of key block b accumulated over the query blocks
-//                     that see it (the band part of dk goes to a per-head
-//                     slice of the workspace), then dq of query block b
-//                     accumulated over the key blocks it sees (scores
+//   attn_bwd_kernel   one workgroup (two waves) per (block b, head), two
+//                     phases: dk, dv of key block b accumulated over the query
+//                     blocks that see it (the band part of dk goes to a
+//                     per-head slice of the workspace), then dq of query block
+//                     b accumulated over the key blocks it sees (scores
 //                     recomputed rather than reduced across workgroups, so no
-//                     atomics and a fixed summation order);
+//                     atomics and a fixed summation order). Under the causal
+//                     mask key block b is seen by nb - b query blocks and query
+//                     block b sees b + 1 key blocks, so every workgroup carries
+//                     the same nb + 1 block steps and the grid drains evenly;
 //   band_sum_kernel   dk_rope[t] = sum over heads of the band slices, in head
 //                     order.
 // Then the latent up-projection's backward (dlatent_kernel, dw_kernel): the
@@ -170,185 +173,237 @@ __global__ __launch_bounds__(256) void row_term_kernel(BwdArgs a, int V) {
   if (live && c == 0) a.Dws[static_cast<int64_t>(h) * a.T + t] = acc;
 }
 
-// the keys' fragments of one block: [k_nope | k_rope] and v
-template <int N, int R, int V>
-__device__ __forceinline__ void load_keys(const BwdArgs &a, int h, int k0, bf16x8 *kf, bf16x8 *vf, int lane) {
-  load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, kf, lane);
-  if constexpr (R > 0) load_frags<R>(a.kr, a.kr_st, k0, a.T, kf + N / 16, lane);
-  load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, k0, a.T, vf, lane);
-}
-
-// the queries' fragments of one block: q and dout
-template <int K, int V>
-__device__ __forceinline__ void load_queries(const BwdArgs &a, int h, int q0, bf16x8 *qf, bf16x8 *gf, int lane) {
-  load_frags<K>(a.q + h * a.q_sh, a.q_st, q0, a.T, qf, lane);
-  load_frags<V>(a.dout + h * a.do_sh, a.do_st, q0, a.T, gf, lane);
-}
-
-// s^T = k q^T (no scale) and dp^T = v dout^T of one block
-template <int K, int V>
-__device__ __forceinline__ void scores_dp(const bf16x8 *kf, const bf16x8 *vf, const bf16x8 *qf, const bf16x8 *gf,
-                                          f32x16 &st, f32x16 &dp) {
-  st = f32x16{};
-  dp = f32x16{};
-#pragma unroll
-  for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
-#pragma unroll
-  for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
-}
-
-// LDS of one wave: the dk/dv phase's q^T, dout^T, p^T and ds^T blocks, or the
-// dq phase's k^T and ds blocks
+// LDS of a workgroup: the dk/dv phase's q^T, dout^T, p^T and ds^T blocks, or
+// the dq phase's k^T and ds blocks
 template <int K, int V>
 constexpr int kBwdLds = (K + V + 2 * BB) * TP;
 
-template <int N, int R, int V>
-__device__ __forceinline__ void dkdv_block(const BwdArgs &a, int h, int k0, uint16_t *lds) {
-  constexpr int K = N + R;
-  uint16_t *const QsT = lds, *const OsT = QsT + K * TP, *const Ps = OsT + V * TP, *const Ss = Ps + BB * TP;
-  const int lane = threadIdx.x;
-  const int k1 = min(k0 + BB, a.T) - 1;   // last key of the block
-  int lo0, hi0, lo1, hi1;
-  doc_of(a, k0, lo0, hi0);
-  doc_of(a, k1, lo1, hi1);
-  // queries that see some key of the block
-  const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? k0 : lo0);
-  const int qend = __builtin_amdgcn_readfirstlane(hi1);
-
-  bf16x8 kf[K / 16], vf[V / 16], qf[K / 16], gf[V / 16];
-  float lse_n = 0.f, D_n = 0.f;   // the next block's log-sum-exp and row term of this lane's query
-  auto load_rows_terms = [&](int q0) {
-    const int q = q0 + (lane & 31);
-    const int64_t i = static_cast<int64_t>(h) * a.T + (q < a.T ? q : 0);
-    lse_n = a.lse[i];
-    D_n = a.Dws[i];
-  };
-  load_keys<N, R, V>(a, h, k0, kf, vf, lane);
-  if (qbeg < qend) {
-    load_queries<K, V>(a, h, qbeg, qf, gf, lane);
-    load_rows_terms(qbeg);
-  }
-
-  f32x16 dk[K / 32] = {}, dv[V / 32] = {};
-  for (int q0 = qbeg; q0 < qend; q0 += BB) {
-    const int q = q0 + (lane & 31);
-    int qlo = 1, qhi = 0;   // no key visible to a query past T
-    if (q < a.T) doc_of(a, q, qlo, qhi);
-    const float lse2 = lse_n * kLog2e, Dq = D_n;
-    __syncthreads();   // the previous block's readers are done with the LDS copies
-    store_transposed<K>(qf, QsT, 0, lane);
-    store_transposed<V>(gf, OsT, 0, lane);
-    f32x16 st, dp;
-    scores_dp<K, V>(kf, vf, qf, gf, st, dp);
-    // the next block's queries load while this one finishes
-    if (q0 + BB < qend) {
-      load_queries<K, V>(a, h, q0 + BB, qf, gf, lane);
-      load_rows_terms(q0 + BB);
-    }
-    probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
-    store_block(st, Ps, false, lane);   // p^T [key][query]
-    store_block(dp, Ss, false, lane);   // ds^T [key][query]
-    __syncthreads();
-    // dv[key][v] += p^T[key][q] dout[q][v]; dk[key][c] += ds^T[key][q] q[q][c]
-#pragma unroll
-    for (int s = 0; s < BB / 16; ++s) {
-      const bf16x8 pa = frag(Ps, TP, 0, s, lane), sa = frag(Ss, TP, 0, s, lane);
-#pragma unroll
-      for (int vt = 0; vt < V / 32; ++vt) dv[vt] = mfma32(pa, frag(OsT, TP, 32 * vt, s, lane), dv[vt]);
-#pragma unroll
-      for (int kt = 0; kt < K / 32; ++kt) dk[kt] = mfma32(sa, frag(QsT, TP, 32 * kt, s, lane), dk[kt]);
-    }
-  }
-  // rows past T are not written; dk_nope and dv to dkv, the band to the head's slice
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = k0 + row_of(r, lane);
-    if (key >= a.T) continue;
-    float *row = a.dkv + (static_cast<int64_t>(key) * a.H + h) * (N + V);
-    float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
-#pragma unroll
-    for (int kt = 0; kt < K / 32; ++kt) {
-      const int c = 32 * kt + (lane & 31);
-      const float g = a.scale * dk[kt][r];
-      if (c < N) row[c] = g;
-      else brow[c - N] = g;
-    }
-#pragma unroll
-    for (int vt = 0; vt < V / 32; ++vt) row[N + 32 * vt + (lane & 31)] = dv[vt][r];
-  }
-}
-
-template <int N, int R, int V>
-__device__ __forceinline__ void dq_block(const BwdArgs &a, int h, int q0, uint16_t *lds) {
-  constexpr int K = N + R;
-  uint16_t *const KsT = lds, *const Ss = KsT + K * TP;
-  const int lane = threadIdx.x;
-  const int q1 = min(q0 + BB, a.T) - 1;
-  int lo0, hi0, lo1, hi1;
-  doc_of(a, q0, lo0, hi0);
-  doc_of(a, q1, lo1, hi1);
-  // keys some query of the block sees
-  const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
-  const int kend = __builtin_amdgcn_readfirstlane(a.causal ? q1 + 1 : hi1);
-
-  bf16x8 kf[K / 16], vf[V / 16], qf[K / 16], gf[V / 16];
-  load_queries<K, V>(a, h, q0, qf, gf, lane);
-  if (kbeg < kend) load_keys<N, R, V>(a, h, kbeg, kf, vf, lane);
-  const int q = q0 + (lane & 31);
-  int qlo = 1, qhi = 0;
-  float lse2 = 0.f, Dq = 0.f;
-  if (q < a.T) {
-    doc_of(a, q, qlo, qhi);
-    lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
-    Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
-  }
-
-  f32x16 dq[K / 32] = {};
-  for (int k0 = kbeg; k0 < kend; k0 += BB) {
-    __syncthreads();
-    store_transposed<K>(kf, KsT, 0, lane);
-    f32x16 st, dp;
-    scores_dp<K, V>(kf, vf, qf, gf, st, dp);
-    if (k0 + BB < kend) load_keys<N, R, V>(a, h, k0 + BB, kf, vf, lane);
-    probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
-    store_block(dp, Ss, true, lane);   // ds [query][key]
-    __syncthreads();
-    // dq[q][c] += ds[q][key] k[key][c]
-#pragma unroll
-    for (int s = 0; s < BB / 16; ++s) {
-      const bf16x8 sa = frag(Ss, TP, 0, s, lane);
-#pragma unroll
-      for (int kt = 0; kt < K / 32; ++kt) dq[kt] = mfma32(sa, frag(KsT, TP, 32 * kt, s, lane), dq[kt]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = q0 + row_of(r, lane);
-    if (t >= a.T) continue;
-    float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K;
-#pragma unroll
-    for (int kt = 0; kt < K / 32; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt][r];
-  }
-}
-
-// One workgroup (one wave) per (block b, head): dk/dv of key block b, then dq
-// of query block b. Under the causal mask key block b is seen by nb - b query
-// blocks and query block b sees b + 1 key blocks, so every workgroup carries
-// the same nb + 1 block steps and the grid drains evenly.
+// Two waves per (block b, head), each under 256 VGPRs so that two waves share
+// a SIMD and cover each other's barriers and LDS round trips. Wave 0 holds the
+// key (or query) side of the scores: it computes s, then p and ds, and the
+// first KS column tiles of dk (or dq); wave 1 holds the value side: dp, which
+// it hands over through LDS in its own register layout, then dv and the last
+// column tiles of dk (or dq). Each wave runs its own loop; the two meet at the
+// same three barriers per block step:
+//   (1) the previous step's readers are done; transposed copies and the s / dp
+//       products, the next block's loads issued;
+//   (2) dp is in LDS; wave 0 forms p and ds into LDS;
+//   (3) the second-stage products of both waves.
 // Workgroups are dealt to the 8 XCDs round robin by launch order; when the
 // grid divides evenly, launch slot i is remapped so that each XCD runs a
 // contiguous run of (head, block) pairs, i.e. whole heads, whose q, k, v and
 // dout then stay in that XCD's L2 instead of every XCD streaming every head.
 template <int N, int R, int V>
-__global__ __launch_bounds__(64) void attn_bwd_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kBwdLds<N + R, V>];
+__global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
+  constexpr int K = N + R;
+  constexpr int KS = 4;   // dk / dq column tiles of wave 0 (the rest go to wave 1)
+  static_assert(K / 32 > KS, "both waves own dk columns");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kBwdLds<K, V>];
+  __shared__ __attribute__((aligned(16))) float dps[16 * 64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nb = gridDim.x, G = nb * gridDim.y;
   int lin = blockIdx.x + nb * blockIdx.y;
   if (G % 8 == 0) lin = (lin % 8) * (G / 8) + lin / 8;
   const int h = lin / nb, b0 = (lin % nb) * BB;
-  dkdv_block<N, R, V>(a, h, b0, lds);
-  __syncthreads();   // the dk/dv phase's readers are done with the LDS
-  dq_block<N, R, V>(a, h, b0, lds);
+  const int b1 = min(b0 + BB, a.T) - 1;
+  int lo0, hi0, lo1, hi1;
+  doc_of(a, b0, lo0, hi0);
+  doc_of(a, b1, lo1, hi1);
+
+  // ---- phase 1: dk, dv of key block b0
+  {
+    uint16_t *const QsT = lds, *const OsT = QsT + K * TP, *const Ps = OsT + V * TP, *const Ss = Ps + BB * TP;
+    const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? b0 : lo0);
+    const int qend = __builtin_amdgcn_readfirstlane(hi1);
+    if (wave == 0) {
+      bf16x8 kf[K / 16], qf[K / 16];
+      float lse_n = 0.f, D_n = 0.f;
+      auto rows_terms = [&](int q0) {
+        const int q = q0 + (lane & 31);
+        const int64_t i = static_cast<int64_t>(h) * a.T + (q < a.T ? q : 0);
+        lse_n = a.lse[i];
+        D_n = a.Dws[i];
+      };
+      load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, b0, a.T, kf, lane);
+      if constexpr (R > 0) load_frags<R>(a.kr, a.kr_st, b0, a.T, kf + N / 16, lane);
+      if (qbeg < qend) {
+        load_frags<K>(a.q + h * a.q_sh, a.q_st, qbeg, a.T, qf, lane);
+        rows_terms(qbeg);
+      }
+      f32x16 dk[KS] = {};
+      for (int q0 = qbeg; q0 < qend; q0 += BB) {
+        const int q = q0 + (lane & 31);
+        int qlo = 1, qhi = 0;
+        if (q < a.T) doc_of(a, q, qlo, qhi);
+        const float lse2 = lse_n * kLog2e, Dq = D_n;
+        __syncthreads();                                   // (1)
+        store_transposed<K>(qf, QsT, 0, lane);
+        f32x16 st = {};
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
+        if (q0 + BB < qend) {
+          load_frags<K>(a.q + h * a.q_sh, a.q_st, q0 + BB, a.T, qf, lane);
+          rows_terms(q0 + BB);
+        }
+        __syncthreads();                                   // (2)
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = dps[r * 64 + lane];
+        probs_t(a, st, dp, b0, q, qlo, qhi, lse2, Dq, lane);
+        store_block(st, Ps, false, lane);   // p^T [key][query]
+        store_block(dp, Ss, false, lane);   // ds^T [key][query]
+        __syncthreads();                                   // (3)
+#pragma unroll
+        for (int s = 0; s < BB / 16; ++s) {
+          const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+#pragma unroll
+          for (int kt = 0; kt < KS; ++kt) dk[kt] = mfma32(sa, frag(QsT, TP, 32 * kt, s, lane), dk[kt]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = b0 + row_of(r, lane);
+        if (key >= a.T) continue;
+        float *row = a.dkv + (static_cast<int64_t>(key) * a.H + h) * (N + V);
+        float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+          const int c = 32 * kt + (lane & 31);
+          const float g = a.scale * dk[kt][r];
+          if (c < N) row[c] = g;
+          else brow[c - N] = g;
+        }
+      }
+    } else {
+      bf16x8 vf[V / 16], gf[V / 16];
+      load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, b0, a.T, vf, lane);
+      if (qbeg < qend) load_frags<V>(a.dout + h * a.do_sh, a.do_st, qbeg, a.T, gf, lane);
+      f32x16 dv[V / 32] = {}, dk[K / 32 - KS] = {};
+      for (int q0 = qbeg; q0 < qend; q0 += BB) {
+        __syncthreads();                                   // (1)
+        store_transposed<V>(gf, OsT, 0, lane);
+        f32x16 dp = {};
+#pragma unroll
+        for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
+        if (q0 + BB < qend) load_frags<V>(a.dout + h * a.do_sh, a.do_st, q0 + BB, a.T, gf, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dps[r * 64 + lane] = dp[r];
+        __syncthreads();                                   // (2)
+        __syncthreads();                                   // (3)
+#pragma unroll
+        for (int s = 0; s < BB / 16; ++s) {
+          const bf16x8 pa = frag(Ps, TP, 0, s, lane), sa = frag(Ss, TP, 0, s, lane);
+#pragma unroll
+          for (int vt = 0; vt < V / 32; ++vt) dv[vt] = mfma32(pa, frag(OsT, TP, 32 * vt, s, lane), dv[vt]);
+#pragma unroll
+          for (int kt = KS; kt < K / 32; ++kt)
+            dk[kt - KS] = mfma32(sa, frag(QsT, TP, 32 * kt, s, lane), dk[kt - KS]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = b0 + row_of(r, lane);
+        if (key >= a.T) continue;
+        float *row = a.dkv + (static_cast<int64_t>(key) * a.H + h) * (N + V);
+        float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
+#pragma unroll
+        for (int kt = KS; kt < K / 32; ++kt) {
+          const int c = 32 * kt + (lane & 31);
+          const float g = a.scale * dk[kt - KS][r];
+          if (c < N) row[c] = g;
+          else brow[c - N] = g;
+        }
+#pragma unroll
+        for (int vt = 0; vt < V / 32; ++vt) row[N + 32 * vt + (lane & 31)] = dv[vt][r];
+      }
+    }
+  }
+  __syncthreads();   // phase 1's readers are done with the LDS
+
+  // ---- phase 2: dq of query block b0
+  {
+    uint16_t *const KsT = lds, *const Ss = KsT + K * TP;
+    const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
+    const int kend = __builtin_amdgcn_readfirstlane(a.causal ? b1 + 1 : hi1);
+    if (wave == 0) {
+      bf16x8 kf[K / 16], qf[K / 16];
+      load_frags<K>(a.q + h * a.q_sh, a.q_st, b0, a.T, qf, lane);
+      auto load_k = [&](int k0) {
+        load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, kf, lane);
+        if constexpr (R > 0) load_frags<R>(a.kr, a.kr_st, k0, a.T, kf + N / 16, lane);
+      };
+      if (kbeg < kend) load_k(kbeg);
+      const int q = b0 + (lane & 31);
+      int qlo = 1, qhi = 0;
+      float lse2 = 0.f, Dq = 0.f;
+      if (q < a.T) {
+        doc_of(a, q, qlo, qhi);
+        lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
+        Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
+      }
+      f32x16 dq[KS] = {};
+      for (int k0 = kbeg; k0 < kend; k0 += BB) {
+        __syncthreads();                                   // (1)
+        store_transposed<K>(kf, KsT, 0, lane);
+        f32x16 st = {};
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
+        if (k0 + BB < kend) load_k(k0 + BB);
+        __syncthreads();                                   // (2)
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = dps[r * 64 + lane];
+        probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
+        store_block(dp, Ss, true, lane);   // ds [query][key]
+        __syncthreads();                                   // (3)
+#pragma unroll
+        for (int s = 0; s < BB / 16; ++s) {
+          const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+#pragma unroll
+          for (int kt = 0; kt < KS; ++kt) dq[kt] = mfma32(sa, frag(KsT, TP, 32 * kt, s, lane), dq[kt]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = b0 + row_of(r, lane);
+        if (t >= a.T) continue;
+        float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K;
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt][r];
+      }
+    } else {
+      bf16x8 vf[V / 16], gf[V / 16];
+      load_frags<V>(a.dout + h * a.do_sh, a.do_st, b0, a.T, gf, lane);
+      if (kbeg < kend) load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, kbeg, a.T, vf, lane);
+      f32x16 dq[K / 32 - KS] = {};
+      for (int k0 = kbeg; k0 < kend; k0 += BB) {
+        __syncthreads();                                   // (1)
+        f32x16 dp = {};
+#pragma unroll
+        for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
+        if (k0 + BB < kend) load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, k0 + BB, a.T, vf, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dps[r * 64 + lane] = dp[r];
+        __syncthreads();                                   // (2)
+        __syncthreads();                                   // (3)
+#pragma unroll
+        for (int s = 0; s < BB / 16; ++s) {
+          const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+#pragma unroll
+          for (int kt = KS; kt < K / 32; ++kt)
+            dq[kt - KS] = mfma32(sa, frag(KsT, TP, 32 * kt, s, lane), dq[kt - KS]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = b0 + row_of(r, lane);
+        if (t >= a.T) continue;
+        float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K;
+#pragma unroll
+        for (int kt = KS; kt < K / 32; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt - KS][r];
+      }
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void band_sum_kernel(BwdArgs a, int R) {
@@ -499,7 +554,7 @@ int run(const BwdArgs &a, hipStream_t s) {
   const unsigned rows = static_cast<unsigned>((static_cast<int64_t>(a.T) * a.H * 16 + 255) / 256);
   row_term_kernel<<<rows, 256, 0, s>>>(a, V);
   const dim3 grid(static_cast<unsigned>((a.T + BB - 1) / BB), static_cast<unsigned>(a.H));
-  attn_bwd_kernel<N, R, V><<<grid, 64, 0, s>>>(a);
+  attn_bwd_kernel<N, R, V><<<grid, 128, 0, s>>>(a);
   const unsigned sums = static_cast<unsigned>((static_cast<int64_t>(a.T) * R + 255) / 256);
   if (R > 0) band_sum_kernel<<<sums, 256, 0, s>>>(a, R);
   return hipGetLastError();
