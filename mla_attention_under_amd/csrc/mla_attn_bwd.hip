@@ -434,7 +434,6 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16(const f32x4 &lo, const f32x4 &hi
 }
 
 constexpr int kDlCols = 64;    // d_latent columns per wave
-constexpr int kDwCols = 64;    // dw columns per wave
 
 // d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]: one wave per 32 tokens x 64
 // latent columns; both operands are contiguous along c, so the fragments come
@@ -495,53 +494,103 @@ __global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
   }
 }
 
-// dw[l][c] = sum_t latent[t][l] dkv[t][c]: one wave per 32 latent rows x 128
-// columns. The contraction runs over tokens, the row index of both operands,
-// so each 32-token step is loaded as row fragments and written column-major to
-// LDS, the next step's loads in flight meanwhile.
-__global__ __launch_bounds__(64) void dw_kernel(UpBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t LT[BB * TP], GT[kDwCols * TP];
-  const int lane = threadIdx.x;
-  const int l0 = blockIdx.y * BB, c0 = blockIdx.x * kDwCols;
-  bf16x8 lf[BB / 16], gf[kDwCols / 16];
-  auto load = [&](int t0) {
-    load_frags<BB>(a.latent + l0, a.L, t0, a.T, lf, lane);
-    const int t = t0 + (lane & 31);
-    const bool tok = t < a.T;
-    const float *row = a.dkv + static_cast<int64_t>(tok ? t : 0) * a.C + c0 + 8 * (lane >> 5);
+// Transposing LDS reads (gfx950 ds_read_b64_tr_b16): lane i of each 16-lane
+// group receives column i of the 4x16 block whose rows its lanes address.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+}
+
+// dw tiles: [32 tokens][128 columns] bf16, row-major with the 16-element
+// blocks of row r XOR-permuted by tr_swz(r) (spreads the transposing reads
+// over the banks)
+constexpr int kDwM = 128, kDwN = 128, kDwT = 32;
+__device__ __forceinline__ int tr_swz(int r) { return (r & 2) | ((r & 1) * 5); }
+__device__ __forceinline__ int tr_pos(int r, int c) { return r * 128 + 16 * ((c >> 4) ^ tr_swz(r)) + (c & 15); }
+
+// MFMA operand of 16 tokens (b) by 32 columns (d) from a [token][column] tile:
+// lane l takes column 32d + l%32; both operands of dw use the same read, so
+// their token orders match.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *tile, int b, int d, int lane) {
+  const int grp = lane >> 4, gl = lane & 15;
+  const int col = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+  const int r0 = 4 * (grp >> 1) + (gl >> 2) + 16 * b, r1 = r0 + 8;
+  const s16x4 lo = read_tr(tile + tr_pos(r0, col)), hi = read_tr(tile + tr_pos(r1, col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// dw[l][c] = sum_t latent[t][l] dkv[t][c]: the contraction runs over tokens,
+// the row index of both operands. A 4-wave workgroup owns 128 x 128 outputs
+// (64 x 64 per wave); each 32-token stage of latent and dkv (the latter
+// rounded to bf16) is stored row-major to LDS and read back transposed, the
+// next stage's global loads in flight during the current stage's products.
+__global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Lt[2][kDwT * kDwM], Gt[2][kDwT * kDwN];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int c0 = blockIdx.x * kDwN, l0 = blockIdx.y * kDwM;
+  u32x4 lreg[2];
+  f32x4 greg[2][2];
+  // thread unit u = tid + 256 i: tile row u / 16, columns 8 (u % 16) .. +7
+  auto gload = [&](int t0) {
 #pragma unroll
-    for (int s = 0; s < kDwCols / 16; ++s) {
-      const bool in = tok && c0 + 16 * s < a.C;
-      const f32x4 lo = in ? *reinterpret_cast<const f32x4 *>(row + 16 * s) : f32x4{};
-      const f32x4 hi = in ? *reinterpret_cast<const f32x4 *>(row + 16 * s + 4) : f32x4{};
-      gf[s] = f32x8_to_bf16(lo, hi);
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, r = u >> 4, c8 = (u & 15) * 8, t = t0 + r;
+      const bool lt = t < a.T && l0 + c8 < a.L, ct = t < a.T && c0 + c8 < a.C;
+      lreg[i] = lt ? *reinterpret_cast<const u32x4 *>(a.latent + static_cast<int64_t>(t) * a.L + l0 + c8)
+                   : u32x4{0u, 0u, 0u, 0u};
+      const float *g = a.dkv + static_cast<int64_t>(ct ? t : 0) * a.C + c0 + c8;
+      greg[i][0] = ct ? *reinterpret_cast<const f32x4 *>(g) : f32x4{};
+      greg[i][1] = ct ? *reinterpret_cast<const f32x4 *>(g + 4) : f32x4{};
     }
   };
-  f32x16 acc[kDwCols / 32] = {};
-  if (a.T > 0) load(0);
-  for (int t0 = 0; t0 < a.T; t0 += BB) {
-    __syncthreads();
-    store_transposed<BB>(lf, LT, 0, lane);
-    store_transposed<kDwCols>(gf, GT, 0, lane);
-    __syncthreads();
-    if (t0 + BB < a.T) load(t0 + BB);
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int s = 0; s < BB / 16; ++s) {
-      const bf16x8 la = frag(LT, TP, 0, s, lane);
-#pragma unroll
-      for (int j = 0; j < kDwCols / 32; ++j) acc[j] = mfma32(la, frag(GT, TP, 32 * j, s, lane), acc[j]);
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, r = u >> 4, c8 = (u & 15) * 8;
+      *reinterpret_cast<u32x4 *>(Lt[buf] + tr_pos(r, c8)) = lreg[i];
+      *reinterpret_cast<u32x4 *>(Gt[buf] + tr_pos(r, c8)) = as_u32x4(f32x8_to_bf16(greg[i][0], greg[i][1]));
     }
+  };
+  f32x16 acc[2][2] = {};
+  const int nst = (a.T + kDwT - 1) / kDwT;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) gload((st + 1) * kDwT);
+#pragma unroll
+    for (int b = 0; b < kDwT / 16; ++b) {
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = tr_frag(Lt[buf], b, 2 * wm + i, lane);
+        bf[i] = tr_frag(Gt[buf], b, 2 * wn + i, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    }
+    // the other buffer's readers finished before the previous stage's barrier
+    if (st + 1 < nst) lstore(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int l = l0 + row_of(r, lane);
-    if (l >= a.L) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < kDwCols / 32; ++j) {
-      const int c = c0 + 32 * j + (lane & 31);
-      if (c < a.C) a.dw[static_cast<int64_t>(l) * a.C + c] = acc[j][r];
+    for (int r = 0; r < 16; ++r) {
+      const int l = l0 + 32 * (2 * wm + i) + row_of(r, lane);
+      if (l >= a.L) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = c0 + 32 * (2 * wn + j) + (lane & 31);
+        if (c < a.C) a.dw[static_cast<int64_t>(l) * a.C + c] = acc[i][j][r];
+      }
     }
-  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n) {
@@ -623,7 +672,7 @@ int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream) {
   // token blocks run fastest: the column tiles of one token block are 8k
   // launch slots apart and so share an XCD (and its L2 copy of their dkv rows)
   dlatent_kernel<<<dim3((a.T + BB - 1) / BB, (a.L + kDlCols - 1) / kDlCols), 64, 0, s>>>(a);
-  dw_kernel<<<dim3((a.C + kDwCols - 1) / kDwCols, (a.L + BB - 1) / BB), 64, 0, s>>>(a);
+  dw_kernel<<<dim3((a.C + kDwN - 1) / kDwN, (a.L + kDwM - 1) / kDwM), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
