@@ -41,7 +41,7 @@ namespace mla {
 namespace {
 
 constexpr int BB = 32;          // keys or queries per block
-constexpr int TP = BB + 8;      // pitch of the transposed (column-major) LDS copies, in bf16
+constexpr int TP = BB + 8;      // pitch of the 32x32 p / ds blocks in LDS, in bf16
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdArgs {
@@ -89,38 +89,42 @@ __device__ __forceinline__ void load_frags(const uint16_t *src, int64_t st, int 
     f[s] = ok ? *reinterpret_cast<const bf16x8 *>(row + 16 * s) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 }
 
-__device__ __forceinline__ uint32_t half_of(const u32x4 &v, int e) {
-  return (v[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-}
-
-// Column-major copy of a block held as fragments (see load_frags):
-// dstT[(c0 + c)*TP + row] for the W columns c. Lanes l and l^1 (adjacent rows)
-// swap fragments and each writes four dwords of two rows, so every store is a
-// dword and no two lanes of a store share a bank.
+// Fragments (see load_frags) to a row-major LDS block of pitch P: one 16-byte
+// store each.
 template <int W>
-__device__ __forceinline__ void store_transposed(const bf16x8 *f, uint16_t *dstT, int c0, int lane) {
-  const bool odd = lane & 1;
-  const int r2 = (lane & 31) & ~1;
+__device__ __forceinline__ void store_rows(const bf16x8 *f, uint16_t *dst, int P, int lane) {
 #pragma unroll
-  for (int s = 0; s < W / 16; ++s) {
-    const u32x4 mine = as_u32x4(f[s]);
-    u32x4 other;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(mine[i], 1);
-    const u32x4 ev = odd ? other : mine, ov = odd ? mine : other;
-    const int cb = c0 + 16 * s + 8 * (lane >> 5) + (odd ? 4 : 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = (odd ? 4 : 0) + j;
-      *reinterpret_cast<uint32_t *>(dstT + (cb + j) * TP + r2) = half_of(ev, e) | (half_of(ov, e) << 16);
-    }
-  }
+  for (int s = 0; s < W / 16; ++s)
+    *reinterpret_cast<bf16x8 *>(dst + (lane & 31) * P + 16 * s + 8 * (lane >> 5)) = f[s];
 }
 
-// MFMA operand of contraction step s from a row-major LDS block: lane l takes
-// row rbase + l%32, elements 16s + 8*(l/32) .. +7.
-__device__ __forceinline__ bf16x8 frag(const uint16_t *m, int pitch, int rbase, int s, int lane) {
-  return *reinterpret_cast<const bf16x8 *>(m + (rbase + (lane & 31)) * pitch + 16 * s + 8 * (lane >> 5));
+// Transposing LDS reads (gfx950 ds_read_b64_tr_b16): lane i of each 16-lane
+// group receives column i of the 4x16 block whose rows its lanes address.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+}
+
+// MFMA operand of contraction step b (rows 16b .. 16b+15 of a row-major
+// [row][column] LDS block of pitch P) for the 32 columns 32d + l%32, read
+// transposed. Element m of lane l comes from row 16b + 8(m/4) + 4(l/32) + m%4:
+// the other operand of the product must list its contraction index in the
+// same order (perm_frag).
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *tile, int P, int b, int d, int lane) {
+  const int grp = lane >> 4, gl = lane & 15;
+  const int col = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+  const int r0 = 4 * (grp >> 1) + (gl >> 2) + 16 * b;
+  const s16x4 lo = read_tr(tile + r0 * P + col), hi = read_tr(tile + (r0 + 8) * P + col);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The matching operand from a row-major [i][k] LDS block of pitch P: row l%32,
+// elements 16b + 4(l/32) .. +3 and 16b + 8 + 4(l/32) .. +3 (tr_frag's order).
+__device__ __forceinline__ bf16x8 perm_frag(const uint16_t *m, int P, int b, int lane) {
+  const uint16_t *row = m + (lane & 31) * P + 16 * b + 4 * (lane >> 5);
+  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row), hi = *reinterpret_cast<const u32x2 *>(row + 8);
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // row i of the block held in register r of lane l (column l%32)
@@ -173,10 +177,11 @@ __global__ __launch_bounds__(256) void row_term_kernel(BwdArgs a, int V) {
   if (live && c == 0) a.Dws[static_cast<int64_t>(h) * a.T + t] = acc;
 }
 
-// LDS of a workgroup: the dk/dv phase's q^T, dout^T, p^T and ds^T blocks, or
-// the dq phase's k^T and ds blocks
+// LDS of a workgroup: the dk/dv phase's q, dout (row-major, read back
+// transposed), p^T and ds^T blocks, or the dq phase's k and ds blocks; rows
+// padded by 8 elements
 template <int K, int V>
-constexpr int kBwdLds = (K + V + 2 * BB) * TP;
+constexpr int kBwdLds = BB * (K + 8) + BB * (V + 8) + 2 * BB * TP;
 
 // Two waves per (block b, head), each under 256 VGPRs so that two waves share
 // a SIMD and cover each other's barriers and LDS round trips. Wave 0 holds the
@@ -185,7 +190,7 @@ constexpr int kBwdLds = (K + V + 2 * BB) * TP;
 // it hands over through LDS in its own register layout, then dv and the last
 // column tiles of dk (or dq). Each wave runs its own loop; the two meet at the
 // same three barriers per block step:
-//   (1) the previous step's readers are done; transposed copies and the s / dp
+//   (1) the previous step's readers are done; row-major copies and the s / dp
 //       products, the next block's loads issued;
 //   (2) dp is in LDS; wave 0 forms p and ds into LDS;
 //   (3) the second-stage products of both waves.
@@ -212,7 +217,8 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
 
   // ---- phase 1: dk, dv of key block b0
   {
-    uint16_t *const QsT = lds, *const OsT = QsT + K * TP, *const Ps = OsT + V * TP, *const Ss = Ps + BB * TP;
+    constexpr int KP = K + 8, VP = V + 8;
+    uint16_t *const Qs = lds, *const Os = Qs + BB * KP, *const Ps = Os + BB * VP, *const Ss = Ps + BB * TP;
     const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? b0 : lo0);
     const int qend = __builtin_amdgcn_readfirstlane(hi1);
     if (wave == 0) {
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
         if (q < a.T) doc_of(a, q, qlo, qhi);
         const float lse2 = lse_n * kLog2e, Dq = D_n;
         __syncthreads();                                   // (1)
-        store_transposed<K>(qf, QsT, 0, lane);
+        store_rows<K>(qf, Qs, KP, lane);
         f32x16 st = {};
 #pragma unroll
         for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
@@ -255,9 +261,9 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
         __syncthreads();                                   // (3)
 #pragma unroll
         for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+          const bf16x8 sa = perm_frag(Ss, TP, s, lane);
 #pragma unroll
-          for (int kt = 0; kt < KS; ++kt) dk[kt] = mfma32(sa, frag(QsT, TP, 32 * kt, s, lane), dk[kt]);
+          for (int kt = 0; kt < KS; ++kt) dk[kt] = mfma32(sa, tr_frag(Qs, KP, s, kt, lane), dk[kt]);
         }
       }
 #pragma unroll
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
       f32x16 dv[V / 32] = {}, dk[K / 32 - KS] = {};
       for (int q0 = qbeg; q0 < qend; q0 += BB) {
         __syncthreads();                                   // (1)
-        store_transposed<V>(gf, OsT, 0, lane);
+        store_rows<V>(gf, Os, VP, lane);
         f32x16 dp = {};
 #pragma unroll
         for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
@@ -292,12 +298,12 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
         __syncthreads();                                   // (3)
 #pragma unroll
         for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 pa = frag(Ps, TP, 0, s, lane), sa = frag(Ss, TP, 0, s, lane);
+          const bf16x8 pa = perm_frag(Ps, TP, s, lane), sa = perm_frag(Ss, TP, s, lane);
 #pragma unroll
-          for (int vt = 0; vt < V / 32; ++vt) dv[vt] = mfma32(pa, frag(OsT, TP, 32 * vt, s, lane), dv[vt]);
+          for (int vt = 0; vt < V / 32; ++vt) dv[vt] = mfma32(pa, tr_frag(Os, VP, s, vt, lane), dv[vt]);
 #pragma unroll
           for (int kt = KS; kt < K / 32; ++kt)
-            dk[kt - KS] = mfma32(sa, frag(QsT, TP, 32 * kt, s, lane), dk[kt - KS]);
+            dk[kt - KS] = mfma32(sa, tr_frag(Qs, KP, s, kt, lane), dk[kt - KS]);
         }
       }
 #pragma unroll
@@ -322,7 +328,8 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
 
   // ---- phase 2: dq of query block b0
   {
-    uint16_t *const KsT = lds, *const Ss = KsT + K * TP;
+    constexpr int KP = K + 8;
+    uint16_t *const Ks = lds, *const Ss = Ks + BB * KP;
     const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
     const int kend = __builtin_amdgcn_readfirstlane(a.causal ? b1 + 1 : hi1);
     if (wave == 0) {
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
       f32x16 dq[KS] = {};
       for (int k0 = kbeg; k0 < kend; k0 += BB) {
         __syncthreads();                                   // (1)
-        store_transposed<K>(kf, KsT, 0, lane);
+        store_rows<K>(kf, Ks, KP, lane);
         f32x16 st = {};
 #pragma unroll
         for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
@@ -358,9 +365,9 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
         __syncthreads();                                   // (3)
 #pragma unroll
         for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+          const bf16x8 sa = perm_frag(Ss, TP, s, lane);
 #pragma unroll
-          for (int kt = 0; kt < KS; ++kt) dq[kt] = mfma32(sa, frag(KsT, TP, 32 * kt, s, lane), dq[kt]);
+          for (int kt = 0; kt < KS; ++kt) dq[kt] = mfma32(sa, tr_frag(Ks, KP, s, kt, lane), dq[kt]);
         }
       }
 #pragma unroll
@@ -388,10 +395,10 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
         __syncthreads();                                   // (3)
 #pragma unroll
         for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 sa = frag(Ss, TP, 0, s, lane);
+          const bf16x8 sa = perm_frag(Ss, TP, s, lane);
 #pragma unroll
           for (int kt = KS; kt < K / 32; ++kt)
-            dq[kt - KS] = mfma32(sa, frag(KsT, TP, 32 * kt, s, lane), dq[kt - KS]);
+            dq[kt - KS] = mfma32(sa, tr_frag(Ks, KP, s, kt, lane), dq[kt - KS]);
         }
       }
 #pragma unroll
@@ -494,14 +501,6 @@ __global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
   }
 }
 
-// Transposing LDS reads (gfx950 ds_read_b64_tr_b16): lane i of each 16-lane
-// group receives column i of the 4x16 block whose rows its lanes address.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-__device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-}
-
 // dw tiles: [32 tokens][128 columns] bf16, row-major with the 16-element
 // blocks of row r XOR-permuted by tr_swz(r) (spreads the transposing reads
 // over the banks)
@@ -512,7 +511,7 @@ __device__ __forceinline__ int tr_pos(int r, int c) { return r * 128 + 16 * ((c 
 // MFMA operand of 16 tokens (b) by 32 columns (d) from a [token][column] tile:
 // lane l takes column 32d + l%32; both operands of dw use the same read, so
 // their token orders match.
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *tile, int b, int d, int lane) {
+__device__ __forceinline__ bf16x8 dw_frag(const uint16_t *tile, int b, int d, int lane) {
   const int grp = lane >> 4, gl = lane & 15;
   const int col = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
   const int r0 = 4 * (grp >> 1) + (gl >> 2) + 16 * b, r1 = r0 + 8;
@@ -567,8 +566,8 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
       bf16x8 af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = tr_frag(Lt[buf], b, 2 * wm + i, lane);
-        bf[i] = tr_frag(Gt[buf], b, 2 * wn + i, lane);
+        af[i] = dw_frag(Lt[buf], b, 2 * wm + i, lane);
+        bf[i] = dw_frag(Gt[buf], b, 2 * wn + i, lane);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
