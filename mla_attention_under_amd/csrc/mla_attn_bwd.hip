@@ -440,63 +440,82 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16(const f32x4 &lo, const f32x4 &hi
                          pack_bf16x2(hi[2], hi[3])});
 }
 
-constexpr int kDlCols = 64;    // d_latent columns per wave
 
-// d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]: one wave per 32 tokens x 64
-// latent columns; both operands are contiguous along c, so the fragments come
-// straight from memory, four contraction steps per group and the next group's
-// loads in flight while one group's products run.
-__global__ __launch_bounds__(64) void dlatent_kernel(UpBwdArgs a) {
-  const int lane = threadIdx.x;
-  const int t0 = blockIdx.x * BB, l0 = blockIdx.y * kDlCols;
-  const int t = t0 + (lane & 31);
-  const bool tok = t < a.T;
-  const float *arow = a.dkv + static_cast<int64_t>(tok ? t : 0) * a.C + 8 * (lane >> 5);
-  const uint16_t *brow[kDlCols / 32];
+// d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]: both operands are
+// contiguous along the contraction c. A 4-wave workgroup owns 64 tokens x 128
+// latent columns (32 x 64 per wave); each 64-column stage of dkv (rounded to
+// bf16) and of the weight rows is stored row-major to LDS, double-buffered,
+// and read back as ordinary row fragments, the next stage's global loads in
+// flight during the current stage's products.
+constexpr int kDlM = 64, kDlN = 128, kDlK = 64, kDlP = kDlK + 8;   // rows, columns, stage, LDS pitch
+__global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kDlM * kDlP], Bs[2][kDlN * kDlP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * kDlM, l0 = blockIdx.y * kDlN;
+  // thread unit u = tid + 256 i covers row u / 8, columns 8 (u % 8) .. +7 of a stage
+  f32x4 areg[2][2];
+  u32x4 breg[4];
+  auto gload = [&](int k0) {
 #pragma unroll
-  for (int j = 0; j < kDlCols / 32; ++j) {
-    const int l = min(l0 + 32 * j + (lane & 31), a.L - 1);
-    brow[j] = a.w + static_cast<int64_t>(l) * a.ldw + a.col0 + 8 * (lane >> 5);
-  }
-  f32x16 acc[kDlCols / 32] = {};
-  constexpr int U = 4;
-  f32x4 alo[U], ahi[U];
-  bf16x8 bf[U][kDlCols / 32];
-  auto load = [&](int k) {
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8, t = t0 + r;
+      const bool ok = t < a.T && k0 + c8 < a.C;
+      const float *g = a.dkv + static_cast<int64_t>(ok ? t : 0) * a.C + k0 + c8;
+      areg[i][0] = ok ? *reinterpret_cast<const f32x4 *>(g) : f32x4{};
+      areg[i][1] = ok ? *reinterpret_cast<const f32x4 *>(g + 4) : f32x4{};
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k + 16 * u;
-      const bool in = kk < a.C;
-      alo[u] = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk) : f32x4{};
-      ahi[u] = in && tok ? *reinterpret_cast<const f32x4 *>(arow + kk + 4) : f32x4{};
-#pragma unroll
-      for (int j = 0; j < kDlCols / 32; ++j)
-        bf[u][j] = in ? *reinterpret_cast<const bf16x8 *>(brow[j] + kk) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8, l = l0 + r;
+      const bool ok = l < a.L && k0 + c8 < a.C;
+      breg[i] = ok ? *reinterpret_cast<const u32x4 *>(a.w + static_cast<int64_t>(l) * a.ldw + a.col0 + k0 + c8)
+                   : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load(0);
-  for (int k = 0; k < a.C; k += 16 * U) {
-    bf16x8 af[U], bcur[U][kDlCols / 32];
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      af[u] = f32x8_to_bf16(alo[u], ahi[u]);
-#pragma unroll
-      for (int j = 0; j < kDlCols / 32; ++j) bcur[u][j] = bf[u][j];
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8;
+      *reinterpret_cast<u32x4 *>(As[buf] + r * kDlP + c8) = as_u32x4(f32x8_to_bf16(areg[i][0], areg[i][1]));
     }
-    if (k + 16 * U < a.C) load(k + 16 * U);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8;
+      *reinterpret_cast<u32x4 *>(Bs[buf] + r * kDlP + c8) = breg[i];
+    }
+  };
+  // row fragment of contraction step s: row rbase + l%32, elements 16s + 8(l/32) .. +7
+  auto rfrag = [&](const uint16_t *m, int rbase, int s) {
+    return *reinterpret_cast<const bf16x8 *>(m + (rbase + (lane & 31)) * kDlP + 16 * s + 8 * (lane >> 5));
+  };
+  f32x16 acc[2] = {};
+  const int nst = (a.C + kDlK - 1) / kDlK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) gload((st + 1) * kDlK);
 #pragma unroll
-      for (int j = 0; j < kDlCols / 32; ++j) acc[j] = mfma32(af[u], bcur[u][j], acc[j]);
+    for (int s = 0; s < kDlK / 16; ++s) {
+      const bf16x8 af = rfrag(As[buf], 32 * wm, s);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = mfma32(af, rfrag(Bs[buf], 64 * wn + 32 * j, s), acc[j]);
+    }
+    // the other buffer's readers finished before the previous stage's barrier
+    if (st + 1 < nst) lstore(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int tt = t0 + row_of(r, lane);
-    if (tt >= a.T) continue;
+    const int t = t0 + 32 * wm + row_of(r, lane);
+    if (t >= a.T) continue;
 #pragma unroll
-    for (int j = 0; j < kDlCols / 32; ++j) {
-      const int l = l0 + 32 * j + (lane & 31);
-      if (l < a.L) a.dl[static_cast<int64_t>(tt) * a.L + l] = acc[j][r];
+    for (int j = 0; j < 2; ++j) {
+      const int l = l0 + 64 * wn + 32 * j + (lane & 31);
+      if (l < a.L) a.dl[static_cast<int64_t>(t) * a.L + l] = acc[j][r];
     }
   }
 }
@@ -670,7 +689,7 @@ int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream) {
   }
   // token blocks run fastest: the column tiles of one token block are 8k
   // launch slots apart and so share an XCD (and its L2 copy of their dkv rows)
-  dlatent_kernel<<<dim3((a.T + BB - 1) / BB, (a.L + kDlCols - 1) / kDlCols), 64, 0, s>>>(a);
+  dlatent_kernel<<<dim3((a.T + kDlM - 1) / kDlM, (a.L + kDlN - 1) / kDlN), 256, 0, s>>>(a);
   dw_kernel<<<dim3((a.C + kDwN - 1) / kDwN, (a.L + kDwM - 1) / kDwM), 256, 0, s>>>(a);
   return hipGetLastError();
 }
