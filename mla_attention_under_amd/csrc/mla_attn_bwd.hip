@@ -442,33 +442,36 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16(const f32x4 &lo, const f32x4 &hi
 
 
 // d_latent[t][l] = sum_c dkv[t][c] w[l][col0 + c]: both operands are
-// contiguous along the contraction c. A 4-wave workgroup owns 64 tokens x 128
-// latent columns (32 x 64 per wave); each 64-column stage of dkv (rounded to
+// contiguous along the contraction c. A 4-wave workgroup owns 64 tokens x 64
+// latent columns (32 x 32 per wave); each 128-column stage of dkv (rounded to
 // bf16) and of the weight rows is stored row-major to LDS, double-buffered,
 // and read back as ordinary row fragments, the next stage's global loads in
 // flight during the current stage's products.
-constexpr int kDlM = 64, kDlN = 128, kDlK = 64, kDlP = kDlK + 8;   // rows, columns, stage, LDS pitch
+constexpr int kDlM = 64, kDlN = 64, kDlK = 128, kDlP = kDlK + 8;  // rows, columns, stage, LDS pitch
+constexpr int kDlJ = kDlN / 64;                                     // 32-column tiles per wave
 __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kDlM * kDlP], Bs[2][kDlN * kDlP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = blockIdx.x * kDlM, l0 = blockIdx.y * kDlN;
-  // thread unit u = tid + 256 i covers row u / 8, columns 8 (u % 8) .. +7 of a stage
-  f32x4 areg[2][2];
-  u32x4 breg[4];
+  // thread unit u = tid + 256 i covers row u / kCH, columns 8 (u % kCH) .. +7 of a stage
+  constexpr int kCH = kDlK / 8, kAU = kDlM * kCH / 256;   // 16-byte chunks per row, dkv chunks per thread
+  f32x4 areg[kAU][2];
+  constexpr int kBU = kDlN * kCH / 256;   // weight chunks per thread
+  u32x4 breg[kBU];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8, t = t0 + r;
+    for (int i = 0; i < kAU; ++i) {
+      const int u = tid + 256 * i, r = u / kCH, c8 = (u % kCH) * 8, t = t0 + r;
       const bool ok = t < a.T && k0 + c8 < a.C;
       const float *g = a.dkv + static_cast<int64_t>(ok ? t : 0) * a.C + k0 + c8;
       areg[i][0] = ok ? *reinterpret_cast<const f32x4 *>(g) : f32x4{};
       areg[i][1] = ok ? *reinterpret_cast<const f32x4 *>(g + 4) : f32x4{};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8, l = l0 + r;
+    for (int i = 0; i < kBU; ++i) {
+      const int u = tid + 256 * i, r = u / kCH, c8 = (u % kCH) * 8, l = l0 + r;
       const bool ok = l < a.L && k0 + c8 < a.C;
       breg[i] = ok ? *reinterpret_cast<const u32x4 *>(a.w + static_cast<int64_t>(l) * a.ldw + a.col0 + k0 + c8)
                    : u32x4{0u, 0u, 0u, 0u};
@@ -476,13 +479,13 @@ __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8;
+    for (int i = 0; i < kAU; ++i) {
+      const int u = tid + 256 * i, r = u / kCH, c8 = (u % kCH) * 8;
       *reinterpret_cast<u32x4 *>(As[buf] + r * kDlP + c8) = as_u32x4(f32x8_to_bf16(areg[i][0], areg[i][1]));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + 256 * i, r = u >> 3, c8 = (u & 7) * 8;
+    for (int i = 0; i < kBU; ++i) {
+      const int u = tid + 256 * i, r = u / kCH, c8 = (u % kCH) * 8;
       *reinterpret_cast<u32x4 *>(Bs[buf] + r * kDlP + c8) = breg[i];
     }
   };
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
   auto rfrag = [&](const uint16_t *m, int rbase, int s) {
     return *reinterpret_cast<const bf16x8 *>(m + (rbase + (lane & 31)) * kDlP + 16 * s + 8 * (lane >> 5));
   };
-  f32x16 acc[2] = {};
+  f32x16 acc[kDlJ] = {};
   const int nst = (a.C + kDlK - 1) / kDlK;
   gload(0);
   lstore(0);
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
     for (int s = 0; s < kDlK / 16; ++s) {
       const bf16x8 af = rfrag(As[buf], 32 * wm, s);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j] = mfma32(af, rfrag(Bs[buf], 64 * wn + 32 * j, s), acc[j]);
+      for (int j = 0; j < kDlJ; ++j) acc[j] = mfma32(af, rfrag(Bs[buf], (kDlN / 2) * wn + 32 * j, s), acc[j]);
     }
     // the other buffer's readers finished before the previous stage's barrier
     if (st + 1 < nst) lstore(buf ^ 1);
@@ -513,8 +516,8 @@ __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
     const int t = t0 + 32 * wm + row_of(r, lane);
     if (t >= a.T) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int l = l0 + 64 * wn + 32 * j + (lane & 31);
+    for (int j = 0; j < kDlJ; ++j) {
+      const int l = l0 + (kDlN / 2) * wn + 32 * j + (lane & 31);
       if (l < a.L) a.dl[static_cast<int64_t>(t) * a.L + l] = acc[j][r];
     }
   }
