@@ -523,10 +523,11 @@ __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
   }
 }
 
-// dw tiles: [32 tokens][128 columns] bf16, row-major with the 16-element
+// dw tiles: [64 tokens][128 columns] bf16, row-major with the 16-element
 // blocks of row r XOR-permuted by tr_swz(r) (spreads the transposing reads
 // over the banks)
-constexpr int kDwM = 128, kDwN = 128, kDwT = 32;
+constexpr int kDwM = 128, kDwN = 128, kDwT = 64;
+constexpr int kDwU = kDwT * 16 / 256;   // 16-byte chunks of each tile per thread and stage
 __device__ __forceinline__ int tr_swz(int r) { return (r & 2) | ((r & 1) * 5); }
 __device__ __forceinline__ int tr_pos(int r, int c) { return r * 128 + 16 * ((c >> 4) ^ tr_swz(r)) + (c & 15); }
 
@@ -543,7 +544,7 @@ __device__ __forceinline__ bf16x8 dw_frag(const uint16_t *tile, int b, int d, in
 
 // dw[l][c] = sum_t latent[t][l] dkv[t][c]: the contraction runs over tokens,
 // the row index of both operands. A 4-wave workgroup owns 128 x 128 outputs
-// (64 x 64 per wave); each 32-token stage of latent and dkv (the latter
+// (64 x 64 per wave); each 64-token stage of latent and dkv (the latter
 // rounded to bf16) is stored row-major to LDS and read back transposed, the
 // next stage's global loads in flight during the current stage's products.
 __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
@@ -552,12 +553,12 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int c0 = blockIdx.x * kDwN, l0 = blockIdx.y * kDwM;
-  u32x4 lreg[2];
-  f32x4 greg[2][2];
+  u32x4 lreg[kDwU];
+  f32x4 greg[kDwU][2];
   // thread unit u = tid + 256 i: tile row u / 16, columns 8 (u % 16) .. +7
   auto gload = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kDwU; ++i) {
       const int u = tid + 256 * i, r = u >> 4, c8 = (u & 15) * 8, t = t0 + r;
       const bool lt = t < a.T && l0 + c8 < a.L, ct = t < a.T && c0 + c8 < a.C;
       lreg[i] = lt ? *reinterpret_cast<const u32x4 *>(a.latent + static_cast<int64_t>(t) * a.L + l0 + c8)
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kDwU; ++i) {
       const int u = tid + 256 * i, r = u >> 4, c8 = (u & 15) * 8;
       *reinterpret_cast<u32x4 *>(Lt[buf] + tr_pos(r, c8)) = lreg[i];
       *reinterpret_cast<u32x4 *>(Gt[buf] + tr_pos(r, c8)) = as_u32x4(f32x8_to_bf16(greg[i][0], greg[i][1]));
