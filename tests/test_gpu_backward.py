@@ -227,3 +227,50 @@ def test_latent_up_proj_bwd_no_tokens_zeroes_dw():
     dl, dw = mla.mla_latent_up_proj_bwd(latent, w, dkv, heads, 0, heads, 32, 32, dw=dw)
     torch.cuda.synchronize()
     assert dl.shape == (0, L) and torch.all(dw == 0)
+
+
+# ---- the other attention workloads at full size, checked on sampled heads
+#
+# Heads are independent apart from the shared band, so the oracle runs on one
+# head (and one document) at a time; dq and dkv of the sampled heads are
+# checked against it with the same derived bound. The band's head sum is
+# checked at full size on the rank shard above. out and lse come from the
+# forward kernel, hence the wider allowance for the row term.
+
+def _pipeline(T, H, seed, cu):
+    d = _inputs(T, H, seed)
+    q, kv, kr = dev(d["q"]), dev(d["kv"]), dev(d["k_rope"])
+    out = torch.empty(T, H, V, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(H, T, dtype=torch.float32, device="cuda")
+    cud = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    mla.mla_attention_fwd(q, kv, kr, out, N, R, V, SCALE, causal=True, lse=lse, cu_seqlens=cud)
+    got = mla.mla_attention_bwd(q, kv, kr, out, dev(d["dout"]), lse, N, R, V, SCALE, causal=True, cu_seqlens=cud)
+    torch.cuda.synchronize()
+    return d, host64(out), [host64(x) for x in got]
+
+
+def _check_sampled(d, out64, got, heads, docs, name):
+    for a, b in docs:
+        for h in heads:
+            sub = {"q": d["q"][a:b, h:h + 1], "kv": d["kv"][a:b, h:h + 1], "k_rope": d["k_rope"][a:b],
+                   "dout": d["dout"][a:b, h:h + 1]}
+            ref = oracle.attention_backward(sub["q"], sub["kv"], sub["k_rope"], sub["dout"], N, SCALE, causal=True)
+            bq, bkv, _ = _bounds(sub, out64[a:b, h:h + 1], True, None, 2.0 ** -6)
+            _check(got[0][a:b, h:h + 1], ref[0], bq, f"{name} dq tokens [{a},{b}) head {h}")
+            _check(got[1][a:b, h:h + 1], ref[1], bkv, f"{name} dkv tokens [{a},{b}) head {h}")
+    assert np.all(np.isfinite(got[2])), f"{name}: non-finite dk_rope"
+
+
+def test_attention_bwd_uneven22_sampled_heads():
+    w = mi.WORKLOADS["uneven22"]
+    print(f"[bwd] uneven22 T={w.T} H={w.H}, heads 0, 13, 21", flush=True)
+    d, out64, got = _pipeline(w.T, w.H, 22, None)
+    _check_sampled(d, out64, got, [0, 13, 21], [(0, w.T)], "uneven22")
+
+
+def test_attention_bwd_varlen16k_sampled_heads():
+    w = mi.WORKLOADS["varlen16k"]
+    cu = [int(x) for x in w.cu_seqlens]
+    print(f"[bwd] varlen16k T={w.T} H={w.H} documents {cu}, head 5", flush=True)
+    d, out64, got = _pipeline(w.T, w.H, 16, cu)
+    _check_sampled(d, out64, got, [5], list(zip(cu[:-1], cu[1:])), "varlen16k")
