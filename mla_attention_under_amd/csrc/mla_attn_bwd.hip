@@ -59,7 +59,9 @@ struct BwdArgs {
   int causal;
 };
 
-// document [lo, hi) holding token t (one document of T tokens without cu)
+// document [lo, hi) holding token t (one document of T tokens without cu);
+// the bounds are clamped to [0, T], so malformed offsets give wrong documents,
+// never an access outside the buffers
 __device__ __forceinline__ void doc_of(const BwdArgs &a, int t, int &lo, int &hi) {
   if (a.cu == nullptr) {
     lo = 0;
@@ -72,8 +74,8 @@ __device__ __forceinline__ void doc_of(const BwdArgs &a, int t, int &lo, int &hi
     if (a.cu[m] <= t) l = m;
     else r = m;
   }
-  lo = a.cu[l];
-  hi = a.cu[l + 1];
+  lo = min(max(a.cu[l], 0), a.T);
+  hi = min(max(a.cu[l + 1], lo), a.T);
 }
 
 // MFMA operands straight from memory: fragment s of lane l is row r0 + l%32
@@ -82,7 +84,7 @@ __device__ __forceinline__ void doc_of(const BwdArgs &a, int t, int &lo, int &hi
 template <int W>
 __device__ __forceinline__ void load_frags(const uint16_t *src, int64_t st, int r0, int lim, bf16x8 *f, int lane) {
   const int r = r0 + (lane & 31);
-  const bool ok = r < lim;
+  const bool ok = r >= 0 && r < lim;
   const uint16_t *row = src + static_cast<int64_t>(ok ? r : 0) * st + 8 * (lane >> 5);
 #pragma unroll
   for (int s = 0; s < W / 16; ++s)
