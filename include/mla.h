@@ -280,7 +280,7 @@ int mla_attention_fwd(const mla_attn_args *a, void *stream);
  *   dkv    : [T][H][N+V]  (= [dk_nope | dv], the layout of kv)
  *   dk_rope: [T][R]
  * Runs bf16 with N=128, R=64, V=128 (MLA_EUNSUPPORTED otherwise), 16-byte
- * aligned inputs and strides that are multiples of 8 elements.
+ * aligned inputs and dk_rope, and strides that are multiples of 8 elements.
  * Workspace: mla_attention_bwd_workspace_size() bytes, 256-byte aligned,
  * contents need not be initialised (row terms and per-head band gradients).
  * The result does not depend on scheduling: every sum runs in a fixed order.

@@ -415,12 +415,24 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
+// four consecutive band elements per thread (R is a multiple of 4), the heads
+// added in order, four heads' loads in flight at a time
 __global__ __launch_bounds__(256) void band_sum_kernel(BwdArgs a, int R) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<int64_t>(a.T) * R) return;
-  float acc = 0.f;
-  for (int h = 0; h < a.H; ++h) acc += a.band[static_cast<int64_t>(h) * a.T * R + i];
-  a.dkr[i] = acc;
+  const int64_t n = static_cast<int64_t>(a.T) * R / 4, stride = static_cast<int64_t>(a.T) * R / 4;
+  if (i >= n) return;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(a.band) + i;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int h = 0;
+  for (; h + 4 <= a.H; h += 4) {
+    const f32x4 x0 = src[h * stride], x1 = src[(h + 1) * stride], x2 = src[(h + 2) * stride], x3 = src[(h + 3) * stride];
+    acc += x0;
+    acc += x1;
+    acc += x2;
+    acc += x3;
+  }
+  for (; h < a.H; ++h) acc += src[h * stride];
+  reinterpret_cast<f32x4 *>(a.dkr)[i] = acc;
 }
 
 // ---- backward of the latent up-projection -------------------------------
@@ -624,11 +636,12 @@ __global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n) {
 
 template <int N, int R, int V>
 int run(const BwdArgs &a, hipStream_t s) {
+  static_assert(R % 4 == 0, "the band sum moves four elements per thread");
   const unsigned rows = static_cast<unsigned>((static_cast<int64_t>(a.T) * a.H * 16 + 255) / 256);
   row_term_kernel<<<rows, 256, 0, s>>>(a, V);
   const dim3 grid(static_cast<unsigned>((a.T + BB - 1) / BB), static_cast<unsigned>(a.H));
   attn_bwd_kernel<N, R, V><<<grid, 128, 0, s>>>(a);
-  const unsigned sums = static_cast<unsigned>((static_cast<int64_t>(a.T) * R + 255) / 256);
+  const unsigned sums = static_cast<unsigned>((static_cast<int64_t>(a.T) * R / 4 + 255) / 256);
   if (R > 0) band_sum_kernel<<<sums, 256, 0, s>>>(a, R);
   return hipGetLastError();
 }

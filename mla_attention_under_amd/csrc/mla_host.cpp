@@ -518,11 +518,11 @@ static int attn_bwd_validate(const mla_attn_bwd_args *a, const char *who) {
     return fail(MLA_EINVAL, "%s: NULL buffer", who);
   const uintptr_t al = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->kv) |
                        reinterpret_cast<uintptr_t>(a->k_rope) | reinterpret_cast<uintptr_t>(a->out) |
-                       reinterpret_cast<uintptr_t>(a->dout);
+                       reinterpret_cast<uintptr_t>(a->dout) | reinterpret_cast<uintptr_t>(a->dk_rope);
   const int64_t st = a->q_stride_t | a->q_stride_h | a->kv_stride_t | a->kv_stride_h | a->kr_stride_t |
                      a->o_stride_t | a->o_stride_h | a->do_stride_t | a->do_stride_h;
   if (al % 16 || st % 8)
-    return fail(MLA_EUNSUPPORTED, "%s: needs 16-byte aligned inputs and strides multiple of 8", who);
+    return fail(MLA_EUNSUPPORTED, "%s: needs 16-byte aligned inputs and dk_rope, strides multiple of 8", who);
   const size_t need = mla::attn_bwd_workspace_bytes(a->T, a->H, a->R);
   if (a->workspace == nullptr || a->workspace_bytes < need || reinterpret_cast<uintptr_t>(a->workspace) % 256)
     return fail(MLA_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", who, need,

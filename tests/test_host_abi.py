@@ -222,6 +222,7 @@ def test_attention_bwd_validation_before_launch(lib):
     assert f(N=64) == mla.MLA_EUNSUPPORTED                  # no kernel for these widths
     assert f(dtype=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
     assert f(dout=0x50002) == mla.MLA_EUNSUPPORTED          # misaligned
+    assert f(dk_rope=0x90004) == mla.MLA_EUNSUPPORTED       # misaligned fp32 output
     assert f(lse=None) == mla.MLA_EINVAL                     # the forward's lse is required
     assert f(dk_rope=None) == mla.MLA_EINVAL
     assert f(sized=False) == mla.MLA_EINVAL                  # workspace too small
