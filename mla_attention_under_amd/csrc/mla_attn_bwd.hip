@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256) void dlatent_kernel(UpBwdArgs a) {
 // dw tiles: [64 tokens][128 columns] bf16, row-major with the 16-element
 // blocks of row r XOR-permuted by tr_swz(r) (spreads the transposing reads
 // over the banks)
-constexpr int kDwM = 128, kDwN = 128, kDwT = 64;
+constexpr int kDwM = 64, kDwN = 128, kDwT = 64;   // latent columns (the first kDwM of a 128-wide tile), dkv columns, tokens
 constexpr int kDwU = kDwT * 16 / 256;   // 16-byte chunks of each tile per thread and stage
 __device__ __forceinline__ int tr_swz(int r) { return (r & 2) | ((r & 1) * 5); }
 __device__ __forceinline__ int tr_pos(int r, int c) { return r * 128 + 16 * ((c >> 4) ^ tr_swz(r)) + (c & 15); }
@@ -557,12 +557,12 @@ __device__ __forceinline__ bf16x8 dw_frag(const uint16_t *tile, int b, int d, in
 }
 
 // dw[l][c] = sum_t latent[t][l] dkv[t][c]: the contraction runs over tokens,
-// the row index of both operands. A 4-wave workgroup owns 128 x 128 outputs
-// (64 x 64 per wave); each 64-token stage of latent and dkv (the latter
+// the row index of both operands. A 4-wave workgroup owns 64 x 128 outputs
+// (32 x 64 per wave); each 64-token stage of latent and dkv (the latter
 // rounded to bf16) is stored row-major to LDS and read back transposed, the
 // next stage's global loads in flight during the current stage's products.
 __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Lt[2][kDwT * kDwM], Gt[2][kDwT * kDwN];
+  __shared__ __attribute__((aligned(16))) uint16_t Lt[2][kDwT * 128], Gt[2][kDwT * kDwN];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kDwU; ++i) {
       const int u = tid + 256 * i, r = u >> 4, c8 = (u & 15) * 8, t = t0 + r;
-      const bool lt = t < a.T && l0 + c8 < a.L, ct = t < a.T && c0 + c8 < a.C;
+      const bool lt = t < a.T && c8 < kDwM && l0 + c8 < a.L, ct = t < a.T && c0 + c8 < a.C;
       lreg[i] = lt ? *reinterpret_cast<const u32x4 *>(a.latent + static_cast<int64_t>(t) * a.L + l0 + c8)
                    : u32x4{0u, 0u, 0u, 0u};
       const float *g = a.dkv + static_cast<int64_t>(ct ? t : 0) * a.C + c0 + c8;
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
       *reinterpret_cast<u32x4 *>(Gt[buf] + tr_pos(r, c8)) = as_u32x4(f32x8_to_bf16(greg[i][0], greg[i][1]));
     }
   };
-  f32x16 acc[2][2] = {};
+  f32x16 acc[2] = {};
   const int nst = (a.T + kDwT - 1) / kDwT;
   gload(0);
   lstore(0);
@@ -600,33 +600,24 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
     if (st + 1 < nst) gload((st + 1) * kDwT);
 #pragma unroll
     for (int b = 0; b < kDwT / 16; ++b) {
-      bf16x8 af[2], bf[2];
+      const bf16x8 af = dw_frag(Lt[buf], b, wm, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = dw_frag(Lt[buf], b, 2 * wm + i, lane);
-        bf[i] = dw_frag(Gt[buf], b, 2 * wn + i, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[j] = mfma32(af, dw_frag(Gt[buf], b, 2 * wn + j, lane), acc[j]);
     }
     // the other buffer's readers finished before the previous stage's barrier
     if (st + 1 < nst) lstore(buf ^ 1);
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int r = 0; r < 16; ++r) {
+    const int l = l0 + 32 * wm + row_of(r, lane);
+    if (l >= a.L) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int l = l0 + 32 * (2 * wm + i) + row_of(r, lane);
-      if (l >= a.L) continue;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = c0 + 32 * (2 * wn + j) + (lane & 31);
-        if (c < a.C) a.dw[static_cast<int64_t>(l) * a.C + c] = acc[i][j][r];
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int c = c0 + 32 * (2 * wn + j) + (lane & 31);
+      if (c < a.C) a.dw[static_cast<int64_t>(l) * a.C + c] = acc[j][r];
     }
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n) {
