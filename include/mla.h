@@ -328,8 +328,9 @@ int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream);
  *   dw       : fp32 [L][heads*(N+V)], overwritten: the gradient of the head
  *              range's columns (the other columns get none from these heads)
  * dkv is rounded to bf16 as an MFMA operand; products accumulate in fp32.
- * Runs bf16 with L and heads*(N+V) multiples of 32 and 16-byte aligned
- * latent, w_kvb and dkv (MLA_EUNSUPPORTED otherwise). T = 0 zeroes dw.
+ * Runs bf16 with L and heads*(N+V) multiples of 32, N+V a multiple of 8, and
+ * 16-byte aligned latent, w_kvb and dkv (MLA_EUNSUPPORTED otherwise).
+ * T = 0 zeroes dw.
  */
 int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *dkv, float *d_latent, float *dw,
                            int64_t T, int L, int heads_total, int head_begin, int heads, int N, int V, int dtype,

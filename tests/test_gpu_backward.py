@@ -1,4 +1,5 @@
-"""GPU parity of mla_attention_bwd against the oracle's attention_backward.
+"""GPU parity of mla_attention_bwd against the oracle's attention_backward, and of
+mla_latent_up_proj_bwd against latent_up_proj_backward.
 
 Tolerance, derived from the kernel's arithmetic rather than fixed: the inputs
 are exact bf16 and every product accumulates in fp32, so the rounding that
