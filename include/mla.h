@@ -125,14 +125,14 @@ int mla_apply_rope(void *x, int64_t tokens, int heads, int64_t stride_t, int64_t
  *   send[T*off_r*F + (t*sizes[r] + h-off_r)*F + col_offset + j]
  * for the rank r holding head h (sizes: HOST list of sp positive ints summing
  * to heads). Columns of send outside [col_offset, col_offset+P) are untouched.
- * The result equals mla_latent_up_proj, then mla_apply_rope on the band, then
- * mla_pack_heads into those columns, bit for bit (the tile is rounded to bf16
- * before the rotation, as the separate calls round it).
+ * The band is rotated in fp32 on the projection's accumulators and rounded to
+ * bf16 once; the other columns equal mla_latent_up_proj (then mla_pack_heads)
+ * bit for bit.
  *   latent : [tokens][L] bf16;  w : [L][w_heads*P] bf16;  send: bf16.
- * Runs bf16 only (MLA_EUNSUPPORTED otherwise) with L, P, F, col_offset,
- * rope_offset multiples of 8, R a multiple of 16, 16-byte aligned buffers and
- * tables (cs_stride a multiple of 8), and each head's band inside one 128-column
- * tile of the projection (true for P = 192, rope_offset = 128, R = 64).
+ * Runs bf16 only (MLA_EUNSUPPORTED otherwise) with L, P, F, col_offset
+ * multiples of 8, 16-byte aligned buffers and tables (cs_stride a multiple of
+ * 8), and, when R > 0, R = 64 with rope_offset and P multiples of 64 (the MLA
+ * query block: P = 192, rope_offset = 128, R = 64).
  * heads <= 256, sp <= 256. tokens == 0 is a no-op.
  */
 int mla_project_pack(const void *latent, const void *w, void *send, int64_t tokens, int L, int w_heads, int head_begin,
@@ -232,10 +232,13 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
  * aligned (0 when none is needed); scratch whose contents need not be
  * initialised and are left arbitrary. Dense causal calls keep there the
  * partial softmax states of the query tiles they split between two
- * workgroups and one arrival flag per split tile (tagged with a per-call
- * value, so no clearing is needed); packed-document calls keep the
- * device-built tile schedule. Calls that may run concurrently need separate
- * workspaces.
+ * workgroups and one arrival flag per split tile. A flag carries a per-call
+ * tag drawn when the call is made, so no clearing is needed, and every call
+ * leaves each of its flags at "merged" for its tag: a launch captured in a
+ * HIP graph (one tag for every replay) can be replayed back to back, with new
+ * inputs, on the same workspace. Packed-document calls keep the device-built
+ * tile schedule. Calls that may run concurrently (overlapping launches or
+ * replays on different streams) need separate workspaces.
  */
 typedef struct mla_attn_args {
   const void *q;

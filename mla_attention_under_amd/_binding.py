@@ -121,19 +121,31 @@ def _check(fn, rc):
 
 
 _ws_cache = {}
+_ws_retired = []
 
 
-def _workspace(nbytes: int, device) -> "torch.Tensor | None":
-    """Device scratch of at least nbytes, reused by every call on that device.
+def _workspace(nbytes: int, device, stream=None) -> "torch.Tensor | None":
+    """Device scratch of at least nbytes for calls on one (device, stream).
 
-    Calls that may overlap on different streams must pass their own workspace.
+    Each stream has its own workspace, so calls on different streams never
+    share scratch, and a launch captured into a HIP graph (on its capture
+    stream) keeps a workspace that later eager calls do not touch. A workspace
+    that grows is replaced, but the old tensor is kept alive for the life of the
+    process: a captured graph still holds its address, so its memory must never
+    return to the caching allocator. Calls that overlap on ONE stream are
+    ordered by the stream, so they may share it.
     """
     if nbytes == 0:
         return None
-    key = torch.device(device)
+    dev = torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev, int(stream.cuda_stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
+        if ws is not None:
+            _ws_retired.append(ws)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 
@@ -330,7 +342,7 @@ def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None,
         assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
     if workspace is None:
         workspace = _workspace(mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens),
-                               q.device)
+                               q.device, stream)
     a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace)
     _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
     return out
@@ -383,7 +395,7 @@ def mla_attention_bwd(q, kv, k_rope, out, dout, lse, N, R, V, scale, causal=True
         assert t.dtype == torch.float32 and t.is_contiguous()
     if workspace is None:
         workspace = _workspace(mla_attention_bwd_workspace_size(q, kv, k_rope, out, dout, N, R, V, scale, causal,
-                                                                cu_seqlens), q.device)
+                                                                cu_seqlens), q.device, stream)
     a = _attn_bwd_args(q, kv, k_rope, out, dout, lse, dq, dkv, dk_rope, N, R, V, scale, causal, cu_seqlens,
                        workspace)
     _check("mla_attention_bwd", lib.mla_attention_bwd(ctypes.byref(a), _stream(stream)))
@@ -444,7 +456,7 @@ def mla_latent_decode_fwd(q, latent_cache, rope_cache, w_kvb, out, heads_total, 
         assert t.is_contiguous()
     if workspace is None:
         workspace = _workspace(mla_latent_decode_workspace_size(q, latent_cache, rope_cache, w_kvb, out, heads_total,
-                                                                head_begin, N, R, V, num_splits, scale), q.device)
+                                                                head_begin, N, R, V, num_splits, scale), q.device, stream)
     a = _decode_args(q, latent_cache, rope_cache, w_kvb, out, heads_total, head_begin, N, R, V, num_splits, scale,
                      lse, workspace)
     _check("mla_latent_decode_fwd", lib.mla_latent_decode_fwd(ctypes.byref(a), _stream(stream)))

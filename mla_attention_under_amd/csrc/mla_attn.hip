@@ -33,7 +33,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "mla_common.cuh"
@@ -228,7 +227,10 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
 // The flag holds (epoch << 1) | 1 after a first arrival of this call and
 // epoch << 1 after the second; any other value (an earlier call, or memory
 // never used) reads as "nobody yet". The epoch is a 62-bit per-call tag
-// (next_call_tag), so the workspace needs no clearing.
+// (next_call_tag), so the workspace needs no clearing. Every path through a
+// split tile ends with its flag at epoch << 1 (the early merge of the
+// one-segment workgroup included), so a captured launch replayed with the
+// same epoch finds every flag at "nobody yet" again.
 __device__ __forceinline__ bool arrive(unsigned long long *flag, unsigned long long epoch) {
   const unsigned long long one = (epoch << 1) | 1ull, done = epoch << 1;
   unsigned long long cur = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -827,6 +829,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   const bool pre = pp.part && qt2 >= 0;
   const int tiles2 = qt2 >= 0 ? key_tiles_of(qt2, a.T) : 0;
   if (early) {
+    // the other workgroup arrived first in this call and never looks at the
+    // flag again: mark the pair done, so that every call leaves every flag at
+    // epoch << 1 and a replay of the same launch (same epoch) starts from
+    // "nobody yet" on every pair
+    if (tid == 0)
+      __hip_atomic_store(a.flags + __builtin_amdgcn_readfirstlane(pp.slot), a.epoch << 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     if (kh == 0) combine_store(other, qt1);
   } else if (pp.part) {
     publish(pp.slot, role);
@@ -998,17 +1007,6 @@ WsLayout ws_layout(int64_t T, int n_seq) {
   return w;
 }
 
-// Dense causal work order. 1 (default): tile pairing with an even split of
-// each pair's key tiles (see pair_plan). 0: one query tile per workgroup,
-// heaviest first (no workspace). MLA_ATTN_ORDER overrides it (for measurement).
-int attn_order() {
-  static const int order = [] {
-    const char *e = getenv("MLA_ATTN_ORDER");
-    return e ? atoi(e) : 1;
-  }();
-  return order;
-}
-
 // Dense causal pairing: two softmax-state records and one arrival flag per
 // (head, pair); the flags follow the records.
 size_t pair_records_bytes(int64_t T, int H) {
@@ -1027,7 +1025,7 @@ bool attn_fast_path(int N, int R, int V, int bf16) { return bf16 && N == 128 && 
 size_t attn_workspace_bytes(int64_t T, int H, int n_seq, int has_cu, int causal, int N, int R, int V, int bf16) {
   if (!attn_fast_path(N, R, V, bf16) || T == 0) return 0;
   if (has_cu) return ws_layout(T, n_seq).bytes;
-  if (causal && attn_order() == 1) return pair_ws_bytes(T, H);
+  if (causal) return pair_ws_bytes(T, H);
   return 0;
 }
 
@@ -1066,7 +1064,7 @@ int launch_attention(const AttnPlan &p, void *stream) {
     a.tasks = nullptr;
     a.task_count = nullptr;
     a.n_qtiles = static_cast<int>((p.T + BM - 1) / BM);
-    a.order = p.causal ? attn_order() : 0;
+    a.order = p.causal ? 1 : 0;   // dense causal: tile pairing (see pair_plan)
     a.part = nullptr;
     a.flags = nullptr;
     a.epoch = 0;

@@ -68,8 +68,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // head h (0-based within the projected range) belongs to the rank whose slab
 // starts at head off[h] and holds qr[h] heads. Its row for token m is
 //   send[T*off*F + (m*qr + h - off)*F + col_off + n % P].
-// Columns [rope_off, rope_off + R) of each block are rotated (RoPE) from the
-// bf16-rounded tile before they leave, exactly as the in-place rotation does.
+// Columns [rope_off, rope_off + R) of each block are rotated (RoPE) in fp32
+// from the accumulators, so the band is rounded to bf16 once; R = 64 at a
+// multiple of 64 in a block whose width is a multiple of 64 (checked on the
+// host), so a head's band is exactly one wave's 64-column group.
 struct SlabOut {
   uint16_t *send;
   const uint16_t *cos, *sin;
@@ -213,6 +215,71 @@ __global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
   // epilogue: registers -> LDS (rows [0,128) in a0, [128,256) in a1, each
   // [128][128] bf16 with 16-byte chunks XOR-swizzled by row) -> 16-byte row stores
   __syncthreads();
+  if constexpr (SLAB) {
+    // RoPE of the band on the fp32 accumulators. The waves whose 64-column
+    // group is a band hold all of it: lane (lrow, half) has columns
+    // 32 i + 8 g + 4 half + e of rows 32 j + lrow. A half-band pair (c, c + 32)
+    // is acc[0] / acc[1] of one lane; an interleaved pair (2p, 2p + 1) comes
+    // through the wave's own 16 KB of LDS (the stage buffers are free here).
+    const int g0 = n0 + 64 * wn;
+    const bool band = so.R > 0 && g0 < ncols && g0 % so.P == so.rope_off;   // uniform per wave
+    float *xs = reinterpret_cast<float *>(wave < 2   ? a0 + 8192 * wave
+                                          : wave < 4 ? a1 + 8192 * (wave - 2)
+                                          : wave < 6 ? a2 + 8192 * (wave - 4)
+                                          : wave == 6 ? b0
+                                                      : b1);
+    // 16-byte chunk c4 (of 16) of row r of the wave's [64][64] fp32 block, XOR-swizzled by row
+    auto xchunk = [&](int r, int c4) { return reinterpret_cast<f32x4 *>(xs + 64 * r + 4 * (c4 ^ (r & 15))); };
+    auto tab = [&](const u32x2 &v, int e) {
+      const uint32_t w = v[e >> 1];
+      return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    };
+    if (band && so.interleaved) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *xchunk(32 * j + lrow, 8 * i + 2 * g + half) =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    }
+    __syncthreads();
+    if (band) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t mt = min(m0 + 64 * wm + 32 * j + lrow, M - 1);   // rows past the end are not stored
+        const uint16_t *cr = so.cos + mt * so.cs_stride, *sr = so.sin + mt * so.cs_stride;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = 8 * g + 4 * half;
+          if (!so.interleaved) {
+            // out[c] = x[c] cos[c] - x[c+32] sin[c], out[c+32] = x[c+32] cos[c+32] + x[c] sin[c+32]
+            const u32x2 ca = *reinterpret_cast<const u32x2 *>(cr + c0), sa = *reinterpret_cast<const u32x2 *>(sr + c0);
+            const u32x2 cb = *reinterpret_cast<const u32x2 *>(cr + c0 + 32),
+                        sb = *reinterpret_cast<const u32x2 *>(sr + c0 + 32);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lo = acc[0][j][4 * g + e], hi = acc[1][j][4 * g + e];
+              acc[0][j][4 * g + e] = rope_re(lo, hi, tab(ca, e), tab(sa, e));
+              acc[1][j][4 * g + e] = rope_im(lo, hi, tab(cb, e), tab(sb, e));
+            }
+          } else {
+            // pair p = c0 + e is (x[2p], x[2p+1]): its real part goes to column p, its imaginary part to p + 32
+            const u32x2 ca = *reinterpret_cast<const u32x2 *>(cr + c0), sa = *reinterpret_cast<const u32x2 *>(sr + c0);
+            const f32x4 in0 = *xchunk(32 * j + lrow, 4 * g + 2 * half), in1 = *xchunk(32 * j + lrow, 4 * g + 2 * half + 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float re = e < 2 ? in0[2 * e] : in1[2 * e - 4], im = e < 2 ? in0[2 * e + 1] : in1[2 * e - 3];
+              acc[0][j][4 * g + e] = rope_re(re, im, tab(ca, e), tab(sa, e));
+              acc[1][j][4 * g + e] = rope_im(re, im, tab(ca, e), tab(sa, e));
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
   uint16_t *Cs = wm < 2 ? a0 : a1;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -236,38 +303,8 @@ __global__ __launch_bounds__(512, 1) void up_proj_bf16_kernel(
       if (m >= M || n >= ncols) continue;
       const uint16_t *rowp = (row < GM / 2 ? a0 : a1) + (row & (GM / 2 - 1)) * GN;
       auto chunk_at = [&](int col) { return *reinterpret_cast<const u32x4 *>(rowp + 8 * ((col >> 3) ^ (row & 15))); };
-      u32x4 v = chunk_at(8 * nc);
+      const u32x4 v = chunk_at(8 * nc);
       const int hh = n / so.P, f = n - hh * so.P;
-      if (f >= so.rope_off && f < so.rope_off + so.R) {
-        // the band lies inside this tile (checked on the host)
-        const int b0 = f - so.rope_off, half = so.R / 2, band = 8 * nc - b0;
-        const bool upper = b0 >= half;
-        float o[8];
-        if (!so.interleaved) {
-          const u32x4 pv = chunk_at(band + (upper ? b0 - half : b0 + half));
-          const u32x4 cv = *reinterpret_cast<const u32x4 *>(so.cos + m * so.cs_stride + b0);
-          const u32x4 sv = *reinterpret_cast<const u32x4 *>(so.sin + m * so.cs_stride + b0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x0 = bf16_elem(v, e), xp = bf16_elem(pv, e), cs = bf16_elem(cv, e), sn = bf16_elem(sv, e);
-            o[e] = upper ? rope_im(xp, x0, cs, sn) : rope_re(x0, xp, cs, sn);
-          }
-        } else {
-          const int p0 = upper ? b0 - half : b0;   // first pair of this output chunk
-          const u32x4 in0 = chunk_at(band + 2 * p0), in1 = chunk_at(band + 2 * p0 + 8);
-          const u32x4 cv = *reinterpret_cast<const u32x4 *>(so.cos + m * so.cs_stride + p0);
-          const u32x4 sv = *reinterpret_cast<const u32x4 *>(so.sin + m * so.cs_stride + p0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const u32x4 &iv = e < 4 ? in0 : in1;
-            const float re = bf16_elem(iv, 2 * (e & 3)), im = bf16_elem(iv, 2 * (e & 3) + 1);
-            const float cs = bf16_elem(cv, e), sn = bf16_elem(sv, e);
-            o[e] = upper ? rope_im(re, im, cs, sn) : rope_re(re, im, cs, sn);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-      }
       const int ro = so.off[hh], qr = so.qr[hh];
       uint16_t *dst = so.send + (so.tokens * ro + static_cast<int64_t>(m) * qr + (hh - ro)) * so.F + so.col_off + f;
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));

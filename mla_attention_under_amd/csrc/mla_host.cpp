@@ -224,14 +224,12 @@ int mla_project_pack(const void *latent, const void *w, void *send, int64_t toke
   const int rc = shard_offsets(sizes, sp, heads, offs, who);
   if (rc != MLA_OK) return rc;
   if (dtype != MLA_BF16) return fail(MLA_EUNSUPPORTED, "%s: bf16 only", who);
-  if (L % 8 || P % 8 || F % 8 || col_offset % 8 || (R > 0 && (rope_offset % 8 || R % 16)))
-    return fail(MLA_EUNSUPPORTED, "%s: L, P, F, col_offset, rope_offset must be multiples of 8 and R of 16", who);
-  if (R > 0)
-    for (int h = 0; h < heads; ++h) {
-      const int64_t b = static_cast<int64_t>(h) * P + rope_offset;
-      if (b / 128 != (b + R - 1) / 128)
-        return fail(MLA_EUNSUPPORTED, "%s: head %d's RoPE band crosses a 128-column tile", who, h);
-    }
+  if (L % 8 || P % 8 || F % 8 || col_offset % 8)
+    return fail(MLA_EUNSUPPORTED, "%s: L, P, F and col_offset must be multiples of 8", who);
+  // the band is rotated on the accumulators of the one wave that holds its 64 columns
+  if (R > 0 && (R != 64 || rope_offset % 64 || P % 64))
+    return fail(MLA_EUNSUPPORTED, "%s: the RoPE band must be 64 wide at a multiple of 64 in a block whose width "
+                "is a multiple of 64 (got R %d at %d of %d)", who, R, rope_offset, P);
   if (tokens == 0) return ok();
   if (latent == nullptr || w == nullptr || send == nullptr || (R > 0 && (cos == nullptr || sin == nullptr)))
     return fail(MLA_EINVAL, "%s: NULL buffer", who);
@@ -442,6 +440,11 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
                        a->o_stride_t | a->o_stride_h;
     if (al % 16 || st % 8)
       return fail(MLA_EUNSUPPORTED, "%s: bf16 tiles need 16-byte aligned buffers and strides multiple of 8", who);
+    // a tile's rows are addressed by 32-bit byte offsets from its first row
+    constexpr int64_t kMaxRowStride = int64_t(1) << 24;
+    if (a->q_stride_t > kMaxRowStride || a->kv_stride_t > kMaxRowStride || a->kr_stride_t > kMaxRowStride)
+      return fail(MLA_EUNSUPPORTED, "%s: token strides above 2^24 elements are not supported by the bf16 tiles",
+                  who);
     const size_t need = mla::attn_workspace_bytes(a->T, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0,
                                                   a->N, a->R, a->V, 1);
     if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need ||

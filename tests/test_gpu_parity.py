@@ -143,12 +143,14 @@ PROJ_CASES = [
     ("kv_part_rank_shard", 256, 512, 128, 0, 128, 256, 448, 192, [16] * 8, -1, 0),
     ("q_part_uneven_ragged", 300, 1536, 128, 0, 128, 192, 448, 0, [22, 22, 21, 21, 21, 21], 128, 64),
     ("q_part_head_range", 37, 512, 32, 8, 12, 192, 448, 0, [5, 4, 3], 128, 64),
+    ("band_second_group", 70, 256, 4, 0, 4, 128, 200, 72, [2, 2], 64, 64),
+    ("band_every_group", 45, 256, 6, 1, 4, 64, 64, 0, [3, 1], 0, 64),
 ]
 
 
 @pytest.mark.parametrize("interleaved", [False, True])
 @pytest.mark.parametrize("name,T,L,w_heads,hb,heads,P,F,col,sizes,ro,R", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
-def test_project_pack_equals_separate_calls(name, T, L, w_heads, hb, heads, P, F, col, sizes, ro, R, interleaved):
+def test_project_pack_matches_oracle_and_separate_calls(name, T, L, w_heads, hb, heads, P, F, col, sizes, ro, R, interleaved):
     if R == 0 and interleaved:
         pytest.skip("no band")
     lat = dev(mi.draw((T, L), 41, 0))
@@ -173,7 +175,21 @@ def test_project_pack_equals_separate_calls(name, T, L, w_heads, hb, heads, P, F
     mla.mla_project_pack(lat, W, send, w_heads, hb, heads, P, F, col, sizes, rope_offset=ro, cos=cos, sin=sin,
                          interleaved=interleaved)
     _sync()
-    assert np.array_equal(bits(send), bits(ref)), name
+    # against the oracle: the fp64 projection, the band rotated, packed into the head slabs
+    part64 = oracle.latent_up_proj(bits(lat), bits(W), hb, heads, P // 2, P - P // 2)
+    if R:
+        part64[..., ro:ro + R] = oracle.rope(part64[..., ro:ro + R], c, s, interleaved)
+    x64 = oracle.widen(bits(fill))
+    x64[..., col:col + P] = part64
+    check_close(oracle.widen(bits(send)), oracle.pack_heads(x64, sizes), name=f"{name} vs oracle")
+    # outside the band, bit for bit the separate calls (the projection rounds once in both); the band is
+    # rotated in fp32 before its one rounding, the separate calls round the projection first
+    got_rows = oracle.unpack_heads(bits(send), sizes, T, F)
+    ref_rows = oracle.unpack_heads(bits(ref), sizes, T, F)
+    keep = np.ones(F, bool)
+    if R:
+        keep[col + ro:col + ro + R] = False
+    assert np.array_equal(got_rows[..., keep], ref_rows[..., keep]), name
 
 
 def test_pack_zero_tokens_is_a_no_op():
@@ -306,7 +322,10 @@ def test_attention_uneven22_sampled_rows():
     out = torch.empty((w.T, w.H, w.V), dtype=torch.bfloat16, device="cuda")
     mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, 1 / math.sqrt(w.K))
     _sync()
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4095], np.random.default_rng(3).integers(0, 4096, 40)]))
+    # the first and last row of every 128-row query tile (each dense causal tile pair, split tile
+    # included), plus random rows
+    tiles = np.arange(0, w.T, 128)
+    rows = np.unique(np.concatenate([tiles, tiles + 127, [1, 2047], np.random.default_rng(3).integers(0, 4096, 40)]))
     kv_ref = oracle.latent_up_proj(d["latent"], d["w_kvb"], 0, w.H, w.N, w.V)
     ref, _ = oracle.attention(d["q"], kv_ref, d["k_rope"], w.N, 1 / math.sqrt(w.K), rows=rows)
     check_close(host64(out)[rows], ref[rows], name="uneven22 sampled")
@@ -334,8 +353,10 @@ def test_attention_varlen16k_sampled_rows():
     d = _attn_inputs(w, w.T)
     got, _ = _run_attn(w, d, w.T, cu=cu)
     rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([np.array(cu[:-1]), np.array(cu[1:]) - 1, [8192 + 127, 8192 + 128],
-                                     rng.integers(0, w.T, 48)]))
+    # the first and last row of every 128-row query tile of every document (each schedule
+    # entry), the document ends, plus random rows
+    tile_rows = [r for a, b in zip(cu, cu[1:]) for t0 in range(a, b, 128) for r in (t0, min(t0 + 127, b - 1))]
+    rows = np.unique(np.concatenate([np.array(tile_rows), np.array(cu[1:]) - 1, rng.integers(0, w.T, 48)]))
     ref, _ = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K), cu_seqlens=cu, rows=rows)
     check_close(got[rows], ref[rows], name="varlen16k sampled")
     # a document's first token returns its own value row
@@ -478,8 +499,9 @@ def test_dense_causal_arbitrary_workspace():
 
 
 def test_dense_causal_graph_replays():
-    """A captured dense causal call (the split-tile flags keep one tag for every
-    replay) gives the eager result on every replay, with eager work between."""
+    """A captured dense causal call gives the eager result on every replay, with
+    eager attention calls (fresh tags, the same workspace on another stream)
+    between the replays."""
     base = mi.WORKLOADS["dsv3_rank"]
     T, H = 2048, 16
     w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
@@ -523,3 +545,35 @@ def test_attention_dominant_keys():
     assert np.isfinite(got).all() and np.isfinite(lse).all()
     check_close(got, ref, name="dominant keys")
     check_close(lse, rlse, name="dominant keys lse")
+
+
+def test_dense_causal_graph_replays_back_to_back_with_new_inputs():
+    """One captured dense causal call (T=2048, H=16) replayed three times in a row.
+    The split-tile flags keep the capture's tag on every replay; new seeded q, kv
+    and k_rope are copied into the captured buffers before each replay, with no
+    other attention call in between, and every replay is checked against the
+    oracle element by element (a stale partial softmax record from the previous
+    replay would be merged into a split tile)."""
+    base = mi.WORKLOADS["dsv3_rank"]
+    T, H = 2048, 16
+    w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    scale = 1 / math.sqrt(w.K)
+    d0 = _attn_inputs(w, T, seed_cfg=100)
+    q, kv, kr = dev(d0["q"]), dev(d0["kv"]), dev(d0["k_rope"])
+    out = torch.full((T, H, w.V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mla.mla_attention_fwd(q, kv, kr, out, w.N, w.R, w.V, scale)
+    _sync()
+    for i in range(3):
+        d = _attn_inputs(w, T, seed_cfg=101 + i)
+        q.copy_(dev(d["q"]))
+        kv.copy_(dev(d["kv"]))
+        kr.copy_(dev(d["k_rope"]))
+        out.fill_(float("nan"))
+        g.replay()
+        _sync()
+        ref, _ = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, scale)
+        check_close(host64(out), ref, name=f"back-to-back replay {i}")

@@ -381,6 +381,8 @@ def test_project_pack_validation_before_launch(lib):
     assert call(sz=(ctypes.c_int * 2)(3, 2)) == mla.MLA_EINVAL   # sizes do not sum to heads
     assert call(dt=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
     assert call(L=500) == mla.MLA_EUNSUPPORTED          # not a multiple of 8
-    assert call(P=184, ro=120) == mla.MLA_EUNSUPPORTED  # a band crosses a 128-column tile
+    assert call(P=184, ro=120) == mla.MLA_EUNSUPPORTED  # block width not a multiple of 64
+    assert call(ro=96, R=64, P=192) == mla.MLA_EUNSUPPORTED   # band not at a multiple of 64
+    assert call(R=32, ro=128) == mla.MLA_EUNSUPPORTED   # band width other than 64
     assert call(send=A) == mla.MLA_EINVAL               # send overlaps the latent
     assert call(T=0) == mla.MLA_OK

@@ -83,6 +83,62 @@ def test_strict_causal_mask_is_caught(monkeypatch):
     assert _any_attention_pin_fails()
 
 
+def _probs_with(score):
+    """attention_probs rebuilt around a planted score function (scale and mask as before)."""
+    def bad(q, kv, k_rope, N, scale, causal=True, cu_seqlens=None, h=0):
+        q, kv, k_rope = om.widen(q), om.widen(kv), om.widen(k_rope)
+        T = q.shape[0]
+        Pm = np.zeros((T, T))
+        for a, b in om.doc_bounds(cu_seqlens, T):
+            if b == a:
+                continue
+            s = score(q[a:b, h], kv[a:b, h, :N], k_rope[a:b], N, scale)
+            if causal:
+                s = np.where(np.tril(np.ones((b - a, b - a), bool)), s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            Pm[a:b, a:b] = e / e.sum(axis=1, keepdims=True)
+        return Pm
+    return bad
+
+
+def _probs_pins_fail():
+    pins = [lambda c=c: tn.test_attention_probs_match_torch_softmax_of_expanded_scores(*c) for c in tn.PROBS_CASES]
+    pins += [lambda c=c: tn.test_attention_probs_times_values_is_the_attention_output(*c) for c in tn.PROBS_CASES]
+    return any(_fails(p) for p in pins)
+
+
+def test_probs_without_the_scale_are_caught(monkeypatch):
+    _patch(monkeypatch, "attention_probs",
+           _probs_with(lambda qh, kn, kr, N, scale: qh[:, :N] @ kn.T + qh[:, N:] @ kr.T))
+    assert _probs_pins_fail()
+
+
+def test_probs_without_the_rope_term_are_caught(monkeypatch):
+    _patch(monkeypatch, "attention_probs", _probs_with(lambda qh, kn, kr, N, scale: scale * (qh[:, :N] @ kn.T)))
+    assert _probs_pins_fail()
+
+
+def test_probs_as_planted_here_are_otherwise_right(monkeypatch):
+    # the rebuilt function with the right score passes every pin, so the two above fail for their mistake
+    _patch(monkeypatch, "attention_probs",
+           _probs_with(lambda qh, kn, kr, N, scale: scale * (qh[:, :N] @ kn.T + qh[:, N:] @ kr.T)))
+    assert not _probs_pins_fail()
+
+
+def test_widen_as_fp16_is_caught(monkeypatch):
+    real = om.widen
+    _patch(monkeypatch, "widen", lambda x: np.asarray(x).view(np.float16).astype(np.float64)
+           if np.asarray(x).dtype == np.uint16 else real(x))
+    assert _fails(tn.test_widen_matches_torch_bfloat16_for_every_bit_pattern)
+
+
+def test_widen_shifted_by_15_is_caught(monkeypatch):
+    real = om.widen
+    _patch(monkeypatch, "widen", lambda x: (np.asarray(x).astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+           if np.asarray(x).dtype == np.uint16 else real(x))
+    assert _fails(tn.test_widen_matches_torch_bfloat16_for_every_bit_pattern)
+
+
 def test_value_and_key_swapped_in_projection_is_caught(monkeypatch):
     orig = om.latent_up_proj
 

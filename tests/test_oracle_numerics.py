@@ -26,6 +26,28 @@ def _tiny(T=9, H=3, N=4, R=2, V=3, seed=0):
     return q, kv, kr
 
 
+# ----------------------------------------------------------------------------- bf16 widening
+
+def test_widen_matches_torch_bfloat16_for_every_bit_pattern():
+    """All 65 536 bf16 encodings: the oracle's bit widening against torch's own
+    bfloat16 -> float64 conversion (NaN patterns must stay NaN, signed zeros keep
+    their sign). Reading the bits as fp16, or shifting by 15, fails here."""
+    pat = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(pat)
+    ref = torch.from_numpy(pat.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127                    # exponent all ones, non-zero mantissa, both signs
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # a few values fixed by the format itself: 1.0 = 0x3f80, -2.0 = 0xc000, the largest finite 0x7f7f
+    assert oracle.widen(np.array([0x3F80, 0xC000, 0x7F7F, 0x0001], np.uint16)).tolist() == [
+        1.0, -2.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    # fp32 input widens exactly
+    x = np.random.default_rng(1).standard_normal(64).astype(np.float32)
+    assert np.array_equal(oracle.widen(x), x.astype(np.float64))
+
+
 # ----------------------------------------------------------------------------- up-projection
 
 def _proj_brute(c, W, hb, heads, N, V):
@@ -147,6 +169,47 @@ def test_probability_rows_sum_to_one_and_respect_the_mask():
         doc = np.repeat([0, 1], [5, 7])
         allowed = (doc[:, None] == doc[None, :]) & (np.arange(12)[None, :] <= np.arange(12)[:, None])
         assert np.all(Pm[~allowed] == 0) and np.all(Pm[allowed] > 0)
+
+
+def _probs_torch(q, kv, kr, N, scale, allowed, h):
+    """torch float64: the key band expanded per head, scaled scores, masked softmax."""
+    T, H, _ = q.shape
+    k = np.concatenate([kv[:, h, :N], kr], axis=1)                    # [T][N+R], this head's expanded key
+    s = scale * (torch.from_numpy(np.ascontiguousarray(q[:, h])) @ torch.from_numpy(k).T)
+    s = s.masked_fill(~torch.from_numpy(allowed), float("-inf"))
+    p = torch.softmax(s, dim=1)
+    return torch.nan_to_num(p, nan=0.0).numpy()                       # rows of empty documents do not exist
+
+
+PROBS_CASES = [(True, None), (False, None), (True, [0, 5, 6, 6, 12, 15]), (False, [0, 9, 15])]
+
+
+@pytest.mark.parametrize("causal,cu", PROBS_CASES)
+def test_attention_probs_match_torch_softmax_of_expanded_scores(causal, cu):
+    """The probability matrix itself, against torch.softmax of scale * q . [k_nope | k_rope]
+    with the causal / document mask. A dropped scale or rope term fails here."""
+    q, kv, kr = _tiny(T=15, H=3, N=4, R=2, V=3, seed=80)
+    q[:, :, 4:] *= 3.0                                 # a strong band, so the rope term is visible
+    scale = 0.45
+    bounds = [(0, 15)] if cu is None else list(zip(cu, cu[1:]))
+    doc = np.zeros(15, int)
+    for i, (a, b) in enumerate(bounds):
+        doc[a:b] = i
+    allowed = doc[:, None] == doc[None, :]
+    if causal:
+        allowed &= np.arange(15)[None, :] <= np.arange(15)[:, None]
+    for h in range(3):
+        Pm = oracle.attention_probs(q, kv, kr, 4, scale, causal=causal, cu_seqlens=cu, h=h)
+        np.testing.assert_allclose(Pm, _probs_torch(q, kv, kr, 4, scale, allowed, h), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal,cu", PROBS_CASES)
+def test_attention_probs_times_values_is_the_attention_output(causal, cu):
+    q, kv, kr = _tiny(T=15, H=3, N=4, R=2, V=3, seed=81)
+    out, _ = oracle.attention(q, kv, kr, 4, 0.6, causal=causal, cu_seqlens=cu)
+    for h in range(3):
+        Pm = oracle.attention_probs(q, kv, kr, 4, 0.6, causal=causal, cu_seqlens=cu, h=h)
+        np.testing.assert_allclose(Pm @ kv[:, h, 4:], out[:, h], rtol=1e-12, atol=1e-13)
 
 
 def test_first_token_of_each_document_returns_its_value_row():
