@@ -265,6 +265,25 @@ size_t mla_attention_workspace_size(const mla_attn_args *a);
 int mla_attention_fwd(const mla_attn_args *a, void *stream);
 
 /*
+ * mla_attention_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, result and validation as mla_attention_fwd,
+ * except that a->workspace and a->workspace_bytes are ignored: the call's
+ * scratch is a fixed array of MLA_NOALLOC_SCRATCH_BYTES inside the library,
+ * one copy per GPU, held until the process ends (its device address is
+ * looked up on the first call on each device). The call allocates nothing.
+ * A call whose mla_attention_workspace_size() exceeds MLA_NOALLOC_SCRATCH_BYTES
+ * fails with MLA_EUNSUPPORTED and launches nothing (48 MiB covers, e.g., dense
+ * causal attention of 16 heads up to T = 8192 or 22 heads at T = 4096, and any
+ * packed-document call up to millions of tokens). Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, or
+ * graphs replayed concurrently) race and give wrong results. Nothing in the
+ * scratch needs clearing between calls.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+int mla_attention_fwd_noalloc(const mla_attn_args *a, void *stream);
+
+/*
  * Backward of mla_attention_fwd (torchtitan "MLA CP optimization", section
  * "Numerical comparison": the method is trained end to end; hyper-parallel
  * `_assemble_key_value`: the shared band is one tensor repeated over the

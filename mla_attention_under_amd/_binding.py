@@ -25,6 +25,7 @@ EXPORTS = (
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
     "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope", "mla_project_pack",
     "mla_attention_bwd_workspace_size", "mla_attention_bwd", "mla_latent_up_proj_bwd",
+    "mla_attention_fwd_noalloc",
 )
 
 
@@ -102,6 +103,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_attention_workspace_size.argtypes = [ctypes.POINTER(mla_attn_args)]
     lib.mla_attention_workspace_size.restype = sz
     lib.mla_attention_fwd.argtypes = [ctypes.POINTER(mla_attn_args), vp]
+    lib.mla_attention_fwd_noalloc.argtypes = [ctypes.POINTER(mla_attn_args), vp]
     lib.mla_attention_bwd_workspace_size.argtypes = [ctypes.POINTER(mla_attn_bwd_args)]
     lib.mla_attention_bwd_workspace_size.restype = sz
     lib.mla_attention_bwd.argtypes = [ctypes.POINTER(mla_attn_bwd_args), vp]
@@ -345,6 +347,21 @@ def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None,
                                q.device, stream)
     a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace)
     _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def mla_attention_fwd_noalloc(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None, cu_seqlens=None,
+                              stream=None):
+    """mla_attention_fwd with the library's fixed per-GPU scratch instead of a workspace: nothing is
+    allocated (for graph capture and serving loops). Calls overlapping on one GPU race on that scratch."""
+    lib = load_library()
+    _dev(q, kv, k_rope, out, lse, cu_seqlens)
+    for t in (q, kv, k_rope, out):
+        assert t.stride(-1) == 1
+    if cu_seqlens is not None:
+        assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, None)
+    _check("mla_attention_fwd_noalloc", lib.mla_attention_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 

@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "mla_common.cuh"
@@ -1018,7 +1019,48 @@ size_t pair_ws_bytes(int64_t T, int H) {
   return pair_records_bytes(T, H) + static_cast<size_t>(H) * static_cast<size_t>(n / 2) * sizeof(unsigned long long);
 }
 
+// Fixed device scratch for mla_attention_fwd_noalloc: the workspace of a call
+// that may not allocate (split-tile records and flags, or the document
+// schedule). Each GPU the library runs on holds its own copy for the life of
+// the process. In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device below and
+// only that address reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+int attn_scratch(void *stream, void **ptr) {
+  *ptr = nullptr;
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {   // the stream's device (the null stream is the current device's)
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // with that device current: every device holds its own copy at its own address
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool attn_fast_path(int N, int R, int V, int bf16) { return bf16 && N == 128 && R == 64 && V == 128; }
 

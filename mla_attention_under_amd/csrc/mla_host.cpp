@@ -462,8 +462,7 @@ size_t mla_attention_workspace_size(const mla_attn_args *a) {
                                    a->dtype == MLA_BF16);
 }
 
-int mla_attention_fwd(const mla_attn_args *a, void *stream) {
-  const char *who = "mla_attention_fwd";
+static int attention_fwd(const mla_attn_args *a, void *stream, const char *who) {
   const int rc = attn_validate(a, who);
   if (rc != MLA_OK) return rc;
   if (a->T == 0) return ok();
@@ -493,6 +492,29 @@ int mla_attention_fwd(const mla_attn_args *a, void *stream) {
   p.ws = a->workspace;
   p.ws_bytes = a->workspace_bytes;
   return launched(mla::launch_attention(p, stream), who);
+}
+
+int mla_attention_fwd(const mla_attn_args *a, void *stream) { return attention_fwd(a, stream, "mla_attention_fwd"); }
+
+int mla_attention_fwd_noalloc(const mla_attn_args *a, void *stream) {
+  const char *who = "mla_attention_fwd_noalloc";
+  static_assert(MLA_NOALLOC_SCRATCH_BYTES == mla::kAttnScratchBytes, "header and library agree on the scratch size");
+  if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
+  mla_attn_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  const size_t need = mla_attention_workspace_size(a);
+  if (need > mla::kAttnScratchBytes)
+    return fail(MLA_EUNSUPPORTED, "%s: this call needs %zu bytes of scratch, more than the %zu bytes the library "
+                "holds per GPU (use mla_attention_fwd with a workspace)", who, need, mla::kAttnScratchBytes);
+  if (need > 0) {
+    void *p = nullptr;
+    const int e = mla::attn_scratch(stream, &p);
+    if (e != 0) return fail(MLA_ELAUNCH, "%s: device scratch unavailable (%s)", who, mla::hip_error_name(e));
+    b.workspace = p;
+    b.workspace_bytes = mla::kAttnScratchBytes;
+  }
+  return attention_fwd(&b, stream, who);
 }
 
 static int attn_bwd_validate(const mla_attn_bwd_args *a, const char *who) {

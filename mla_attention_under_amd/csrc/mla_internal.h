@@ -99,6 +99,11 @@ struct AttnPlan {
 bool attn_fast_path(int N, int R, int V, int bf16);
 size_t attn_workspace_bytes(int64_t T, int H, int n_seq, int has_cu, int causal, int N, int R, int V, int bf16);
 int launch_attention(const AttnPlan &p, void *stream);
+// Fixed device scratch for calls that may not allocate (one copy per GPU):
+// its size, and its device address on the stream's device (looked up once per
+// device). Returns 0 or a hipError_t value.
+constexpr size_t kAttnScratchBytes = size_t(48) << 20;
+int attn_scratch(void *stream, void **ptr);
 
 // ---- attention backward --------------------------------------------------
 struct AttnBwdPlan {

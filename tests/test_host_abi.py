@@ -186,6 +186,12 @@ def test_attention_validation_before_launch(lib):
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn())) > 0          # dense causal
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn(causal=0))) == 0  # non-causal needs none
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn(N=16, R=8, V=16))) == 0   # generic kernel
+    # the no-alloc variant: beyond its fixed scratch (128 heads at T=4096, dense causal) it launches nothing
+    g = lambda **kw: lib.mla_attention_fwd_noalloc(ctypes.byref(_attn(**kw)), None)  # noqa: E731
+    assert g(T=4096, H=128, q_stride_t=128 * 192, kv_stride_t=128 * 256, o_stride_t=128 * 128) == mla.MLA_EUNSUPPORTED
+    assert b"scratch" in lib.mla_last_error()
+    assert g(R=63) == mla.MLA_EINVAL                       # validated like mla_attention_fwd
+    assert lib.mla_attention_fwd_noalloc(None, None) == mla.MLA_EINVAL
 
 
 def _attn_bwd(**kw):
