@@ -36,7 +36,7 @@
 #include <mutex>
 #include <type_traits>
 
-#include "mla_common.cuh"
+#include "mla_common.h"
 #include "mla_internal.h"
 
 namespace mla {

@@ -34,7 +34,7 @@
 
 #include <cstdint>
 
-#include "mla_common.cuh"
+#include "mla_common.h"
 #include "mla_internal.h"
 
 namespace mla {

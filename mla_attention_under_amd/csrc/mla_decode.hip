@@ -27,7 +27,7 @@
 
 #include <algorithm>
 
-#include "mla_common.cuh"
+#include "mla_common.h"
 #include "mla_internal.h"
 
 namespace mla {

@@ -271,46 +271,37 @@ int mla_project_pack(const void *latent, const void *w, void *send, int64_t toke
 }
 
 namespace {
-// documents as [start, end) from cumulative ends; checks them
-int doc_ranges(const int64_t *ends, int n, std::vector<std::pair<int64_t, int64_t>> &docs, const char *who) {
+// A half-open token interval.
+struct Span {
+  int64_t lo = 0, hi = 0;
+  int64_t size() const { return hi > lo ? hi - lo : 0; }
+};
+Span meet(Span a, Span b) { return Span{std::max(a.lo, b.lo), std::min(a.hi, b.hi)}; }
+
+// Packed documents given by their cumulative ends (documents tile [0, total)
+// back to back, empty ones allowed): checks the ends.
+int check_ends(const int64_t *ends, int n, const char *who) {
   if (ends == nullptr || n < 1) return fail(MLA_EINVAL, "%s: need at least one document end", who);
-  int64_t prev = 0;
-  docs.clear();
-  for (int i = 0; i < n; ++i) {
-    if (ends[i] < prev) return fail(MLA_EINVAL, "%s: document ends must be non-negative and non-decreasing", who);
-    docs.emplace_back(prev, ends[i]);
-    prev = ends[i];
-  }
+  for (int i = 0; i < n; ++i)
+    if (ends[i] < (i ? ends[i - 1] : 0))
+      return fail(MLA_EINVAL, "%s: document ends must be non-negative and non-decreasing", who);
   return MLA_OK;
 }
 
-struct Partition {
-  int64_t key_begin = 0, key_end = 0;
-  std::vector<int64_t> q_ends, k_ends;   // one sequence, cumulative
-};
-
-// the documents' causal prefixes seen by the queries [rank*len, (rank+1)*len)
-int partition_of(const std::vector<std::pair<int64_t, int64_t>> &docs, int64_t len, int64_t rank, Partition &out,
-                 const char *who) {
-  const int64_t q0 = rank * len, q1 = q0 + len;
-  int64_t nq = 0, nk = 0;
-  bool first = true;
-  out.q_ends.clear();
-  out.k_ends.clear();
-  for (const auto &d : docs) {
-    const int64_t s = std::max(d.first, q0), e = std::min(d.second, q1);
-    if (s >= e) continue;
-    if (first) out.key_begin = d.first;
-    first = false;
-    nq += e - s;
-    nk += e - d.first;
-    out.q_ends.push_back(nq);
-    out.k_ends.push_back(nk);
-  }
-  if (nq != len)
+// Keys needed by the queries of partition r, i.e. the token range
+// Q = [r*len, (r+1)*len): a query sees its own document up to itself, so the
+// documents meeting Q contribute the causal prefixes that end at their
+// clipped ends, and those prefixes tile one interval: from the start of the
+// document holding the first query to the end of Q. Fails when the documents
+// end before Q does.
+int key_span(const int64_t *ends, int n, int64_t len, int64_t r, Span &keys, const char *who) {
+  const Span q{r * len, (r + 1) * len};
+  if (ends[n - 1] < q.hi)
     return fail(MLA_EINVAL, "%s: the documents do not cover the queries [%lld, %lld)", who,
-                static_cast<long long>(q0), static_cast<long long>(q1));
-  out.key_end = q1;
+                static_cast<long long>(q.lo), static_cast<long long>(q.hi));
+  // first document whose end lies past the first query: it holds that query
+  const int64_t *first = std::upper_bound(ends, ends + n, q.lo);
+  keys = Span{first == ends ? 0 : first[-1], q.hi};
   return MLA_OK;
 }
 }  // namespace
@@ -324,23 +315,32 @@ int mla_causal_partition(const int64_t *doc_ends, int n_docs, int64_t query_leng
   if (query_rank > INT64_MAX / query_length - 1) return fail(MLA_EINVAL, "%s: query range overflows", who);
   if (key_begin == nullptr || key_end == nullptr || query_ends == nullptr || key_ends == nullptr || n_out == nullptr)
     return fail(MLA_EINVAL, "%s: NULL output", who);
-  std::vector<std::pair<int64_t, int64_t>> docs;
-  int rc = doc_ranges(doc_ends, n_docs, docs, who);
+  int rc = check_ends(doc_ends, n_docs, who);
   if (rc != MLA_OK) return rc;
-  Partition p;
-  rc = partition_of(docs, query_length, query_rank, p, who);
+  Span keys;
+  rc = key_span(doc_ends, n_docs, query_length, query_rank, keys, who);
   if (rc != MLA_OK) return rc;
-  const int64_t m = static_cast<int64_t>(p.q_ends.size());
+  const Span q{query_rank * query_length, (query_rank + 1) * query_length};
+  // Each document meeting Q ends its share at c = min(its end, Q's end); since
+  // the documents are contiguous, the cumulative query count up to it is c -
+  // Q.lo and the cumulative key count c - keys.lo.
+  std::vector<int64_t> cut;
+  for (int i = 0; i < n_docs; ++i) {
+    const Span d{i ? doc_ends[i - 1] : 0, doc_ends[i]};
+    if (meet(d, q).size() > 0) cut.push_back(std::min(d.hi, q.hi));
+  }
+  const int64_t m = static_cast<int64_t>(cut.size());
   if (m * batch > cap)
     return fail(MLA_EINVAL, "%s: %lld output entries needed, capacity %d", who, static_cast<long long>(m * batch),
                 cap);
-  for (int i = 0; i < batch; ++i)
+  const int64_t nq = q.size(), nk = keys.size();   // per-sequence totals, the batch strides
+  for (int b = 0; b < batch; ++b)
     for (int64_t j = 0; j < m; ++j) {
-      query_ends[i * m + j] = p.q_ends[j] + i * p.q_ends.back();
-      key_ends[i * m + j] = p.k_ends[j] + i * p.k_ends.back();
+      query_ends[b * m + j] = b * nq + (cut[j] - q.lo);
+      key_ends[b * m + j] = b * nk + (cut[j] - keys.lo);
     }
-  *key_begin = p.key_begin;
-  *key_end = p.key_end;
+  *key_begin = keys.lo;
+  *key_end = keys.hi;
   *n_out = static_cast<int>(m * batch);
   return ok();
 }
@@ -355,24 +355,24 @@ int mla_kv_exchange_ranges(const int64_t *doc_ends, int n_docs, int64_t source_l
   if (source_length > 0 && degree > INT64_MAX / source_length) return fail(MLA_EINVAL, "%s: ranges overflow", who);
   if (send_offset == nullptr || send_count == nullptr || recv_count == nullptr || local_only == nullptr)
     return fail(MLA_EINVAL, "%s: NULL output", who);
-  std::vector<std::pair<int64_t, int64_t>> docs;
-  int rc = doc_ranges(doc_ends, n_docs, docs, who);
+  int rc = check_ends(doc_ends, n_docs, who);
   if (rc != MLA_OK) return rc;
-  std::vector<Partition> dest(degree);
+  // every rank's source tokens and the keys its queries need
+  std::vector<Span> src(degree), need(degree);
   for (int p = 0; p < degree; ++p) {
-    rc = partition_of(docs, query_length, p / head_copies, dest[p], who);
+    src[p] = Span{p * source_length, (p + 1) * source_length};
+    rc = key_span(doc_ends, n_docs, query_length, p / head_copies, need[p], who);
     if (rc != MLA_OK) return rc;
   }
-  const int64_t s0 = rank * source_length, s1 = s0 + source_length;
+  // what moves from a to b is a's source inside b's need; nothing moves at all
+  // when every rank's need lies inside its own source
   bool local = true;
   for (int p = 0; p < degree; ++p) {
-    const int64_t b = std::max(s0, dest[p].key_begin), e = std::min(s1, dest[p].key_end);
-    send_offset[p] = b < e ? b - s0 : 0;
-    send_count[p] = b < e ? e - b : 0;
-    const int64_t rb = std::max(p * source_length, dest[rank].key_begin);
-    const int64_t re = std::min((p + 1) * source_length, dest[rank].key_end);
-    recv_count[p] = std::max<int64_t>(0, re - rb);
-    local = local && p * source_length <= dest[p].key_begin && dest[p].key_end <= (p + 1) * source_length;
+    const Span out = meet(src[rank], need[p]);
+    send_count[p] = out.size();
+    send_offset[p] = out.size() ? out.lo - src[rank].lo : 0;
+    recv_count[p] = meet(src[p], need[rank]).size();
+    local = local && meet(src[p], need[p]).size() == need[p].size();
   }
   *local_only = local ? 1 : 0;
   return ok();
