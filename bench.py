@@ -115,6 +115,57 @@ def _median_us(torch, fn, reps, before=None):
     return ts[len(ts) // 2]
 
 
+def _pct(xs):
+    """p10 / median / p90 / mean of a list of durations (us)."""
+    xs = sorted(xs)
+    n = len(xs)
+    q = lambda f: xs[min(n - 1, int(round(f * (n - 1))))]  # noqa: E731
+    return {"p10": round(q(0.1), 3), "median": round(q(0.5), 3), "p90": round(q(0.9), 3),
+            "mean": round(sum(xs) / n, 3)}
+
+
+def _mfma_peak(torch, mla):
+    """Dense bf16 MFMA rate and shader clock under an all-MFMA load (include/mla_peak.h): 256 workgroups of 8
+    waves, each wave four independent 32x32x16 MFMA chains from registers. Median of 5 event-timed launches."""
+    blocks, iters = 256, 4000
+    clocks = torch.empty(blocks * 16, dtype=torch.int64, device="cuda")
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        mla.mla_peak_mfma_bf16(blocks, iters, clocks, sink)
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mla.mla_peak_mfma_bf16(blocks, iters, clocks, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    sec = sorted(ts)[len(ts) // 2]
+    c = clocks.view(blocks * 8, 2).double().cpu()
+    ghz = float((c[:, 0] / (c[:, 1] / 100e6)).mean()) / 1e9
+    flops = 2.0 * 32 * 32 * 16 * 4 * iters * 8 * blocks
+    tf = flops / sec / 1e12
+    return {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3),
+            "spec_tflops_at_clock": round(PEAK_BF16_TFLOPS * ghz / 2.4, 1),
+            "note": "256 x 8 waves of four independent 32x32x16 bf16 MFMA chains, no memory traffic; clock from "
+                    "s_memtime / s_memrealtime; the data-sheet 2500 TFLOP/s assumes 2.4 GHz"}
+
+
+def _flushed(torch, fn, reps, sweep):
+    """Event-timed calls of fn, each after a read-only sweep of `sweep` (512 MB, twice the 256 MB Infinity Cache)
+    so the call starts with cold caches (a writing sweep would leave dirty lines to write back during the call)."""
+    ts = []
+    for _ in range(reps):
+        sweep.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return _pct(ts)
+
+
 def _expanded(torch, mla):
     """Expanded pack ([q | k_nope | k_rope | v] per head -> head slabs), back-to-back event timing.
     Bytes = q + kv + one k_rope row per token read, payload written."""
@@ -449,10 +500,40 @@ def main():
             ev[k][i][1].record()
     torch.cuda.synchronize()
     kern_us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in kernels}
+    kern_pct = {k: _pct([1e3 * a.elapsed_time(b) for a, b in ev[k]]) for k in kernels}
+
+    # ---- per-step pass: events around every whole step, back to back (for p10 / p90 of the step)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    _busy(torch)
+    for i in range(args.steps):
+        sev[i][0].record()
+        step()
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    step_pct = _pct([1e3 * a.elapsed_time(b) for a, b in sev])
+
+    # ---- cold caches: a 512 MB read-only sweep before every timed step / pack
+    sweep = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    reps_cold = max(10, min(args.steps, 50))
+    step_cold = _flushed(torch, step, reps_cold, sweep)
+    pack_cold = _flushed(torch, calls["pack"], reps_cold, sweep)
+    del sweep
+    mfma_peak = _mfma_peak(torch, mla)
 
     attn_tflops = flops_attn / (kern_us["attention"] * 1e-6) / 1e12
     extra = {
         "kernel_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "kernel_us_pct": kern_pct,
+        "step_us_pct": step_pct,
+        "cold_cache": {
+            "step_us": step_cold,
+            "step_tflops_median": round(flops_step / (step_cold["median"] * 1e-6) / 1e12, 2),
+            "pack_us": pack_cold,
+            "pack_gbps_median": round(bytes_pack / (pack_cold["median"] * 1e-6) / 1e9, 1),
+            "note": "each timed step / pack after a 512 MB read-only sweep (twice the Infinity Cache); value and "
+                    "the other figures are back to back with inputs resident"},
+        "mfma_peak_measured": mfma_peak,
         "up_proj_tflops": round(flops_up / (kern_us["up_proj"] * 1e-6) / 1e12, 2),
         "attention_tflops": round(attn_tflops, 2),
         "compute_only_tflops": round(flops_step / ((kern_us["up_proj"] + kern_us["attention"]) * 1e-6) / 1e12, 2),
@@ -501,6 +582,8 @@ def main():
     traffic = _traffic("attention", "dsv3_rank")
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "measured_peak": extra["mfma_peak_measured"]["tflops"],
+            "frac_of_measured_peak": round(attn_tflops / extra["mfma_peak_measured"]["tflops"], 4),
             "kernel": "mla_attention_fwd (attn_fwd_kernel<128,64,128>)",
             "algorithmic": f"{flops_attn / 1e9:.3f} GFLOP per launch = 2*H*T(T+1)/2*(N+R+V)"}
     line = {

@@ -27,6 +27,8 @@ EXPORTS = (
     "mla_attention_bwd_workspace_size", "mla_attention_bwd", "mla_latent_up_proj_bwd",
     "mla_attention_fwd_noalloc",
 )
+# the measurement probe declared in include/mla_peak.h
+PEAK_EXPORTS = ("mla_peak_mfma_bf16",)
 
 
 class MlaError(RuntimeError):
@@ -111,7 +113,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_latent_decode_workspace_size.argtypes = [ctypes.POINTER(mla_decode_args)]
     lib.mla_latent_decode_workspace_size.restype = sz
     lib.mla_latent_decode_fwd.argtypes = [ctypes.POINTER(mla_decode_args), vp]
-    for name in EXPORTS:
+    lib.mla_peak_mfma_bf16.argtypes = [i32, i32, vp, vp, vp]
+    for name in EXPORTS + PEAK_EXPORTS:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
     _lib = lib
     return lib
@@ -478,3 +481,13 @@ def mla_latent_decode_fwd(q, latent_cache, rope_cache, w_kvb, out, heads_total, 
                      lse, workspace)
     _check("mla_latent_decode_fwd", lib.mla_latent_decode_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def mla_peak_mfma_bf16(blocks, iters, clocks, sink, stream=None):
+    """Launch the MFMA peak probe (include/mla_peak.h): clocks int64 [blocks*16], sink float32 [blocks*512]."""
+    lib = load_library()
+    _dev(clocks, sink)
+    assert clocks.numel() >= blocks * 16 and sink.numel() >= blocks * 512
+    rc = lib.mla_peak_mfma_bf16(blocks, iters, _ptr(clocks), _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise MlaError("mla_peak_mfma_bf16", rc, "bad argument" if rc == -1 else "launch failed")

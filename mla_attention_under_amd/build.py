@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_host.cpp", "mla_pack.hip", "mla_gemm.hip", "mla_attn.hip", "mla_decode.hip", "mla_rope.hip", "mla_attn_bwd.hip"]
+SOURCES = ["mla_host.cpp", "mla_pack.hip", "mla_gemm.hip", "mla_attn.hip", "mla_decode.hip", "mla_rope.hip", "mla_attn_bwd.hip",
+           "mla_peak.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.

@@ -38,6 +38,16 @@ def test_header_declares_the_four_path_calls():
     assert set(fns) == set(mla.EXPORTS)
 
 
+def test_peak_probe_header_matches_the_exports(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mla_peak.h")).read(), flags=re.S)
+    fns = sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mla_\w+)\s*\(", text, flags=re.M)))
+    assert fns == sorted(mla.PEAK_EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
+    for f in fns:
+        assert re.search(rf"\bT {f}$", out, flags=re.M), f
+    assert lib.mla_peak_mfma_bf16(0, 10, None, None, None) == -1      # bad argument: nothing launched
+
+
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (mla_\w+)$", out, flags=re.M))
