@@ -65,7 +65,7 @@ __all__ = [
     "pack_heads", "unpack_heads", "latent_up_proj", "attention_probs",
     "attention", "decode_split_kv", "decode_reference", "doc_bounds",
     "ulysses_materialise_k_first", "ulysses_latent_first",
-    "pack_expanded", "causal_partition", "kv_exchange_ranges", "rope",
+    "pack_expanded", "causal_partition", "kv_exchange_ranges", "rope", "key_bounds",
     "attention_backward", "latent_up_proj_backward",
 ]
 
@@ -192,6 +192,14 @@ def doc_bounds(cu_seqlens=None, T: int | None = None, ends=None) -> list[tuple[i
     return [(a, b) for a, b in zip(cu, cu[1:])]
 
 
+def key_bounds(cu_seqlens_k=None, T_k: int | None = None, n_docs: int = 1) -> list[tuple[int, int]]:
+    """Key document [start, end) ranges: from cu_seqlens_k (leading 0), else one range of T_k keys."""
+    if cu_seqlens_k is None:
+        assert n_docs == 1, "documents of queries need the keys' document offsets"
+        return [(0, int(T_k))]
+    return doc_bounds(cu_seqlens_k)
+
+
 def _scores(q, kv, k_rope, h, rows, cols, N, scale):
     """s[t][j] = scale * (q_nope[t]·k_nope[j] + q_rope[t]·k_rope[j]) for head h."""
     qn, qr = q[rows, h, :N], q[rows, h, N:]
@@ -218,39 +226,61 @@ def attention_probs(q, kv, k_rope, N, scale, causal=True, cu_seqlens=None, h=0):
 
 
 def attention(q, kv, k_rope, N: int, scale: float, causal: bool = True, cu_seqlens=None,
-              rows=None):
+              rows=None, cu_seqlens_k=None):
     """Causal (or full) softmax attention of one rank's heads.
 
-    q [T][H][N+R] (= [q_nope | q_rope]), kv [T][H][N+V] (= [k_nope | v]),
-    k_rope [T][R] shared by every head. Query t of a document attends to keys j
-    of the same document with j <= t when causal. Returns out [T][H][V] and
-    lse [H][T] (natural log of the softmax denominator, including the max).
-    ``rows`` optionally restricts the computation to those query rows (the rest
-    of ``out``/``lse`` is NaN) so large workloads can be sampled.
+    q [T_q][H][N+R] (= [q_nope | q_rope]), kv [T_k][H][N+V] (= [k_nope | v]),
+    k_rope [T_k][R] shared by every head. Query documents come from cu_seqlens
+    (over the T_q query rows) and key documents from cu_seqlens_k (over the
+    T_k key rows; None: the same offsets as the queries, which needs T_k =
+    T_q). A query attends to the keys of its own document; when causal, the
+    i-th query of a document (0-based) sees the document's keys j <= i +
+    (keys - queries of that document): the last query lines up with the last
+    key, so with equal lengths this is j <= i (no look-ahead), and a chunk of
+    queries at the end of a longer key sequence sees the whole prefix before
+    it. A query that sees no key (more queries than keys) has output 0 and
+    lse -inf. Returns out [T_q][H][V] and lse [H][T_q] (natural log of the
+    softmax denominator, including the max). ``rows`` optionally restricts the
+    computation to those query rows (the rest of ``out``/``lse`` is NaN) so
+    large workloads can be sampled.
     """
     q, kv, k_rope = widen(q), widen(kv), widen(k_rope)
     T, H, _ = q.shape
+    T_k = kv.shape[0]
     V = kv.shape[2] - N
     out = np.full((T, H, V), np.nan)
     lse = np.full((H, T), np.nan)
     want = None if rows is None else np.zeros(T, bool)
     if want is not None:
         want[np.asarray(rows)] = True
-    for a, b in doc_bounds(cu_seqlens, T):
+    qdocs = doc_bounds(cu_seqlens, T)
+    if cu_seqlens_k is None and cu_seqlens is not None:
+        if T_k != T:
+            raise ValueError("documents of queries and keys with T_k != T_q need cu_seqlens_k")
+        kdocs = qdocs
+    else:
+        kdocs = key_bounds(cu_seqlens_k, T_k, len(qdocs))
+    if len(kdocs) != len(qdocs):
+        raise ValueError("cu_seqlens and cu_seqlens_k describe different document counts")
+    for (a, b), (ka, kb) in zip(qdocs, kdocs):
         if b == a:
             continue
         qi = np.arange(a, b) if want is None else np.arange(a, b)[want[a:b]]
         if qi.size == 0:
             continue
+        shift = (kb - ka) - (b - a)                      # the last query lines up with the last key
         for h in range(H):
-            s = _scores(q, kv, k_rope, h, qi, slice(a, b), N, scale)
+            s = _scores(q, kv, k_rope, h, qi, slice(ka, kb), N, scale)
             if causal:
-                s = np.where(np.arange(a, b)[None, :] <= qi[:, None], s, -np.inf)
-            m = s.max(axis=1, keepdims=True)
-            e = np.exp(s - m)
+                s = np.where((np.arange(ka, kb) - ka)[None, :] <= (qi - a)[:, None] + shift, s, -np.inf)
+            seen = np.isfinite(s).any(axis=1) if s.shape[1] else np.zeros(len(qi), bool)
+            m = np.where(seen, s.max(axis=1) if s.shape[1] else 0.0, 0.0)[:, None]
+            e = np.where(seen[:, None], np.exp(s - m), 0.0)
             den = e.sum(axis=1, keepdims=True)
-            out[qi, h, :] = (e / den) @ kv[a:b, h, N:]
-            lse[h, qi] = (m + np.log(den))[:, 0]
+            o = np.zeros((len(qi), V))
+            o[seen] = (e[seen] / den[seen]) @ kv[ka:kb, h, N:]
+            out[qi, h, :] = o
+            lse[h, qi] = np.where(seen, (m + np.log(np.where(seen[:, None], den, 1.0)))[:, 0], -np.inf)
     return out, lse
 
 

@@ -139,6 +139,20 @@ def test_widen_shifted_by_15_is_caught(monkeypatch):
     assert _fails(tn.test_widen_matches_torch_bfloat16_for_every_bit_pattern)
 
 
+def test_cross_length_alignment_from_the_first_key_is_caught(monkeypatch):
+    # causal mask j <= i counted from the first key (top-left) instead of lining up the last query with the last key
+    real = om.attention
+
+    def bad(q, kv, k_rope, N, scale, causal=True, cu_seqlens=None, rows=None, cu_seqlens_k=None):
+        qq = om.widen(q)
+        if cu_seqlens is None and om.widen(kv).shape[0] != qq.shape[0] and causal:
+            n = qq.shape[0]
+            return real(q, np.asarray(kv)[:n], np.asarray(k_rope)[:n], N, scale, causal, None, rows)
+        return real(q, kv, k_rope, N, scale, causal, cu_seqlens, rows, cu_seqlens_k)
+    _patch(monkeypatch, "attention", bad)
+    assert _fails(tn.test_a_chunk_of_queries_reproduces_the_full_causal_rows)
+
+
 def test_value_and_key_swapped_in_projection_is_caught(monkeypatch):
     orig = om.latent_up_proj
 

@@ -212,6 +212,83 @@ def test_attention_probs_times_values_is_the_attention_output(causal, cu):
         np.testing.assert_allclose(Pm @ kv[:, h, 4:], out[:, h], rtol=1e-12, atol=1e-13)
 
 
+# ---- separate query and key lengths (chunked prefill, attention over a projected cache)
+
+def test_a_chunk_of_queries_reproduces_the_full_causal_rows():
+    """Queries [c0, c1) of a sequence attending to its keys [0, c1) give exactly the rows [c0, c1) of the full
+    causal attention: the last query of the chunk lines up with the last key. Pins the causal alignment for
+    T_q != T_k."""
+    q, kv, kr = _tiny(T=20, H=2, N=4, R=2, V=3, seed=90)
+    full, flse = oracle.attention(q, kv, kr, 4, 0.4)
+    for c0, c1 in [(13, 20), (5, 12), (0, 6), (19, 20)]:
+        out, lse = oracle.attention(q[c0:c1], kv[:c1], kr[:c1], 4, 0.4)
+        np.testing.assert_allclose(out, full[c0:c1], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse, flse[:, c0:c1], rtol=1e-13, atol=1e-14)
+
+
+def _bottom_right_allowed(qlens, klens, causal=True):
+    Tq, Tk = sum(qlens), sum(klens)
+    allowed = np.zeros((Tq, Tk), bool)
+    qa = ka = 0
+    for nq, nk in zip(qlens, klens):
+        for i in range(nq):
+            for j in range(nk):
+                allowed[qa + i, ka + j] = (j <= i + nk - nq) if causal else True
+        qa, ka = qa + nq, ka + nk
+    return allowed
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_cross_length_documents_match_sdpa_with_the_bottom_right_mask(causal):
+    qlens, klens = [3, 1, 4, 2], [7, 1, 4, 9]          # a chunk over a prefix, one query, equal, a short chunk
+    rng = np.random.default_rng(91)
+    q = rng.standard_normal((sum(qlens), 2, 6))
+    kv = rng.standard_normal((sum(klens), 2, 7))
+    kr = rng.standard_normal((sum(klens), 2))
+    cq, ck = np.concatenate([[0], np.cumsum(qlens)]), np.concatenate([[0], np.cumsum(klens)])
+    out, _ = oracle.attention(q, kv, kr, 4, 0.3, causal=causal, cu_seqlens=list(cq), cu_seqlens_k=list(ck))
+    allowed = _bottom_right_allowed(qlens, klens, causal)
+    k = np.concatenate([kv[:, :, :4], np.broadcast_to(kr[:, None, :], (kv.shape[0], 2, 2))], axis=2)
+    Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))
+    K = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))
+    V = torch.from_numpy(np.ascontiguousarray(kv[:, :, 4:].transpose(1, 0, 2)))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=torch.from_numpy(allowed), scale=0.3)
+    np.testing.assert_allclose(out, ref.numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+    # packed == each document on its own
+    for d in range(len(qlens)):
+        o2, _ = oracle.attention(q[cq[d]:cq[d + 1]], kv[ck[d]:ck[d + 1]], kr[ck[d]:ck[d + 1]], 4, 0.3, causal=causal)
+        np.testing.assert_array_equal(out[cq[d]:cq[d + 1]], o2)
+
+
+def test_queries_that_see_no_key_give_zero_rows():
+    # 5 queries over 3 keys, causal: query i sees keys j <= i - 2, so the first two see nothing
+    q, kv, kr = _tiny(T=5, H=2, N=4, R=2, V=3, seed=92)
+    out, lse = oracle.attention(q, kv[:3], kr[:3], 4, 0.5)
+    assert np.all(out[:2] == 0) and np.all(np.isneginf(lse[:, :2]))
+    for i in range(2, 5):
+        o, l_ = oracle.attention(q[i:i + 1], kv[:i - 1], kr[:i - 1], 4, 0.5, causal=False)
+        np.testing.assert_allclose(out[i], o[0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[:, i], l_[:, 0], rtol=1e-13, atol=1e-14)
+
+
+def test_one_query_over_a_cache_is_a_plain_softmax_either_way():
+    # a single query per document over its whole cache (decode): the causal bound admits every key
+    rng = np.random.default_rng(93)
+    q = rng.standard_normal((3, 2, 6))
+    kv = rng.standard_normal((30, 2, 7))
+    kr = rng.standard_normal((30, 2))
+    cq, ck = [0, 1, 2, 3], [0, 10, 22, 30]
+    a, _ = oracle.attention(q, kv, kr, 4, 0.25, causal=True, cu_seqlens=cq, cu_seqlens_k=ck)
+    b, _ = oracle.attention(q, kv, kr, 4, 0.25, causal=False, cu_seqlens=cq, cu_seqlens_k=ck)
+    np.testing.assert_array_equal(a, b)
+    for d in range(3):
+        s = 0.25 * (kv[ck[d]:ck[d + 1], :, :4].transpose(1, 0, 2) @ q[d, :, :4, None])[..., 0] \
+            + 0.25 * (q[d, :, 4:] @ kr[ck[d]:ck[d + 1]].T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(a[d], np.einsum("hj,jhv->hv", p, kv[ck[d]:ck[d + 1], :, 4:]), rtol=1e-12)
+
+
 def test_first_token_of_each_document_returns_its_value_row():
     q, kv, kr = _tiny(T=11, H=2, N=4, R=2, V=3, seed=40)
     cu = [0, 4, 11]
