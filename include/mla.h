@@ -212,22 +212,40 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
  * (torchtitan "MLA CP optimization", section "Ulysses CP":
  * k_THK = concat(k_nope_THN, expand_per_head(k_shared_TR)),
  * out_THV = attention(q_THK, k_THK, v_THV); hyper-parallel
- * `_assemble_key_value` and `MLAContextParallel.__call__`):
+ * `_assemble_key_value` and `MLAContextParallel.__call__`, which passes the
+ * query and key lengths separately):
  *   s[t][j] = scale * (q[t][h][:N] . kv[j][h][:N] + q[t][h][N:] . k_rope[j][:])
  *   out[t][h][:] = sum_j softmax_j(s[t][.]) * kv[j][h][N:N+V]
- * over the keys j of t's document, and with j <= t when causal (no look-ahead).
- * The shared band is read once per key tile and never expanded in memory.
- *   q      : [T][H][N+R] rows at q + t*q_stride_t + h*q_stride_h
- *   kv     : [T][H][N+V] rows at kv + t*kv_stride_t + h*kv_stride_h
- *   k_rope : [T][R]      rows at k_rope + t*kr_stride_t
- *   out    : [T][H][V]   rows at out + t*o_stride_t + h*o_stride_h
- *   lse    : optional fp32 [H][T] (NULL to skip): natural-log softmax denominator
- *   cu_seqlens : optional DEVICE int32 array of n_seq+1 non-decreasing offsets
- *            starting at 0 and ending at T (packed documents; hyper-parallel
- *            `_causal_partition` uses the same ends without the leading 0).
- *            NULL means one document of T tokens.
+ * over the keys j of t's document. When causal, the i-th query of a document
+ * (0-based) sees the document's keys with local index <= i + (keys - queries
+ * of the document): the last query lines up with the last key, which is
+ * "no look-ahead" when the lengths are equal and lets a chunk of queries
+ * attend over the whole prefix before it (chunked prefill, attention over an
+ * already-projected cache). A query that sees no key (more queries than keys)
+ * gets output 0 and lse -inf. The shared band is read once per key tile and
+ * never expanded in memory.
+ *   q      : [T_q][H][N+R] rows at q + t*q_stride_t + h*q_stride_h
+ *   kv     : [T_k][H][N+V] rows at kv + j*kv_stride_t + h*kv_stride_h
+ *   k_rope : [T_k][R]      rows at k_rope + j*kr_stride_t
+ *   out    : [T_q][H][V]   rows at out + t*o_stride_t + h*o_stride_h
+ *   lse    : optional fp32 [H][T_q] (NULL to skip): natural-log softmax denominator
+ *   cu_seqlens   : optional DEVICE int32 array of n_seq+1 non-decreasing query
+ *            offsets starting at 0 and ending at T_q (packed documents;
+ *            hyper-parallel `_causal_partition` uses the same ends without the
+ *            leading 0). NULL means one document of T_q queries.
+ *   cu_seqlens_k : optional DEVICE int32 array of n_seq+1 key offsets ending at
+ *            T_k, the keys of the same documents. NULL means the query offsets
+ *            (then T_k must equal T_q), or one document of T_k keys when
+ *            cu_seqlens is NULL too. Needs cu_seqlens.
+ * Device offsets cannot be checked on the host: the kernels clamp them to
+ * [0, T_q] / [0, T_k], so malformed offsets give wrong documents, never an
+ * access outside the buffers.
  * The packed q+kv rows of mla_pack_heads can be read in place with
  * q_stride_h = kv_stride_h = F and kv = q + K.
+ * Split-KV reductions are not an argument here: the dense causal path splits
+ * paired query tiles between workgroups by itself, and the decode step with
+ * one query per sequence over a long cache is mla_latent_decode_fwd
+ * (num_splits).
  * Workspace: mla_attention_workspace_size() bytes of device memory, 256-byte
  * aligned (0 when none is needed); scratch whose contents need not be
  * initialised and are left arbitrary. Dense causal calls keep there the
@@ -251,8 +269,9 @@ typedef struct mla_attn_args {
   int64_t o_stride_t, o_stride_h;
   float *lse;
   const int32_t *cu_seqlens;
+  const int32_t *cu_seqlens_k;
   int n_seq;
-  int64_t T;
+  int64_t T_q, T_k;
   int H, N, R, V;
   float scale;
   int causal;

@@ -43,8 +43,9 @@ class mla_attn_args(ctypes.Structure):
         ("kv", ctypes.c_void_p), ("kv_stride_t", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
         ("k_rope", ctypes.c_void_p), ("kr_stride_t", ctypes.c_int64),
         ("out", ctypes.c_void_p), ("o_stride_t", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
-        ("lse", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("n_seq", ctypes.c_int),
-        ("T", ctypes.c_int64), ("H", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int), ("V", ctypes.c_int),
+        ("lse", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("n_seq", ctypes.c_int), ("T_q", ctypes.c_int64), ("T_k", ctypes.c_int64),
+        ("H", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int), ("V", ctypes.c_int),
         ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -309,7 +310,7 @@ def mla_latent_up_proj(latent, w_kvb, kv_out, heads_total, head_begin, heads, N,
     return kv_out
 
 
-def _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace):
+def _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace, cu_seqlens_k=None):
     T, H = q.shape[0], q.shape[1]
     a = mla_attn_args()
     a.q, a.q_stride_t, a.q_stride_h = q.data_ptr(), q.stride(0), q.stride(1)
@@ -318,52 +319,60 @@ def _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, work
     a.out, a.o_stride_t, a.o_stride_h = out.data_ptr(), out.stride(0), out.stride(1)
     a.lse = None if lse is None else lse.data_ptr()
     a.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
+    a.cu_seqlens_k = None if cu_seqlens_k is None else cu_seqlens_k.data_ptr()
     a.n_seq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    a.T, a.H, a.N, a.R, a.V = T, H, N, R, V
+    a.T_q, a.T_k = T, kv.shape[0]
+    a.H, a.N, a.R, a.V = H, N, R, V
     a.scale, a.causal, a.dtype = float(scale), int(bool(causal)), _dtype(q)
     if workspace is not None:
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return a
 
 
-def mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal=True, cu_seqlens=None) -> int:
-    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, None, cu_seqlens, None)
+def mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal=True, cu_seqlens=None,
+                                 cu_seqlens_k=None) -> int:
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, None, cu_seqlens, None, cu_seqlens_k)
     return int(load_library().mla_attention_workspace_size(ctypes.byref(a)))
 
 
+def _check_offsets(*cus):
+    for cu in cus:
+        if cu is not None:
+            assert cu.dtype == torch.int32 and cu.is_contiguous()
+
+
 def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None, cu_seqlens=None,
-                      workspace=None, stream=None):
-    """q [T][H][N+R], kv [T][H][N+V], k_rope [T][R] (last dims unit-stride) -> out [T][H][V].
+                      workspace=None, stream=None, cu_seqlens_k=None):
+    """q [T_q][H][N+R], kv [T_k][H][N+V], k_rope [T_k][R] (last dims unit-stride) -> out [T_q][H][V].
 
     Strided views are passed through (e.g. q and kv read in place from a packed
-    [T][H][F] buffer). cu_seqlens: int32 device tensor [n_seq+1] or None.
-    The workspace, when needed and not given, is allocated through PyTorch.
+    [T][H][F] buffer). cu_seqlens / cu_seqlens_k: int32 device tensors [n_seq+1]
+    of query / key document offsets, or None. The workspace, when needed and not
+    given, is allocated through PyTorch.
     """
     lib = load_library()
-    _dev(q, kv, k_rope, out, lse, cu_seqlens, workspace)
+    _dev(q, kv, k_rope, out, lse, cu_seqlens, cu_seqlens_k, workspace)
     for t in (q, kv, k_rope, out):
         assert t.stride(-1) == 1
-    if cu_seqlens is not None:
-        assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    _check_offsets(cu_seqlens, cu_seqlens_k)
     if workspace is None:
-        workspace = _workspace(mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens),
-                               q.device, stream)
-    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace)
+        workspace = _workspace(mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens,
+                                                            cu_seqlens_k), q.device, stream)
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace, cu_seqlens_k)
     _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
     return out
 
 
 def mla_attention_fwd_noalloc(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None, cu_seqlens=None,
-                              stream=None):
+                              stream=None, cu_seqlens_k=None):
     """mla_attention_fwd with the library's fixed per-GPU scratch instead of a workspace: nothing is
     allocated (for graph capture and serving loops). Calls overlapping on one GPU race on that scratch."""
     lib = load_library()
-    _dev(q, kv, k_rope, out, lse, cu_seqlens)
+    _dev(q, kv, k_rope, out, lse, cu_seqlens, cu_seqlens_k)
     for t in (q, kv, k_rope, out):
         assert t.stride(-1) == 1
-    if cu_seqlens is not None:
-        assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
-    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, None)
+    _check_offsets(cu_seqlens, cu_seqlens_k)
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, None, cu_seqlens_k)
     _check("mla_attention_fwd_noalloc", lib.mla_attention_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 

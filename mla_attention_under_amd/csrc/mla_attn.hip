@@ -55,7 +55,8 @@ struct AttnArgs {
   uint16_t *out;
   float *lse;
   int64_t q_st, q_sh, kv_st, kv_sh, kr_st, o_st, o_sh;
-  const int32_t *cu;      // nullptr: one document [0, T)
+  const int32_t *cu;      // query offsets; nullptr: one document [0, T)
+  const int32_t *cu_k;    // key offsets of the same documents (nullptr with cu == nullptr: [0, T_k))
   const int2 *tasks;      // packed documents: (query start, document) per task, sorted
   const int *task_count;
   int n_qtiles;           // dense: query tiles per head
@@ -63,7 +64,7 @@ struct AttnArgs {
   float *part;            // dense causal pairing: two softmax-state records per pair
   unsigned long long *flags;   // dense causal pairing: one arrival flag per pair
   unsigned long long epoch;    // this call's flag tag (see arrive)
-  int T, H;
+  int T, T_k, H;           // query rows, key rows, heads
   float scale_log2;       // scale * log2(e)
   int causal;
 };
@@ -132,9 +133,15 @@ struct PairPlan {
   int slot;      // split-tile slot in the workspace, -1 if none
 };
 
-__device__ __forceinline__ int key_tiles_of(int qt, int T) { return (min((qt + 1) * BM, T) + BN - 1) / BN; }
+// Key tiles a dense causal query tile needs: its last query, min((qt+1)BM, T) - 1,
+// sees the keys up to itself shifted by T_k - T (the sequence's last query lines
+// up with its last key).
+__device__ __forceinline__ int key_tiles_of(int qt, int T, int T_k) {
+  const int hi = min(max(min((qt + 1) * BM, T) + (T_k - T), 0), T_k);
+  return (hi + BN - 1) / BN;
+}
 
-__device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T, int shift) {
+__device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T, int T_k, int shift) {
   PairPlan pp;
   const int pairs = n / 2;
   pp.qt2 = -1;
@@ -143,11 +150,11 @@ __device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T, int sh
   if (k >= 2 * pairs) {                      // middle tile
     pp.qt = pairs;
     pp.t0 = 0;
-    pp.t1 = key_tiles_of(pairs, T);
+    pp.t1 = key_tiles_of(pairs, T, T_k);
     return pp;
   }
   const int i = k >> 1, j = n - 1 - i;
-  const int ui = key_tiles_of(i, T), uj = key_tiles_of(j, T);
+  const int ui = key_tiles_of(i, T, T_k), uj = key_tiles_of(j, T, T_k);
   // key tiles of j done by the first workgroup: half the pair's work, less
   // the shift for the second segment's fixed cost
   const int x = max(0, (ui + uj + 1) / 2 - ui - shift);
@@ -279,20 +286,25 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // the stage buffer this query block's waves use for the key-half merge and the output transpose
   uint16_t *const xs_own = qb == 0 ? kb0 : qb == 1 ? kb1 : qb == 2 ? kb2 : vb0;
 
-  // ---- which head, document and segments
-  int h, doc_lo, doc_hi;
+  // ---- which head, document and segments. Queries of the document are
+  // [doc_lo, doc_hi), its keys [kdoc_lo, kdoc_hi); when causal, query t sees
+  // the keys j <= t + kshift (the document's last query lines up with its last
+  // key; kshift = 0 for equal lengths).
+  int h, doc_lo, doc_hi, kdoc_lo, kdoc_hi;
   PairPlan pp;
   if (a.tasks == nullptr) {
     const int b = blockIdx.x, H = a.H, n = a.n_qtiles;
     h = b % H;
     doc_lo = 0;
     doc_hi = a.T;
+    kdoc_lo = 0;
+    kdoc_hi = a.T_k;
     if (a.causal && a.order == 1) {
-      pp = pair_plan(b / H, h, n, a.T, kPairShift);
+      pp = pair_plan(b / H, h, n, a.T, a.T_k, kPairShift);
     } else {                                  // heaviest first
       pp.qt = n - 1 - b / H;
       pp.t0 = 0;
-      pp.t1 = a.causal ? key_tiles_of(pp.qt, a.T) : (a.T + BN - 1) / BN;
+      pp.t1 = a.causal ? key_tiles_of(pp.qt, a.T, a.T_k) : (a.T_k + BN - 1) / BN;
       pp.part = 0;
       pp.qt2 = -1;
       pp.slot = -1;
@@ -304,10 +316,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const int2 task = a.tasks[t];
     doc_lo = min(max(a.cu[task.y], 0), a.T);          // the same clamping as the schedule
     doc_hi = min(max(a.cu[task.y + 1], doc_lo), a.T);
+    kdoc_lo = min(max(a.cu_k[task.y], 0), a.T_k);
+    kdoc_hi = min(max(a.cu_k[task.y + 1], kdoc_lo), a.T_k);
     pp.qt = (task.x - doc_lo) / BM;
     const int q_end = min(task.x + BM, doc_hi);
+    const int k_end = a.causal ? min(max(q_end + (kdoc_hi - doc_hi), kdoc_lo), kdoc_hi) : kdoc_hi;
     pp.t0 = 0;
-    pp.t1 = ((a.causal ? q_end : doc_hi) - doc_lo + BN - 1) / BN;
+    pp.t1 = (k_end - kdoc_lo + BN - 1) / BN;
     pp.part = 0;
     pp.qt2 = -1;
     pp.slot = -1;
@@ -315,13 +330,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   h = __builtin_amdgcn_readfirstlane(h);
   doc_lo = __builtin_amdgcn_readfirstlane(doc_lo);
   doc_hi = __builtin_amdgcn_readfirstlane(doc_hi);
+  kdoc_lo = __builtin_amdgcn_readfirstlane(kdoc_lo);
+  kdoc_hi = __builtin_amdgcn_readfirstlane(kdoc_hi);
+  const int kshift = kdoc_hi - doc_hi;
 
   // ---- zero the stages once: loads past the buffer range may leave LDS
   // untouched, and a masked key's zero probability must not meet a stale
-  // NaN. Only a partial key tile reads past the range: with dense tiles and
-  // T a multiple of the key tile every tile is whole (a query tile's causal
-  // key range ends at a multiple of BM or at T).
-  if (a.tasks != nullptr || a.T % BN != 0) {
+  // NaN. Only a partial key tile reads past the range: with dense tiles, T_k
+  // a multiple of the key tile and (causal) T_k - T too, every tile is whole
+  // (a query tile's causal key range ends at a multiple of BM plus T_k - T, or
+  // at T_k).
+  if (a.tasks != nullptr || a.T_k % BN != 0 || (a.causal && (a.T_k - a.T) % BN != 0)) {
     u32x4 z{0, 0, 0, 0};
     for (int i = tid; i < (KN_E + KR_E) / 8; i += 64 * NW) {
       reinterpret_cast<u32x4 *>(kb0)[i] = z;
@@ -416,7 +435,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
                      int mode) __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
-    const int kv_hi = a.causal ? q_end : doc_hi;
+    const int kv_hi = a.causal ? min(max(q_end + kshift, kdoc_lo), kdoc_hi) : kdoc_hi;   // keys end (exclusive)
     const int qi = q0 + 32 * qb + lrow;
     const int wq_first = q0 + 32 * qb;
     const int nt = t1 - t0;
@@ -447,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       l_run = 0.f;
     }
 
-    auto j0_of = [&](int t) { return doc_lo + (t0 + t) * BN; };
+    auto j0_of = [&](int t) { return kdoc_lo + (t0 + t) * BN; };
     // rows past the visible keys (a whole tile past the end included) lie
     // outside the buffer range: nothing is read for them
     // rows of the tile at key j0 that are visible, 0..BN (uniform)
@@ -553,8 +572,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     auto X = [&](int t) __attribute__((always_inline)) {
       const int jh = j0_of(t) + 32 * kh;               // first key of this wave's half
       // mask keys past the diagonal / the visible end (uniform test)
-      if (jh + 31 >= kv_hi || (a.causal && jh + 31 > wq_first)) {
-        const int lim = a.causal ? min(qi, kv_hi - 1) : kv_hi - 1;
+      if (jh + 31 >= kv_hi || (a.causal && jh + 31 > wq_first + kshift)) {
+        const int lim = a.causal ? min(qi + kshift, kv_hi - 1) : kv_hi - 1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = jh + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -828,7 +847,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // segment's first transfers right after its record stores, so that they
   // land while it arrives (the arrival waits for the stores only)
   const bool pre = pp.part && qt2 >= 0;
-  const int tiles2 = qt2 >= 0 ? key_tiles_of(qt2, a.T) : 0;
+  const int tiles2 = qt2 >= 0 ? key_tiles_of(qt2, a.T, a.T_k) : 0;
   if (early) {
     // the other workgroup arrived first in this call and never looks at the
     // flag again: mark the pair done, so that every call leaves every flag at
@@ -865,8 +884,9 @@ constexpr int kSchedBins = 4096;
 // Document bounds are clamped to [0, T] with end >= start, so malformed offsets
 // yield wrong documents but never an out-of-range access; at most max_tasks
 // tasks are written.
-__global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int32_t *__restrict__ cu, int n_seq,
-                                                                      int T, int causal, int max_tasks,
+__global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int32_t *__restrict__ cu,
+                                                                      const int32_t *__restrict__ cu_k, int n_seq,
+                                                                      int T, int T_k, int causal, int max_tasks,
                                                                       int2 *__restrict__ tasks,
                                                                       int *__restrict__ count,
                                                                       int *__restrict__ doc_first) {
@@ -878,10 +898,16 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int3
   __syncthreads();
   auto lo_of = [&](int d) { return min(max(cu[d], 0), T); };
   auto hi_of = [&](int d) { return min(max(cu[d + 1], lo_of(d)), T); };
+  auto klen_of = [&](int d) {
+    const int klo = min(max(cu_k[d], 0), T_k);
+    return min(max(cu_k[d + 1], klo), T_k) - klo;
+  };
   auto tiles_of = [&](int d) { return (hi_of(d) - lo_of(d) + BM - 1) / BM; };
+  // key tiles of query tile t of document d (causal: the document's last
+  // query lines up with its last key)
   auto work_of = [&](int d, int t) {
-    const int lo = lo_of(d), hi = hi_of(d);
-    const int kv = causal ? min(lo + (t + 1) * BM, hi) - lo : hi - lo;
+    const int lo = lo_of(d), hi = hi_of(d), nk = klen_of(d);
+    const int kv = causal ? min(max(min(lo + (t + 1) * BM, hi) - lo + (nk - (hi - lo)), 0), nk) : nk;
     return min((kv + BN - 1) / BN, kSchedBins - 1);
   };
   // exclusive prefix sum of tiles per document, in chunks of kSchedThreads
@@ -958,14 +984,17 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnPlan p) {
   if (idx >= p.T * p.H) return;
   const int64_t t = idx / p.H;
   const int h = static_cast<int>(idx % p.H);
-  int64_t lo = 0, hi = p.T;
+  int64_t lo = 0, hi = p.T, klo = 0, khi = p.T_k;
   if (p.cu != nullptr) {
     int d = 0;
     while (d + 1 < p.n_seq && p.cu[d + 1] <= t) ++d;
     lo = min(max<int64_t>(p.cu[d], 0), p.T);
     hi = min(max<int64_t>(p.cu[d + 1], lo), p.T);
+    klo = min(max<int64_t>(p.cu_k[d], 0), p.T_k);
+    khi = min(max<int64_t>(p.cu_k[d + 1], klo), p.T_k);
   }
-  const int64_t kend = p.causal ? min(t + 1, hi) : hi;
+  // causal: the document's last query lines up with its last key
+  const int64_t kend = p.causal ? min(max(t + 1 + (khi - hi), klo), khi) : khi;
   const T *qp = q + t * p.q_st + h * p.q_sh;
   auto score = [&](int64_t j) {
     const T *kp = kv + j * p.kv_st + h * p.kv_sh;
@@ -976,15 +1005,15 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnPlan p) {
     return acc * p.scale;
   };
   float m = -INFINITY;
-  for (int64_t j = lo; j < kend; ++j) m = fmaxf(m, score(j));
+  for (int64_t j = klo; j < kend; ++j) m = fmaxf(m, score(j));
   float l = 0.f;
-  for (int64_t j = lo; j < kend; ++j) l += expf(score(j) - m);
+  for (int64_t j = klo; j < kend; ++j) l += expf(score(j) - m);
   T *op = out + t * p.o_st + h * p.o_sh;
   constexpr int CH = 16;
   for (int v0 = 0; v0 < p.V; v0 += CH) {
     float acc[CH];
     for (int i = 0; i < CH; ++i) acc[i] = 0.f;
-    for (int64_t j = lo; j < kend; ++j) {
+    for (int64_t j = klo; j < kend; ++j) {
       const float w = expf(score(j) - m) / l;
       const T *vp = kv + j * p.kv_st + h * p.kv_sh + p.N;
       for (int i = 0; i < CH && v0 + i < p.V; ++i) acc[i] += w * load_f32(vp, v0 + i);
@@ -1097,10 +1126,12 @@ int launch_attention(const AttnPlan &p, void *stream) {
   a.o_st = p.o_st;
   a.o_sh = p.o_sh;
   a.T = static_cast<int>(p.T);
+  a.T_k = static_cast<int>(p.T_k);
   a.H = p.H;
   a.scale_log2 = p.scale * kLog2e;
   a.causal = p.causal;
   a.cu = p.cu;
+  a.cu_k = p.cu_k;
   int64_t tasks;
   if (p.cu == nullptr) {
     a.tasks = nullptr;
@@ -1123,8 +1154,8 @@ int launch_attention(const AttnPlan &p, void *stream) {
     int2 *task_arr = reinterpret_cast<int2 *>(ws + w.tasks_off);
     int *first = reinterpret_cast<int *>(ws + w.first_off);
     const int max_tasks = static_cast<int>((p.T + BM - 1) / BM + p.n_seq);
-    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p.cu, p.n_seq,
-                       static_cast<int>(p.T), p.causal, max_tasks, task_arr, count, first);
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p.cu, p.cu_k, p.n_seq,
+                       static_cast<int>(p.T), static_cast<int>(p.T_k), p.causal, max_tasks, task_arr, count, first);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.tasks = task_arr;

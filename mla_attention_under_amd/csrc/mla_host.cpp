@@ -412,14 +412,20 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
 static int attn_validate(const mla_attn_args *a, const char *who) {
   if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
   if (!valid_dtype(a->dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, a->dtype);
-  if (a->T < 0 || a->H < 1 || a->N < 1 || a->R < 0 || a->V < 1)
-    return fail(MLA_EINVAL, "%s: need T >= 0, H >= 1, N >= 1, R >= 0, V >= 1", who);
+  if (a->T_q < 0 || a->T_k < 0 || a->H < 1 || a->N < 1 || a->R < 0 || a->V < 1)
+    return fail(MLA_EINVAL, "%s: need T_q >= 0, T_k >= 0, H >= 1, N >= 1, R >= 0, V >= 1", who);
   if (a->R % 2) return fail(MLA_EINVAL, "%s: the RoPE band width R=%d must be even", who, a->R);
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
     return fail(MLA_EINVAL, "%s: scale must be finite and positive", who);
-  if (a->T > 0x7fffffffLL) return fail(MLA_EUNSUPPORTED, "%s: T above 2^31-1", who);
+  if (a->T_q > 0x7fffffffLL || a->T_k > 0x7fffffffLL)
+    return fail(MLA_EUNSUPPORTED, "%s: T_q or T_k above 2^31-1", who);
   if (a->cu_seqlens != nullptr && a->n_seq < 1)
     return fail(MLA_EINVAL, "%s: cu_seqlens needs n_seq >= 1", who);
+  if (a->cu_seqlens_k != nullptr && a->cu_seqlens == nullptr)
+    return fail(MLA_EINVAL, "%s: cu_seqlens_k needs the queries' cu_seqlens", who);
+  if (a->cu_seqlens != nullptr && a->cu_seqlens_k == nullptr && a->T_k != a->T_q)
+    return fail(MLA_EINVAL, "%s: T_k (%lld) != T_q (%lld) with documents needs cu_seqlens_k", who,
+                static_cast<long long>(a->T_k), static_cast<long long>(a->T_q));
   const int64_t K = static_cast<int64_t>(a->N) + a->R;
   if (a->q_stride_h < K || a->q_stride_t < a->H * a->q_stride_h - (a->q_stride_h - K))
     return fail(MLA_EINVAL, "%s: q strides (%lld, %lld) overlap rows of width %lld", who,
@@ -431,8 +437,9 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
   if (a->kr_stride_t < a->R) return fail(MLA_EINVAL, "%s: k_rope stride below R", who);
   if (a->o_stride_h < a->V || a->o_stride_t < a->o_stride_h * (a->H - 1) + a->V)
     return fail(MLA_EINVAL, "%s: out strides overlap rows of width V", who);
-  if (a->T == 0) return MLA_OK;
-  if (!a->q || !a->kv || !a->out || (a->R > 0 && !a->k_rope)) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  if (a->T_q == 0) return MLA_OK;
+  if (!a->q || !a->out || (a->T_k > 0 && (!a->kv || (a->R > 0 && !a->k_rope))))
+    return fail(MLA_EINVAL, "%s: NULL buffer", who);
   if (mla::attn_fast_path(a->N, a->R, a->V, a->dtype == MLA_BF16)) {
     const uintptr_t al = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->kv) |
                          reinterpret_cast<uintptr_t>(a->k_rope) | reinterpret_cast<uintptr_t>(a->out);
@@ -445,7 +452,7 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
     if (a->q_stride_t > kMaxRowStride || a->kv_stride_t > kMaxRowStride || a->kr_stride_t > kMaxRowStride)
       return fail(MLA_EUNSUPPORTED, "%s: token strides above 2^24 elements are not supported by the bf16 tiles",
                   who);
-    const size_t need = mla::attn_workspace_bytes(a->T, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0,
+    const size_t need = mla::attn_workspace_bytes(a->T_q, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0,
                                                   a->N, a->R, a->V, 1);
     if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need ||
                      reinterpret_cast<uintptr_t>(a->workspace) % 256))
@@ -457,15 +464,15 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
 
 size_t mla_attention_workspace_size(const mla_attn_args *a) {
   if (a == nullptr) return 0;
-  if (a->T < 0 || a->H < 1) return 0;
-  return mla::attn_workspace_bytes(a->T, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0, a->N, a->R, a->V,
-                                   a->dtype == MLA_BF16);
+  if (a->T_q < 0 || a->H < 1) return 0;
+  return mla::attn_workspace_bytes(a->T_q, a->H, a->n_seq, a->cu_seqlens != nullptr, a->causal != 0, a->N, a->R,
+                                   a->V, a->dtype == MLA_BF16);
 }
 
 static int attention_fwd(const mla_attn_args *a, void *stream, const char *who) {
   const int rc = attn_validate(a, who);
   if (rc != MLA_OK) return rc;
-  if (a->T == 0) return ok();
+  if (a->T_q == 0) return ok();
   mla::AttnPlan p;
   p.q = a->q;
   p.q_st = a->q_stride_t;
@@ -480,8 +487,11 @@ static int attention_fwd(const mla_attn_args *a, void *stream, const char *who) 
   p.o_sh = a->o_stride_h;
   p.lse = a->lse;
   p.cu = a->cu_seqlens;
+  // keys' offsets: their own, else the queries' (then T_k == T_q, checked above)
+  p.cu_k = a->cu_seqlens_k != nullptr ? a->cu_seqlens_k : a->cu_seqlens;
   p.n_seq = a->cu_seqlens ? a->n_seq : 1;
-  p.T = a->T;
+  p.T = a->T_q;
+  p.T_k = a->T_k;
   p.H = a->H;
   p.N = a->N;
   p.R = a->R;

@@ -85,9 +85,11 @@ struct AttnPlan {
   void *out;
   int64_t o_st, o_sh;
   float *lse;
-  const int32_t *cu;   // device cu_seqlens or nullptr
+  const int32_t *cu;   // device query offsets (cu_seqlens) or nullptr
+  const int32_t *cu_k; // device key offsets or nullptr (then one document of T_k keys)
   int n_seq;
-  int64_t T;
+  int64_t T;           // query rows
+  int64_t T_k;         // key rows
   int H, N, R, V;
   float scale;
   int causal;

@@ -577,3 +577,80 @@ def test_dense_causal_graph_replays_back_to_back_with_new_inputs():
         _sync()
         ref, _ = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, scale)
         check_close(host64(out), ref, name=f"back-to-back replay {i}")
+
+
+# ------------------------------------------------------------------------- separate query and key lengths
+
+def _cross_inputs(T_q, T_k, H, seed):
+    base = mi.WORKLOADS["dsv3_rank"]
+    wq = mi.Workload(base.name, base.cfg, T=T_q, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    wk = mi.Workload(base.name, base.cfg, T=max(T_k, 1), H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    q = mi.shard_inputs(wq, T=T_q, seed_cfg=seed)["q"]
+    dk = mi.shard_inputs(wk, T=max(T_k, 1), seed_cfg=seed + 1)
+    kv = mi.draw((max(T_k, 1), H, wk.P), seed + 1, 9)[:T_k]
+    return wq, q, kv, dk["k_rope"][:T_k]
+
+
+def _run_cross(w, q, kv, kr, causal, cu=None, cu_k=None):
+    T_q = q.shape[0]
+    qd, kvd, krd = dev(q), dev(kv), dev(kr)
+    out = torch.full((T_q, w.H, w.V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((w.H, T_q), float("nan"), dtype=torch.float32, device="cuda")
+    cud = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    cukd = None if cu_k is None else torch.tensor(cu_k, dtype=torch.int32, device="cuda")
+    mla.mla_attention_fwd(qd, kvd, krd, out, w.N, w.R, w.V, 1 / math.sqrt(w.K), causal=causal, lse=lse,
+                          cu_seqlens=cud, cu_seqlens_k=cukd)
+    _sync()
+    return host64(out), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("T_q,T_k,H,causal", [
+    (512, 2048, 3, True),      # a chunk at the end of the sequence, key shift a multiple of 64
+    (100, 1000, 2, True),      # shift 900: partial key tiles
+    (2048, 4096, 16, True),    # the rank shard's queries over twice the keys (paired query tiles, split tiles)
+    (77, 333, 2, False),
+    (200, 70, 2, True),        # more queries than keys: the first 130 rows see nothing
+    (1, 2048, 4, True),
+])
+def test_attention_query_chunk_over_longer_keys(T_q, T_k, H, causal):
+    w, q, kv, kr = _cross_inputs(T_q, T_k, H, 400 + T_q + T_k)
+    got, lse = _run_cross(w, q, kv, kr, causal)
+    tiles = np.arange(0, T_q, 128)
+    rows = np.unique(np.concatenate([tiles, np.minimum(tiles + 127, T_q - 1), [T_q - 1],
+                                     np.random.default_rng(T_q).integers(0, T_q, 24)]))
+    ref, rlse = oracle.attention(q, kv, kr, w.N, 1 / math.sqrt(w.K), causal=causal, rows=rows)
+    check_close(got[rows], ref[rows], name=f"chunk T_q={T_q} T_k={T_k}")
+    seen = np.isfinite(rlse[:, rows])
+    assert np.array_equal(np.isfinite(lse[:, rows]), seen), "rows with no visible key must give lse -inf"
+    check_close(lse[:, rows][seen], rlse[:, rows][seen], name=f"chunk lse T_q={T_q} T_k={T_k}")
+    if T_q > T_k and causal:
+        assert np.all(got[:T_q - T_k] == 0), "queries that see no key give zero rows"
+
+
+def test_attention_with_no_keys():
+    w, q, kv, kr = _cross_inputs(40, 0, 2, 450)
+    got, lse = _run_cross(w, q, kv, kr, True)
+    assert np.all(got == 0) and np.all(np.isneginf(lse))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_documents_with_their_own_key_offsets(causal):
+    cu = [0, 3, 4, 132, 200, 200, 457]
+    cu_k = [0, 700, 701, 829, 1000, 1064, 1100]      # a chunk over its prefix, one query, equal, short, keys only, ...
+    w, q, kv, kr = _cross_inputs(cu[-1], cu_k[-1], 2, 460)
+    got, lse = _run_cross(w, q, kv, kr, causal, cu=cu, cu_k=cu_k)
+    ref, rlse = oracle.attention(q, kv, kr, w.N, 1 / math.sqrt(w.K), causal=causal, cu_seqlens=cu, cu_seqlens_k=cu_k)
+    check_close(got, ref, name=f"documents with key offsets causal={causal}")
+    seen = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(lse), seen)
+    check_close(lse[seen], rlse[seen], name="documents with key offsets lse")
+
+
+def test_attention_one_query_per_sequence_over_its_cache():
+    """Decode shape through the general call: 4 sequences, one query each, over caches of 1000..1500 keys."""
+    cu = [0, 1, 2, 3, 4]
+    cu_k = [0, 1000, 1500, 3000, 3100]
+    w, q, kv, kr = _cross_inputs(4, 3100, 16, 470)
+    got, _ = _run_cross(w, q, kv, kr, True, cu=cu, cu_k=cu_k)
+    ref, _ = oracle.attention(q, kv, kr, w.N, 1 / math.sqrt(w.K), causal=True, cu_seqlens=cu, cu_seqlens_k=cu_k)
+    check_close(got, ref, name="one query per sequence")

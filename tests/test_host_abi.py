@@ -66,7 +66,8 @@ def test_struct_layouts_match_the_header():
 #define P(s, f) printf(#s "." #f " %zu\n", offsetof(s, f));
 int main(void) {
   P(mla_attn_args, q) P(mla_attn_args, kv_stride_h) P(mla_attn_args, out) P(mla_attn_args, lse)
-  P(mla_attn_args, cu_seqlens) P(mla_attn_args, n_seq) P(mla_attn_args, T) P(mla_attn_args, V)
+  P(mla_attn_args, cu_seqlens) P(mla_attn_args, cu_seqlens_k) P(mla_attn_args, n_seq) P(mla_attn_args, T_q)
+  P(mla_attn_args, T_k) P(mla_attn_args, V)
   P(mla_attn_args, scale) P(mla_attn_args, dtype) P(mla_attn_args, workspace) P(mla_attn_args, workspace_bytes)
   P(mla_decode_args, lse) P(mla_decode_args, B) P(mla_decode_args, S) P(mla_decode_args, num_splits)
   P(mla_decode_args, scale) P(mla_decode_args, workspace) P(mla_decode_args, workspace_bytes)
@@ -165,7 +166,7 @@ def _attn(**kw):
     from mla_attention_under_amd._binding import mla_attn_args
     a = mla_attn_args()
     a.q, a.kv, a.k_rope, a.out = 0x10000, 0x20000, 0x30000, 0x40000
-    a.T, a.H, a.N, a.R, a.V = 256, 2, 128, 64, 128
+    a.T_q, a.T_k, a.H, a.N, a.R, a.V = 256, 256, 2, 128, 64, 128
     a.q_stride_h, a.q_stride_t = 192, 384
     a.kv_stride_h, a.kv_stride_t = 256, 512
     a.kr_stride_t = 64
@@ -189,16 +190,20 @@ def test_attention_validation_before_launch(lib):
     assert f() == mla.MLA_EINVAL                              # missing workspace (dense causal pairing)
     assert f(workspace=0x60000, workspace_bytes=64) == mla.MLA_EINVAL   # too small
     assert f(cu_seqlens=0x50000, n_seq=0) == mla.MLA_EINVAL
-    assert f(T=0) == mla.MLA_OK
+    assert f(T_q=0) == mla.MLA_OK
+    assert f(T_k=-1) == mla.MLA_EINVAL
+    assert f(cu_seqlens_k=0x50000, n_seq=2) == mla.MLA_EINVAL          # key offsets without query offsets
+    assert f(cu_seqlens=0x50000, n_seq=2, T_k=300, workspace=0x60000, workspace_bytes=1 << 20) == mla.MLA_EINVAL
     assert lib.mla_attention_fwd(None, None) == mla.MLA_EINVAL
-    a = _attn(cu_seqlens=0x50000, n_seq=4, T=16384)
+    a = _attn(cu_seqlens=0x50000, n_seq=4, T_q=16384, T_k=16384)
     assert lib.mla_attention_workspace_size(ctypes.byref(a)) > 0
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn())) > 0          # dense causal
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn(causal=0))) == 0  # non-causal needs none
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn(N=16, R=8, V=16))) == 0   # generic kernel
     # the no-alloc variant: beyond its fixed scratch (128 heads at T=4096, dense causal) it launches nothing
     g = lambda **kw: lib.mla_attention_fwd_noalloc(ctypes.byref(_attn(**kw)), None)  # noqa: E731
-    assert g(T=4096, H=128, q_stride_t=128 * 192, kv_stride_t=128 * 256, o_stride_t=128 * 128) == mla.MLA_EUNSUPPORTED
+    assert g(T_q=4096, T_k=4096, H=128, q_stride_t=128 * 192, kv_stride_t=128 * 256,
+             o_stride_t=128 * 128) == mla.MLA_EUNSUPPORTED
     assert b"scratch" in lib.mla_last_error()
     assert g(R=63) == mla.MLA_EINVAL                       # validated like mla_attention_fwd
     assert lib.mla_attention_fwd_noalloc(None, None) == mla.MLA_EINVAL
