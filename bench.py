@@ -396,6 +396,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the uneven22 pack/unpack, varlen16k and decode32 measurements")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache passes and the MFMA peak probe (for kernel traces whose averages should "
+                         "cover back-to-back calls only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain contiguous copy of 1 GiB (the pack kernel with one rank) 3 times, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -514,19 +517,21 @@ def main():
     step_pct = _pct([1e3 * a.elapsed_time(b) for a, b in sev])
 
     # ---- cold caches: a 512 MB read-only sweep before every timed step / pack
-    sweep = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    reps_cold = max(10, min(args.steps, 50))
-    step_cold = _flushed(torch, step, reps_cold, sweep)
-    pack_cold = _flushed(torch, calls["pack"], reps_cold, sweep)
-    del sweep
-    mfma_peak = _mfma_peak(torch, mla)
+    step_cold = pack_cold = mfma_peak = None
+    if not args.no_cold:
+        sweep = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        reps_cold = max(10, min(args.steps, 50))
+        step_cold = _flushed(torch, step, reps_cold, sweep)
+        pack_cold = _flushed(torch, calls["pack"], reps_cold, sweep)
+        del sweep
+        mfma_peak = _mfma_peak(torch, mla)
 
     attn_tflops = flops_attn / (kern_us["attention"] * 1e-6) / 1e12
     extra = {
         "kernel_us": {k: round(v, 3) for k, v in kern_us.items()},
         "kernel_us_pct": kern_pct,
         "step_us_pct": step_pct,
-        "cold_cache": {
+        "cold_cache": None if step_cold is None else {
             "step_us": step_cold,
             "step_tflops_median": round(flops_step / (step_cold["median"] * 1e-6) / 1e12, 2),
             "pack_us": pack_cold,
@@ -582,8 +587,8 @@ def main():
     traffic = _traffic("attention", "dsv3_rank")
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "measured_peak": extra["mfma_peak_measured"]["tflops"],
-            "frac_of_measured_peak": round(attn_tflops / extra["mfma_peak_measured"]["tflops"], 4),
+            "measured_peak": mfma_peak and mfma_peak["tflops"],
+            "frac_of_measured_peak": mfma_peak and round(attn_tflops / mfma_peak["tflops"], 4),
             "kernel": "mla_attention_fwd (attn_fwd_kernel<128,64,128>)",
             "algorithmic": f"{flops_attn / 1e9:.3f} GFLOP per launch = 2*H*T(T+1)/2*(N+R+V)"}
     line = {
