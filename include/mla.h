@@ -372,10 +372,18 @@ int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream);
  * Runs bf16 with L and heads*(N+V) multiples of 32, N+V a multiple of 8, and
  * 16-byte aligned latent, w_kvb and dkv (MLA_EUNSUPPORTED otherwise).
  * T = 0 zeroes dw.
+ * workspace (optional, 256-byte aligned, contents need not be initialised):
+ * with T, L and heads*(N+V) multiples of 128 and workspace_bytes at least
+ * mla_latent_up_proj_bwd_workspace_size(), each product's contraction is
+ * split over more workgroups and the fp32 partials are summed in a fixed
+ * order (the results do not depend on scheduling either way); otherwise, or
+ * with workspace NULL, single-pass kernels run and the workspace is unused.
+ * The workspace must not be shared with work running concurrently.
  */
+size_t mla_latent_up_proj_bwd_workspace_size(int64_t T, int L, int heads, int N, int V);
 int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *dkv, float *d_latent, float *dw,
                            int64_t T, int L, int heads_total, int head_begin, int heads, int N, int V, int dtype,
-                           void *stream);
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Latent-cache decode: one new query token per sequence attends over its whole

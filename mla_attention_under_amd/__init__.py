@@ -9,5 +9,5 @@ from ._binding import (  # noqa: F401
     mla_latent_decode_fwd, mla_latent_decode_workspace_size, mla_latent_up_proj, mla_pack_heads,
     mla_unpack_heads, mla_pack_expanded, mla_causal_partition, mla_kv_exchange_ranges, mla_apply_rope,
     mla_project_pack, mla_attention_bwd, mla_attention_bwd_workspace_size,
-    mla_latent_up_proj_bwd, mla_peak_mfma_bf16, PEAK_EXPORTS,
+    mla_latent_up_proj_bwd, mla_latent_up_proj_bwd_workspace_size, mla_peak_mfma_bf16, PEAK_EXPORTS,
 )

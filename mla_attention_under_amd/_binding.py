@@ -24,7 +24,8 @@ EXPORTS = (
     "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
     "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope", "mla_project_pack",
-    "mla_attention_bwd_workspace_size", "mla_attention_bwd", "mla_latent_up_proj_bwd",
+    "mla_attention_bwd_workspace_size", "mla_attention_bwd", "mla_latent_up_proj_bwd_workspace_size",
+    "mla_latent_up_proj_bwd",
     "mla_attention_fwd_noalloc",
 )
 # the measurement probe declared in include/mla_peak.h
@@ -110,7 +111,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_attention_bwd_workspace_size.argtypes = [ctypes.POINTER(mla_attn_bwd_args)]
     lib.mla_attention_bwd_workspace_size.restype = sz
     lib.mla_attention_bwd.argtypes = [ctypes.POINTER(mla_attn_bwd_args), vp]
-    lib.mla_latent_up_proj_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.mla_latent_up_proj_bwd_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    lib.mla_latent_up_proj_bwd_workspace_size.restype = sz
+    lib.mla_latent_up_proj_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.mla_latent_decode_workspace_size.argtypes = [ctypes.POINTER(mla_decode_args)]
     lib.mla_latent_decode_workspace_size.restype = sz
     lib.mla_latent_decode_fwd.argtypes = [ctypes.POINTER(mla_decode_args), vp]
@@ -431,12 +434,19 @@ def mla_attention_bwd(q, kv, k_rope, out, dout, lse, N, R, V, scale, causal=True
     return dq, dkv, dk_rope
 
 
+def mla_latent_up_proj_bwd_workspace_size(T, L, heads, N, V) -> int:
+    return int(load_library().mla_latent_up_proj_bwd_workspace_size(T, L, heads, N, V))
+
+
 def mla_latent_up_proj_bwd(latent, w_kvb, dkv, w_heads, head_begin, heads, N, V, d_latent=None, dw=None,
-                           stream=None):
+                           workspace=None, split=True, stream=None):
     """Gradients of mla_latent_up_proj: (d_latent [T][L], dw [L][heads*(N+V)]), fp32.
 
     latent [T][L] and w_kvb [L][w_heads*(N+V)] bf16; dkv [T][heads][N+V] fp32
     (mla_attention_bwd's dkv); dw covers the head range's weight columns.
+    split=False passes no workspace (the single-pass kernels); otherwise a
+    workspace of the size the library asks for is taken from the per-stream cache
+    unless one is given.
     """
     lib = load_library()
     _dev(latent, w_kvb, dkv, d_latent, dw)
@@ -448,9 +458,14 @@ def mla_latent_up_proj_bwd(latent, w_kvb, dkv, w_heads, head_begin, heads, N, V,
     d_latent = torch.empty(T, L, **f32) if d_latent is None else d_latent
     dw = torch.empty(L, heads * (N + V), **f32) if dw is None else dw
     assert d_latent.is_contiguous() and dw.is_contiguous()
+    if not split:
+        workspace = None
+    elif workspace is None:
+        workspace = _workspace(mla_latent_up_proj_bwd_workspace_size(T, L, heads, N, V), latent.device, stream)
     _check("mla_latent_up_proj_bwd", lib.mla_latent_up_proj_bwd(
         latent.data_ptr(), w_kvb.data_ptr(), dkv.data_ptr(), d_latent.data_ptr(), dw.data_ptr(), T, L, w_heads,
-        head_begin, heads, N, V, _dtype(latent), _stream(stream)))
+        head_begin, heads, N, V, _dtype(latent), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
     return d_latent, dw
 
 

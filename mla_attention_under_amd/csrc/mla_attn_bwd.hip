@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "mla_common.h"
 #include "mla_internal.h"
@@ -620,6 +621,207 @@ __global__ __launch_bounds__(256) void dw_kernel(UpBwdArgs a) {
   }
 }
 
+// ---- split contraction for whole tiles -------------------------------------
+// With T, L and C multiples of 128 and a workspace, both products run as
+// 128x128 output tiles whose contraction is cut into 2S parts of nks 64-wide
+// slices. One 8-wave workgroup per CU holds two groups of 4 waves (64x64 each,
+// 32x32x16 MFMA); group g of split s multiplies part 2s + g, the second group's
+// sums join the first group's through LDS, and the first group writes the fp32
+// partial tile of split s (streaming stores: no dirty lines left in L2 for the
+// end-of-kernel write-back). split_sum_kernel adds the S partials in split
+// order, so the summation order is fixed and the result does not depend on
+// scheduling. Each wave issues 16 MFMAs per 64-wide slice against 8 fragment
+// reads, where the single-pass kernels above issue one MFMA per two reads.
+// Operands move global -> registers -> LDS (bf16, XOR-swizzled), two register
+// sets deep and one LDS buffer ahead of the slice being multiplied.
+//   d_latent: out[t][l], contraction over c; dkv [t][c] and w [l][col0 + c]
+//             are both contiguous along c, stored [row][64] and read as
+//             ordinary row fragments;
+//   dw:       out[l][c], contraction over t; latent [t][l] and dkv [t][c] are
+//             contiguous along the output index, stored [64 t][128] and read
+//             back transposed (ds_read_b64_tr_b16).
+constexpr int kSM = 128, kSN = 128, kSK = 64;
+struct SplitArgs {
+  const float *dkv;
+  const uint16_t *latent, *w;
+  float *out;             // partials [S][M][N], or the output itself when S == 1
+  int M, N;               // output rows, columns
+  int nks;                // 64-wide slices per split
+  int tiles_m, tiles_n;
+  int64_t L, C, ldw, col0;
+};
+
+__device__ __forceinline__ int rs_swz(int m) { return (m ^ (m >> 3)) & 7; }              // [row][64]: 8 chunks
+__device__ __forceinline__ int ts_swz(int k) { return (k & 2) | ((k & 1) * 5); }         // [64][128]: 8 segments
+__device__ __forceinline__ int rs_pos(int m, int c8) { return m * kSK + 8 * ((c8 >> 3) ^ rs_swz(m)); }
+__device__ __forceinline__ int ts_pos(int k, int c) { return k * kSN + 16 * ((c >> 4) ^ ts_swz(k)) + (c & 15); }
+
+template <bool DW>
+__global__ __launch_bounds__(512, 1) void up_bwd_split_kernel(SplitArgs a) {
+  // two groups of 4 waves, each with its own double-buffered slices
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_all[2 * 2 * (kSM * kSK + kSK * kSN)];
+  // consecutive workgroups go to different XCDs (round robin over 8): give
+  // each XCD a contiguous run of (split, tile) pairs, so the tiles of one
+  // split, which read the same contraction slices, share an L2
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int lin = G % 8 == 0 ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int split = lin / tiles, tile = lin % tiles;
+  const int m0 = (tile % a.tiles_m) * kSM, n0 = (tile / a.tiles_m) * kSN;
+  const int grp2 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // contraction part 2 split + grp2
+  const int kbeg = (2 * split + grp2) * a.nks * kSK;
+  uint16_t (*As)[kSM * kSK] = reinterpret_cast<uint16_t (*)[kSM * kSK]>(lds_all + grp2 * 2 * (kSM * kSK + kSK * kSN));
+  uint16_t (*Bs)[kSK * kSN] = reinterpret_cast<uint16_t (*)[kSK * kSN]>(lds_all + grp2 * 2 * (kSM * kSK + kSK * kSN) +
+                                                                        2 * kSM * kSK);
+
+  const int tid = threadIdx.x & 255, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int half = lane >> 5, lrow = lane & 31, grp = lane >> 4, gl = lane & 15;
+
+  // staging: thread unit u = tid + 256 i holds 8 consecutive elements of
+  // one operand row (fp32 dkv as two f32x4, rounded to bf16 on the way to LDS);
+  // two register sets, so a slice's loads are issued two slices before it is
+  // multiplied
+  f32x4 dreg[2][4][2];
+  u32x4 hreg[2][4];
+  auto gload = [&](int set, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      if constexpr (!DW) {   // dkv rows m0.., columns k0..k0+63; w rows n0.., same columns
+        const int r = u >> 3, c8 = (u & 7) * 8;
+        const float *g = a.dkv + (m0 + r) * a.C + k0 + c8;
+        dreg[set][i][0] = *reinterpret_cast<const f32x4 *>(g);
+        dreg[set][i][1] = *reinterpret_cast<const f32x4 *>(g + 4);
+        hreg[set][i] = *reinterpret_cast<const u32x4 *>(a.w + (n0 + r) * a.ldw + a.col0 + k0 + c8);
+      } else {               // tokens k0 + r: latent columns m0.., dkv columns n0..
+        const int r = u >> 4, c8 = (u & 15) * 8;
+        const int64_t t = k0 + r;
+        hreg[set][i] = *reinterpret_cast<const u32x4 *>(a.latent + t * a.L + m0 + c8);
+        const float *g = a.dkv + t * a.C + n0 + c8;
+        dreg[set][i][0] = *reinterpret_cast<const f32x4 *>(g);
+        dreg[set][i][1] = *reinterpret_cast<const f32x4 *>(g + 4);
+      }
+    }
+  };
+  auto lstore = [&](int buf, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const u32x4 d = as_u32x4(f32x8_to_bf16(dreg[set][i][0], dreg[set][i][1]));
+      if constexpr (!DW) {
+        const int r = u >> 3, c8 = (u & 7) * 8;
+        *reinterpret_cast<u32x4 *>(As[buf] + rs_pos(r, c8)) = d;
+        *reinterpret_cast<u32x4 *>(Bs[buf] + rs_pos(r, c8)) = hreg[set][i];
+      } else {
+        const int r = u >> 4, c8 = (u & 15) * 8;
+        *reinterpret_cast<u32x4 *>(As[buf] + ts_pos(r, c8)) = hreg[set][i];
+        *reinterpret_cast<u32x4 *>(Bs[buf] + ts_pos(r, c8)) = d;
+      }
+    }
+  };
+  // operand fragment of contraction step ks for the 32 output rows (A) or
+  // columns (B) starting at x0: lane l takes index x0 + l%32 and contraction
+  // elements 16ks + 8(l/32) .. +7 in natural order (both forms)
+  auto frag = [&](const uint16_t *t, int x0, int ks) __attribute__((always_inline)) {
+    if constexpr (!DW) {
+      const int m = x0 + lrow;
+      return *reinterpret_cast<const bf16x8 *>(t + rs_pos(m, 16 * ks + 8 * half));
+    } else {
+      const int x = x0 + 16 * (grp & 1) + 4 * (gl & 3);
+      const int k0r = 16 * ks + 8 * (grp >> 1) + (gl >> 2), k1r = k0r + 4;
+      const s16x4 lo = read_tr(t + ts_pos(k0r, x)), hi = read_tr(t + ts_pos(k1r, x));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // slice st: LDS buffer st % 2, register set st % 2
+  gload(0, kbeg);
+  if (a.nks > 1) gload(1, kbeg + kSK);
+  lstore(0, 0);
+  __syncthreads();
+  auto slice = [&](int st, auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    const int buf = st & 1;
+    // set `set` went to LDS before this slice: refill it with slice st + 2
+    if (st + 2 < a.nks) gload(set, kbeg + (st + 2) * kSK);
+    bf16x8 af[kSK / 16][2], bf[kSK / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < kSK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[ks][i] = frag(As[buf], 64 * wm + 32 * i, ks);
+        bf[ks][i] = frag(Bs[buf], 64 * wn + 32 * i, ks);
+      }
+#pragma unroll
+    for (int ks = 0; ks < kSK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[ks][i], bf[ks][j], acc[i][j]);
+    // the other buffer's readers finished before the previous slice's barrier
+    if (st + 1 < a.nks) lstore(buf ^ 1, set ^ 1);
+    __syncthreads();
+  };
+  for (int st = 0; st < a.nks; st += 2) {
+    slice(st, std::integral_constant<int, 0>());
+    if (st + 1 < a.nks) slice(st + 1, std::integral_constant<int, 1>());
+  }
+  // the second group's sums meet the first group's through LDS (first + second)
+  float *red = reinterpret_cast<float *>(lds_all);
+  if (grp2 == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave * 4 + i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (grp2 == 1) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((wave * 4 + i * 2 + j) * 16 + r) * 64 + lane];
+  float *out = a.out + static_cast<int64_t>(split) * a.M * a.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + 64 * wm + 32 * i + row_of(r, lane);
+        __builtin_nontemporal_store(acc[i][j][r], out + m * a.N + n0 + 64 * wn + 32 * j + lrow);
+      }
+}
+
+// out[i] = sum over s of part[s][i], s = 0, 1, ..., S-1 in that order
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *part, float *out, int64_t n4, int S) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(part) + i;
+  f32x4 v = p[0];
+  for (int s = 1; s < S; ++s) {
+    const f32x4 w = p[s * n4];
+    v[0] += w[0];
+    v[1] += w[1];
+    v[2] += w[2];
+    v[3] += w[3];
+  }
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(out) + i);
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) x[i] = 0.f;
@@ -697,11 +899,68 @@ int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream) {
     zero_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p.dw, n);
     return hipGetLastError();
   }
+  const UpBwdSplits sp = up_bwd_splits(p.T, p.L, p.C);
+  if (sp.aligned && p.ws != nullptr && p.ws_bytes >= sp.ws_bytes) {
+    SplitArgs g;
+    g.dkv = p.dkv;
+    g.latent = a.latent;
+    g.w = a.w;
+    g.L = p.L;
+    g.C = p.C;
+    g.ldw = p.ldw;
+    g.col0 = p.col0;
+    float *ws = static_cast<float *>(p.ws);
+    // d_latent [T][L]: contraction over the C columns
+    g.M = a.T;
+    g.N = p.L;
+    g.tiles_m = a.T / kSM;
+    g.tiles_n = p.L / kSN;
+    g.nks = p.C / kSK / (2 * sp.s_dl);
+    g.out = sp.s_dl > 1 ? ws : p.d_latent;
+    up_bwd_split_kernel<false><<<g.tiles_m * g.tiles_n * sp.s_dl, 512, 0, s>>>(g);
+    const int64_t n_dl = static_cast<int64_t>(a.T) * p.L / 4;
+    if (sp.s_dl > 1)
+      split_sum_kernel<<<static_cast<unsigned>((n_dl + 255) / 256), 256, 0, s>>>(ws, p.d_latent, n_dl, sp.s_dl);
+    // dw [L][C]: contraction over the T tokens (the workspace is free again:
+    // the sum above runs first on the stream)
+    g.M = p.L;
+    g.N = p.C;
+    g.tiles_m = p.L / kSM;
+    g.tiles_n = p.C / kSN;
+    g.nks = a.T / kSK / (2 * sp.s_dw);
+    g.out = sp.s_dw > 1 ? ws : p.dw;
+    up_bwd_split_kernel<true><<<g.tiles_m * g.tiles_n * sp.s_dw, 512, 0, s>>>(g);
+    const int64_t n_dw = static_cast<int64_t>(p.L) * p.C / 4;
+    if (sp.s_dw > 1)
+      split_sum_kernel<<<static_cast<unsigned>((n_dw + 255) / 256), 256, 0, s>>>(ws, p.dw, n_dw, sp.s_dw);
+    return hipGetLastError();
+  }
   // token blocks run fastest: the column tiles of one token block are 8k
   // launch slots apart and so share an XCD (and its L2 copy of their dkv rows)
   dlatent_kernel<<<dim3((a.T + kDlM - 1) / kDlM, (a.L + kDlN - 1) / kDlN), 256, 0, s>>>(a);
   dw_kernel<<<dim3((a.C + kDwN - 1) / kDwN, (a.L + kDwM - 1) / kDwM), 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// Split counts: the largest power of two (at most 8) that keeps a launch
+// within 256 workgroups (one per CU) with 2S equal parts of whole 64-wide
+// slices; the workspace holds one product's partials at a time.
+UpBwdSplits up_bwd_splits(int64_t T, int L, int C) {
+  UpBwdSplits r;
+  r.aligned = T > 0 && T % kSM == 0 && L % kSM == 0 && C % kSN == 0 && T <= (1LL << 24) && L <= (1 << 20) &&
+              C <= (1 << 24);   // grid sizes stay below 2^31
+  if (!r.aligned) return r;
+  auto pick = [](int64_t tiles, int64_t slices) {
+    int s = 1;
+    while (s < 8 && tiles * s * 2 <= 256 && slices % (s * 4) == 0) s *= 2;
+    return s;
+  };
+  r.s_dl = pick(T / kSM * (L / kSN), C / kSK);
+  r.s_dw = pick(static_cast<int64_t>(L / kSM) * (C / kSN), T / kSK);
+  const size_t dl = r.s_dl > 1 ? static_cast<size_t>(r.s_dl) * T * L * 4 : 0;
+  const size_t dw = r.s_dw > 1 ? static_cast<size_t>(r.s_dw) * L * C * 4 : 0;
+  r.ws_bytes = dl > dw ? dl : dw;
+  return r;
 }
 
 }  // namespace mla

@@ -604,9 +604,16 @@ int mla_attention_bwd(const mla_attn_bwd_args *a, void *stream) {
   return launched(mla::launch_attention_bwd(p, stream), who);
 }
 
+size_t mla_latent_up_proj_bwd_workspace_size(int64_t T, int L, int heads, int N, int V) {
+  if (T < 0 || L < 1 || heads < 1 || N < 1 || V < 1) return 0;
+  const int64_t C = (static_cast<int64_t>(N) + V) * heads;
+  if (T > (1LL << 30) || C > (1LL << 30)) return 0;
+  return mla::up_bwd_splits(T, L, static_cast<int>(C)).ws_bytes;
+}
+
 int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *dkv, float *d_latent, float *dw,
                            int64_t T, int L, int heads_total, int head_begin, int heads, int N, int V, int dtype,
-                           void *stream) {
+                           void *workspace, size_t workspace_bytes, void *stream) {
   const char *who = "mla_latent_up_proj_bwd";
   if (T < 0 || L < 1 || N < 1 || V < 1 || heads < 1 || head_begin < 0 || head_begin + heads > heads_total)
     return fail(MLA_EINVAL, "%s: need T >= 0, L, N, V >= 1 and a head range inside the %d heads", who, heads_total);
@@ -620,6 +627,8 @@ int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *d
   const uintptr_t al = reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w_kvb) |
                        reinterpret_cast<uintptr_t>(dkv);
   if (al % 16) return fail(MLA_EUNSUPPORTED, "%s: latent, w_kvb and dkv must be 16-byte aligned", who);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MLA_EINVAL, "%s: the workspace must be 256-byte aligned", who);
   mla::UpProjBwdPlan p;
   p.latent = latent;
   p.w = w_kvb;
@@ -631,6 +640,8 @@ int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *d
   p.C = static_cast<int>(C);
   p.ldw = P * heads_total;
   p.col0 = P * head_begin;
+  p.ws = workspace;
+  p.ws_bytes = workspace == nullptr ? 0 : workspace_bytes;
   return launched(mla::launch_up_proj_bwd(p, stream), who);
 }
 

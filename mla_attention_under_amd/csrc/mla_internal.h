@@ -134,8 +134,18 @@ struct UpProjBwdPlan {
   int64_t T;
   int L, C;
   int64_t ldw, col0;
+  void *ws;            // optional: partial products of the split path
+  size_t ws_bytes;
 };
 int launch_up_proj_bwd(const UpProjBwdPlan &p, void *stream);
+// split path of the up-projection backward: taken for T, L, C multiples of 128
+// when the workspace holds ws_bytes; s_dl / s_dw are the contraction splits
+struct UpBwdSplits {
+  bool aligned = false;
+  int s_dl = 1, s_dw = 1;
+  size_t ws_bytes = 0;
+};
+UpBwdSplits up_bwd_splits(int64_t T, int L, int C);
 
 // ---- latent-cache decode ------------------------------------------------
 struct DecodePlan {

@@ -198,6 +198,10 @@ UP_CASES = [
     ("ragged_tokens", 37, 96, 2, 0, 2, 16, 16),
     ("uneven_columns", 100, 32, 4, 3, 1, 16, 48),
     ("dsv3_rank", 2048, 512, 128, 16, 16, 128, 128),
+    # multiples of 128: the split contraction (d_latent and dw in 2 splits of 2 parts, one slice each)
+    ("aligned_split", 256, 128, 4, 1, 2, 64, 64),
+    # d_latent in 2 parts of 3 slices (one split), dw in 4 splits of 2 parts of one slice
+    ("aligned_multi_slice", 512, 128, 3, 0, 3, 64, 64),
 ]
 
 
@@ -217,6 +221,32 @@ def test_latent_up_proj_bwd_matches_oracle(name, T, L, ht, hb, heads, Nn, Vv):
     cols = slice(hb * P, (hb + heads) * P)
     _check(host64(dw), ref_dw[:, cols], b_dw, f"{name} dw")
     assert not np.any(ref_dw[:, :hb * P]) and not np.any(ref_dw[:, (hb + heads) * P:])
+
+
+@pytest.mark.parametrize("name", ["dsv3_rank", "aligned_multi_slice"])
+def test_latent_up_proj_bwd_single_pass_and_split_agree(name):
+    """Without a workspace the single-pass kernels run: both forms meet the oracle's bounds, and the split form
+    gives the same bits on a second call (its partials are summed in a fixed order)."""
+    _, T, L, ht, hb, heads, Nn, Vv = next(c for c in UP_CASES if c[0] == name)
+    print(f"[up_bwd] {name} single pass and split", flush=True)
+    assert mla.mla_latent_up_proj_bwd_workspace_size(T, L, heads, Nn, Vv) > 0
+    P = Nn + Vv
+    cfg = W.cfg * 1000 + 79
+    latent = mi.draw((T, L), cfg, 3)
+    w = mi.draw((L, ht * P), cfg, 4, std=0.05)
+    dkv = mi.normal_f32((T, heads, P), cfg, 5)
+    args = (dev(latent), dev(w), dev(dkv), ht, hb, heads, Nn, Vv)
+    one = mla.mla_latent_up_proj_bwd(*args, split=False)
+    spl = mla.mla_latent_up_proj_bwd(*args)
+    again = mla.mla_latent_up_proj_bwd(*args)
+    torch.cuda.synchronize()
+    ref_dl, ref_dw = oracle.latent_up_proj_backward(latent, w, hb, heads, dkv, Nn, Vv)
+    b_dl, b_dw = _up_bounds(latent, w, dkv, hb, heads, P)
+    cols = slice(hb * P, (hb + heads) * P)
+    for form, (dl, dw) in (("single pass", one), ("split", spl)):
+        _check(host64(dl), ref_dl, b_dl, f"{name} {form} d_latent")
+        _check(host64(dw), ref_dw[:, cols], b_dw, f"{name} {form} dw")
+    assert torch.equal(spl[0], again[0]) and torch.equal(spl[1], again[1])
 
 
 def test_latent_up_proj_bwd_no_tokens_zeroes_dw():

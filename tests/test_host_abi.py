@@ -254,7 +254,8 @@ def test_attention_bwd_validation_before_launch(lib):
 
 
 def test_up_proj_bwd_validation_before_launch(lib):
-    f = lambda *a: lib.mla_latent_up_proj_bwd(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, *a, None)  # noqa: E731
+    f = lambda *a: lib.mla_latent_up_proj_bwd(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, *a,  # noqa: E731
+                                              None, 0, None)
     # T, L, heads_total, head_begin, heads, N, V, dtype
     assert f(64, 512, 128, 16, 16, 128, 128, mla.MLA_F32) == mla.MLA_EUNSUPPORTED   # bf16 only
     assert f(64, 500, 128, 16, 16, 128, 128, mla.MLA_BF16) == mla.MLA_EUNSUPPORTED   # L % 32
@@ -262,9 +263,25 @@ def test_up_proj_bwd_validation_before_launch(lib):
     assert f(64, 512, 128, 120, 16, 128, 128, mla.MLA_BF16) == mla.MLA_EINVAL       # head range outside
     assert f(-1, 512, 128, 16, 16, 128, 128, mla.MLA_BF16) == mla.MLA_EINVAL
     assert lib.mla_latent_up_proj_bwd(0x10008, 0x20000, 0x30000, 0x40000, 0x50000, 64, 512, 128, 16, 16, 128, 128,
-                                      mla.MLA_BF16, None) == mla.MLA_EUNSUPPORTED     # misaligned latent
+                                      mla.MLA_BF16, None, 0, None) == mla.MLA_EUNSUPPORTED   # misaligned latent
     assert lib.mla_latent_up_proj_bwd(0x10000, 0x20000, 0x30000, 0x40000, None, 64, 512, 128, 16, 16, 128, 128,
-                                      mla.MLA_BF16, None) == mla.MLA_EINVAL           # no dw
+                                      mla.MLA_BF16, None, 0, None) == mla.MLA_EINVAL          # no dw
+    assert lib.mla_latent_up_proj_bwd(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 64, 512, 128, 16, 16, 128, 128,
+                                      mla.MLA_BF16, 0x60010, 1 << 20, None) == mla.MLA_EINVAL   # misaligned workspace
+
+
+def test_up_proj_bwd_workspace_size(lib):
+    ws = lib.mla_latent_up_proj_bwd_workspace_size
+    # the rank shard: d_latent split 4 ways (64 tiles of 128x128), dw 2 ways (128 tiles): 4 x [2048][512] fp32
+    assert ws(2048, 512, 16, 128, 128) == 4 * 2048 * 512 * 4
+    assert ws(2048, 512, 16, 128, 128) >= 2 * 512 * 4096 * 4
+    # not a multiple of 128 in T, L or heads*(N+V): the single-pass kernels, no workspace
+    assert ws(2000, 512, 16, 128, 128) == 0
+    assert ws(2048, 480, 16, 128, 128) == 0
+    assert ws(2048, 512, 1, 32, 32) == 0
+    # enough tiles in both products without splitting: no workspace
+    assert ws(65536, 512, 128, 128, 128) == 0
+    assert ws(-1, 512, 16, 128, 128) == 0
 
 
 def test_decode_validation_before_launch(lib):
