@@ -23,6 +23,12 @@ ARCH = "gfx950"
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source additions. The attention backward's four-wave kernel keeps about
+# 330 values live at one wave per SIMD; with the default MFMA register form the
+# compiler parks its dk / dv accumulators in AGPRs and copies them through
+# VGPRs every step (about 350 v_accvgpr moves per step), while the VGPR form
+# leaves them in place.
+FILE_FLAGS = {"mla_attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():
@@ -34,7 +40,7 @@ def _hipcc():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in line)

@@ -69,45 +69,11 @@ struct AttnArgs {
   int causal;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 // per-row XOR swizzles of the unpadded LDS tiles (16-byte chunks / 32-byte segments)
 __device__ __forceinline__ int kn_swz(int key) { return key & 15; }
 __device__ __forceinline__ int kr_swz(int key) { return (key ^ (key >> 3)) & 7; }
 __device__ __forceinline__ int v_swz(int key) { return (key & 2) | ((key & 1) * 5); }
 
-// Buffer resource (base, byte range) as four scalar dwords for the transfer below.
-__device__ __forceinline__ u32x4 dma_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = static_cast<uint32_t>(b), hi = static_cast<uint32_t>(b >> 32) & 0xffffu;
-  return u32x4{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lo)),
-               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(hi)),
-               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), static_cast<uint32_t>(kBufferDword3)};
-}
-
-// One 1 KB global->LDS transfer of a wave: lane l copies the 16 bytes at byte
-// voff of the buffer (zero outside its range) to lds_dst + 16 l. Written as
-// inline assembly so that the compiler does not track it: completion is
-// awaited explicitly with vmcnt before the barrier that publishes the tile.
-// (Tracked, its alias analysis loses the buffers apart in the unrolled ring
-// and waits for every transfer in flight before reading any tile.)
-__device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds_dst, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds_dst));
-}
-
-// LDS byte address of a shared-memory pointer (uniform)
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
-      static_cast<int>(reinterpret_cast<uintptr_t>((lds_void *)(p)))));
-}
-
-// 4 bf16 of V^T from a row-major V tile: ds_read_b64_tr_b16 hands lane i of
-// each 16-lane group column i of the 4x16 block whose rows its lanes address.
-__device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-}
 
 // Causal pairing of query tiles (dense, one sequence). Query tiles i and
 // n-1-i of a head together hold U = u(i) + u(n-1-i) key tiles, nearly the

@@ -10,20 +10,15 @@
 //   dv = p^T dout, dp = dout v^T, ds = p (dp - D), dq = scale ds k,
 //   dk = scale ds^T q; dk_rope = sum over heads of dk[..., N:].
 //
-// Three launches, all on blocks of 32 keys by 32 queries with the score block
-// kept transposed (keys are rows, queries are the lanes' columns, so a lane's
-// log-sum-exp and row term are one register each):
+// Three launches:
 //   row_term_kernel   D[h][t] from out and dout;
-//   attn_bwd_kernel   one workgroup (two waves) per (block b, head), two
-//                     phases: dk, dv of key block b accumulated over the query
-//                     blocks that see it (the band part of dk goes to a
-//                     per-head slice of the workspace), then dq of query block
-//                     b accumulated over the key blocks it sees (scores
+//   attn_bwd8_kernel  one workgroup (eight waves) per (block b of 128 tokens,
+//                     head), two phases: dk, dv of key block b accumulated over
+//                     the query steps that see it (the band part of dk goes to
+//                     a per-head slice of the workspace), then dq of query
+//                     block b accumulated over the key steps it sees (scores
 //                     recomputed rather than reduced across workgroups, so no
-//                     atomics and a fixed summation order). Under the causal
-//                     mask key block b is seen by nb - b query blocks and query
-//                     block b sees b + 1 key blocks, so every workgroup carries
-//                     the same nb + 1 block steps and the grid drains evenly;
+//                     atomics and a fixed summation order);
 //   band_sum_kernel   dk_rope[t] = sum over heads of the band slices, in head
 //                     order.
 // Then the latent up-projection's backward (dlatent_kernel, dw_kernel): the
@@ -41,8 +36,6 @@
 namespace mla {
 namespace {
 
-constexpr int BB = 32;          // keys or queries per block
-constexpr int TP = BB + 8;      // pitch of the 32x32 p / ds blocks in LDS, in bf16
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdArgs {
@@ -92,70 +85,8 @@ __device__ __forceinline__ void load_frags(const uint16_t *src, int64_t st, int 
     f[s] = ok ? *reinterpret_cast<const bf16x8 *>(row + 16 * s) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 }
 
-// Fragments (see load_frags) to a row-major LDS block of pitch P: one 16-byte
-// store each.
-template <int W>
-__device__ __forceinline__ void store_rows(const bf16x8 *f, uint16_t *dst, int P, int lane) {
-#pragma unroll
-  for (int s = 0; s < W / 16; ++s)
-    *reinterpret_cast<bf16x8 *>(dst + (lane & 31) * P + 16 * s + 8 * (lane >> 5)) = f[s];
-}
-
-// Transposing LDS reads (gfx950 ds_read_b64_tr_b16): lane i of each 16-lane
-// group receives column i of the 4x16 block whose rows its lanes address.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-__device__ __forceinline__ s16x4 read_tr(const uint16_t *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-}
-
-// MFMA operand of contraction step b (rows 16b .. 16b+15 of a row-major
-// [row][column] LDS block of pitch P) for the 32 columns 32d + l%32, read
-// transposed. Element m of lane l comes from row 16b + 8(m/4) + 4(l/32) + m%4:
-// the other operand of the product must list its contraction index in the
-// same order (perm_frag).
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *tile, int P, int b, int d, int lane) {
-  const int grp = lane >> 4, gl = lane & 15;
-  const int col = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
-  const int r0 = 4 * (grp >> 1) + (gl >> 2) + 16 * b;
-  const s16x4 lo = read_tr(tile + r0 * P + col), hi = read_tr(tile + (r0 + 8) * P + col);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// The matching operand from a row-major [i][k] LDS block of pitch P: row l%32,
-// elements 16b + 4(l/32) .. +3 and 16b + 8 + 4(l/32) .. +3 (tr_frag's order).
-__device__ __forceinline__ bf16x8 perm_frag(const uint16_t *m, int P, int b, int lane) {
-  const uint16_t *row = m + (lane & 31) * P + 16 * b + 4 * (lane >> 5);
-  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row), hi = *reinterpret_cast<const u32x2 *>(row + 8);
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
 // row i of the block held in register r of lane l (column l%32)
 __device__ __forceinline__ int row_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// p^T and ds^T of one block, from the transposed scores and dp^T:
-//   p = exp(scale*s - lse_j), ds = p (dp - D_j), zero where key i is not
-// visible to query j (another document, past the diagonal, past T).
-__device__ __forceinline__ void probs_t(const BwdArgs &a, f32x16 &st, f32x16 &dp, int k0, int q, int qlo, int qhi,
-                                        float lse2, float Dq, int lane) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = k0 + row_of(r, lane);
-    const bool vis = key >= qlo && key < qhi && (!a.causal || key <= q);
-    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], a.scale * kLog2e, -lse2)) : 0.f;
-    st[r] = p;
-    dp[r] = p * (dp[r] - Dq);
-  }
-}
-
-// block values (C layout) to a row-major bf16 LDS block [i][j], or its transpose
-__device__ __forceinline__ void store_block(const f32x16 &v, uint16_t *m, bool transpose, int lane) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = row_of(r, lane), j = lane & 31;
-    m[transpose ? j * TP + i : i * TP + j] = f32_to_bf16(v[r]);
-  }
-}
 
 __global__ __launch_bounds__(256) void row_term_kernel(BwdArgs a, int V) {
   // 16 lanes per (t, h) row, 8 elements each per pass
@@ -180,239 +111,461 @@ __global__ __launch_bounds__(256) void row_term_kernel(BwdArgs a, int V) {
   if (live && c == 0) a.Dws[static_cast<int64_t>(h) * a.T + t] = acc;
 }
 
-// LDS of a workgroup: the dk/dv phase's q, dout (row-major, read back
-// transposed), p^T and ds^T blocks, or the dq phase's k and ds blocks; rows
-// padded by 8 elements
-template <int K, int V>
-constexpr int kBwdLds = BB * (K + 8) + BB * (V + 8) + 2 * BB * TP;
-
-// Two waves per (block b, head), each under 256 VGPRs so that two waves share
-// a SIMD and cover each other's barriers and LDS round trips. Wave 0 holds the
-// key (or query) side of the scores: it computes s, then p and ds, and the
-// first KS column tiles of dk (or dq); wave 1 holds the value side: dp, which
-// it hands over through LDS in its own register layout, then dv and the last
-// column tiles of dk (or dq). Each wave runs its own loop; the two meet at the
-// same three barriers per block step:
-//   (1) the previous step's readers are done; row-major copies and the s / dp
-//       products, the next block's loads issued;
-//   (2) dp is in LDS; wave 0 forms p and ds into LDS;
-//   (3) the second-stage products of both waves.
-// Workgroups are dealt to the 8 XCDs round robin by launch order; when the
-// grid divides evenly, launch slot i is remapped so that each XCD runs a
-// contiguous run of (head, block) pairs, i.e. whole heads, whose q, k, v and
-// dout then stay in that XCD's L2 instead of every XCD streaming every head.
+// ---- eight-wave form ---------------------------------------------------------
+// One workgroup of eight waves (two per SIMD) per (block b of 128 tokens, head).
+// Phase 1 accumulates dk and dv of key block b over 32-query steps, phase 2 dq
+// of query block b over 32-key steps. Under the causal mask the two phases
+// together take (T + 128) / 32 steps for every b, so the grid drains evenly.
+// The four 32-token groups g of the block each have two waves, g and g + 4,
+// which share a SIMD and split the group's products between them:
+//   phase 1 (keys own0 = 128b + 32g): wave g computes s = q k^T and p, writes
+//     p to LDS and accumulates dv = p^T dout; wave g + 4 computes dp = dout v^T,
+//     reads p, forms ds = p (dp - D) and accumulates dk = ds^T q;
+//   phase 2 (queries own0): wave g computes s^T = k q^T and p^T, wave g + 4
+//     dp^T = v dout^T; they swap p^T and dp^T through LDS, both form ds, and
+//     each accumulates three of the six 32-column tiles of dq = ds k.
+// Each wave keeps only its own operand as register fragments (k or v, q or
+// dout), so no product is computed twice; a step has two barriers (stage
+// ready; the exchange written).
+//
+// The streamed block of each step (q, dout, lse, D in phase 1; k, v in phase
+// 2) goes to one of kStages LDS stages by buffer_load ... lds, kStages - 1
+// steps ahead. The scores come out with a lane per owned token: phase 1 s and
+// dp have lane = key, registers = queries; phase 2 s^T and dp^T lane = query,
+// registers = keys. Registers 8s .. 8s+7 of such a block, packed to bf16, are
+// directly the A operand of the next product over the 16 streamed tokens
+// 16s + 8(m/4) + 4(l/32) + m%4 (m = element), and the B operand comes from
+// the stage through the transposing read, whose element order is the same
+// (st_tr).
+constexpr int kWB = 128;   // tokens per workgroup block
+constexpr int kSB = 32;    // streamed tokens per step
+constexpr int kStages = 3;
+// A stage: three row-major bf16 parts of kSB rows, chunk c (16 bytes) of row r
+// at r * CH + (c ^ st_swz(r)) (CH = chunks per row), then lse and D (phase 1).
+// The swizzle spreads both the row fragment reads (8 rows, one chunk) and the
+// transposing reads (4 rows, two neighbouring chunks) over the banks: with
+// eight waves per CU they ran at 127 and 99 B/clk against 128 and 64 for
+// chunk ^ (row & 7).
 template <int N, int R, int V>
-__global__ __launch_bounds__(128, 2) void attn_bwd_kernel(BwdArgs a) {
+struct Stage {
+  static constexpr int kN = kSB * N, kR = kSB * R, kV = kSB * V;   // elements of the parts
+  static constexpr int kLse = kN + kR + kV;                        // element offset of lse (fp32 x 32), then D
+  static constexpr int kElems = kLse + 2 * kSB * 2;
+};
+
+// element (r, col) of a stage part with CH chunks per row
+__device__ __forceinline__ int st_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int CH>
+__device__ __forceinline__ int st_elem(int r, int col) {
+  return (r * CH + ((col >> 3) ^ st_swz(r))) * 8 + (col & 7);
+}
+// row fragment of k step s (lane l: row l%32, columns 16s + 8(l/32) .. +7)
+template <int CH>
+__device__ __forceinline__ bf16x8 st_row(const uint16_t *part, int s, int lane) {
+  return *reinterpret_cast<const bf16x8 *>(part + st_elem<CH>(lane & 31, 16 * s + 8 * (lane >> 5)));
+}
+// Transposed fragment of contraction step b for the columns 32d + l%32:
+// element m of lane l comes from row 16b + 8(m/4) + 4(l/32) + m%4, the order
+// in which registers 8b .. 8b+7 of a score block hold their rows (row_of).
+template <int CH>
+__device__ __forceinline__ bf16x8 st_tr(const uint16_t *part, int b, int d, int lane) {
+  const int grp = lane >> 4, gl = lane & 15;
+  const int col = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+  const int r0 = 4 * (grp >> 1) + (gl >> 2) + 16 * b;
+  const s16x4 lo = read_tr(part + st_elem<CH>(r0, col)), hi = read_tr(part + st_elem<CH>(r0 + 8, col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// the A operand of k step s from registers 8s .. 8s+7 of a score block
+__device__ __forceinline__ bf16x8 pack_frag(const f32x16 &v, int s) {
+  return as_bf16x8(u32x4{pack_bf16x2(v[8 * s], v[8 * s + 1]), pack_bf16x2(v[8 * s + 2], v[8 * s + 3]),
+                         pack_bf16x2(v[8 * s + 4], v[8 * s + 5]), pack_bf16x2(v[8 * s + 6], v[8 * s + 7])});
+}
+// a score block through LDS: register 4j + e of lane l at f32x4 j*64 + l, element e
+__device__ __forceinline__ void xch_put(float *buf, const f32x16 &v, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    reinterpret_cast<f32x4 *>(buf)[64 * j + lane] = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+}
+__device__ __forceinline__ f32x16 xch_get(const float *buf, int lane) {
+  f32x16 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 x = reinterpret_cast<const f32x4 *>(buf)[64 * j + lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
+  }
+  return v;
+}
+
+// Transfers of one part of kSB rows x CH chunks into a stage by the waves
+// ws = 0 .. NW-1 of a set: chunk p of the part (LDS order) is row p / CH,
+// logical chunk (p % CH) ^ st_swz(row), read from byte row * row_bytes +
+// col_bytes + 16 chunk of the buffer (rows past its range read zero).
+template <int CH, int NW>
+__device__ __forceinline__ void stage_part(const u32x4 &rsrc, uint32_t lds, int64_t row_bytes, int col_bytes,
+                                           int ws, int lane) {
+  constexpr int I = kSB * CH / (64 * NW);
+  static_assert(I * 64 * NW == kSB * CH, "whole transfers per wave");
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    const int p = 64 * (I * ws + i) + lane, r = p / CH, c = (p % CH) ^ st_swz(r);
+    dma16(rsrc, lds + 1024 * (I * ws + i), static_cast<uint32_t>(r * row_bytes + col_bytes + 16 * c));
+  }
+}
+
+template <int N, int R, int V>
+__global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
+  static_assert(N == 128 && R == 64 && V == 128, "stage layout, transfer split and fragment counts");
   constexpr int K = N + R;
-  constexpr int KS = 4;   // dk / dq column tiles of wave 0 (the rest go to wave 1)
-  static_assert(K / 32 > KS, "both waves own dk columns");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kBwdLds<K, V>];
-  __shared__ __attribute__((aligned(16))) float dps[16 * 64];
+  using St = Stage<N, R, V>;
+  constexpr int CN = N / 8, CR = R / 8, CV = V / 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t stages[kStages][St::kElems];
+  __shared__ __attribute__((aligned(1024))) float xch[2][4][16 * 64];   // [p, dp][group] score blocks
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int g4 = wave & 3, second = wave >> 2;   // token group, which of its two waves
   const int nb = gridDim.x, G = nb * gridDim.y;
   int lin = blockIdx.x + nb * blockIdx.y;
-  if (G % 8 == 0) lin = (lin % 8) * (G / 8) + lin / 8;
-  const int h = lin / nb, b0 = (lin % nb) * BB;
-  const int b1 = min(b0 + BB, a.T) - 1;
+  if (G % 8 == 0) lin = (lin % 8) * (G / 8) + lin / 8;   // each XCD runs whole heads
+  const int h = lin / nb, b0 = (lin % nb) * kWB;
+  const int b_end = min(b0 + kWB, a.T);
+  const int own0 = b0 + 32 * g4;                          // the group's 32 owned tokens
+  const int own = own0 + (lane & 31);
+  const float c2 = a.scale * kLog2e;
+  const bool nocausal = !a.causal;
   int lo0, hi0, lo1, hi1;
   doc_of(a, b0, lo0, hi0);
-  doc_of(a, b1, lo1, hi1);
+  doc_of(a, b_end - 1, lo1, hi1);
 
-  // ---- phase 1: dk, dv of key block b0
+  // Issue order of a product block, pinned (the scheduler would otherwise put
+  // each LDS read right before its MFMA and wait for it there): `ahead` reads
+  // first, then one MFMA per `per` reads, then the last MFMAs.
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  auto pin = [&](auto n_mfma, auto per, auto ahead) __attribute__((always_inline)) {
+    constexpr int M = decltype(n_mfma)::value, P = decltype(per)::value, A = decltype(ahead)::value;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, A, 0);
+#pragma unroll
+    for (int i = 0; i < M - A / P; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, P, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < A / P; ++i) __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  auto settle = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The second waves issue all transfers, kBatch per wave and step (steps
+  // past the end issue empty ones), in the time they would otherwise wait for
+  // p. When step t starts, the batches of steps t+1 .. t+kStages-2 are the
+  // only ones issued after its own: waiting until at most that many transfers
+  // are pending means step t's have landed (the first waves have none pending).
+  constexpr int kBatch = 6;
+  constexpr int kPend = kBatch * (kStages - 2);
+  static_assert(kPend < 64, "vmcnt field");
+  auto wait_stage = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((kPend & 15) | ((kPend >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();         // every wave's transfers landed; stage (t-1) % kStages is free
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the empty transfer that evens out a wave's batch in phase 2 (it writes
+  // zeros over the stage's lse / D slots, which phase 2 does not read)
+  auto pad_transfer = [&](uint32_t base) __attribute__((always_inline)) {
+    const u32x4 r0 = dma_rsrc(a.kr, 0);
+    if (lane < 16) dma16(r0, base + 2 * St::kLse, static_cast<uint32_t>(16 * lane));
+  };
+
+  // ---- phase 1: dv (first waves) and dk (second waves) of keys own0 .. own0+31
   {
-    constexpr int KP = K + 8, VP = V + 8;
-    uint16_t *const Qs = lds, *const Os = Qs + BB * KP, *const Ps = Os + BB * VP, *const Ss = Ps + BB * TP;
     const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? b0 : lo0);
     const int qend = __builtin_amdgcn_readfirstlane(hi1);
-    if (wave == 0) {
-      bf16x8 kf[K / 16], qf[K / 16];
-      float lse_n = 0.f, D_n = 0.f;
-      auto rows_terms = [&](int q0) {
-        const int q = q0 + (lane & 31);
-        const int64_t i = static_cast<int64_t>(h) * a.T + (q < a.T ? q : 0);
-        lse_n = a.lse[i];
-        D_n = a.Dws[i];
-      };
-      load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, b0, a.T, kf, lane);
-      if constexpr (R > 0) load_frags<R>(a.kr, a.kr_st, b0, a.T, kf + N / 16, lane);
-      if (qbeg < qend) {
-        load_frags<K>(a.q + h * a.q_sh, a.q_st, qbeg, a.T, qf, lane);
-        rows_terms(qbeg);
+    // six transfers per second wave: the q rows and band, the dout rows, lse
+    // and D; rows at or past qend are never visible and read zero
+    auto issue = [&](int stg, int q0) __attribute__((always_inline)) {
+      const int ws = wave - 4;
+      const uint32_t rows = static_cast<uint32_t>(max(0, min(kSB, qend - q0)));
+      const uint16_t *qrow = a.q + static_cast<int64_t>(q0) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
+      const uint16_t *grow = a.dout + static_cast<int64_t>(q0) * a.do_st + static_cast<int64_t>(h) * a.do_sh;
+      const u32x4 rq = dma_rsrc(qrow, rows * static_cast<uint32_t>(a.q_st) * 2);
+      const u32x4 rg = dma_rsrc(grow, rows * static_cast<uint32_t>(a.do_st) * 2);
+      const uint32_t base = lds_addr(stages[stg]);
+      stage_part<CN, 4>(rq, base, a.q_st * 2, 0, ws, lane);
+      stage_part<CR, 4>(rq, base + 2 * St::kN, a.q_st * 2, 2 * N, ws, lane);
+      stage_part<CV, 4>(rg, base + 2 * (St::kN + St::kR), a.do_st * 2, 0, ws, lane);
+      // lse (waves 4, 6) and D (waves 5, 7): the two copies write the same bytes
+      const int which = ws & 1;
+      const float *src = (which == 0 ? a.lse : a.Dws) + static_cast<int64_t>(h) * a.T + min(q0, a.T);
+      const u32x4 rl = dma_rsrc(src, rows * 4);
+      if (lane < 8) dma16(rl, base + 2 * St::kLse + 128 * which, static_cast<uint32_t>(16 * lane));
+    };
+    int klo = 1, khi = 0;   // the owned key's document (empty past T)
+    if (own < a.T) doc_of(a, own, klo, khi);
+    const int nst = (qend - qbeg + kSB - 1) / kSB;
+    // The two waves of a group run their own loops (so each holds only its
+    // own registers) with the same barriers in the same order.
+    auto run1 = [&](auto second_c) __attribute__((always_inline)) {
+      constexpr bool SECOND = decltype(second_c)::value;
+      constexpr int NF = SECOND ? V / 16 : K / 16, NT = SECOND ? K / 32 : V / 32;
+      bf16x8 of[NF];   // the owned operand: k (first wave) or v (second wave)
+      if constexpr (!SECOND) {
+        load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, own0, a.T, of, lane);
+        load_frags<R>(a.kr, a.kr_st, own0, a.T, of + N / 16, lane);
+      } else {
+        load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, own0, a.T, of, lane);
       }
-      f32x16 dk[KS] = {};
-      for (int q0 = qbeg; q0 < qend; q0 += BB) {
-        const int q = q0 + (lane & 31);
-        int qlo = 1, qhi = 0;
-        if (q < a.T) doc_of(a, q, qlo, qhi);
-        const float lse2 = lse_n * kLog2e, Dq = D_n;
-        __syncthreads();                                   // (1)
-        store_rows<K>(qf, Qs, KP, lane);
-        f32x16 st = {};
+      f32x16 acc[NT] = {};   // dv (first wave) or dk (second wave)
+      // nothing the compiler tracks may be pending inside the loop (its wait
+      // for one would also drain every transfer in flight)
+      settle();
+      if constexpr (SECOND)
+        if (nst > 0)
 #pragma unroll
-        for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
-        if (q0 + BB < qend) {
-          load_frags<K>(a.q + h * a.q_sh, a.q_st, q0 + BB, a.T, qf, lane);
-          rows_terms(q0 + BB);
-        }
-        __syncthreads();                                   // (2)
-        f32x16 dp;
+          for (int i = 0; i < kStages - 1; ++i) issue(i, qbeg + kSB * i);
+      // every query of a step lies in every owned key's document when it lies in
+      // the last key's document start and the first key's document end
+      const int vis_lo = __builtin_amdgcn_readlane(klo, 31), vis_hi = __builtin_amdgcn_readlane(khi, 0);
+      for (int t = 0; t < nst; ++t) {
+        const int q0 = qbeg + kSB * t;
+        wait_stage();
+        const uint16_t *sg = stages[t % kStages];
+        const uint16_t *Qn = sg, *Qr = sg + St::kN, *Gv = sg + St::kN + St::kR;
+        const float *Ls = reinterpret_cast<const float *>(sg + St::kLse), *Ds = Ls + kSB;
+        // nothing visible when the group's keys all follow the step's queries or lie past T
+        const bool idle = own0 >= a.T || (a.causal && q0 + kSB - 1 < own0);
+        // everything visible: no mask to apply
+        const bool full = q0 >= vis_lo && q0 + kSB <= vis_hi && (nocausal || q0 >= own0 + kSB - 1);
+        (void)full;
+        f32x16 s = {};
+        if constexpr (!SECOND) {   // s = q k^T, then p; dv += p^T dout
+          if (!idle) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = dps[r * 64 + lane];
-        probs_t(a, st, dp, b0, q, qlo, qhi, lse2, Dq, lane);
-        store_block(st, Ps, false, lane);   // p^T [key][query]
-        store_block(dp, Ss, false, lane);   // ds^T [key][query]
-        __syncthreads();                                   // (3)
+            for (int k = 0; k < N / 16; ++k) s = mfma32(st_row<CN>(Qn, k, lane), of[k], s);
 #pragma unroll
-        for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 sa = perm_frag(Ss, TP, s, lane);
+            for (int k = 0; k < R / 16; ++k) s = mfma32(st_row<CR>(Qr, k, lane), of[N / 16 + k], s);
+            pin(std::integral_constant<int, K / 16>(), I1(), I4());
+            // registers 4j .. 4j+3 hold queries q0 + 8j + 4(l/32) + 0..3
+            if (full) {
 #pragma unroll
-          for (int kt = 0; kt < KS; ++kt) dk[kt] = mfma32(sa, tr_frag(Qs, KP, s, kt, lane), dk[kt]);
+              for (int j = 0; j < 4; ++j) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + 8 * j + 4 * (lane >> 5));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  s[4 * j + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * j + e], c2, -l4[e] * kLog2e));
+              }
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int qi = 8 * j + 4 * (lane >> 5);
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + qi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int q = q0 + qi + e;
+                  const bool vis = (q >= klo) & (q < khi) & (nocausal | (q >= own));   // no short circuit: no branches
+                  // exp2(-inf) = 0: the mask is a select, not a branch around the exponential
+                  s[4 * j + e] = __builtin_amdgcn_exp2f(vis ? __builtin_fmaf(s[4 * j + e], c2, -l4[e] * kLog2e)
+                                                            : -__builtin_inff());
+                }
+              }
+            }
+            xch_put(xch[0][g4], s, lane);
+          }
+          sync();   // p is in LDS
+          if (!idle) {
+            const bf16x8 pa0 = pack_frag(s, 0), pa1 = pack_frag(s, 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < V / 32; ++d) acc[d] = mfma32(pa0, st_tr<CV>(Gv, 0, d, lane), acc[d]);
+#pragma unroll
+            for (int d = 0; d < V / 32; ++d) acc[d] = mfma32(pa1, st_tr<CV>(Gv, 1, d, lane), acc[d]);
+            pin(std::integral_constant<int, (kSB / 16) * V / 32>(), I2(), I8());
+          }
+        } else {                   // dp = dout v^T; ds = p (dp - D); dk += ds^T q
+          if (!idle) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < V / 16; ++k) s = mfma32(st_row<CV>(Gv, k, lane), of[k], s);
+            pin(std::integral_constant<int, V / 16>(), I1(), I4());
+          }
+          issue((t + kStages - 1) % kStages, q0 + kSB * (kStages - 1));
+          sync();   // p is in LDS
+          if (!idle) {
+            const f32x4 *pb = reinterpret_cast<const f32x4 *>(xch[0][g4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const f32x4 p4 = pb[64 * j + lane];
+              const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Ds + 8 * j + 4 * (lane >> 5));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[4 * j + e] = p4[e] * (s[4 * j + e] - d4[e]);
+            }
+            const bf16x8 sa0 = pack_frag(s, 0), sa1 = pack_frag(s, 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < kSB / 16; ++k) {
+              const bf16x8 sa = k == 0 ? sa0 : sa1;
+#pragma unroll
+              for (int d = 0; d < N / 32; ++d) acc[d] = mfma32(sa, st_tr<CN>(Qn, k, d, lane), acc[d]);
+#pragma unroll
+              for (int d = 0; d < R / 32; ++d)
+                acc[N / 32 + d] = mfma32(sa, st_tr<CR>(Qr, k, d, lane), acc[N / 32 + d]);
+            }
+            pin(std::integral_constant<int, (kSB / 16) * K / 32>(), I2(), I8());
+          }
         }
       }
+      // register r holds key own0 + row_of(r), lane l%32 the column: dv, or dk
+      // scaled (its band part to this head's slice)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = b0 + row_of(r, lane);
+        const int key = own0 + row_of(r, lane);
         if (key >= a.T) continue;
         float *row = a.dkv + (static_cast<int64_t>(key) * a.H + h) * (N + V);
-        float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
+        if constexpr (SECOND) {
+          float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
 #pragma unroll
-        for (int kt = 0; kt < KS; ++kt) {
-          const int c = 32 * kt + (lane & 31);
-          const float g = a.scale * dk[kt][r];
-          if (c < N) row[c] = g;
-          else brow[c - N] = g;
+          for (int d = 0; d < N / 32; ++d) row[32 * d + (lane & 31)] = a.scale * acc[d][r];
+#pragma unroll
+          for (int d = 0; d < R / 32; ++d) brow[32 * d + (lane & 31)] = a.scale * acc[N / 32 + d][r];
+        } else {
+#pragma unroll
+          for (int d = 0; d < V / 32; ++d) row[N + 32 * d + (lane & 31)] = acc[d][r];
         }
       }
-    } else {
-      bf16x8 vf[V / 16], gf[V / 16];
-      load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, b0, a.T, vf, lane);
-      if (qbeg < qend) load_frags<V>(a.dout + h * a.do_sh, a.do_st, qbeg, a.T, gf, lane);
-      f32x16 dv[V / 32] = {}, dk[K / 32 - KS] = {};
-      for (int q0 = qbeg; q0 < qend; q0 += BB) {
-        __syncthreads();                                   // (1)
-        store_rows<V>(gf, Os, VP, lane);
-        f32x16 dp = {};
-#pragma unroll
-        for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
-        if (q0 + BB < qend) load_frags<V>(a.dout + h * a.do_sh, a.do_st, q0 + BB, a.T, gf, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dps[r * 64 + lane] = dp[r];
-        __syncthreads();                                   // (2)
-        __syncthreads();                                   // (3)
-#pragma unroll
-        for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 pa = perm_frag(Ps, TP, s, lane), sa = perm_frag(Ss, TP, s, lane);
-#pragma unroll
-          for (int vt = 0; vt < V / 32; ++vt) dv[vt] = mfma32(pa, tr_frag(Os, VP, s, vt, lane), dv[vt]);
-#pragma unroll
-          for (int kt = KS; kt < K / 32; ++kt)
-            dk[kt - KS] = mfma32(sa, tr_frag(Qs, KP, s, kt, lane), dk[kt - KS]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = b0 + row_of(r, lane);
-        if (key >= a.T) continue;
-        float *row = a.dkv + (static_cast<int64_t>(key) * a.H + h) * (N + V);
-        float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
-#pragma unroll
-        for (int kt = KS; kt < K / 32; ++kt) {
-          const int c = 32 * kt + (lane & 31);
-          const float g = a.scale * dk[kt - KS][r];
-          if (c < N) row[c] = g;
-          else brow[c - N] = g;
-        }
-#pragma unroll
-        for (int vt = 0; vt < V / 32; ++vt) row[N + 32 * vt + (lane & 31)] = dv[vt][r];
-      }
-    }
+    };
+    if (second) run1(std::true_type());
+    else run1(std::false_type());
   }
-  __syncthreads();   // phase 1's readers are done with the LDS
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // the trailing (empty) transfers landed
+  __syncthreads();                      // and every wave is done with the stages
 
-  // ---- phase 2: dq of query block b0
+  // ---- phase 2: dq of queries own0 .. own0+31, tiles 0-2 (first wave) and 3-5 (second)
   {
-    constexpr int KP = K + 8;
-    uint16_t *const Ks = lds, *const Ss = Ks + BB * KP;
     const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
-    const int kend = __builtin_amdgcn_readfirstlane(a.causal ? b1 + 1 : hi1);
-    if (wave == 0) {
-      bf16x8 kf[K / 16], qf[K / 16];
-      load_frags<K>(a.q + h * a.q_sh, a.q_st, b0, a.T, qf, lane);
-      auto load_k = [&](int k0) {
-        load_frags<N>(a.kv + h * a.kv_sh, a.kv_st, k0, a.T, kf, lane);
-        if constexpr (R > 0) load_frags<R>(a.kr, a.kr_st, k0, a.T, kf + N / 16, lane);
-      };
-      if (kbeg < kend) load_k(kbeg);
-      const int q = b0 + (lane & 31);
-      int qlo = 1, qhi = 0;
-      float lse2 = 0.f, Dq = 0.f;
-      if (q < a.T) {
-        doc_of(a, q, qlo, qhi);
-        lse2 = a.lse[static_cast<int64_t>(h) * a.T + q] * kLog2e;
-        Dq = a.Dws[static_cast<int64_t>(h) * a.T + q];
-      }
-      f32x16 dq[KS] = {};
-      for (int k0 = kbeg; k0 < kend; k0 += BB) {
-        __syncthreads();                                   // (1)
-        store_rows<K>(kf, Ks, KP, lane);
-        f32x16 st = {};
-#pragma unroll
-        for (int s = 0; s < K / 16; ++s) st = mfma32(kf[s], qf[s], st);
-        if (k0 + BB < kend) load_k(k0 + BB);
-        __syncthreads();                                   // (2)
-        f32x16 dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = dps[r * 64 + lane];
-        probs_t(a, st, dp, k0, q, qlo, qhi, lse2, Dq, lane);
-        store_block(dp, Ss, true, lane);   // ds [query][key]
-        __syncthreads();                                   // (3)
-#pragma unroll
-        for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 sa = perm_frag(Ss, TP, s, lane);
-#pragma unroll
-          for (int kt = 0; kt < KS; ++kt) dq[kt] = mfma32(sa, tr_frag(Ks, KP, s, kt, lane), dq[kt]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = b0 + row_of(r, lane);
-        if (t >= a.T) continue;
-        float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K;
-#pragma unroll
-        for (int kt = 0; kt < KS; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt][r];
-      }
-    } else {
-      bf16x8 vf[V / 16], gf[V / 16];
-      load_frags<V>(a.dout + h * a.do_sh, a.do_st, b0, a.T, gf, lane);
-      if (kbeg < kend) load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, kbeg, a.T, vf, lane);
-      f32x16 dq[K / 32 - KS] = {};
-      for (int k0 = kbeg; k0 < kend; k0 += BB) {
-        __syncthreads();                                   // (1)
-        f32x16 dp = {};
-#pragma unroll
-        for (int s = 0; s < V / 16; ++s) dp = mfma32(vf[s], gf[s], dp);
-        if (k0 + BB < kend) load_frags<V>(a.kv + h * a.kv_sh + N, a.kv_st, k0 + BB, a.T, vf, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dps[r * 64 + lane] = dp[r];
-        __syncthreads();                                   // (2)
-        __syncthreads();                                   // (3)
-#pragma unroll
-        for (int s = 0; s < BB / 16; ++s) {
-          const bf16x8 sa = perm_frag(Ss, TP, s, lane);
-#pragma unroll
-          for (int kt = KS; kt < K / 32; ++kt)
-            dq[kt - KS] = mfma32(sa, tr_frag(Ks, KP, s, kt, lane), dq[kt - KS]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = b0 + row_of(r, lane);
-        if (t >= a.T) continue;
-        float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K;
-#pragma unroll
-        for (int kt = KS; kt < K / 32; ++kt) row[32 * kt + (lane & 31)] = a.scale * dq[kt - KS][r];
-      }
+    const int kend = __builtin_amdgcn_readfirstlane(a.causal ? b_end : hi1);
+    // five transfers per second wave (k rows, band, v rows) and an empty one
+    auto issue = [&](int stg, int k0) __attribute__((always_inline)) {
+      const int ws = wave - 4;
+      const uint32_t rows = static_cast<uint32_t>(max(0, min(kSB, kend - k0)));
+      const uint16_t *krow = a.kv + static_cast<int64_t>(k0) * a.kv_st + static_cast<int64_t>(h) * a.kv_sh;
+      const u32x4 rk = dma_rsrc(krow, rows * static_cast<uint32_t>(a.kv_st) * 2);
+      const u32x4 rr = dma_rsrc(a.kr + static_cast<int64_t>(k0) * a.kr_st, rows * static_cast<uint32_t>(a.kr_st) * 2);
+      const uint32_t base = lds_addr(stages[stg]);
+      stage_part<CN, 4>(rk, base, a.kv_st * 2, 0, ws, lane);
+      stage_part<CR, 4>(rr, base + 2 * St::kN, a.kr_st * 2, 0, ws, lane);
+      stage_part<CV, 4>(rk, base + 2 * (St::kN + St::kR), a.kv_st * 2, 2 * N, ws, lane);
+      pad_transfer(base);
+    };
+    int qlo = 1, qhi = 0;
+    float lse2 = 0.f, Dq = 0.f;
+    if (own < a.T) {
+      doc_of(a, own, qlo, qhi);
+      lse2 = a.lse[static_cast<int64_t>(h) * a.T + own] * kLog2e;
+      Dq = a.Dws[static_cast<int64_t>(h) * a.T + own];
     }
+    const int nst = (kend - kbeg + kSB - 1) / kSB;
+    auto run2 = [&](auto second_c) __attribute__((always_inline)) {
+      constexpr bool SECOND = decltype(second_c)::value;
+      constexpr int NF = SECOND ? V / 16 : K / 16;
+      bf16x8 of[NF];   // the owned operand: q (first wave) or dout (second wave)
+      if constexpr (!SECOND) load_frags<K>(a.q + h * a.q_sh, a.q_st, own0, a.T, of, lane);
+      else load_frags<V>(a.dout + h * a.do_sh, a.do_st, own0, a.T, of, lane);
+      f32x16 dq[3] = {};   // dq tiles 0-2 (first wave) or 3-5 (second wave)
+      settle();
+      if constexpr (SECOND)
+        if (nst > 0)
+#pragma unroll
+          for (int i = 0; i < kStages - 1; ++i) issue(i, kbeg + kSB * i);
+      // every key of a step lies in every owned query's document (see phase 1)
+      const int vis_lo = __builtin_amdgcn_readlane(qlo, 31), vis_hi = __builtin_amdgcn_readlane(qhi, 0);
+      for (int t = 0; t < nst; ++t) {
+        const int k0 = kbeg + kSB * t;
+        wait_stage();
+        const uint16_t *sg = stages[t % kStages];
+        const uint16_t *Kn = sg, *Kr = sg + St::kN, *Vv = sg + St::kN + St::kR;
+        // nothing visible when the step's keys all follow the group's queries or the queries lie past T
+        const bool idle = own0 >= a.T || (a.causal && k0 > own0 + 31);
+        const bool full = k0 >= vis_lo && k0 + kSB <= vis_hi && (nocausal || k0 + kSB - 1 <= own0);
+        f32x16 s = {};
+        if (!idle) {
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (!SECOND) {   // s^T = k q^T, then p^T
+#pragma unroll
+            for (int k = 0; k < N / 16; ++k) s = mfma32(st_row<CN>(Kn, k, lane), of[k], s);
+#pragma unroll
+            for (int k = 0; k < R / 16; ++k) s = mfma32(st_row<CR>(Kr, k, lane), of[N / 16 + k], s);
+            pin(std::integral_constant<int, K / 16>(), I1(), I4());
+            if (full) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = k0 + row_of(r, lane);
+                const bool vis = (key >= qlo) & (key < qhi) & (nocausal | (key <= own));
+                s[r] = __builtin_amdgcn_exp2f(vis ? __builtin_fmaf(s[r], c2, -lse2) : -__builtin_inff());
+              }
+            }
+          } else {                   // dp^T = v dout^T
+#pragma unroll
+            for (int k = 0; k < V / 16; ++k) s = mfma32(st_row<CV>(Vv, k, lane), of[k], s);
+            pin(std::integral_constant<int, V / 16>(), I1(), I4());
+          }
+          xch_put(xch[SECOND ? 1 : 0][g4], s, lane);
+        }
+        if constexpr (SECOND) issue((t + kStages - 1) % kStages, k0 + kSB * (kStages - 1));
+        sync();   // p^T and dp^T are in LDS
+        if (!idle) {
+          // ds = p (dp - D), with the other wave's half of the pair
+          const f32x4 *ob = reinterpret_cast<const f32x4 *>(xch[SECOND ? 0 : 1][g4]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 o4 = ob[64 * j + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e;
+              s[r] = SECOND ? o4[e] * (s[r] - Dq) : s[r] * (o4[e] - Dq);
+            }
+          }
+          const bf16x8 sa0 = pack_frag(s, 0), sa1 = pack_frag(s, 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int k = 0; k < kSB / 16; ++k) {
+            const bf16x8 sa = k == 0 ? sa0 : sa1;
+            if constexpr (!SECOND) {
+#pragma unroll
+              for (int d = 0; d < 3; ++d) dq[d] = mfma32(sa, st_tr<CN>(Kn, k, d, lane), dq[d]);
+            } else {
+              dq[0] = mfma32(sa, st_tr<CN>(Kn, k, 3, lane), dq[0]);
+#pragma unroll
+              for (int d = 0; d < R / 32; ++d) dq[1 + d] = mfma32(sa, st_tr<CR>(Kr, k, d, lane), dq[1 + d]);
+            }
+          }
+          pin(std::integral_constant<int, (kSB / 16) * 3>(), I2(), I8());
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = own0 + row_of(r, lane);
+        if (t >= a.T) continue;
+        float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K + (SECOND ? 96 : 0);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) row[32 * d + (lane & 31)] = a.scale * dq[d][r];
+      }
+    };
+    if (second) run2(std::true_type());
+    else run2(std::false_type());
   }
 }
 
@@ -832,8 +985,8 @@ int run(const BwdArgs &a, hipStream_t s) {
   static_assert(R % 4 == 0, "the band sum moves four elements per thread");
   const unsigned rows = static_cast<unsigned>((static_cast<int64_t>(a.T) * a.H * 16 + 255) / 256);
   row_term_kernel<<<rows, 256, 0, s>>>(a, V);
-  const dim3 grid(static_cast<unsigned>((a.T + BB - 1) / BB), static_cast<unsigned>(a.H));
-  attn_bwd_kernel<N, R, V><<<grid, 128, 0, s>>>(a);
+  const dim3 grid(static_cast<unsigned>((a.T + kWB - 1) / kWB), static_cast<unsigned>(a.H));
+  attn_bwd8_kernel<N, R, V><<<grid, 512, 0, s>>>(a);
   const unsigned sums = static_cast<unsigned>((static_cast<int64_t>(a.T) * R / 4 + 255) / 256);
   if (R > 0) band_sum_kernel<<<sums, 256, 0, s>>>(a, R);
   return hipGetLastError();

@@ -49,9 +49,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 static_assert(DT == 16 * SPLIT_WAVES && DL == 128 * SPLIT_WAVES, "split work division");
 static_assert(KS * (DEPTH - 1) < 64, "vmcnt field");
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 // Latent rows in LDS are unpadded 1 KB rows of 64 sixteen-byte chunks; chunk
 // c of row r sits at c ^ kswz(r). The writes (one chunk of 16 rows per lane
 // group) and the transposing reads (two neighbouring chunks of four

@@ -38,32 +38,8 @@ static_assert(kDmaPerSlice < 16, "vmcnt field");
 static_assert(GM / 2 * GN <= A_E, "half the output tile fits one A buffer");
 constexpr uint32_t kOob = 0x80000000u;            // a byte offset past every buffer range
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 __device__ __forceinline__ int a_swz(int m) { return (m ^ (m >> 3)) & 7; }            // 8 chunks per row
 __device__ __forceinline__ int b_swz(int k) { return (k & 2) | ((k & 1) * 5); }       // 8 segments per row
-
-// Buffer resource as four scalar dwords.
-__device__ __forceinline__ u32x4 dma_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = static_cast<uint32_t>(b), hi = static_cast<uint32_t>(b >> 32) & 0xffffu;
-  return u32x4{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lo)),
-               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(hi)),
-               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), static_cast<uint32_t>(kBufferDword3)};
-}
-// One 1 KB global->LDS transfer of a wave (lane l: 16 bytes at byte voff of
-// the buffer, zero outside its range, to lds_dst + 16 l). Inline assembly so
-// the compiler does not track it: completion is awaited explicitly with
-// vmcnt before the barrier that publishes the slice.
-__device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds_dst, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds_dst));
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
-      static_cast<int>(reinterpret_cast<uintptr_t>((lds_void *)(p)))));
-}
 
 // Slab-layout output (the projection written straight into the token->head
 // pack): column n of the projection is element n % P of head n / P's block;
