@@ -272,11 +272,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
   // only ones issued after its own: waiting until at most that many transfers
   // are pending means step t's have landed (the first waves have none pending).
   constexpr int kBatch = 6;
-  constexpr int kPend = kBatch * (kStages - 2);
-  static_assert(kPend < 64, "vmcnt field");
-  auto wait_stage = [&]() __attribute__((always_inline)) {
+  using Pend1 = std::integral_constant<int, kBatch * (kStages - 2)>;
+  auto wait_stage = [&](auto pend_c) __attribute__((always_inline)) {
+    constexpr int P = decltype(pend_c)::value;   // this wave's transfers of the later batches
+    static_assert(P < 64, "vmcnt field");
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((kPend & 15) | ((kPend >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((P & 15) | ((P >> 4) << 14) | (7 << 4) | (15 << 8));
     __builtin_amdgcn_s_barrier();         // every wave's transfers landed; stage (t-1) % kStages is free
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
       const int vis_lo = __builtin_amdgcn_readlane(klo, 31), vis_hi = __builtin_amdgcn_readlane(khi, 0);
       for (int t = 0; t < nst; ++t) {
         const int q0 = qbeg + kSB * t;
-        wait_stage();
+        wait_stage(Pend1());
         const uint16_t *sg = stages[t % kStages];
         const uint16_t *Qn = sg, *Qr = sg + St::kN, *Gv = sg + St::kN + St::kR;
         const float *Ls = reinterpret_cast<const float *>(sg + St::kLse), *Ds = Ls + kSB;
@@ -454,18 +455,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
   {
     const int kbeg = __builtin_amdgcn_readfirstlane(lo0);
     const int kend = __builtin_amdgcn_readfirstlane(a.causal ? b_end : hi1);
-    // five transfers per second wave (k rows, band, v rows) and an empty one
+    // the second waves move the k and v rows (four transfers each), the first
+    // waves the band and an empty transfer (two each), in the time each would
+    // otherwise wait for the other's half of the pair
     auto issue = [&](int stg, int k0) __attribute__((always_inline)) {
-      const int ws = wave - 4;
+      const int ws = wave & 3;
       const uint32_t rows = static_cast<uint32_t>(max(0, min(kSB, kend - k0)));
       const uint16_t *krow = a.kv + static_cast<int64_t>(k0) * a.kv_st + static_cast<int64_t>(h) * a.kv_sh;
       const u32x4 rk = dma_rsrc(krow, rows * static_cast<uint32_t>(a.kv_st) * 2);
       const u32x4 rr = dma_rsrc(a.kr + static_cast<int64_t>(k0) * a.kr_st, rows * static_cast<uint32_t>(a.kr_st) * 2);
       const uint32_t base = lds_addr(stages[stg]);
-      stage_part<CN, 4>(rk, base, a.kv_st * 2, 0, ws, lane);
-      stage_part<CR, 4>(rr, base + 2 * St::kN, a.kr_st * 2, 0, ws, lane);
-      stage_part<CV, 4>(rk, base + 2 * (St::kN + St::kR), a.kv_st * 2, 2 * N, ws, lane);
-      pad_transfer(base);
+      if (second) {
+        stage_part<CN, 4>(rk, base, a.kv_st * 2, 0, ws, lane);
+        stage_part<CV, 4>(rk, base + 2 * (St::kN + St::kR), a.kv_st * 2, 2 * N, ws, lane);
+      } else {
+        stage_part<CR, 4>(rr, base + 2 * St::kN, a.kr_st * 2, 0, ws, lane);
+        pad_transfer(base);
+      }
     };
     int qlo = 1, qhi = 0;
     float lse2 = 0.f, Dq = 0.f;
@@ -483,15 +489,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
       else load_frags<V>(a.dout + h * a.do_sh, a.do_st, own0, a.T, of, lane);
       f32x16 dq[3] = {};   // dq tiles 0-2 (first wave) or 3-5 (second wave)
       settle();
-      if constexpr (SECOND)
-        if (nst > 0)
+      if (nst > 0)
 #pragma unroll
-          for (int i = 0; i < kStages - 1; ++i) issue(i, kbeg + kSB * i);
+        for (int i = 0; i < kStages - 1; ++i) issue(i, kbeg + kSB * i);
+      using Pend2 = std::integral_constant<int, (SECOND ? 4 : 2) * (kStages - 2)>;
       // every key of a step lies in every owned query's document (see phase 1)
       const int vis_lo = __builtin_amdgcn_readlane(qlo, 31), vis_hi = __builtin_amdgcn_readlane(qhi, 0);
       for (int t = 0; t < nst; ++t) {
         const int k0 = kbeg + kSB * t;
-        wait_stage();
+        wait_stage(Pend2());
         const uint16_t *sg = stages[t % kStages];
         const uint16_t *Kn = sg, *Kr = sg + St::kN, *Vv = sg + St::kN + St::kR;
         // nothing visible when the step's keys all follow the group's queries or the queries lie past T
@@ -524,7 +530,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
           }
           xch_put(xch[SECOND ? 1 : 0][g4], s, lane);
         }
-        if constexpr (SECOND) issue((t + kStages - 1) % kStages, k0 + kSB * (kStages - 1));
+        issue((t + kStages - 1) % kStages, k0 + kSB * (kStages - 1));
         sync();   // p^T and dp^T are in LDS
         if (!idle) {
           // ds = p (dp - D), with the other wave's half of the pair
@@ -555,6 +561,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
           pin(std::integral_constant<int, (kSB / 16) * 3>(), I2(), I8());
         }
       }
+      // the trailing (empty) transfers land before the workgroup gives up its LDS
+      __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = own0 + row_of(r, lane);
