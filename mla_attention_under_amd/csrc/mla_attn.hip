@@ -153,26 +153,28 @@ __device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T, int T_
 constexpr int kRecFloats = 4 * (4 * 16 + 2) * 64;   // 4 query blocks x (64 O + m + l) x 64 lanes
 
 // normalise the state of query block qb of the tile starting at q0 and store
-// it. The lane layout (a lane holds 8-byte pieces of one query row) goes
-// through the wave's own free stage buffer xs, so every query row leaves as
-// 16 whole 16-byte chunks, streamed past L2 with nontemporal stores (no dirty
-// lines left for the end-of-kernel write-back).
-template <int DBLK>
+// its columns [col0, col0 + 32 NDB) from o[0 .. NDB). The lane layout (a lane
+// holds 8-byte pieces of one query row) goes through the wave's own free
+// stage region xs, so every query row leaves as whole 16-byte chunks, streamed
+// past L2 with nontemporal stores (no dirty lines left for the end-of-kernel
+// write-back). The wave of key half 0 also writes the row's log-sum-exp.
+template <int NDB, int DBLK>
 __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[DBLK], float m_run, float l_run,
-                                           int h, int q0, int q_end, int qb, int lane, uint16_t *xs) {
-  constexpr int XLD = 32 * DBLK + 8;   // padded row of xs (bf16)
+                                           int h, int q0, int q_end, int qb, int lane, uint16_t *xs, int col0,
+                                           bool write_lse) {
+  constexpr int XLD = 32 * NDB + 8;   // padded row of xs (bf16)
   const int half = lane >> 5, row = lane & 31;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int d = 0; d < DBLK; ++d)
+  for (int d = 0; d < NDB; ++d)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       *reinterpret_cast<u32x2 *>(xs + row * XLD + 32 * d + 8 * g + 4 * half) =
           u32x2{pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
                 pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
   // one wave writes and reads xs, and its LDS accesses complete in order
-  constexpr int CPR = 32 * DBLK / 8;   // 16-byte chunks per output row
+  constexpr int CPR = 32 * NDB / 8;   // 16-byte chunks per stored row piece
   const int rsub = lane / CPR, c = lane % CPR;
 #pragma unroll
   for (int i = 0; i < 32 * CPR / 64; ++i) {
@@ -181,10 +183,10 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
     const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + rr * XLD + 8 * c);
     if (qi < q_end)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(a.out + static_cast<int64_t>(qi) * a.o_st +
-                                                               static_cast<int64_t>(h) * a.o_sh + 8 * c));
+                                                               static_cast<int64_t>(h) * a.o_sh + col0 + 8 * c));
   }
   const int qi = q0 + 32 * qb + row;
-  if (a.lse != nullptr && half == 0 && qi < q_end)
+  if (write_lse && a.lse != nullptr && half == 0 && qi < q_end)
     a.lse[static_cast<int64_t>(h) * a.T + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
 }
 
@@ -355,16 +357,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
                                                  : 2 * (KN_E + kkey * R + 8 * ((cidx - 2 * NSTEPS) ^ kr_swz(kkey))));
   }
   const int vrow0 = 32 * kh + 4 * (grp >> 1) + (gl >> 2);   // first V row of the transposing reads
+  // Register block d of the output (o[d]) holds column block dblk_of(d): the
+  // wave of key half 1 runs the blocks rotated by half, so that after the key
+  // halves merge every wave keeps o[0 .. DBLK/2) (its columns) and hands
+  // o[DBLK/2 ..) to its partner with compile-time register indices only (a
+  // run-time index into o would move o to scratch memory).
+  auto dblk_of = [&](int d) { return (d + (DBLK / 2) * kh) % DBLK; };
   const float c = a.scale_log2;
 
   f32x16 o[DBLK];
   float m_run, l_run;
   bf16x8 qf[KSTEPS];   // Q^T fragments of the current segment's query block
   // ---- a split tile's partial state, stored past this XCD's L2. A lane's
-  // 2*DBLK*8+1 float pairs (O^T pieces, then (m, l)) leave as 8-byte
+  // DBLK*8+1 float pairs (O^T pieces, then (m, l)) leave as 8-byte
   // agent-scope stores; pair i of lane l sits at float 128 i + 2 l of its
-  // query block's record.
-  constexpr int RPAIRS = DBLK * 8 + 1;
+  // query block's record. After the key halves merge, the wave of key half kh
+  // keeps column blocks 2 kh and 2 kh + 1 of its query block (in o[0], o[1]):
+  // it stores, publishes and reads pairs [OWN kh, OWN kh + OWN) and (m, l).
+  constexpr int DOWN = DBLK / 2;          // column blocks a wave keeps
+  constexpr int OWN = DOWN * 8;           // their float pairs
+  constexpr int ML = DBLK * 8;            // the (m, l) pair
+  static_assert(DBLK % 2 == 0, "column blocks split between the key halves");
   auto rec_of = [&](int slot, int role) {
     return reinterpret_cast<unsigned long long *>(a.part + static_cast<int64_t>(slot) * (2 * kRecFloats) +
                                                   role * kRecFloats + qb * REC * 64) + lane;
@@ -376,7 +389,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // arriving, and its merging waves load the other record while the key
   // halves merge.
   __shared__ int early_second;
-  unsigned long long other[RPAIRS];
+  unsigned long long other[OWN + 1];   // this wave's pairs of the other record, then (m, l)
+  // this wave's pairs of a record: its own column blocks, then (m, l)
+  auto load_own = [&](const unsigned long long *rec, unsigned long long (&v)[OWN + 1]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < OWN; ++i)
+      v[i] = __hip_atomic_load(rec + 64 * (OWN * kh + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v[OWN] = __hip_atomic_load(rec + 64 * ML, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // the stage region this wave stores its rows through (its half of its query
+  // block's merge buffer, which only it reads after the merge)
+  uint16_t *const xs_wave = xs_own + kh * (DOWN * 4 * 64 * 8);
   bool early = false;
 
   // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
@@ -475,7 +498,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(kb) + koff[ks]);
       };
       auto vread = [&](int b, int d) {
-        const int dcol = 32 * d + 16 * (grp & 1) + 4 * (gl & 3);
+        const int dcol = 32 * dblk_of(d) + 16 * (grp & 1) + 4 * (gl & 3);
         const int r0 = vrow0 + 16 * b, r1 = r0 + 8;
         const s16x4 lo = read_tr(vprev + r0 * V + 16 * ((dcol >> 4) ^ v_swz(r0)) + (dcol & 15));
         const s16x4 hi = read_tr(vprev + r1 * V + 16 * ((dcol >> 4) ^ v_swz(r1)) + (dcol & 15));
@@ -680,77 +703,79 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     }
 
     // merge the two key halves of each query block through LDS in one round
-    // (every stage buffer is free): query block b's O^T in 16-byte pieces in
-    // kb0 / kb1 / kb2 / vb0, the (m, l) pairs in vb1. The next segment's first
-    // barrier keeps its transfers off these buffers until the reads are done.
+    // (every stage buffer is free). The wave of key half kh keeps column
+    // blocks 2 kh, 2 kh + 1 and hands the other two to its partner: query
+    // block b's O^T pieces in 16-byte pieces in kb0 / kb1 / kb2 / vb0 (blocks
+    // 0-1 in the first 8 KB, 2-3 in the next), the (m, l) pairs in vb1. Both
+    // waves form the same (m, l), key half 0's term first. The next segment's
+    // first barrier keeps its transfers off these buffers until the reads are
+    // done.
     {
       f32x4 *xo = reinterpret_cast<f32x4 *>(xs_own);
-      f32x2_t *xml = reinterpret_cast<f32x2_t *>(vb1) + 64 * qb;
-      if (kh == 1) {
+      f32x2_t *xml = reinterpret_cast<f32x2_t *>(vb1) + 128 * qb;
+      // o[DOWN ..] hold the partner's column blocks (see dblk_of)
+      const int dx = DOWN * (1 - kh);   // first column block handed over
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d)
+      for (int d = 0; d < DOWN; ++d)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            xo[(4 * d + g) * 64 + lane] = f32x4{o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2], o[d][4 * g + 3]};
-        xml[lane] = f32x2_t{m_run, l_run};
-      }
+        for (int g = 0; g < 4; ++g)
+          xo[(4 * (dx + d) + g) * 64 + lane] =
+              f32x4{o[DOWN + d][4 * g], o[DOWN + d][4 * g + 1], o[DOWN + d][4 * g + 2], o[DOWN + d][4 * g + 3]};
+      xml[64 * kh + lane] = f32x2_t{m_run, l_run};
       if (probe != nullptr && tid == 0) early_second = flag_seen == ((a.epoch << 1) | 1ull);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();
       if (probe != nullptr) early = __builtin_amdgcn_readfirstlane(early_second) != 0;
-      if (early && kh == 0) {
+      if (early) load_own(other_rec, other);
+      const f32x2_t ml = xml[64 * (1 - kh) + lane];
+      const float m0 = kh == 0 ? m_run : ml.x, l0 = kh == 0 ? l_run : ml.y;   // key half 0
+      const float m1 = kh == 0 ? ml.x : m_run, l1 = kh == 0 ? ml.y : l_run;   // key half 1
+      const float mn = fmaxf(m0, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m0 - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+      const float a_own = kh == 0 ? a0 : a1, a_oth = kh == 0 ? a1 : a0;
+      l_run = l0 * a0 + l1 * a1;
+      m_run = mn;
 #pragma unroll
-        for (int i = 0; i < RPAIRS; ++i)
-          other[i] = __hip_atomic_load(other_rec + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (kh == 0) {
-        const f32x2_t ml = xml[lane];
-        const float m1 = ml.x, l1 = ml.y;
-        const float mn = fmaxf(m_run, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-        l_run = l_run * a0 + l1 * a1;
-        m_run = mn;
+      for (int d = 0; d < DOWN; ++d)
 #pragma unroll
-        for (int d = 0; d < DBLK; ++d)
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = xo[(4 * (DOWN * kh + d) + g) * 64 + lane];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v = xo[(4 * d + g) * 64 + lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[d][4 * g + e] = o[d][4 * g + e] * a0 + v[e] * a1;
-          }
-      }
+          for (int e = 0; e < 4; ++e) o[d][4 * g + e] = o[d][4 * g + e] * a_own + v[e] * a_oth;
+        }
     }
   };
 
   auto publish = [&](int slot, int role) {
-    if (kh != 0) return;
     unsigned long long *rec = rec_of(slot, role);
     auto put = [&](int i, float x, float y) {
       __hip_atomic_store(rec + 64 * i, (static_cast<unsigned long long>(__float_as_uint(y)) << 32) | __float_as_uint(x),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+    for (int d = 0; d < DOWN; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) put(d * 8 + r / 2, o[d][r], o[d][r + 1]);
-    put(DBLK * 8, m_run, l_run);
+      for (int r = 0; r < 16; r += 2) put(OWN * kh + d * 8 + r / 2, o[d][r], o[d][r + 1]);
+    if (kh == 0) put(ML, m_run, l_run);
   };
-  // ---- the merging waves combine their own state with the other record
-  // (RPAIRS pairs in v) and store the rows of split tile qt
-  auto combine_store = [&](const unsigned long long (&v)[RPAIRS], int qt) __attribute__((always_inline)) {
-    const float m1 = __uint_as_float(static_cast<unsigned>(v[DBLK * 8]));
-    const float l1 = __uint_as_float(static_cast<unsigned>(v[DBLK * 8] >> 32));
+  // ---- every wave combines its own state with its pairs of the other record
+  // (its column blocks' pairs, then (m, l), in v) and stores its columns of
+  // the rows of split tile qt
+  auto combine_store = [&](const unsigned long long (&v)[OWN + 1], int qt) __attribute__((always_inline)) {
+    const float m1 = __uint_as_float(static_cast<unsigned>(v[OWN]));
+    const float l1 = __uint_as_float(static_cast<unsigned>(v[OWN] >> 32));
     const float mn = fmaxf(m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+    for (int d = 0; d < DOWN; ++d)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const unsigned long long x = v[d * 8 + r / 2];
         o[d][r] = o[d][r] * a0 + __uint_as_float(static_cast<unsigned>(x)) * a1;
         o[d][r + 1] = o[d][r + 1] * a0 + __uint_as_float(static_cast<unsigned>(x >> 32)) * a1;
       }
-    store_rows<DBLK>(a, o, mn, l_run * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_own);
+    store_rows<DOWN>(a, o, mn, l_run * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_wave, 32 * DOWN * kh,
+                     kh == 0);
   };
   // ---- after publishing: arrive at the pair's flag; the second arrival
   // combines its own state (still in registers) with the other workgroup's
@@ -772,31 +797,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
     const bool second = __builtin_amdgcn_readfirstlane(second_arrival) != 0;
     if (defer) return second;
-    if (!second || kh != 0) return false;
-    const unsigned long long *r1 = rec_of(slot, 1 - role);
-#pragma unroll
-    for (int i = 0; i < RPAIRS; ++i) other[i] = __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!second) return false;
+    load_own(rec_of(slot, 1 - role), other);
     combine_store(other, qt);
     return false;
   };
   // ---- a deferred second arrival: both records of split tile qt (this
   // workgroup's own is role 0) are combined and stored
   auto merge_records = [&](int slot, int qt) __attribute__((always_inline)) {
-    if (kh != 0) return;
-    const unsigned long long *r0 = rec_of(slot, 0), *r1 = rec_of(slot, 1);
+    unsigned long long mine[OWN + 1];
+    load_own(rec_of(slot, 0), mine);
+    load_own(rec_of(slot, 1), other);
 #pragma unroll
-    for (int i = 0; i < RPAIRS; ++i) other[i] = __hip_atomic_load(r1 + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+    for (int d = 0; d < DOWN; ++d)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const unsigned long long x = __hip_atomic_load(r0 + 64 * (d * 8 + r / 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long x = mine[d * 8 + r / 2];
         o[d][r] = __uint_as_float(static_cast<unsigned>(x));
         o[d][r + 1] = __uint_as_float(static_cast<unsigned>(x >> 32));
       }
-    const unsigned long long ml = __hip_atomic_load(r0 + 64 * (DBLK * 8), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    m_run = __uint_as_float(static_cast<unsigned>(ml));
-    l_run = __uint_as_float(static_cast<unsigned>(ml >> 32));
+    m_run = __uint_as_float(static_cast<unsigned>(mine[OWN]));
+    l_run = __uint_as_float(static_cast<unsigned>(mine[OWN] >> 32));
     combine_store(other, qt);
   };
 
@@ -822,12 +843,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     if (tid == 0)
       __hip_atomic_store(a.flags + __builtin_amdgcn_readfirstlane(pp.slot), a.epoch << 1, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    if (kh == 0) combine_store(other, qt1);
+    combine_store(other, qt1);
   } else if (pp.part) {
     publish(pp.slot, role);
     if (pre) segment(qt2, 0, tiles2, nullptr, nullptr, 1);
-  } else if (kh == 0) {
-    store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_own);
+  } else {
+    store_rows<DOWN>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_wave, 32 * DOWN * kh, kh == 0);
   }
   // a workgroup with a second segment arrives before running it (its state
   // of the split tile is still in registers), so that usually the other
@@ -837,7 +858,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   if (pp.part && !early) deferred = arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1, pre);
   if (qt2 >= 0) {
     segment(qt2, 0, tiles2, nullptr, nullptr, pre ? 2 : 0);
-    if (kh == 0) store_rows<DBLK>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_own);
+    store_rows<DOWN>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_wave, 32 * DOWN * kh, kh == 0);
   }
   if (deferred) merge_records(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
 }
