@@ -200,22 +200,22 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
 // agent-scope fence would write back and invalidate the L2 that the other
 // workgroups of the XCD are reading their K/V tiles from).
 //
-// The flag holds (epoch << 1) | 1 after a first arrival of this call and
-// epoch << 1 after the second; any other value (an earlier call, or memory
-// never used) reads as "nobody yet". The epoch is a 62-bit per-call tag
-// (next_call_tag), so the workspace needs no clearing. Every path through a
-// split tile ends with its flag at epoch << 1 (the early merge of the
-// one-segment workgroup included), so a captured launch replayed with the
-// same epoch finds every flag at "nobody yet" again.
-__device__ __forceinline__ bool arrive(unsigned long long *flag, unsigned long long epoch) {
-  const unsigned long long one = (epoch << 1) | 1ull, done = epoch << 1;
-  unsigned long long cur = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bool second;
-  do {   // lock-free: a failed exchange means the other workgroup's succeeded
-    second = cur == one;
-  } while (!__hip_atomic_compare_exchange_strong(flag, &cur, second ? done : one, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  return second;
+// An arrival is one atomic exchange that leaves (epoch << 1) | 1 ("first
+// arrival of this call") in the flag; the workgroup that gets that value back
+// is second. Any other old value (an earlier call, memory never used, or
+// epoch << 1, "merged") means first. The epoch is a 62-bit per-call tag
+// (next_call_tag), so the workspace needs no clearing. The second arrival
+// marks the pair merged (epoch << 1), and so does the one-segment
+// workgroup's early merge, so every call leaves every split-tile flag at
+// epoch << 1 and a captured launch replayed with the same epoch finds every
+// flag at "nobody yet" again. The exchange's result is needed only when the
+// arriving workgroup is done with its own segments, so the two-segment
+// workgroup issues it without waiting for it.
+__device__ __forceinline__ unsigned long long arrive_swap(unsigned long long *flag, unsigned long long epoch) {
+  return __hip_atomic_exchange(flag, (epoch << 1) | 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void mark_merged(unsigned long long *flag, unsigned long long epoch) {
+  __hip_atomic_store(flag, epoch << 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int N, int R, int V>
@@ -231,8 +231,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = 8;              // waves per workgroup
   constexpr int KN_I = BN * NCH / (64 * NW), KR_I = BN * RCH / (64 * NW), V_I = BN * VCH / (64 * NW);   // DMA instrs per wave
   constexpr int REC = DBLK * 16 + 2; // floats per lane of a wave's softmax state: O, m, l
-  constexpr int kFirstDma = KSTEPS / 2 + 2 * (KN_I + KR_I) + V_I;   // a segment's first transfers per wave
-  static_assert(kFirstDma < 16, "vmcnt field");
   static_assert(N == 128 && R == 64 && V == 128, "swizzles and DMA splits are laid out for 128/64/128");
   static_assert(4 * REC * 64 == kRecFloats, "workspace record size");
   static_assert(REC * 64 * 4 <= (KN_E + KR_E) * 2, "a query block's state fits one K buffer");
@@ -389,6 +387,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // arriving, and its merging waves load the other record while the key
   // halves merge.
   __shared__ int early_second;
+  unsigned long long arrive_old = 0;   // the two-segment workgroup's arrival (its exchange's old value)
   unsigned long long other[OWN + 1];   // this wave's pairs of the other record, then (m, l)
   // this wave's pairs of a record: its own column blocks, then (m, l)
   auto load_own = [&](const unsigned long long *rec, unsigned long long (&v)[OWN + 1]) __attribute__((always_inline)) {
@@ -421,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // starts its first transfers (Q, K_0, V_0, K_1) and leaves the softmax
   // state alone; mode 2 runs a segment whose first transfers mode 1 started.
   auto segment = [&](int qt, int t0, int t1, const unsigned long long *probe, const unsigned long long *other_rec,
-                     int mode) __attribute__((always_inline)) {
+                     int mode, unsigned long long *arrive_flag) __attribute__((always_inline)) {
     const int q0 = doc_lo + qt * BM;
     const int q_end = min(q0 + BM, doc_hi);
     const int kv_hi = a.causal ? min(max(q_end + kshift, kdoc_lo), kdoc_hi) : kdoc_hi;   // keys end (exclusive)
@@ -676,6 +675,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70 | (KN_I + KR_I + V_I));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
+      // every wave's older memory operations are complete here (the counter
+      // retires in issue order), the previous segment's record stores
+      // included: the arrival of the two-segment workgroup
+      if (arrive_flag != nullptr && tid == 0) arrive_old = arrive_swap(arrive_flag, a.epoch);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qbuf + 512 * ks + 8 * lane);
       // every wave holds its Q before step 0's transfers reuse kb2 and vb1
@@ -777,33 +780,28 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     store_rows<DOWN>(a, o, mn, l_run * a0 + l1 * a1, h, doc_lo + qt * BM, doc_hi, qb, lane, xs_wave, 32 * DOWN * kh,
                      kh == 0);
   };
-  // ---- after publishing: arrive at the pair's flag; the second arrival
-  // combines its own state (still in registers) with the other workgroup's
-  // record of split tile qt and stores the rows
-  // (defer: the stage buffers already hold the next segment's first tiles, so
-  // a second arrival only returns true and merges after that segment, see
-  // merge_records)
+  // ---- the one-segment workgroup, after publishing: arrive at the pair's
+  // flag once its record stores are complete; a second arrival combines its
+  // own state (still in registers) with the other workgroup's record of split
+  // tile qt and stores the rows
   __shared__ int second_arrival;
-  auto arrive_and_merge = [&](int slot, int role, int qt, bool defer) __attribute__((always_inline)) {
-    // this wave's record stores are complete: vmcnt(0), or, after the next
-    // segment's first transfers (issued after the stores; the counter
-    // retires in issue order), all but those
-    if (defer)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kFirstDma);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+  const unsigned long long first_mark = (a.epoch << 1) | 1ull;
+  auto arrive_and_merge = [&](int slot, int role, int qt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (tid == 0) second_arrival = arrive(a.flags + slot, a.epoch);
+    if (tid == 0) {
+      const bool sec = arrive_swap(a.flags + slot, a.epoch) == first_mark;
+      if (sec) mark_merged(a.flags + slot, a.epoch);
+      second_arrival = sec;
+    }
     __syncthreads();
-    const bool second = __builtin_amdgcn_readfirstlane(second_arrival) != 0;
-    if (defer) return second;
-    if (!second) return false;
+    if (__builtin_amdgcn_readfirstlane(second_arrival) == 0) return;
     load_own(rec_of(slot, 1 - role), other);
     combine_store(other, qt);
-    return false;
   };
-  // ---- a deferred second arrival: both records of split tile qt (this
-  // workgroup's own is role 0) are combined and stored
+  // ---- the two-segment workgroup arriving second: both records of split
+  // tile qt (its own is role 0) are combined and stored after its second
+  // segment
   auto merge_records = [&](int slot, int qt) __attribute__((always_inline)) {
     unsigned long long mine[OWN + 1];
     load_own(rec_of(slot, 0), mine);
@@ -827,12 +825,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     const bool probe = pp.part && qt2 < 0;
     const int slot = __builtin_amdgcn_readfirstlane(pp.slot);
     segment(qt1, __builtin_amdgcn_readfirstlane(pp.t0), __builtin_amdgcn_readfirstlane(pp.t1),
-            probe ? a.flags + slot : nullptr, probe ? rec_of(slot, 0) : nullptr, 0);
+            probe ? a.flags + slot : nullptr, probe ? rec_of(slot, 0) : nullptr, 0, nullptr);
   }
   const int role = qt2 >= 0 ? 0 : 1;
   // a workgroup with a split tile and a second segment starts the second
-  // segment's first transfers right after its record stores, so that they
-  // land while it arrives (the arrival waits for the stores only)
+  // segment's first transfers right after its record stores and arrives at
+  // that segment's first barrier (see segment)
   const bool pre = pp.part && qt2 >= 0;
   const int tiles2 = qt2 >= 0 ? key_tiles_of(qt2, a.T, a.T_k) : 0;
   if (early) {
@@ -840,27 +838,38 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     // flag again: mark the pair done, so that every call leaves every flag at
     // epoch << 1 and a replay of the same launch (same epoch) starts from
     // "nobody yet" on every pair
-    if (tid == 0)
-      __hip_atomic_store(a.flags + __builtin_amdgcn_readfirstlane(pp.slot), a.epoch << 1, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) mark_merged(a.flags + __builtin_amdgcn_readfirstlane(pp.slot), a.epoch);
     combine_store(other, qt1);
   } else if (pp.part) {
     publish(pp.slot, role);
-    if (pre) segment(qt2, 0, tiles2, nullptr, nullptr, 1);
+    if (pre) segment(qt2, 0, tiles2, nullptr, nullptr, 1, nullptr);
   } else {
     store_rows<DOWN>(a, o, m_run, l_run, h, doc_lo + qt1 * BM, doc_hi, qb, lane, xs_wave, 32 * DOWN * kh, kh == 0);
   }
-  // a workgroup with a second segment arrives before running it (its state
-  // of the split tile is still in registers), so that usually the other
-  // workgroup of the pair, which has no second segment, arrives second and
-  // merges the split tile
-  bool deferred = false;
-  if (pp.part && !early) deferred = arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1, pre);
+  // The workgroup with a second segment arrives early in it, so that usually
+  // the other workgroup of the pair, which has no second segment, finds it
+  // arrived and merges the split tile (early); if it arrives second after
+  // all, it merges after its second segment.
+  if (pp.part && !early && !pre) arrive_and_merge(__builtin_amdgcn_readfirstlane(pp.slot), role, qt1);
   if (qt2 >= 0) {
-    segment(qt2, 0, tiles2, nullptr, nullptr, pre ? 2 : 0);
+    unsigned long long *const flag = pre ? a.flags + __builtin_amdgcn_readfirstlane(pp.slot) : nullptr;
+    segment(qt2, 0, tiles2, nullptr, nullptr, pre ? 2 : 0, flag);
+    if (pre && tiles2 == 0) {   // no first barrier in the segment: arrive here
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (tid == 0) arrive_old = arrive_swap(flag, a.epoch);
+    }
     store_rows<DOWN>(a, o, m_run, l_run, h, doc_lo + qt2 * BM, doc_hi, qb, lane, xs_wave, 32 * DOWN * kh, kh == 0);
   }
-  if (deferred) merge_records(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
+  if (pre) {
+    if (tid == 0) {
+      const bool sec = arrive_old == first_mark;
+      if (sec) mark_merged(a.flags + __builtin_amdgcn_readfirstlane(pp.slot), a.epoch);
+      second_arrival = sec;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(second_arrival) != 0) merge_records(__builtin_amdgcn_readfirstlane(pp.slot), qt1);
+  }
 }
 
 // ---- packed-document schedule: all (document, query tile) tasks, heaviest first
