@@ -208,6 +208,21 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
                        void *stream);
 
 /*
+ * The same up-projection with the weight as torch.nn.Linear stores wkv_b
+ * (hyper-parallel `_validate_up_projections`: weight shape
+ * (heads * head_dim, in_features)):
+ *   kv_out[t][h][j] = sum_l latent[t][l] * w_lin[(head_begin + h)*(N+V) + j][l]
+ *   w_lin  : [heads_total*(N+V)][L], the transpose of mla_latent_up_proj's w_kvb
+ * Same arguments, rules and errors as mla_latent_up_proj (MLA_BF16 needs L and
+ * N+V multiples of 8 and 16-byte aligned pointers). With the same weight
+ * values the result equals mla_latent_up_proj's bit for bit (same products in
+ * the same order).
+ */
+int mla_latent_up_proj_linear(const void *latent, const void *w_lin, void *kv_out, int64_t T, int L,
+                              int heads_total, int head_begin, int heads, int N, int V, int dtype,
+                              void *stream);
+
+/*
  * Attention of one rank's heads with a head-shared RoPE key band
  * (torchtitan "MLA CP optimization", section "Ulysses CP":
  * k_THK = concat(k_nope_THN, expand_per_head(k_shared_TR)),

@@ -21,7 +21,7 @@ MLA_BF16, MLA_F32 = 0, 1
 # every symbol include/mla.h declares
 EXPORTS = (
     "mla_last_error", "mla_version", "mla_head_shard_sizes", "mla_pack_heads", "mla_unpack_heads",
-    "mla_latent_up_proj", "mla_attention_workspace_size", "mla_attention_fwd",
+    "mla_latent_up_proj", "mla_latent_up_proj_linear", "mla_attention_workspace_size", "mla_attention_fwd",
     "mla_latent_decode_workspace_size", "mla_latent_decode_fwd",
     "mla_pack_expanded", "mla_causal_partition", "mla_kv_exchange_ranges", "mla_apply_rope", "mla_project_pack",
     "mla_attention_bwd_workspace_size", "mla_attention_bwd", "mla_latent_up_proj_bwd_workspace_size",
@@ -97,6 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in (lib.mla_pack_heads, lib.mla_unpack_heads):
         fn.argtypes = [vp, vp, i64, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
     lib.mla_latent_up_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.mla_latent_up_proj_linear.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.mla_pack_expanded.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, ctypes.POINTER(i32), i32, i32, vp]
     lib.mla_apply_rope.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp, i64, i32, i32, vp]
     lib.mla_project_pack.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32), i32,
@@ -309,6 +310,19 @@ def mla_latent_up_proj(latent, w_kvb, kv_out, heads_total, head_begin, heads, N,
     assert w_kvb.shape == (L, heads_total * (N + V)) and kv_out.numel() == T * heads * (N + V)
     _check("mla_latent_up_proj", lib.mla_latent_up_proj(
         _ptr(latent), _ptr(w_kvb), _ptr(kv_out), T, L, heads_total, head_begin, heads, N, V, _dtype(latent),
+        _stream(stream)))
+    return kv_out
+
+
+def mla_latent_up_proj_linear(latent, w_lin, kv_out, heads_total, head_begin, heads, N, V, stream=None):
+    """latent [T][L], w_lin [heads_total*(N+V)][L] (torch.nn.Linear's weight) -> kv_out [T][heads][N+V]."""
+    lib = load_library()
+    _dev(latent, w_lin, kv_out)
+    assert latent.is_contiguous() and w_lin.is_contiguous() and kv_out.is_contiguous()
+    T, L = latent.shape
+    assert w_lin.shape == (heads_total * (N + V), L) and kv_out.numel() == T * heads * (N + V)
+    _check("mla_latent_up_proj_linear", lib.mla_latent_up_proj_linear(
+        _ptr(latent), _ptr(w_lin), _ptr(kv_out), T, L, heads_total, head_begin, heads, N, V, _dtype(latent),
         _stream(stream)))
     return kv_out
 

@@ -3,6 +3,11 @@
 // (torchtitan "MLA CP optimization", sections "K/V all-gather CP" and "Ulysses CP";
 // hyper-parallel `_head_projection_request` selects the rows of the head range,
 // here the column block [col0, col0 + ncols) of the [L][heads_total*(N+V)] weight).
+// The weight may also come as torch.nn.Linear stores it, [heads_total*(N+V)][L]
+// (k-contiguous, the layout hyper-parallel `_validate_up_projections` checks):
+// then its tile is staged like the latent's and read with plain 16-byte reads,
+// and the products and their k order are the same, so both layouts give the same
+// bits.
 //
 // bf16 path: one 128x128 output tile per 256-thread workgroup (4 waves of
 // 64x64), two workgroups per CU (64 KB of LDS and 138 registers each), K
@@ -58,7 +63,9 @@ struct SlabOut {
   int16_t off[kMaxSlabHeads], qr[kMaxSlabHeads];
 };
 
-template <bool SLAB>
+// WT: the weight is [ncols-block rows][ldw] k-contiguous (element (k, n) at
+// W[(col0 + n) * ldw + k]) instead of [K][ldw] n-contiguous.
+template <bool SLAB, bool WT>
 __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, uint16_t *__restrict__ C,
     int M, int K, int64_t ldw, int64_t col0, int ncols, int tiles_m, int tiles_n, SlabOut so) {
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
   // Transfer plan: wave w fills A chunks [64*(A_I w + i), +64) and B chunks
   // [64*(B_I w + i), +64); lane l loads the global chunk the swizzle puts there.
   uint32_t a_off[A_I], b_off[B_I];
-  int a_k[A_I];
+  int a_k[A_I], b_k[B_I];
 #pragma unroll
   for (int i = 0; i < A_I; ++i) {
     const int p = 64 * (A_I * wave + i) + lane;
@@ -95,20 +102,36 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < B_I; ++i) {
     const int p = 64 * (B_I * wave + i) + lane;
-    const int k = p >> 4, cp = p & 15;
-    const int c = 2 * ((cp >> 1) ^ b_swz(k)) + (cp & 1);
-    b_off[i] = static_cast<uint32_t>((k * ldw + 8 * c) * 2);
+    if constexpr (WT) {   // [GN rows n][GK] like the latent's tile
+      const int n = p >> 3, c = (p & 7) ^ a_swz(n);
+      b_k[i] = 8 * c;
+      b_off[i] = static_cast<uint32_t>((n * ldw + 8 * c) * 2);
+    } else {              // [GK rows k][GN], 32-byte segments swizzled per row
+      const int k = p >> 4, cp = p & 15;
+      const int c = 2 * ((cp >> 1) ^ b_swz(k)) + (cp & 1);
+      b_k[i] = 0;
+      b_off[i] = static_cast<uint32_t>((k * ldw + 8 * c) * 2);
+    }
   }
   const u32x4 ra = dma_rsrc(A + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(min(M - m0, GM) * K * 2));
+  // k-contiguous weight: rows [col0 + n0, + min(ncols - n0, GN)) of the transposed weight
+  const u32x4 rbt = WT ? dma_rsrc(W + (col0 + n0) * ldw, static_cast<uint32_t>(min(ncols - n0, GN) * ldw * 2))
+                       : u32x4{0, 0, 0, 0};
   auto issue = [&](uint16_t *as, uint16_t *bs, int k0) {
-    const u32x4 rb = dma_rsrc(W + static_cast<int64_t>(k0) * ldw + col0 + n0,
-                              static_cast<uint32_t>(min(K - k0, GK) * ldw * 2));
     const uint32_t la = lds_addr(as), lb = lds_addr(bs);
 #pragma unroll
     for (int i = 0; i < A_I; ++i)
       dma16(ra, la + 1024 * (A_I * wave + i), k0 + a_k[i] < K ? a_off[i] + 2 * k0 : kOob);
+    if constexpr (WT) {
 #pragma unroll
-    for (int i = 0; i < B_I; ++i) dma16(rb, lb + 1024 * (B_I * wave + i), b_off[i]);
+      for (int i = 0; i < B_I; ++i)
+        dma16(rbt, lb + 1024 * (B_I * wave + i), k0 + b_k[i] < K ? b_off[i] + 2 * k0 : kOob);
+    } else {
+      const u32x4 rb = dma_rsrc(W + static_cast<int64_t>(k0) * ldw + col0 + n0,
+                                static_cast<uint32_t>(min(K - k0, GK) * ldw * 2));
+#pragma unroll
+      for (int i = 0; i < B_I; ++i) dma16(rb, lb + 1024 * (B_I * wave + i), b_off[i]);
+    }
   };
 
   f32x16 acc[2][2];
@@ -120,13 +143,18 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // one 64-wide k slice from buffers (as, bs): weight^T via transposing
-  // reads, latent^T direct
+  // reads (or direct, k-contiguous weight), latent^T direct
   auto slice = [&](const uint16_t *As, const uint16_t *Bs) __attribute__((always_inline)) {
     bf16x8 wf[GK / 16][2], lf[GK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
+        if constexpr (WT) {
+          const int n = 64 * wn + 32 * i + lrow;
+          wf[ks][i] = *reinterpret_cast<const bf16x8 *>(Bs + n * GK + 8 * ((2 * ks + half) ^ a_swz(n)));
+          continue;
+        }
         const int n = 64 * wn + 32 * i + 16 * (grp & 1) + 4 * (gl & 3);
         // lanes of half h take k = 16ks + 8h + 0..7 in natural order (the latent operand's order)
         const int k0r = 16 * ks + 8 * (grp >> 1) + (gl >> 2), k1r = k0r + 4;
@@ -285,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void up_proj_bf16_kernel(
 }
 
 // Plain per-element kernel for fp32 (and any shape the tiled kernel does not take).
-template <typename T>
+template <typename T, bool WT>
 __global__ __launch_bounds__(256) void up_proj_generic_kernel(const T *__restrict__ A, const T *__restrict__ W,
                                                               T *__restrict__ C, int64_t M, int K, int64_t ldw,
                                                               int64_t col0, int64_t ncols) {
@@ -294,7 +322,8 @@ __global__ __launch_bounds__(256) void up_proj_generic_kernel(const T *__restric
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t m = idx / ncols, n = idx % ncols;
     float acc = 0.f;
-    for (int k = 0; k < K; ++k) acc += load_f32(A, m * K + k) * load_f32(W, k * ldw + col0 + n);
+    for (int k = 0; k < K; ++k)
+      acc += load_f32(A, m * K + k) * load_f32(W, WT ? (col0 + n) * ldw + k : k * ldw + col0 + n);
     store_f32(C, idx, acc);
   }
 }
@@ -306,28 +335,44 @@ int launch_up_proj(const UpProjPlan &p, void *stream) {
   if (p.T == 0) return hipSuccess;
   const uintptr_t al = reinterpret_cast<uintptr_t>(p.latent) | reinterpret_cast<uintptr_t>(p.w) |
                        reinterpret_cast<uintptr_t>(p.out);
-  const bool tiled = p.bf16 && p.L % 8 == 0 && p.ldw % 8 == 0 && p.col0 % 8 == 0 && p.ncols % 8 == 0 &&
-                     al % 16 == 0 && p.T < (1LL << 31) && p.ncols < (1LL << 31);
+  // (k-contiguous weight: every row starts 16-byte aligned when ldw % 8 == 0,
+  // whatever col0; the transposed weight's rows fit the 32-bit transfer range)
+  const bool tiled = p.bf16 && p.L % 8 == 0 && p.ldw % 8 == 0 && (p.w_kmajor || p.col0 % 8 == 0) &&
+                     p.ncols % 8 == 0 && al % 16 == 0 && p.T < (1LL << 31) && p.ncols < (1LL << 31) &&
+                     (!p.w_kmajor || static_cast<int64_t>(GN) * p.ldw * 2 < (1LL << 32));
   if (tiled) {
     const int tm = static_cast<int>((p.T + GM - 1) / GM);
     const int tn = static_cast<int>((p.ncols + GN - 1) / GN);
     SlabOut none{};
-    hipLaunchKernelGGL(up_proj_bf16_kernel<false>, dim3(tm * tn), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w),
-                       static_cast<uint16_t *>(p.out), static_cast<int>(p.T), p.L, p.ldw, p.col0,
-                       static_cast<int>(p.ncols), tm, tn, none);
+    if (p.w_kmajor)
+      hipLaunchKernelGGL((up_proj_bf16_kernel<false, true>), dim3(tm * tn), dim3(256), 0, s,
+                         static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w),
+                         static_cast<uint16_t *>(p.out), static_cast<int>(p.T), p.L, p.ldw, p.col0,
+                         static_cast<int>(p.ncols), tm, tn, none);
+    else
+      hipLaunchKernelGGL((up_proj_bf16_kernel<false, false>), dim3(tm * tn), dim3(256), 0, s,
+                         static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w),
+                         static_cast<uint16_t *>(p.out), static_cast<int>(p.T), p.L, p.ldw, p.col0,
+                         static_cast<int>(p.ncols), tm, tn, none);
     return hipGetLastError();
   }
   const int64_t total = p.T * p.ncols;
   const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 65536));
+  auto generic = [&](auto zero) {
+    using T = decltype(zero);
+    if (p.w_kmajor)
+      hipLaunchKernelGGL((up_proj_generic_kernel<T, true>), dim3(blocks), dim3(256), 0, s,
+                         static_cast<const T *>(p.latent), static_cast<const T *>(p.w), static_cast<T *>(p.out), p.T,
+                         p.L, p.ldw, p.col0, p.ncols);
+    else
+      hipLaunchKernelGGL((up_proj_generic_kernel<T, false>), dim3(blocks), dim3(256), 0, s,
+                         static_cast<const T *>(p.latent), static_cast<const T *>(p.w), static_cast<T *>(p.out), p.T,
+                         p.L, p.ldw, p.col0, p.ncols);
+  };
   if (p.bf16)
-    hipLaunchKernelGGL(up_proj_generic_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w),
-                       static_cast<uint16_t *>(p.out), p.T, p.L, p.ldw, p.col0, p.ncols);
+    generic(uint16_t{0});
   else
-    hipLaunchKernelGGL(up_proj_generic_kernel<float>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const float *>(p.latent), static_cast<const float *>(p.w),
-                       static_cast<float *>(p.out), p.T, p.L, p.ldw, p.col0, p.ncols);
+    generic(0.f);
   return hipGetLastError();
 }
 
@@ -353,7 +398,7 @@ int launch_project_pack(const ProjectPackPlan &p, void *stream) {
   const int64_t ncols = static_cast<int64_t>(p.heads) * p.P;
   const int tm = static_cast<int>((p.T + GM - 1) / GM);
   const int tn = static_cast<int>((ncols + GN - 1) / GN);
-  hipLaunchKernelGGL(up_proj_bf16_kernel<true>, dim3(tm * tn), dim3(256), 0, s,
+  hipLaunchKernelGGL((up_proj_bf16_kernel<true, false>), dim3(tm * tn), dim3(256), 0, s,
                      static_cast<const uint16_t *>(p.latent), static_cast<const uint16_t *>(p.w), nullptr,
                      static_cast<int>(p.T), p.L, p.ldw, p.col0, static_cast<int>(ncols), tm, tn, so);
   return hipGetLastError();

@@ -409,6 +409,38 @@ int mla_latent_up_proj(const void *latent, const void *w_kvb, void *kv_out, int6
   return launched(mla::launch_up_proj(p, stream), who);
 }
 
+int mla_latent_up_proj_linear(const void *latent, const void *w_lin, void *kv_out, int64_t T, int L,
+                              int heads_total, int head_begin, int heads, int N, int V, int dtype, void *stream) {
+  const char *who = "mla_latent_up_proj_linear";
+  if (!valid_dtype(dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, dtype);
+  if (T < 0 || L < 1 || N < 1 || V < 1 || heads < 1 || heads_total < 1)
+    return fail(MLA_EINVAL, "%s: need T >= 0 and L, N, V, heads, heads_total >= 1", who);
+  if (head_begin < 0 || head_begin + heads > heads_total)
+    return fail(MLA_EINVAL, "%s: head range [%d, %d) outside the %d heads of the weight", who, head_begin,
+                head_begin + heads, heads_total);
+  if (T == 0) return ok();
+  if (latent == nullptr || w_lin == nullptr || kv_out == nullptr) return fail(MLA_EINVAL, "%s: NULL buffer", who);
+  const int64_t P = static_cast<int64_t>(N) + V;
+  const int64_t eb = elem_bytes(dtype);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(w_lin) |
+                       reinterpret_cast<uintptr_t>(kv_out);
+  if (al % eb) return fail(MLA_EINVAL, "%s: buffers must be aligned to the element size", who);
+  if (dtype == MLA_BF16 && (L % 8 || P % 8 || al % 16))
+    return fail(MLA_EUNSUPPORTED, "%s: bf16 needs L and N+V multiples of 8 and 16-byte aligned buffers", who);
+  mla::UpProjPlan p;
+  p.latent = latent;
+  p.w = w_lin;
+  p.out = kv_out;
+  p.T = T;
+  p.L = L;
+  p.ldw = L;                 // row stride of the [heads_total*(N+V)][L] weight
+  p.col0 = head_begin * P;   // first weight row of the head range
+  p.ncols = heads * P;
+  p.bf16 = dtype == MLA_BF16;
+  p.w_kmajor = true;
+  return launched(mla::launch_up_proj(p, stream), who);
+}
+
 static int attn_validate(const mla_attn_args *a, const char *who) {
   if (a == nullptr) return fail(MLA_EINVAL, "%s: args is NULL", who);
   if (!valid_dtype(a->dtype)) return fail(MLA_EINVAL, "%s: unknown dtype %d", who, a->dtype);

@@ -48,12 +48,13 @@ int launch_rope(const RopePlan &p, void *stream);
 // ---- latent up-projection -------------------------------------------------
 struct UpProjPlan {
   const void *latent;  // [T][L]
-  const void *w;       // [L][ldw], columns [col0, col0 + ncols)
+  const void *w;       // [L][ldw], columns [col0, col0 + ncols); w_kmajor: [rows][ldw], rows [col0, col0 + ncols)
   void *out;           // [T][ncols]
   int64_t T;
   int L;
   int64_t ldw, col0, ncols;
   int bf16;
+  bool w_kmajor = false;   // the weight as torch.nn.Linear stores it (k-contiguous)
 };
 int launch_up_proj(const UpProjPlan &p, void *stream);
 

@@ -247,6 +247,28 @@ def test_up_proj_generic_widths():
     check_close(got, ref, name="N=40 V=24 L=40")
 
 
+@pytest.mark.parametrize("wname,T,hb,heads", [
+    ("tiny", 37, 1, 2), ("dsv3_rank", 2048, 0, 16), ("uneven22", 300, 22, 22),
+    ("dsv3_rank", 129, 0, 16), ("dsv3_rank", 1000, 5, 3), ("odd", 200, 1, 3),
+])
+def test_up_proj_linear_layout(wname, T, hb, heads):
+    # the weight as torch.nn.Linear stores it ([heads_total*(N+V)][L]): the oracle's product, and the same bits as
+    # the [L][heads_total*(N+V)] entry point on the same values
+    w = (mi.Workload("odd", 11, T=200, H=3, L=40, N=40, R=8, V=24, heads_total=5) if wname == "odd"
+         else mi.WORKLOADS[wname])
+    d = mi.shard_inputs(w, T=T)
+    lat, W = dev(d["latent"]), dev(d["w_kvb"])
+    W_lin = dev(np.ascontiguousarray(d["w_kvb"].T))
+    out = torch.empty((T, heads, w.P), dtype=lat.dtype, device="cuda")
+    out_rm = torch.empty_like(out)
+    mla.mla_latent_up_proj_linear(lat, W_lin, out, w.heads_total, hb, heads, w.N, w.V)
+    mla.mla_latent_up_proj(lat, W, out_rm, w.heads_total, hb, heads, w.N, w.V)
+    _sync()
+    ref = oracle.latent_up_proj(d["latent"], d["w_kvb"], hb, heads, w.N, w.V)
+    check_close(host64(out), ref, bf16=w.bf16, name=f"nn.Linear weight, {wname} T={T} heads[{hb},{hb + heads})")
+    assert torch.equal(out.view(torch.int16) if w.bf16 else out, out_rm.view(torch.int16) if w.bf16 else out_rm)
+
+
 # ------------------------------------------------------------------------- attention
 
 def _attn_inputs(w, T, seed_cfg=None, kv_direct=True):

@@ -162,6 +162,18 @@ def test_up_proj_validation_before_launch(lib):
     assert f(FAKE, FAKE, FAKE2, 0, 32, 4, 0, 2, 16, 16, 0, None) == mla.MLA_OK            # T = 0
 
 
+def test_up_proj_linear_validation_before_launch(lib):
+    f = lib.mla_latent_up_proj_linear
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, 3, 2, 16, 16, 0, None) == mla.MLA_EINVAL    # head range past W
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, -1, 2, 16, 16, 0, None) == mla.MLA_EINVAL
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, 0, 2, 16, 0, 0, None) == mla.MLA_EINVAL     # V = 0
+    assert f(FAKE, None, FAKE2, 16, 32, 4, 0, 2, 16, 16, 0, None) == mla.MLA_EINVAL    # NULL weight
+    assert f(FAKE, FAKE, FAKE2, 16, 30, 4, 0, 2, 16, 16, 0, None) == mla.MLA_EUNSUPPORTED   # bf16 needs L%8
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, 0, 2, 12, 16, 0, None) == mla.MLA_EUNSUPPORTED   # bf16 needs (N+V)%8
+    assert f(FAKE, FAKE, FAKE2, 0, 32, 4, 0, 2, 16, 16, 0, None) == mla.MLA_OK            # T = 0
+    assert f(FAKE, FAKE, FAKE2, 16, 32, 4, 0, 2, 16, 16, 7, None) == mla.MLA_EINVAL     # unknown dtype
+
+
 def _attn(**kw):
     from mla_attention_under_amd._binding import mla_attn_args
     a = mla_attn_args()
