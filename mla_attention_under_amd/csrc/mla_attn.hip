@@ -382,10 +382,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   };
   // The workgroup without a second segment usually finishes the split tile
   // long after the other one has arrived. It reads the pair's flag during
-  // its last key step; if the other workgroup has arrived (flag = first
-  // arrival of this call), it is certainly second: it skips publishing and
-  // arriving, and its merging waves load the other record while the key
-  // halves merge.
+  // its last key step (the step's closing barrier publishes what it saw); if
+  // the other workgroup has arrived (flag = first arrival of this call), it is
+  // certainly second: it skips publishing and arriving, and its waves start
+  // loading the other record before the key halves merge.
   __shared__ int early_second;
   unsigned long long arrive_old = 0;   // the two-segment workgroup's arrival (its exchange's old value)
   unsigned long long other[OWN + 1];   // this wave's pairs of the other record, then (m, l)
@@ -644,10 +644,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         if (t < nt) X(t);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(dma)::value)
+      if constexpr (decltype(dma)::value) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerStep);   // vmcnt(5): this step's transfers may stay in flight
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+      } else {
+        // the segment's last step: vmcnt(0), which includes the pair-flag
+        // probe, so the early-merge decision is published by this barrier
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (probe != nullptr && tid == 0) early_second = flag_seen == ((a.epoch << 1) | 1ull);
+        __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0)
+      }
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -703,6 +708,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       if (probe != nullptr && tid == 0) flag_seen = __hip_atomic_load(probe, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int rl = (nt - 1) % 3;                     // t == nt: the last PV product
       step(yes, no, no, nt, kb0, rl == 0 ? vb0 : rl == 1 ? vb1 : vb2, kb0, vb0);
+      // an early merge starts loading the other record now, so that the
+      // loads are in flight while the key halves merge
+      if (probe != nullptr) {
+        early = __builtin_amdgcn_readfirstlane(early_second) != 0;
+        if (early) load_own(other_rec, other);
+      }
     }
 
     // merge the two key halves of each query block through LDS in one round
@@ -725,11 +736,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
           xo[(4 * (dx + d) + g) * 64 + lane] =
               f32x4{o[DOWN + d][4 * g], o[DOWN + d][4 * g + 1], o[DOWN + d][4 * g + 2], o[DOWN + d][4 * g + 3]};
       xml[64 * kh + lane] = f32x2_t{m_run, l_run};
-      if (probe != nullptr && tid == 0) early_second = flag_seen == ((a.epoch << 1) | 1ull);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();
-      if (probe != nullptr) early = __builtin_amdgcn_readfirstlane(early_second) != 0;
-      if (early) load_own(other_rec, other);
       const f32x2_t ml = xml[64 * (1 - kh) + lane];
       const float m0 = kh == 0 ? m_run : ml.x, l0 = kh == 0 ? l_run : ml.y;   // key half 0
       const float m1 = kh == 0 ? ml.x : m_run, l1 = kh == 0 ? ml.y : l_run;   // key half 1
