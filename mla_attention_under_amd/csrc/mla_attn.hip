@@ -306,7 +306,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // a multiple of the key tile and (causal) T_k - T too, every tile is whole
   // (a query tile's causal key range ends at a multiple of BM plus T_k - T, or
   // at T_k).
+  // The stage buffers are untouched until the first segment's transfers
+  // unless they are zeroed here: then every wave's zeroing must be done
+  // before any wave's transfers land (see segment).
+  bool stages_busy = false;
   if (a.tasks != nullptr || a.T_k % BN != 0 || (a.causal && (a.T_k - a.T) % BN != 0)) {
+    stages_busy = true;
     u32x4 z{0, 0, 0, 0};
     for (int i = tid; i < (KN_E + KR_E) / 8; i += 64 * NW) {
       reinterpret_cast<u32x4 *>(kb0)[i] = z;
@@ -661,9 +666,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
 
     if (mode != 2) {
       // the previous segment's LDS readers (and the stage zeroing) are done
-      // with the buffers; its global stores may stay in flight
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
+      // with the buffers; its global stores may stay in flight. A first
+      // segment over stages nobody has touched skips the barrier, so each
+      // wave starts its transfers as soon as it is running (the prologue's
+      // own wait and barrier come before any stage is read).
+      if (stages_busy) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+      }
+      stages_busy = true;
       if (nt > 0) {
         // K_t lives in kb[t % 3], V_t in vb[t % 3]
         issue_q();
