@@ -297,24 +297,32 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
   {
     const int qbeg = __builtin_amdgcn_readfirstlane(a.causal ? b0 : lo0);
     const int qend = __builtin_amdgcn_readfirstlane(hi1);
-    // six transfers per second wave: the q rows and band, the dout rows, lse
-    // and D; rows at or past qend are never visible and read zero
-    auto issue = [&](int stg, int q0) __attribute__((always_inline)) {
+    // six transfers per second wave: the q rows and band (part 0), the dout
+    // rows, lse and D (part 1); rows at or past qend are never visible and
+    // read zero
+    auto issue_part = [&](int part, int stg, int q0) __attribute__((always_inline)) {
       const int ws = wave - 4;
       const uint32_t rows = static_cast<uint32_t>(max(0, min(kSB, qend - q0)));
-      const uint16_t *qrow = a.q + static_cast<int64_t>(q0) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
-      const uint16_t *grow = a.dout + static_cast<int64_t>(q0) * a.do_st + static_cast<int64_t>(h) * a.do_sh;
-      const u32x4 rq = dma_rsrc(qrow, rows * static_cast<uint32_t>(a.q_st) * 2);
-      const u32x4 rg = dma_rsrc(grow, rows * static_cast<uint32_t>(a.do_st) * 2);
       const uint32_t base = lds_addr(stages[stg]);
-      stage_part<CN, 4>(rq, base, a.q_st * 2, 0, ws, lane);
-      stage_part<CR, 4>(rq, base + 2 * St::kN, a.q_st * 2, 2 * N, ws, lane);
-      stage_part<CV, 4>(rg, base + 2 * (St::kN + St::kR), a.do_st * 2, 0, ws, lane);
-      // lse (waves 4, 6) and D (waves 5, 7): the two copies write the same bytes
-      const int which = ws & 1;
-      const float *src = (which == 0 ? a.lse : a.Dws) + static_cast<int64_t>(h) * a.T + min(q0, a.T);
-      const u32x4 rl = dma_rsrc(src, rows * 4);
-      if (lane < 8) dma16(rl, base + 2 * St::kLse + 128 * which, static_cast<uint32_t>(16 * lane));
+      if (part == 0) {
+        const uint16_t *qrow = a.q + static_cast<int64_t>(q0) * a.q_st + static_cast<int64_t>(h) * a.q_sh;
+        const u32x4 rq = dma_rsrc(qrow, rows * static_cast<uint32_t>(a.q_st) * 2);
+        stage_part<CN, 4>(rq, base, a.q_st * 2, 0, ws, lane);
+        stage_part<CR, 4>(rq, base + 2 * St::kN, a.q_st * 2, 2 * N, ws, lane);
+      } else {
+        const uint16_t *grow = a.dout + static_cast<int64_t>(q0) * a.do_st + static_cast<int64_t>(h) * a.do_sh;
+        const u32x4 rg = dma_rsrc(grow, rows * static_cast<uint32_t>(a.do_st) * 2);
+        stage_part<CV, 4>(rg, base + 2 * (St::kN + St::kR), a.do_st * 2, 0, ws, lane);
+        // lse (waves 4, 6) and D (waves 5, 7): the two copies write the same bytes
+        const int which = ws & 1;
+        const float *src = (which == 0 ? a.lse : a.Dws) + static_cast<int64_t>(h) * a.T + min(q0, a.T);
+        const u32x4 rl = dma_rsrc(src, rows * 4);
+        if (lane < 8) dma16(rl, base + 2 * St::kLse + 128 * which, static_cast<uint32_t>(16 * lane));
+      }
+    };
+    auto issue = [&](int stg, int q0) __attribute__((always_inline)) {
+      issue_part(0, stg, q0);
+      issue_part(1, stg, q0);
     };
     int klo = 1, khi = 0;   // the owned key's document (empty past T)
     if (own < a.T) doc_of(a, own, klo, khi);
@@ -399,13 +407,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
             pin(std::integral_constant<int, (kSB / 16) * V / 32>(), I2(), I8());
           }
         } else {                   // dp = dout v^T; ds = p (dp - D); dk += ds^T q
+          // half of the step's transfers before the dp products (the first
+          // wave's score products keep the matrix pipe busy meanwhile), half
+          // after them (while the first wave exponentiates)
+          issue_part(0, (t + kStages - 1) % kStages, q0 + kSB * (kStages - 1));
           if (!idle) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < V / 16; ++k) s = mfma32(st_row<CV>(Gv, k, lane), of[k], s);
             pin(std::integral_constant<int, V / 16>(), I1(), I4());
           }
-          issue((t + kStages - 1) % kStages, q0 + kSB * (kStages - 1));
+          issue_part(1, (t + kStages - 1) % kStages, q0 + kSB * (kStages - 1));
           sync();   // p is in LDS
           if (!idle) {
             const f32x4 *pb = reinterpret_cast<const f32x4 *>(xch[0][g4]);
@@ -463,20 +475,30 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
     // the second waves move the k and v rows (four transfers each), the first
     // waves the band and an empty transfer (two each), in the time each would
     // otherwise wait for the other's half of the pair
-    auto issue = [&](int stg, int k0) __attribute__((always_inline)) {
+    // part 0: the k rows (second waves) or the band (first waves); part 1:
+    // the v rows or the empty transfer
+    auto issue_part = [&](int part, int stg, int k0) __attribute__((always_inline)) {
       const int ws = wave & 3;
       const uint32_t rows = static_cast<uint32_t>(max(0, min(kSB, kend - k0)));
-      const uint16_t *krow = a.kv + static_cast<int64_t>(k0) * a.kv_st + static_cast<int64_t>(h) * a.kv_sh;
-      const u32x4 rk = dma_rsrc(krow, rows * static_cast<uint32_t>(a.kv_st) * 2);
-      const u32x4 rr = dma_rsrc(a.kr + static_cast<int64_t>(k0) * a.kr_st, rows * static_cast<uint32_t>(a.kr_st) * 2);
       const uint32_t base = lds_addr(stages[stg]);
       if (second) {
-        stage_part<CN, 4>(rk, base, a.kv_st * 2, 0, ws, lane);
-        stage_part<CV, 4>(rk, base + 2 * (St::kN + St::kR), a.kv_st * 2, 2 * N, ws, lane);
-      } else {
+        const uint16_t *krow = a.kv + static_cast<int64_t>(k0) * a.kv_st + static_cast<int64_t>(h) * a.kv_sh;
+        const u32x4 rk = dma_rsrc(krow, rows * static_cast<uint32_t>(a.kv_st) * 2);
+        if (part == 0)
+          stage_part<CN, 4>(rk, base, a.kv_st * 2, 0, ws, lane);
+        else
+          stage_part<CV, 4>(rk, base + 2 * (St::kN + St::kR), a.kv_st * 2, 2 * N, ws, lane);
+      } else if (part == 0) {
+        const u32x4 rr =
+            dma_rsrc(a.kr + static_cast<int64_t>(k0) * a.kr_st, rows * static_cast<uint32_t>(a.kr_st) * 2);
         stage_part<CR, 4>(rr, base + 2 * St::kN, a.kr_st * 2, 0, ws, lane);
+      } else {
         pad_transfer(base);
       }
+    };
+    auto issue = [&](int stg, int k0) __attribute__((always_inline)) {
+      issue_part(0, stg, k0);
+      issue_part(1, stg, k0);
     };
     int qlo = 1, qhi = 0;
     float lse2 = 0.f, Dq = 0.f;
@@ -509,6 +531,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
         const bool idle = own0 >= a.T || (a.causal && k0 > own0 + 31);
         const bool full = k0 >= vis_lo && k0 + kSB <= vis_hi && (nocausal || k0 + kSB - 1 <= own0);
         f32x16 s = {};
+        // half of the step's transfers before the products, half after them
+        issue_part(0, (t + kStages - 1) % kStages, k0 + kSB * (kStages - 1));
         if (!idle) {
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (!SECOND) {   // s^T = k q^T, then p^T
@@ -535,7 +559,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
           }
           xch_put(xch[SECOND ? 1 : 0][g4], s, lane);
         }
-        issue((t + kStages - 1) % kStages, k0 + kSB * (kStages - 1));
+        issue_part(1, (t + kStages - 1) % kStages, k0 + kSB * (kStages - 1));
         sync();   // p^T and dp^T are in LDS
         if (!idle) {
           // ds = p (dp - D), with the other wave's half of the pair
