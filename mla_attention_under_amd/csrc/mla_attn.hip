@@ -8,14 +8,16 @@
 //  * One workgroup = 8 waves = 128 queries of one head: 4 query blocks of 32 x
 //    2 key halves. A 64-key tile is split between the halves (32 keys each);
 //    the two partial softmax states of a query block are merged through LDS
-//    at the end. Every SIMD runs two waves (<= 256 registers each), so one
-//    wave's softmax overlaps the other's MFMAs, and each K/V tile brought into
-//    LDS (80 KB, double-buffered) serves 128 queries.
-//  * Tiles move global->LDS with buffer_load ... lds (no staging registers),
-//    double-buffered, one barrier per tile. The key tile is assembled from two
-//    sources: k_nope from this head's projected kv rows and the shared k_rope
-//    row (one copy for all heads), so the expanded key never exists in HBM.
-//    Loads past the visible keys fall outside the buffer range and read zero.
+//    at the end, after which each of the two waves keeps half of the output
+//    columns. Every SIMD runs two waves (<= 256 registers each) half a tile
+//    apart, so one wave's softmax overlaps the other's MFMAs, and each K/V
+//    tile brought into LDS serves 128 queries.
+//  * Tiles move global->LDS with buffer_load ... lds (no staging registers)
+//    into rings of three K and three V buffers (120 KB), two tiles ahead, with
+//    two barriers per tile. The key tile is assembled from two sources: k_nope
+//    from this head's projected kv rows and the shared k_rope row (one copy
+//    for all heads), so the expanded key never exists in HBM. Loads past the
+//    visible keys fall outside the buffer range and read zero.
 //  * LDS rows are unpadded and XOR-swizzled per row, so MFMA operand reads and
 //    the transposing reads do not conflict on banks.
 //  * Scores are computed transposed, S^T = K Q^T (32x32x16 MFMA), so lane l
@@ -27,9 +29,10 @@
 //    running output is rescaled only when a row max grows by more than 2^8
 //    (exact: any reference max gives the same quotient).
 //  * Work order: dense causal query tiles are paired (i, n-1-i) and every pair
-//    is split into two workgroups of equal key-tile count; the tile that
-//    straddles both is merged by whichever finishes second (see arrive).
-//    Packed documents use a device-built schedule sorted by key-tile count.
+//    is split into two workgroups of nearly equal key-tile count; the tile
+//    that straddles both is merged by whichever arrives second (see
+//    arrive_swap). Packed documents use a device-built schedule sorted by
+//    key-tile count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -407,7 +410,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   bool early = false;
 
   // ---- one segment: query tile qt over key tiles [t0, t1); leaves the merged
-  // (both key halves) softmax state in the waves with kh == 0.
+  // (both key halves) softmax state with each wave of a query block holding
+  // its half of the columns in o[0 .. DBLK/2) and the common (m, l).
   //
   // Per tile t a wave does M_t = {O += V_{t-1}^T P_{t-1}^T, S_t = K_t Q^T} on
   // the matrix cores and then X_t = softmax(S_t) -> P_t on the vector ALUs.
