@@ -93,8 +93,14 @@ def cpu_baseline(w, d, x_pack, sizes, flops_step):
         el = time.perf_counter() - t0
         if el >= 10.0 or (n >= 1 and el / n > 15.0):
             break
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:  # pragma: no cover - not Linux
+        pass
     return {"value": round(flops_step * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
             "sample": f"{n} full step(s) of the same workload (pack, up-projection, attention of all "
                       f"{w.H} heads, unpack) in float64 NumPy, {el:.1f} s"}
 
