@@ -336,13 +336,18 @@ int launch_up_proj(const UpProjPlan &p, void *stream) {
   const uintptr_t al = reinterpret_cast<uintptr_t>(p.latent) | reinterpret_cast<uintptr_t>(p.w) |
                        reinterpret_cast<uintptr_t>(p.out);
   // (k-contiguous weight: every row starts 16-byte aligned when ldw % 8 == 0,
-  // whatever col0; the transposed weight's rows fit the 32-bit transfer range)
+  // whatever col0.) A tile's transfers address its rows by 32-bit byte
+  // offsets: the latent's GM rows, the k-contiguous weight's GN rows or the
+  // row-major weight's GK rows must fit 4 GiB, and the grid 2^31 workgroups.
+  const int64_t tm64 = (p.T + GM - 1) / GM, tn64 = (p.ncols + GN - 1) / GN;
   const bool tiled = p.bf16 && p.L % 8 == 0 && p.ldw % 8 == 0 && (p.w_kmajor || p.col0 % 8 == 0) &&
                      p.ncols % 8 == 0 && al % 16 == 0 && p.T < (1LL << 31) && p.ncols < (1LL << 31) &&
-                     (!p.w_kmajor || static_cast<int64_t>(GN) * p.ldw * 2 < (1LL << 32));
+                     static_cast<int64_t>(GM) * p.L * 2 < (1LL << 32) &&
+                     static_cast<int64_t>(p.w_kmajor ? GN : GK) * p.ldw * 2 < (1LL << 32) &&
+                     tm64 * tn64 < (1LL << 31);
   if (tiled) {
-    const int tm = static_cast<int>((p.T + GM - 1) / GM);
-    const int tn = static_cast<int>((p.ncols + GN - 1) / GN);
+    const int tm = static_cast<int>(tm64);
+    const int tn = static_cast<int>(tn64);
     SlabOut none{};
     if (p.w_kmajor)
       hipLaunchKernelGGL((up_proj_bf16_kernel<false, true>), dim3(tm * tn), dim3(256), 0, s,

@@ -239,6 +239,12 @@ int mla_project_pack(const void *latent, const void *w, void *send, int64_t toke
   if (al % 16 || (R > 0 && (cs_stride % 8 || (tokens > 1 && cs_stride < R))))
     return fail(MLA_EUNSUPPORTED, "%s: buffers must be 16-byte aligned, table rows multiples of 8 elements", who);
   if (tokens >= (int64_t(1) << 31)) return fail(MLA_EUNSUPPORTED, "%s: too many tokens", who);
+  // the tiles address their rows by 32-bit byte offsets: 128 latent rows and 64 weight rows must fit 4 GiB
+  if (int64_t(128) * L * 2 >= (int64_t(1) << 32) || int64_t(64) * w_heads * P * 2 >= (int64_t(1) << 32))
+    return fail(MLA_EUNSUPPORTED, "%s: latent width %d or weight width %lld too large for the tiles", who, L,
+                static_cast<long long>(int64_t(w_heads) * P));
+  if ((tokens + 127) / 128 * ((int64_t(heads) * P + 127) / 128) >= (int64_t(1) << 31))
+    return fail(MLA_EUNSUPPORTED, "%s: more than 2^31 output tiles", who);
   const uint64_t sb = static_cast<uint64_t>(tokens) * heads * F * 2;
   const uintptr_t ps = reinterpret_cast<uintptr_t>(send), pl = reinterpret_cast<uintptr_t>(latent),
                   pw = reinterpret_cast<uintptr_t>(w);

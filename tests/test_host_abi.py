@@ -435,4 +435,9 @@ def test_project_pack_validation_before_launch(lib):
     assert call(ro=96, R=64, P=192) == mla.MLA_EUNSUPPORTED   # band not at a multiple of 64
     assert call(R=32, ro=128) == mla.MLA_EUNSUPPORTED   # band width other than 64
     assert call(send=A) == mla.MLA_EINVAL               # send overlaps the latent
+    # tiles address rows by 32-bit byte offsets; the grid holds at most 2^31 - 1 workgroups
+    assert call(L=1 << 24) == mla.MLA_EUNSUPPORTED      # 128 latent rows of 32 MiB
+    assert call(wh=1 << 18) == mla.MLA_EUNSUPPORTED     # 64 weight rows of 96 MiB
+    big = (ctypes.c_int * 2)(128, 128)
+    assert call(sz=big, T=1 << 30, wh=256, heads=256) == mla.MLA_EUNSUPPORTED   # 2^23 x 384 tiles
     assert call(T=0) == mla.MLA_OK
