@@ -133,7 +133,8 @@ int mla_apply_rope(void *x, int64_t tokens, int heads, int64_t stride_t, int64_t
  * multiples of 8, 16-byte aligned buffers and tables (cs_stride a multiple of
  * 8), and, when R > 0, R = 64 with rope_offset and P multiples of 64 (the MLA
  * query block: P = 192, rope_offset = 128, R = 64).
- * heads <= 256, sp <= 256. tokens == 0 is a no-op.
+ * heads <= 256, sp <= 256, L < 2^24 and w_heads*P < 2^25 (the tiles' 32-bit
+ * row offsets). tokens == 0 is a no-op.
  */
 int mla_project_pack(const void *latent, const void *w, void *send, int64_t tokens, int L, int w_heads, int head_begin,
                      int heads, int P, int F, int col_offset, const int *sizes, int sp, int rope_offset, int R,
@@ -255,6 +256,10 @@ int mla_latent_up_proj_linear(const void *latent, const void *w_lin, void *kv_ou
  * Device offsets cannot be checked on the host: the kernels clamp them to
  * [0, T_q] / [0, T_k], so malformed offsets give wrong documents, never an
  * access outside the buffers.
+ * bf16 with N=128, R=64, V=128 runs the MFMA tiles, which need 16-byte
+ * aligned buffers, strides that are multiples of 8 elements and token strides
+ * of at most 2^24 elements (MLA_EUNSUPPORTED otherwise); other widths and
+ * MLA_F32 run a plain kernel.
  * The packed q+kv rows of mla_pack_heads can be read in place with
  * q_stride_h = kv_stride_h = F and kv = q + K.
  * Split-KV reductions are not an argument here: the dense causal path splits
@@ -336,7 +341,8 @@ int mla_attention_fwd_noalloc(const mla_attn_args *a, void *stream);
  *   dkv    : [T][H][N+V]  (= [dk_nope | dv], the layout of kv)
  *   dk_rope: [T][R]
  * Runs bf16 with N=128, R=64, V=128 (MLA_EUNSUPPORTED otherwise), 16-byte
- * aligned inputs and dk_rope, and strides that are multiples of 8 elements.
+ * aligned inputs and dk_rope, strides that are multiples of 8 elements and
+ * token strides of at most 2^24 elements.
  * Workspace: mla_attention_bwd_workspace_size() bytes, 256-byte aligned,
  * contents need not be initialised (row terms and per-head band gradients).
  * The result does not depend on scheduling: every sum runs in a fixed order.

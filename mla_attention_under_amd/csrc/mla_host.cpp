@@ -596,6 +596,11 @@ static int attn_bwd_validate(const mla_attn_bwd_args *a, const char *who) {
                      a->o_stride_t | a->o_stride_h | a->do_stride_t | a->do_stride_h;
   if (al % 16 || st % 8)
     return fail(MLA_EUNSUPPORTED, "%s: needs 16-byte aligned inputs and dk_rope, strides multiple of 8", who);
+  // a stage's rows are addressed by 32-bit byte offsets from its first row
+  constexpr int64_t kMaxRowStride = int64_t(1) << 24;
+  if (a->q_stride_t > kMaxRowStride || a->kv_stride_t > kMaxRowStride || a->kr_stride_t > kMaxRowStride ||
+      a->do_stride_t > kMaxRowStride)
+    return fail(MLA_EUNSUPPORTED, "%s: token strides above 2^24 elements are not supported", who);
   const size_t need = mla::attn_bwd_workspace_bytes(a->T, a->H, a->R);
   if (a->workspace == nullptr || a->workspace_bytes < need || reinterpret_cast<uintptr_t>(a->workspace) % 256)
     return fail(MLA_EINVAL, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", who, need,

@@ -261,6 +261,8 @@ def test_attention_bwd_validation_before_launch(lib):
     assert f(sized=False) == mla.MLA_EINVAL                  # workspace too small
     assert f(workspace=0x100010) == mla.MLA_EINVAL           # workspace misaligned
     assert f(cu_seqlens=0x50000, n_seq=0) == mla.MLA_EINVAL
+    assert f(kv_stride_t=(1 << 24) + 8) == mla.MLA_EUNSUPPORTED   # beyond the stages' 32-bit row offsets
+    assert f(do_stride_t=(1 << 24) + 8) == mla.MLA_EUNSUPPORTED
     assert f(T=0, sized=False) == mla.MLA_OK
     assert lib.mla_attention_bwd(None, None) == mla.MLA_EINVAL
 
