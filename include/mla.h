@@ -422,6 +422,7 @@ int mla_latent_up_proj_bwd(const void *latent, const void *w_kvb, const float *d
  *   out          : [B][H][V]
  *   lse          : optional fp32 [B][H]
  * MLA_BF16 only; 1 <= num_splits <= min(S, 256) (more than 256: MLA_EUNSUPPORTED).
+ * B <= 2^20 sequences per call (MLA_EUNSUPPORTED beyond).
  * Workspace: mla_latent_decode_workspace_size() bytes, 256-byte aligned;
  * contents need not be initialised.
  */

@@ -1123,12 +1123,13 @@ int launch_attention(const AttnPlan &p, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.T == 0) return hipSuccess;
   if (!attn_fast_path(p.N, p.R, p.V, p.bf16)) {
-    const int64_t n = p.T * p.H;
-    const int blocks = static_cast<int>((n + 255) / 256);
+    const int64_t blocks = (p.T * p.H + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks));
     if (p.bf16)
-      hipLaunchKernelGGL(attn_generic_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_generic_kernel<uint16_t>, grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_generic_kernel<float>, dim3(blocks), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_generic_kernel<float>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
   }
   AttnArgs a;

@@ -702,6 +702,7 @@ static int decode_validate(const mla_decode_args *a, const char *who) {
   if (a->num_splits > a->S) return fail(MLA_EINVAL, "%s: more splits (%d) than cached positions", who, a->num_splits);
   if (a->num_splits > mla::kDecodeMaxSplits)
     return fail(MLA_EUNSUPPORTED, "%s: at most %d splits", who, mla::kDecodeMaxSplits);
+  if (a->B > (1 << 20)) return fail(MLA_EUNSUPPORTED, "%s: at most 2^20 sequences per call", who);
   if ((a->S + 64) * static_cast<int64_t>(a->L) * 2 >= (1LL << 32))
     return fail(MLA_EUNSUPPORTED, "%s: a sequence's latent cache must stay below 4 GiB", who);
   if (!mla::decode_supported(a->L, a->N, a->R, a->V) || a->H > 16)

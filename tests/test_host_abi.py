@@ -317,6 +317,7 @@ def test_decode_validation_before_launch(lib):
     assert f(dtype=mla.MLA_F32) == mla.MLA_EUNSUPPORTED
     assert f(L=256) == mla.MLA_EUNSUPPORTED
     assert f(num_splits=257) == mla.MLA_EUNSUPPORTED
+    assert f(B=(1 << 20) + 1) == mla.MLA_EUNSUPPORTED       # beyond the per-call sequence count
     assert f(B=0) == mla.MLA_OK
     assert lib.mla_latent_decode_workspace_size(ctypes.byref(args())) > 0
 
