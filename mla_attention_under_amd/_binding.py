@@ -184,6 +184,43 @@ def _dev(*ts):
             raise ValueError("tensors must live on the GPU")
 
 
+def _need(cond, fn, what):
+    """Caller errors the C ABI cannot see (it gets pointers, not tensor sizes): checked before any launch."""
+    if not cond:
+        raise ValueError(f"{fn}: {what}")
+
+
+def _same_dtype(fn, *ts):
+    _need(len({t.dtype for t in ts if t is not None}) == 1, fn, "all inputs and outputs must share one dtype")
+
+
+def _shape_at_least(t, dims, fn, name):
+    """t has len(dims) dims, each at least dims[i] (None: any), e.g. a strided view of a wider buffer."""
+    _need(t.dim() == len(dims) and all(d is None or t.shape[i] >= d for i, d in enumerate(dims)), fn,
+          f"{name} has shape {tuple(t.shape)}, need {tuple(dims)}")
+
+
+def _attn_shapes(fn, q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k):
+    _need(q.dim() == 3 and kv.dim() == 3 and out.dim() == 3 and k_rope.dim() == 2, fn,
+          "q, kv, out are [T][H][.] and k_rope [T_k][R]")
+    T, H, T_k = q.shape[0], q.shape[1], kv.shape[0]
+    _shape_at_least(q, (T, H, N + R), fn, "q")
+    _shape_at_least(kv, (T_k, H, N + V), fn, "kv")
+    _shape_at_least(k_rope, (T_k, R), fn, "k_rope")
+    _need(tuple(out.shape[:2]) == (T, H) and out.shape[2] >= V, fn, f"out has shape {tuple(out.shape)}")
+    _need(kv.shape[1] == H and k_rope.shape[0] == T_k, fn, "kv / k_rope rows do not match")
+    _same_dtype(fn, q, kv, k_rope, out)
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == H * T, fn,
+              "lse must be a contiguous fp32 [H][T_q] tensor")
+    for cu in (cu_seqlens, cu_seqlens_k):
+        if cu is not None:
+            _need(cu.dtype == torch.int32 and cu.is_contiguous() and cu.dim() == 1 and cu.numel() >= 2, fn,
+                  "document offsets are contiguous int32 [n_seq + 1] tensors")
+    if cu_seqlens is not None and cu_seqlens_k is not None:
+        _need(cu_seqlens_k.numel() == cu_seqlens.numel(), fn, "query and key offsets list the same documents")
+
+
 def mla_head_shard_sizes(q_heads: int, kv_heads: int, sp: int) -> list[int]:
     lib = load_library()
     out = (ctypes.c_int * max(sp, 1))()
@@ -264,6 +301,11 @@ def mla_project_pack(latent, w, send, w_heads, head_begin, heads, P, F, col_offs
     T, L = latent.shape
     assert latent.is_contiguous() and w.is_contiguous() and send.is_contiguous()
     assert w.shape == (L, w_heads * P) and send.numel() == T * heads * F
+    _same_dtype("mla_project_pack", latent, w, send, cos, sin)
+    _need((cos is None) == (sin is None), "mla_project_pack", "give both RoPE tables or neither")
+    if cos is not None:
+        _need(cos.dim() == 2 and cos.shape[0] >= T and cos.stride(-1) == 1 and sin.shape == cos.shape and
+              sin.stride() == cos.stride(), "mla_project_pack", "cos and sin are [T][R] tables with one stride")
     R = 0 if cos is None else cos.shape[1]
     cs = 0 if cos is None else cos.stride(0)
     arr = (ctypes.c_int * len(sizes))(*sizes)
@@ -308,6 +350,7 @@ def mla_latent_up_proj(latent, w_kvb, kv_out, heads_total, head_begin, heads, N,
     assert latent.is_contiguous() and w_kvb.is_contiguous() and kv_out.is_contiguous()
     T, L = latent.shape
     assert w_kvb.shape == (L, heads_total * (N + V)) and kv_out.numel() == T * heads * (N + V)
+    _same_dtype("mla_latent_up_proj", latent, w_kvb, kv_out)
     _check("mla_latent_up_proj", lib.mla_latent_up_proj(
         _ptr(latent), _ptr(w_kvb), _ptr(kv_out), T, L, heads_total, head_begin, heads, N, V, _dtype(latent),
         _stream(stream)))
@@ -321,6 +364,7 @@ def mla_latent_up_proj_linear(latent, w_lin, kv_out, heads_total, head_begin, he
     assert latent.is_contiguous() and w_lin.is_contiguous() and kv_out.is_contiguous()
     T, L = latent.shape
     assert w_lin.shape == (heads_total * (N + V), L) and kv_out.numel() == T * heads * (N + V)
+    _same_dtype("mla_latent_up_proj_linear", latent, w_lin, kv_out)
     _check("mla_latent_up_proj_linear", lib.mla_latent_up_proj_linear(
         _ptr(latent), _ptr(w_lin), _ptr(kv_out), T, L, heads_total, head_begin, heads, N, V, _dtype(latent),
         _stream(stream)))
@@ -372,6 +416,7 @@ def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None,
     for t in (q, kv, k_rope, out):
         assert t.stride(-1) == 1
     _check_offsets(cu_seqlens, cu_seqlens_k)
+    _attn_shapes("mla_attention_fwd", q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k)
     if workspace is None:
         workspace = _workspace(mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens,
                                                             cu_seqlens_k), q.device, stream)
@@ -389,6 +434,7 @@ def mla_attention_fwd_noalloc(q, kv, k_rope, out, N, R, V, scale, causal=True, l
     for t in (q, kv, k_rope, out):
         assert t.stride(-1) == 1
     _check_offsets(cu_seqlens, cu_seqlens_k)
+    _attn_shapes("mla_attention_fwd_noalloc", q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k)
     a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, None, cu_seqlens_k)
     _check("mla_attention_fwd_noalloc", lib.mla_attention_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return out
@@ -432,13 +478,21 @@ def mla_attention_bwd(q, kv, k_rope, out, dout, lse, N, R, V, scale, causal=True
     _dev(q, kv, k_rope, out, dout, lse, cu_seqlens, dq, dkv, dk_rope, workspace)
     for t in (q, kv, k_rope, out, dout):
         assert t.stride(-1) == 1
+    fn = "mla_attention_bwd"
+    _attn_shapes(fn, q, kv, k_rope, out, N, R, V, lse, cu_seqlens, None)
+    _need(lse is not None, fn, "the forward's lse is required")
     T, H = q.shape[0], q.shape[1]
+    _need(kv.shape[0] == T, fn, "queries and keys are the same tokens")
+    _need(dout.dim() == 3 and tuple(dout.shape[:2]) == (T, H) and dout.shape[2] >= V and dout.dtype == q.dtype, fn,
+          "dout has the shape and dtype of out")
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(T, H, N + R, **f32) if dq is None else dq
     dkv = torch.empty(T, H, N + V, **f32) if dkv is None else dkv
     dk_rope = torch.empty(T, R, **f32) if dk_rope is None else dk_rope
     for t in (dq, dkv, dk_rope, lse):
         assert t.dtype == torch.float32 and t.is_contiguous()
+    _need(tuple(dq.shape) == (T, H, N + R) and tuple(dkv.shape) == (T, H, N + V) and tuple(dk_rope.shape) == (T, R),
+          fn, "dq [T][H][N+R], dkv [T][H][N+V] and dk_rope [T][R]")
     if workspace is None:
         workspace = _workspace(mla_attention_bwd_workspace_size(q, kv, k_rope, out, dout, N, R, V, scale, causal,
                                                                 cu_seqlens), q.device, stream)
@@ -468,10 +522,15 @@ def mla_latent_up_proj_bwd(latent, w_kvb, dkv, w_heads, head_begin, heads, N, V,
         assert t.is_contiguous()
     T, L = latent.shape
     assert dkv.dtype == torch.float32 and dkv.shape == (T, heads, N + V)
+    fn = "mla_latent_up_proj_bwd"
+    _need(tuple(w_kvb.shape) == (L, w_heads * (N + V)), fn, "w_kvb is [L][w_heads*(N+V)]")
+    _same_dtype(fn, latent, w_kvb)
     f32 = dict(dtype=torch.float32, device=latent.device)
     d_latent = torch.empty(T, L, **f32) if d_latent is None else d_latent
     dw = torch.empty(L, heads * (N + V), **f32) if dw is None else dw
     assert d_latent.is_contiguous() and dw.is_contiguous()
+    _need(d_latent.dtype == dw.dtype == torch.float32 and tuple(d_latent.shape) == (T, L) and
+          tuple(dw.shape) == (L, heads * (N + V)), fn, "d_latent [T][L] and dw [L][heads*(N+V)], fp32")
     if not split:
         workspace = None
     elif workspace is None:
@@ -512,6 +571,18 @@ def mla_latent_decode_fwd(q, latent_cache, rope_cache, w_kvb, out, heads_total, 
     _dev(q, latent_cache, rope_cache, w_kvb, out, lse, workspace)
     for t in (q, latent_cache, rope_cache, w_kvb, out):
         assert t.is_contiguous()
+    fn = "mla_latent_decode_fwd"
+    _need(q.dim() == 3 and latent_cache.dim() == 3 and rope_cache.dim() == 3, fn,
+          "q [B][H][N+R], latent_cache [B][S][L], rope_cache [B][S][R]")
+    B, H = q.shape[0], q.shape[1]
+    S, L = latent_cache.shape[1], latent_cache.shape[2]
+    _need(tuple(q.shape) == (B, H, N + R) and tuple(latent_cache.shape[:1]) == (B,) and
+          tuple(rope_cache.shape) == (B, S, R) and tuple(w_kvb.shape) == (L, heads_total * (N + V)) and
+          tuple(out.shape) == (B, H, V), fn, "shapes do not match q [B][H][N+R] ... out [B][H][V]")
+    _same_dtype(fn, q, latent_cache, rope_cache, w_kvb, out)
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H, fn,
+              "lse must be a contiguous fp32 [B][H] tensor")
     if workspace is None:
         workspace = _workspace(mla_latent_decode_workspace_size(q, latent_cache, rope_cache, w_kvb, out, heads_total,
                                                                 head_begin, N, R, V, num_splits, scale), q.device, stream)

@@ -444,3 +444,53 @@ def test_project_pack_validation_before_launch(lib):
     big = (ctypes.c_int * 2)(128, 128)
     assert call(sz=big, T=1 << 30, wh=256, heads=256) == mla.MLA_EUNSUPPORTED   # 2^23 x 384 tiles
     assert call(T=0) == mla.MLA_OK
+
+
+def test_binding_rejects_mismatched_tensors_before_any_call(monkeypatch):
+    """The C ABI sees pointers, not sizes: the binding checks shapes and dtypes first (invalid cases only, so no
+    call ever reaches the library; host tensors stand in with the device check switched off)."""
+    import torch
+    from mla_attention_under_amd import _binding as b
+    monkeypatch.setattr(b, "_dev", lambda *ts: None)
+    bf = dict(dtype=torch.bfloat16)
+    T, H, N, R, V = 8, 2, 128, 64, 128
+    q, kv, kr = torch.zeros(T, H, N + R, **bf), torch.zeros(T, H, N + V, **bf), torch.zeros(T, R, **bf)
+    out, lse = torch.zeros(T, H, V, **bf), torch.zeros(H, T)
+    fwd = lambda **kw: b.mla_attention_fwd(**dict(dict(q=q, kv=kv, k_rope=kr, out=out, N=N, R=R, V=V,  # noqa: E731
+                                                        scale=0.1, lse=lse), **kw))
+    for bad in (dict(out=torch.zeros(T, H, V // 2, **bf)),                # output rows too narrow
+                dict(out=torch.zeros(T - 1, H, V, **bf)),                 # too few output rows
+                dict(kv=torch.zeros(T, H + 1, N + V, **bf)),              # heads disagree
+                dict(k_rope=torch.zeros(T + 1, R, **bf)),                 # band rows disagree with kv
+                dict(q=torch.zeros(T, H, N + R)),                         # fp32 q with bf16 kv
+                dict(lse=torch.zeros(H, T - 1)),                          # lse too small
+                dict(cu_seqlens=torch.tensor([0, T], dtype=torch.int32),
+                     cu_seqlens_k=torch.tensor([0, 4, T], dtype=torch.int32))):   # different document counts
+        with pytest.raises(ValueError):
+            fwd(**bad)
+    with pytest.raises(ValueError):
+        b.mla_attention_fwd_noalloc(q, kv, kr, torch.zeros(T, H, 64, **bf), N, R, V, 0.1)
+    f32 = dict(dtype=torch.float32)
+    bwd = lambda **kw: b.mla_attention_bwd(**dict(dict(q=q, kv=kv, k_rope=kr, out=out, dout=out, lse=lse,  # noqa
+                                                        N=N, R=R, V=V, scale=0.1), **kw))
+    for bad in (dict(dq=torch.zeros(T, H, N, **f32)), dict(dkv=torch.zeros(T, H - 1, N + V, **f32)),
+                dict(dk_rope=torch.zeros(T - 1, R, **f32)), dict(dout=torch.zeros(T, H, V - 8, **bf)),
+                dict(lse=None), dict(kv=torch.zeros(T + 8, H, N + V, **bf), k_rope=torch.zeros(T + 8, R, **bf))):
+        with pytest.raises(ValueError):
+            bwd(**bad)
+    lat, w = torch.zeros(T, 512, **bf), torch.zeros(512, 4 * (N + V), **bf)
+    with pytest.raises(ValueError):
+        b.mla_latent_up_proj(lat, w.float(), torch.zeros(T, H, N + V, **bf), 4, 0, H, N, V)
+    with pytest.raises(ValueError):
+        b.mla_latent_up_proj_bwd(lat, w, torch.zeros(T, H, N + V, **f32), 4, 0, H, N, V,
+                                 dw=torch.zeros(512, N + V, **f32))
+    B, S = 2, 64
+    dq_ = torch.zeros(B, H, N + R, **bf)
+    cache, rope = torch.zeros(B, S, 512, **bf), torch.zeros(B, S, R, **bf)
+    for bad in (dict(out=torch.zeros(B, H, V - 8, **bf)), dict(rope_cache=torch.zeros(B, S - 1, R, **bf)),
+                dict(lse=torch.zeros(B * H - 1)), dict(w_kvb=torch.zeros(512, 3 * (N + V), **bf))):
+        args = dict(q=dq_, latent_cache=cache, rope_cache=rope, w_kvb=w, out=torch.zeros(B, H, V, **bf),
+                    heads_total=4, head_begin=0, N=N, R=R, V=V, num_splits=2, scale=0.1)
+        args.update(bad)
+        with pytest.raises(ValueError):
+            b.mla_latent_decode_fwd(**args)
