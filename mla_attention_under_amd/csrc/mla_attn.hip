@@ -89,10 +89,11 @@ __device__ __forceinline__ int v_swz(int key) { return (key & 2) | ((key & 1) * 
 // workgroup alone.
 //
 // Key tiles the two-segment workgroup gives up to the other: its second
-// segment's first transfers, its publish and its arrival cost about four key
+// segment's first transfers, its publish and its arrival cost several key
 // tiles more than the other workgroup's tail (which usually finds the pair
-// already arrived and merges without publishing; measured best at 4).
-constexpr int kPairShift = 4;
+// already arrived and merges without publishing). Measured on the 2048-token
+// causal shard, kernel trace and whole step, shifts 2..5: 3 is best.
+constexpr int kPairShift = 3;
 
 struct PairPlan {
   int qt;        // query tile of the first segment
