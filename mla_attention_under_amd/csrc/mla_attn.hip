@@ -427,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // previous step, then a barrier.
   // probe: the pair flag to read for an early second arrival (nullptr: none);
   // its record is other_rec. mode 0 runs the whole segment; mode 1 only
-  // starts its first transfers (Q, K_0, V_0, K_1) and leaves the softmax
+  // starts its first transfers (Q, K_0) and leaves the softmax
   // state alone; mode 2 runs a segment whose first transfers mode 1 started.
   auto segment = [&](int qt, int t0, int t1, const unsigned long long *probe, const unsigned long long *other_rec,
                      int mode, unsigned long long *arrive_flag) __attribute__((always_inline)) {
@@ -684,16 +684,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         // K_t lives in kb[t % 3], V_t in vb[t % 3]
         issue_q();
         issue_k(kb0, 0);
-        issue_v(vb0, 0);
-        issue_k(kb1, 1);
       }
       if (mode == 1) return;
     }
     if (nt > 0) {
-      // Q and K_0 have landed once only the five newest transfers (V_0, K_1)
-      // are left; they land during step 0, whose closing wait covers them
+      // Q and K_0 are the only transfers step 0 needs: wait for them alone.
+      // V_0 and K_1 follow once this wave has read its Q (issuing a transfer
+      // stalls the wave while the CU's memory queue is full, and the first
+      // transfers of all workgroups arrive at once); step 0's closing wait
+      // covers them.
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (KN_I + KR_I + V_I));
+      __builtin_amdgcn_s_waitcnt(0x0F70);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // every wave's older memory operations are complete here (the counter
@@ -702,6 +703,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       if (arrive_flag != nullptr && tid == 0) arrive_old = arrive_swap(arrive_flag, a.epoch);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qbuf + 512 * ks + 8 * lane);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_v(vb0, 0);
+      issue_k(kb1, 1);
+      __builtin_amdgcn_sched_barrier(0);
       // every wave holds its Q before step 0's transfers reuse kb2 and vb1
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();
