@@ -420,11 +420,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   // half a tile apart, so while one does M the other does X:
   //     step t, first half:   kh 0: M_t   kh 1: X_{t-1}
   //     step t, second half:  kh 0: X_t   kh 1: M_t
-  // In its vector half-phase of step t every wave also starts its share of
-  // the transfers of K_{t+2} and V_{t+1} (five 1 KB transfers) into the
-  // buffers that held K_{t-1} and V_{t-2}, which no wave reads after step
-  // t-1. A step ends with each wave waiting only for its transfers of the
-  // previous step, then a barrier.
+  // Every wave starts its share of the transfers of K_{t+2} and V_{t+1}
+  // (five 1 KB transfers) in step t, into the buffers that held K_{t-1} and
+  // V_{t-2}, which no wave reads after step t-1: the three K transfers at
+  // the start of its vector half-phase, the two V transfers at the end of its
+  // matrix half-phase, once its MFMAs are issued. A step ends with each wave
+  // waiting only for its transfers of the previous step, then a barrier.
   // probe: the pair flag to read for an early second arrival (nullptr: none);
   // its record is other_rec. mode 0 runs the whole segment; mode 1 only
   // starts its first transfers (Q, K_0) and leaves the softmax
@@ -627,17 +628,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     auto step = [&](auto pv, auto sv, auto dma, int t, const uint16_t *kcur, const uint16_t *vprev,
                     uint16_t *kdst, uint16_t *vdst) __attribute__((always_inline)) {
       const int jk = t + 2, jv = t + 1;
-      // the vector half-phase also starts this wave's share of the transfers:
-      // its wave is latency-bound with issue slots to spare, the matrix wave is not
-      auto transfers = [&]() __attribute__((always_inline)) {
+      // Issuing a transfer stalls the wave while the CU's memory queue is
+      // full. The vector half-phase (softmax) is the longer half, so it starts
+      // only the K transfers; the matrix wave starts the V transfers after its
+      // last MFMA is issued, in time it would otherwise wait at the barrier
+      // (the three K transfers there as well made the step slower).
+      auto transfers_k = [&]() __attribute__((always_inline)) {
+        if constexpr (decltype(dma)::value) issue_k(kdst, jk);
+      };
+      auto transfers_v = [&]() __attribute__((always_inline)) {
         if constexpr (decltype(dma)::value) {
-          issue_k(kdst, jk);
+          __builtin_amdgcn_sched_barrier(0);
           issue_v(vdst, jv);
+          __builtin_amdgcn_sched_barrier(0);
         }
       };
-      if (kh == 0) M(pv, sv, kcur, vprev);
+      if (kh == 0) {
+        M(pv, sv, kcur, vprev);
+        transfers_v();
+      }
       if (kh == 1) {
-        transfers();
+        transfers_k();
         if (t >= 1) X(t - 1);
       }
       // Phase alignment only: both half-phases read buffers that landed before
@@ -648,9 +659,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (kh == 1) M(pv, sv, kcur, vprev);
+      if (kh == 1) {
+        M(pv, sv, kcur, vprev);
+        transfers_v();
+      }
       if (kh == 0) {
-        transfers();
+        transfers_k();
         if (t < nt) X(t);
       }
       __builtin_amdgcn_sched_barrier(0);
