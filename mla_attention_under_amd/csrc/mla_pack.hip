@@ -38,14 +38,20 @@ struct PackArgs {
 // Ranks are interleaved in the block order (block b serves rank b % sp), so the
 // workgroups in flight at any moment cover whole x rows of a few tokens and
 // one stretch of every slab, rather than one rank's column of every x row.
-// Streaming (nontemporal) stores for large outputs; small outputs (up to
-// kCachedStoreBytes) stay in the caches, which measured faster for them
-// (an 8.4 MB unpack: 5.3 -> 4.1 us) and slower for large ones. Likewise
-// streaming loads only for sources beyond kCachedLoadBytes: a source that
-// fits the 256 MB Infinity Cache is read through it (the 29.4 MB rank-shard
-// pack: 10.5 -> 7.7 us back to back), a larger one streams past it (the
-// 470 MB uneven shard pack is 5 % slower with ordinary loads).
-constexpr uint64_t kCachedStoreBytes = 16ull << 20;
+// Streaming (nontemporal) stores for large outputs, ordinary stores (which
+// leave the output in the caches) for small ones; the bound depends on the
+// direction. Chosen in the attention step, where each copy runs between the
+// other kernels: the 29.4 MB rank-shard pack output is faster through the
+// caches (10.3 -> 10.0 us) and the 8.4 MB output unpack faster streamed
+// (5.1 -> 4.7 us); run back to back, the opposite choices measured faster.
+// Copies far beyond the 256 MB Infinity Cache stream either way. Streaming
+// loads only for sources beyond kCachedLoadBytes: a source that fits the
+// Infinity Cache is read through it (the rank-shard pack: 12.8 -> 10.0 us in
+// the step), a larger one streams past it (the 470 MB uneven shard pack is
+// 5 % slower with ordinary loads).
+constexpr uint64_t kCachedStoreBytesPack = 64ull << 20;
+constexpr uint64_t kCachedStoreBytesUnpack = 4ull << 20;
+constexpr uint64_t kCachedStoreBytesExpanded = 16ull << 20;   // the expanded pack, measured back to back
 constexpr uint64_t kCachedLoadBytes = 64ull << 20;
 template <typename Chunk, typename Index, bool kStream, bool kStreamLoad>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
@@ -113,7 +119,7 @@ hipError_t run(const PackPlan &p, hipStream_t s) {
   if (blocks * static_cast<uint64_t>(p.sp) > 0x7fffffffULL) return hipErrorInvalidConfiguration;
   const uint64_t all = a.tokens * static_cast<uint64_t>(p.heads_total) * a.row_chunks;
   const dim3 grid(static_cast<unsigned>(blocks * static_cast<uint64_t>(p.sp)));
-  const bool stream = all * sizeof(Chunk) > kCachedStoreBytes;
+  const bool stream = all * sizeof(Chunk) > (p.to_slabs ? kCachedStoreBytesPack : kCachedStoreBytesUnpack);
   const bool stream_load = all * sizeof(Chunk) > kCachedLoadBytes;
   const bool narrow = all + kThreads * kUnroll < 0xffffffffULL;
   if (narrow && stream_load)
@@ -202,7 +208,7 @@ hipError_t run_expanded(const PackExpandedPlan &p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (blocks * static_cast<uint64_t>(p.sp) > 0x7fffffffULL) return hipErrorInvalidConfiguration;
   const uint64_t all = a.tokens * static_cast<uint64_t>(p.heads_total) * wc;   // output chunks
-  const bool stream = all * sizeof(Chunk) > kCachedStoreBytes;
+  const bool stream = all * sizeof(Chunk) > kCachedStoreBytesExpanded;
   const bool narrow = all + kThreads < 0xffffffffULL;
   const dim3 grid(static_cast<unsigned>(blocks * static_cast<uint64_t>(p.sp)));
   if (narrow && stream)
