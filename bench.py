@@ -56,14 +56,23 @@ def _traffic(kernel: str, workload: str, launches_per_unit=1):
     return rec["bytes_per_launch"]
 
 
+_lead_buf = []
+
+
 def _busy(torch, ms=30):
-    """Keep the GPU busy so the host can queue the timed launches ahead of it."""
-    try:
-        torch.cuda._sleep(int(ms * 2.4e6))
-    except Exception:  # pragma: no cover - the spin kernel is part of torch on ROCm
-        x = torch.empty(1 << 26, device="cuda")
-        for _ in range(max(1, ms // 2)):
-            x.fill_(1.0)
+    """Keep the GPU loaded for roughly `ms` so the host can queue the timed launches ahead of it.
+
+    The lead is a stream of 256 MB fills (about 0.05-0.1 ms each), not an idle spin. After 30 ms of one
+    spinning wave the chip had lowered its clock, and the steps of the next 10 ms ran up to 20 % slower
+    (events every 20 steps: 58.7, 61.6, 64.8, 65.0, ... 55.7 us), which put about 6 % on a 200-step
+    average. Behind the fills the step runs at its steady rate from the first event on. The fills also
+    evict the Infinity Cache, so the first timed launch finds its inputs in HBM.
+    """
+    if not _lead_buf:
+        _lead_buf.append(torch.empty(1 << 26, dtype=torch.float32, device="cuda"))
+    x = _lead_buf[0]
+    for _ in range(max(1, 10 * ms)):
+        x.fill_(1.0)
 
 
 def cpu_baseline(w, d, x_pack, sizes, flops_step):
@@ -463,11 +472,14 @@ def main():
     y = torch.empty((T // sp, sp * H, V), dtype=torch.bfloat16, device="cuda")
     out_flat = out.view(-1)
 
+    # the caller's workspace, allocated once, as a serving loop holds it
+    ws_attn = torch.empty(max(1, mla.mla_attention_workspace_size(q, kv, kr, out, N, R, V, scale)), dtype=torch.uint8,
+                          device="cuda")
     kernels = ["pack", "up_proj", "attention", "unpack"]
     calls = {
         "pack": lambda: mla.mla_pack_heads(xp, send, sizes),
         "up_proj": lambda: mla.mla_latent_up_proj(latent, W, kv, w.heads_total, 0, H, N, V),
-        "attention": lambda: mla.mla_attention_fwd(q, kv, kr, out, N, R, V, scale),
+        "attention": lambda: mla.mla_attention_fwd(q, kv, kr, out, N, R, V, scale, workspace=ws_attn),
         "unpack": lambda: mla.mla_unpack_heads(out_flat, y, [H] * sp),
     }
 
