@@ -6,8 +6,9 @@ input, all in libmla.so:
   1. pack      : token->head pack of the rank's local [q | kv] rows,
                  [256 tokens][128 heads][448] -> 8 slabs of 16 heads
   2. up-proj   : latent [2048][512] x wkv_b [512][16*256] -> kv [2048][16][256]
-  3. attention : causal, shared 64-wide RoPE band, q [2048][16][192] -> out [2048][16][128]
-  4. unpack    : head->token restore of the output, 8 x [256][16][128] -> [256][128][128]
+  3. attention : causal, shared 64-wide RoPE band, q [2048][16][192] -> out, written
+                 straight into the head->token restored layout [256][128][128] (the
+                 unpack of 8 x [256][16][128], fused into the attention's row stores)
 (the DeepSeek-V3-shaped rank of 128 heads over sp=8: T=2048, H=16, L=512,
 N=128, R=64, V=128, bf16 storage with fp32 accumulation).
 
@@ -475,11 +476,13 @@ def main():
     # the caller's workspace, allocated once, as a serving loop holds it
     ws_attn = torch.empty(max(1, mla.mla_attention_workspace_size(q, kv, kr, out, N, R, V, scale)), dtype=torch.uint8,
                           device="cuda")
-    kernels = ["pack", "up_proj", "attention", "unpack"]
+    kernels = ["pack", "up_proj", "attention"]
     calls = {
         "pack": lambda: mla.mla_pack_heads(xp, send, sizes),
         "up_proj": lambda: mla.mla_latent_up_proj(latent, W, kv, w.heads_total, 0, H, N, V),
-        "attention": lambda: mla.mla_attention_fwd(q, kv, kr, out, N, R, V, scale, workspace=ws_attn),
+        # the output goes straight to y: query chunk r (rank r's 256 tokens) into heads [16r, 16r+16)
+        "attention": lambda: mla.mla_attention_fwd(q, kv, kr, y, N, R, V, scale, workspace=ws_attn, unpack_sp=sp),
+        # the separate restore copy, timed on its own (not part of the step)
         "unpack": lambda: mla.mla_unpack_heads(out_flat, y, [H] * sp),
     }
 
@@ -511,17 +514,17 @@ def main():
 
     # ---- per-kernel pass: events around every launch, on the launch stream
     ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for k in kernels}
+              for _ in range(args.steps)] for k in kernels + ["unpack"]}
     torch.cuda.synchronize()
     _busy(torch)
     for i in range(args.steps):
-        for k in kernels:
+        for k in kernels + ["unpack"]:
             ev[k][i][0].record()
             calls[k]()
             ev[k][i][1].record()
     torch.cuda.synchronize()
-    kern_us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in kernels}
-    kern_pct = {k: _pct([1e3 * a.elapsed_time(b) for a, b in ev[k]]) for k in kernels}
+    kern_us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in kernels + ["unpack"]}
+    kern_pct = {k: _pct([1e3 * a.elapsed_time(b) for a, b in ev[k]]) for k in kernels + ["unpack"]}
 
     # ---- per-step pass: events around every whole step, back to back (for p10 / p90 of the step)
     sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -616,7 +619,8 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "dsv3_rank", "T": T, "H": H, "L": L, "N": N, "R": R, "V": V, "heads_total": 128,
                    "sp": sp, "pack": "[256][128][448] -> 8 x 16 heads", "causal": True,
-                   "step": "pack + up_proj + attention + unpack", "flops_per_step": flops_step},
+                   "step": "pack + up_proj + attention (head->token unpack fused into its output stores)",
+                   "flops_per_step": flops_step},
         "roofline": roof,
     }
     line.update(extra)

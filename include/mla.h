@@ -243,7 +243,20 @@ int mla_latent_up_proj_linear(const void *latent, const void *w_lin, void *kv_ou
  *   q      : [T_q][H][N+R] rows at q + t*q_stride_t + h*q_stride_h
  *   kv     : [T_k][H][N+V] rows at kv + j*kv_stride_t + h*kv_stride_h
  *   k_rope : [T_k][R]      rows at k_rope + j*kr_stride_t
- *   out    : [T_q][H][V]   rows at out + t*o_stride_t + h*o_stride_h
+ *   out    : [T_q][H][V]   rows at out + t*o_stride_t + h*o_stride_h, or, with
+ *            o_chunk_tokens = C > 0, at out + (t/C)*o_stride_chunk +
+ *            (t%C)*o_stride_t + h*o_stride_h: the queries in chunks of C.
+ *            With C = T_q/sp, o_stride_chunk = H*V, o_stride_t = sp*H*V and
+ *            o_stride_h = V, chunk r (the queries of sequence rank r) lands in
+ *            its heads' columns of a token-major [T_q/sp][sp*H][V] buffer:
+ *            the output leaves already in the layout that mla_unpack_heads
+ *            gives after the head->token exchange (torchtitan "Ulysses CP";
+ *            hyper-parallel `restore_output`), with no separate copy. The
+ *            chunks' rows must not overlap: either o_stride_chunk >=
+ *            C*o_stride_t (chunks one after another) or o_stride_t >=
+ *            (ceil(T_q/C)-1)*o_stride_chunk + (H-1)*o_stride_h + V and
+ *            o_stride_chunk >= (H-1)*o_stride_h + V (chunks side by side in a
+ *            row); MLA_EINVAL otherwise. o_chunk_tokens = 0 is one chunk.
  *   lse    : optional fp32 [H][T_q] (NULL to skip): natural-log softmax denominator
  *   cu_seqlens   : optional DEVICE int32 array of n_seq+1 non-decreasing query
  *            offsets starting at 0 and ending at T_q (packed documents;
@@ -298,6 +311,7 @@ typedef struct mla_attn_args {
   int dtype;
   void *workspace;
   size_t workspace_bytes;
+  int64_t o_chunk_tokens, o_stride_chunk;   /* 0, 0: out rows at t*o_stride_t (see out above) */
 } mla_attn_args;
 
 size_t mla_attention_workspace_size(const mla_attn_args *a);

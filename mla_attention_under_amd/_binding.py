@@ -49,6 +49,7 @@ class mla_attn_args(ctypes.Structure):
         ("H", ctypes.c_int), ("N", ctypes.c_int), ("R", ctypes.c_int), ("V", ctypes.c_int),
         ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("o_chunk_tokens", ctypes.c_int64), ("o_stride_chunk", ctypes.c_int64),
     ]
 
 
@@ -200,14 +201,19 @@ def _shape_at_least(t, dims, fn, name):
           f"{name} has shape {tuple(t.shape)}, need {tuple(dims)}")
 
 
-def _attn_shapes(fn, q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k):
+def _attn_shapes(fn, q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k, unpack_sp=None):
     _need(q.dim() == 3 and kv.dim() == 3 and out.dim() == 3 and k_rope.dim() == 2, fn,
           "q, kv, out are [T][H][.] and k_rope [T_k][R]")
     T, H, T_k = q.shape[0], q.shape[1], kv.shape[0]
     _shape_at_least(q, (T, H, N + R), fn, "q")
     _shape_at_least(kv, (T_k, H, N + V), fn, "kv")
     _shape_at_least(k_rope, (T_k, R), fn, "k_rope")
-    _need(tuple(out.shape[:2]) == (T, H) and out.shape[2] >= V, fn, f"out has shape {tuple(out.shape)}")
+    if unpack_sp is None:
+        _need(tuple(out.shape[:2]) == (T, H) and out.shape[2] >= V, fn, f"out has shape {tuple(out.shape)}")
+    else:
+        _need(unpack_sp >= 1 and T % unpack_sp == 0, fn, f"T_q={T} is not a multiple of unpack_sp={unpack_sp}")
+        _need(tuple(out.shape[:2]) == (T // unpack_sp, unpack_sp * H) and out.shape[2] >= V, fn,
+              f"out has shape {tuple(out.shape)}, the unpacked layout is [T_q/sp][sp*H][V]")
     _need(kv.shape[1] == H and k_rope.shape[0] == T_k, fn, "kv / k_rope rows do not match")
     _same_dtype(fn, q, kv, k_rope, out)
     if lse is not None:
@@ -371,13 +377,17 @@ def mla_latent_up_proj_linear(latent, w_lin, kv_out, heads_total, head_begin, he
     return kv_out
 
 
-def _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace, cu_seqlens_k=None):
+def _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace, cu_seqlens_k=None,
+               unpack_sp=None):
     T, H = q.shape[0], q.shape[1]
     a = mla_attn_args()
     a.q, a.q_stride_t, a.q_stride_h = q.data_ptr(), q.stride(0), q.stride(1)
     a.kv, a.kv_stride_t, a.kv_stride_h = kv.data_ptr(), kv.stride(0), kv.stride(1)
     a.k_rope, a.kr_stride_t = k_rope.data_ptr(), k_rope.stride(0)
     a.out, a.o_stride_t, a.o_stride_h = out.data_ptr(), out.stride(0), out.stride(1)
+    if unpack_sp is not None:
+        # query chunk r = rank r's tokens, written to heads [r*H, (r+1)*H) of the token-major rows
+        a.o_chunk_tokens, a.o_stride_chunk = T // unpack_sp, H * out.stride(1)
     a.lse = None if lse is None else lse.data_ptr()
     a.cu_seqlens = None if cu_seqlens is None else cu_seqlens.data_ptr()
     a.cu_seqlens_k = None if cu_seqlens_k is None else cu_seqlens_k.data_ptr()
@@ -403,30 +413,33 @@ def _check_offsets(*cus):
 
 
 def mla_attention_fwd(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None, cu_seqlens=None,
-                      workspace=None, stream=None, cu_seqlens_k=None):
+                      workspace=None, stream=None, cu_seqlens_k=None, unpack_sp=None):
     """q [T_q][H][N+R], kv [T_k][H][N+V], k_rope [T_k][R] (last dims unit-stride) -> out [T_q][H][V].
 
     Strided views are passed through (e.g. q and kv read in place from a packed
     [T][H][F] buffer). cu_seqlens / cu_seqlens_k: int32 device tensors [n_seq+1]
     of query / key document offsets, or None. The workspace, when needed and not
-    given, is allocated through PyTorch.
+    given, is allocated through PyTorch. With unpack_sp = sp, out is the
+    token-major [T_q/sp][sp*H][V] buffer that follows the head->token exchange:
+    query t of head h is written to out[t % (T_q/sp)][(t // (T_q/sp))*H + h],
+    which is mla_unpack_heads(out [T_q][H][V], y, [H]*sp) without the copy.
     """
     lib = load_library()
     _dev(q, kv, k_rope, out, lse, cu_seqlens, cu_seqlens_k, workspace)
     for t in (q, kv, k_rope, out):
         assert t.stride(-1) == 1
     _check_offsets(cu_seqlens, cu_seqlens_k)
-    _attn_shapes("mla_attention_fwd", q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k)
+    _attn_shapes("mla_attention_fwd", q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k, unpack_sp)
     if workspace is None:
         workspace = _workspace(mla_attention_workspace_size(q, kv, k_rope, out, N, R, V, scale, causal, cu_seqlens,
                                                             cu_seqlens_k), q.device, stream)
-    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace, cu_seqlens_k)
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, workspace, cu_seqlens_k, unpack_sp)
     _check("mla_attention_fwd", lib.mla_attention_fwd(ctypes.byref(a), _stream(stream)))
     return out
 
 
 def mla_attention_fwd_noalloc(q, kv, k_rope, out, N, R, V, scale, causal=True, lse=None, cu_seqlens=None,
-                              stream=None, cu_seqlens_k=None):
+                              stream=None, cu_seqlens_k=None, unpack_sp=None):
     """mla_attention_fwd with the library's fixed per-GPU scratch instead of a workspace: nothing is
     allocated (for graph capture and serving loops). Calls overlapping on one GPU race on that scratch."""
     lib = load_library()
@@ -434,8 +447,9 @@ def mla_attention_fwd_noalloc(q, kv, k_rope, out, N, R, V, scale, causal=True, l
     for t in (q, kv, k_rope, out):
         assert t.stride(-1) == 1
     _check_offsets(cu_seqlens, cu_seqlens_k)
-    _attn_shapes("mla_attention_fwd_noalloc", q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k)
-    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, None, cu_seqlens_k)
+    _attn_shapes("mla_attention_fwd_noalloc", q, kv, k_rope, out, N, R, V, lse, cu_seqlens, cu_seqlens_k,
+                 unpack_sp)
+    a = _attn_args(q, kv, k_rope, out, N, R, V, scale, causal, lse, cu_seqlens, None, cu_seqlens_k, unpack_sp)
     _check("mla_attention_fwd_noalloc", lib.mla_attention_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 

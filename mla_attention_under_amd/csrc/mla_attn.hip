@@ -58,6 +58,8 @@ struct AttnArgs {
   uint16_t *out;
   float *lse;
   int64_t q_st, q_sh, kv_st, kv_sh, kr_st, o_st, o_sh;
+  int64_t o_sc;           // output chunk stride (queries in chunks of o_chunk rows)
+  int o_chunk;            // queries per output chunk, 0: one chunk
   const int32_t *cu;      // query offsets; nullptr: one document [0, T)
   const int32_t *cu_k;    // key offsets of the same documents (nullptr with cu == nullptr: [0, T_k))
   const int2 *tasks;      // packed documents: (query start, document) per task, sorted
@@ -156,6 +158,16 @@ __device__ __forceinline__ PairPlan pair_plan(int k, int h, int n, int T, int T_
 // l the partial denominator of this lane's keys.
 constexpr int kRecFloats = 4 * (4 * 16 + 2) * 64;   // 4 query blocks x (64 O + m + l) x 64 lanes
 
+// element offset of query row qi's output rows: in chunks of o_chunk queries
+// when o_chunk > 0 (e.g. sequence ranks' queries written straight into the
+// token-major layout that follows the head->token exchange)
+__device__ __forceinline__ int64_t out_row(const AttnArgs &a, int qi) {
+  if (a.o_chunk == 0) return static_cast<int64_t>(qi) * a.o_st;
+  const unsigned c = static_cast<unsigned>(qi) / static_cast<unsigned>(a.o_chunk);
+  const unsigned r = static_cast<unsigned>(qi) - c * static_cast<unsigned>(a.o_chunk);
+  return static_cast<int64_t>(c) * a.o_sc + static_cast<int64_t>(r) * a.o_st;
+}
+
 // normalise the state of query block qb of the tile starting at q0 and store
 // its columns [col0, col0 + 32 NDB) from o[0 .. NDB). The lane layout (a lane
 // holds 8-byte pieces of one query row) goes through the wave's own free
@@ -186,7 +198,7 @@ __device__ __forceinline__ void store_rows(const AttnArgs &a, const f32x16 (&o)[
     const int qi = q0 + 32 * qb + rr;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + rr * XLD + 8 * c);
     if (qi < q_end)
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(a.out + static_cast<int64_t>(qi) * a.o_st +
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(a.out + out_row(a, qi) +
                                                                static_cast<int64_t>(h) * a.o_sh + col0 + 8 * c));
   }
   const int qi = q0 + 32 * qb + row;
@@ -1047,7 +1059,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnPlan p) {
   for (int64_t j = klo; j < kend; ++j) m = fmaxf(m, score(j));
   float l = 0.f;
   for (int64_t j = klo; j < kend; ++j) l += expf(score(j) - m);
-  T *op = out + t * p.o_st + h * p.o_sh;
+  T *op = out + (p.o_chunk ? (t / p.o_chunk) * p.o_sc + (t % p.o_chunk) * p.o_st : t * p.o_st) + h * p.o_sh;
   constexpr int CH = 16;
   for (int v0 = 0; v0 < p.V; v0 += CH) {
     float acc[CH];
@@ -1165,6 +1177,8 @@ int launch_attention(const AttnPlan &p, void *stream) {
   a.kr_st = p.kr_st;
   a.o_st = p.o_st;
   a.o_sh = p.o_sh;
+  a.o_sc = p.o_sc;
+  a.o_chunk = static_cast<int>(p.o_chunk);   // < T <= 2^31 - 1
   a.T = static_cast<int>(p.T);
   a.T_k = static_cast<int>(p.T_k);
   a.H = p.H;

@@ -473,8 +473,20 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
   if (a->kv_stride_h < P || a->kv_stride_t < a->kv_stride_h * (a->H - 1) + P)
     return fail(MLA_EINVAL, "%s: kv strides overlap rows of width N+V=%lld", who, static_cast<long long>(P));
   if (a->kr_stride_t < a->R) return fail(MLA_EINVAL, "%s: k_rope stride below R", who);
-  if (a->o_stride_h < a->V || a->o_stride_t < a->o_stride_h * (a->H - 1) + a->V)
-    return fail(MLA_EINVAL, "%s: out strides overlap rows of width V", who);
+  const int64_t o_head_span = a->o_stride_h * (a->H - 1) + a->V;   // one token's rows of all heads
+  if (a->o_chunk_tokens < 0) return fail(MLA_EINVAL, "%s: o_chunk_tokens is negative", who);
+  if (a->o_chunk_tokens == 0 || a->o_chunk_tokens >= a->T_q) {
+    if (a->o_stride_h < a->V || a->o_stride_t < o_head_span)
+      return fail(MLA_EINVAL, "%s: out strides overlap rows of width V", who);
+  } else {
+    // chunks one after another, or side by side within a token row
+    const int64_t C = a->o_chunk_tokens, chunks = (a->T_q + C - 1) / C;
+    const bool stacked = a->o_stride_t >= o_head_span && a->o_stride_chunk >= C * a->o_stride_t;
+    const bool side = a->o_stride_chunk >= o_head_span && a->o_stride_t >= (chunks - 1) * a->o_stride_chunk + o_head_span;
+    if (a->o_stride_h < a->V || !(stacked || side))
+      return fail(MLA_EINVAL, "%s: out chunk strides (%lld per chunk, %lld per token) overlap rows", who,
+                  static_cast<long long>(a->o_stride_chunk), static_cast<long long>(a->o_stride_t));
+  }
   if (a->T_q == 0) return MLA_OK;
   if (!a->q || !a->out || (a->T_k > 0 && (!a->kv || (a->R > 0 && !a->k_rope))))
     return fail(MLA_EINVAL, "%s: NULL buffer", who);
@@ -482,7 +494,7 @@ static int attn_validate(const mla_attn_args *a, const char *who) {
     const uintptr_t al = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->kv) |
                          reinterpret_cast<uintptr_t>(a->k_rope) | reinterpret_cast<uintptr_t>(a->out);
     const int64_t st = a->q_stride_t | a->q_stride_h | a->kv_stride_t | a->kv_stride_h | a->kr_stride_t |
-                       a->o_stride_t | a->o_stride_h;
+                       a->o_stride_t | a->o_stride_h | a->o_stride_chunk;
     if (al % 16 || st % 8)
       return fail(MLA_EUNSUPPORTED, "%s: bf16 tiles need 16-byte aligned buffers and strides multiple of 8", who);
     // a tile's rows are addressed by 32-bit byte offsets from its first row
@@ -523,6 +535,8 @@ static int attention_fwd(const mla_attn_args *a, void *stream, const char *who) 
   p.out = a->out;
   p.o_st = a->o_stride_t;
   p.o_sh = a->o_stride_h;
+  p.o_chunk = a->o_chunk_tokens < a->T_q ? a->o_chunk_tokens : 0;
+  p.o_sc = p.o_chunk ? a->o_stride_chunk : 0;
   p.lse = a->lse;
   p.cu = a->cu_seqlens;
   // keys' offsets: their own, else the queries' (then T_k == T_q, checked above)

@@ -85,6 +85,7 @@ struct AttnPlan {
   int64_t kr_st;
   void *out;
   int64_t o_st, o_sh;
+  int64_t o_chunk, o_sc;   // queries per output chunk (0: one chunk) and the chunk stride
   float *lse;
   const int32_t *cu;   // device query offsets (cu_seqlens) or nullptr
   const int32_t *cu_k; // device key offsets or nullptr (then one document of T_k keys)

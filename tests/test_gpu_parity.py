@@ -386,6 +386,54 @@ def test_attention_varlen16k_sampled_rows():
         np.testing.assert_allclose(got[a], oracle.widen(d["kv"])[a, :, w.N:], atol=1e-2, rtol=0)
 
 
+def _unpacked(w, d, T, sp, causal=True, cu=None, noalloc=False):
+    """The attention written straight into the token-major [T/sp][sp*H][V] layout (unpack_sp), and the same call
+    into [T][H][V] followed by mla_unpack_heads, both into NaN-filled buffers."""
+    q, kv, kr = dev(d["q"]), dev(d["kv"]), dev(d["k_rope"])
+    cud = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+    scale = 1 / math.sqrt(w.K)
+    fwd = mla.mla_attention_fwd_noalloc if noalloc else mla.mla_attention_fwd
+    y = torch.full((T // sp, sp * w.H, w.V), float("nan"), dtype=q.dtype, device="cuda")
+    lse_y = torch.full((w.H, T), float("nan"), dtype=torch.float32, device="cuda")
+    fwd(q, kv, kr, y, w.N, w.R, w.V, scale, causal=causal, lse=lse_y, cu_seqlens=cud, unpack_sp=sp)
+    out = torch.full((T, w.H, w.V), float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((w.H, T), float("nan"), dtype=torch.float32, device="cuda")
+    fwd(q, kv, kr, out, w.N, w.R, w.V, scale, causal=causal, lse=lse, cu_seqlens=cud)
+    y2 = torch.full_like(y, float("nan"))
+    mla.mla_unpack_heads(out.reshape(-1), y2, [w.H] * sp)
+    _sync()
+    return y, y2, out, lse_y, lse
+
+
+@pytest.mark.parametrize("T,H,sp,causal", [(384, 2, 3, True), (200, 3, 5, True), (256, 2, 4, False)])
+def test_attention_unpacked_output_against_oracle(T, H, sp, causal):
+    """Output chunks of T/sp queries land in rank r's head columns; chunks of 40 queries cut 128-query tiles."""
+    w = mi.WORKLOADS["dsv3_rank"]
+    w = mi.Workload(w.name, w.cfg, T=T, H=H, L=w.L, N=w.N, R=w.R, V=w.V, heads_total=H)
+    d = _attn_inputs(w, T)
+    y, _, _, lse_y, _ = _unpacked(w, d, T, sp, causal=causal)
+    ref, rlse = oracle.attention(d["q"], d["kv"], d["k_rope"], w.N, 1 / math.sqrt(w.K), causal=causal)
+    ref_y = oracle.unpack_heads(ref.reshape(-1), [H] * sp, T // sp, w.V)
+    check_close(host64(y), ref_y, name=f"unpacked T={T} H={H} sp={sp}")
+    check_close(lse_y.cpu().numpy().astype(np.float64), rlse, name=f"unpacked lse T={T}")
+
+
+@pytest.mark.parametrize("case", ["dsv3_causal", "dsv3_noncausal", "documents", "noalloc", "tiny_fp32"])
+def test_attention_unpacked_output_equals_unpack_call(case):
+    """The fused layout is the separate unpack of the same call, bit for bit (rank shard: T=2048, H=16, sp=8)."""
+    if case == "tiny_fp32":
+        w, T, sp = mi.WORKLOADS["tiny"], 64, 4
+    else:
+        w, T, sp = mi.WORKLOADS["dsv3_rank"], 2048, 8
+    d = _attn_inputs(w, T)
+    cu = [0, 300, 301, 1100, 2048] if case == "documents" else None
+    y, y2, out, lse_y, lse = _unpacked(w, d, T, sp, causal=case != "dsv3_noncausal", cu=cu,
+                                       noalloc=case == "noalloc")
+    assert torch.isfinite(out).all()
+    assert np.array_equal(bits(y), bits(y2)), case
+    assert np.array_equal(bits(lse_y), bits(lse)), case
+
+
 def test_attention_reads_packed_rows_in_place():
     """torchtitan 'Ulysses CP' order on one rank: every simulated rank projects its own
     tokens for all heads and packs [q | kv] rows by the shard list; rank r's slab of

@@ -69,6 +69,7 @@ int main(void) {
   P(mla_attn_args, cu_seqlens) P(mla_attn_args, cu_seqlens_k) P(mla_attn_args, n_seq) P(mla_attn_args, T_q)
   P(mla_attn_args, T_k) P(mla_attn_args, V)
   P(mla_attn_args, scale) P(mla_attn_args, dtype) P(mla_attn_args, workspace) P(mla_attn_args, workspace_bytes)
+  P(mla_attn_args, o_chunk_tokens) P(mla_attn_args, o_stride_chunk)
   P(mla_decode_args, lse) P(mla_decode_args, B) P(mla_decode_args, S) P(mla_decode_args, num_splits)
   P(mla_decode_args, scale) P(mla_decode_args, workspace) P(mla_decode_args, workspace_bytes)
   P(mla_attn_bwd_args, dout) P(mla_attn_bwd_args, do_stride_h) P(mla_attn_bwd_args, lse) P(mla_attn_bwd_args, dq)
@@ -207,6 +208,17 @@ def test_attention_validation_before_launch(lib):
     assert f(cu_seqlens_k=0x50000, n_seq=2) == mla.MLA_EINVAL          # key offsets without query offsets
     assert f(cu_seqlens=0x50000, n_seq=2, T_k=300, workspace=0x60000, workspace_bytes=1 << 20) == mla.MLA_EINVAL
     assert lib.mla_attention_fwd(None, None) == mla.MLA_EINVAL
+    # output in query chunks (the unpacked layout): chunk rows must not overlap
+    assert f(o_chunk_tokens=-1) == mla.MLA_EINVAL
+    assert f(o_chunk_tokens=128, o_stride_chunk=0) == mla.MLA_EINVAL and b"chunk" in lib.mla_last_error()
+    assert f(o_chunk_tokens=128, o_stride_chunk=256) == mla.MLA_EINVAL and b"chunk" in lib.mla_last_error()
+    assert f(o_chunk_tokens=128, o_stride_chunk=200, o_stride_t=512) == mla.MLA_EINVAL   # heads of two chunks overlap
+    # side by side (sp=2: [128][2*2][128]) and one after another pass the layout check (then need the workspace)
+    assert f(o_chunk_tokens=128, o_stride_chunk=256, o_stride_t=512) == mla.MLA_EINVAL
+    assert b"workspace" in lib.mla_last_error()
+    assert f(o_chunk_tokens=128, o_stride_chunk=128 * 256) == mla.MLA_EINVAL and b"workspace" in lib.mla_last_error()
+    assert f(o_chunk_tokens=300, o_stride_chunk=0) == mla.MLA_EINVAL and b"workspace" in lib.mla_last_error()
+    assert f(o_chunk_tokens=128, o_stride_chunk=260, o_stride_t=520) == mla.MLA_EUNSUPPORTED   # tiles need % 8
     a = _attn(cu_seqlens=0x50000, n_seq=4, T_q=16384, T_k=16384)
     assert lib.mla_attention_workspace_size(ctypes.byref(a)) > 0
     assert lib.mla_attention_workspace_size(ctypes.byref(_attn())) > 0          # dense causal
@@ -465,7 +477,10 @@ def test_binding_rejects_mismatched_tensors_before_any_call(monkeypatch):
                 dict(q=torch.zeros(T, H, N + R)),                         # fp32 q with bf16 kv
                 dict(lse=torch.zeros(H, T - 1)),                          # lse too small
                 dict(cu_seqlens=torch.tensor([0, T], dtype=torch.int32),
-                     cu_seqlens_k=torch.tensor([0, 4, T], dtype=torch.int32))):   # different document counts
+                     cu_seqlens_k=torch.tensor([0, 4, T], dtype=torch.int32)),    # different document counts
+                dict(unpack_sp=3, out=torch.zeros(2, 3 * H, V, **bf)),        # T not a multiple of sp
+                dict(unpack_sp=2, out=torch.zeros(T, H, V, **bf)),            # not the [T/sp][sp*H][V] layout
+                dict(unpack_sp=4, out=torch.zeros(T // 4, 4 * H, V - 8, **bf))):   # rows too narrow
         with pytest.raises(ValueError):
             fwd(**bad)
     with pytest.raises(ValueError):
