@@ -418,11 +418,14 @@ def test_attention_unpacked_output_against_oracle(T, H, sp, causal):
     check_close(lse_y.cpu().numpy().astype(np.float64), rlse, name=f"unpacked lse T={T}")
 
 
-@pytest.mark.parametrize("case", ["dsv3_causal", "dsv3_noncausal", "documents", "noalloc", "tiny_fp32"])
+@pytest.mark.parametrize("case", ["dsv3_causal", "dsv3_noncausal", "documents", "noalloc", "tiny_fp32", "uneven22"])
 def test_attention_unpacked_output_equals_unpack_call(case):
-    """The fused layout is the separate unpack of the same call, bit for bit (rank shard: T=2048, H=16, sp=8)."""
+    """The fused layout is the separate unpack of the same call, bit for bit (rank shard: T=2048, H=16, sp=8;
+    the uneven shard: T=4096, H=22, chunks of 512)."""
     if case == "tiny_fp32":
         w, T, sp = mi.WORKLOADS["tiny"], 64, 4
+    elif case == "uneven22":
+        w, T, sp = mi.WORKLOADS["uneven22"], 4096, 8
     else:
         w, T, sp = mi.WORKLOADS["dsv3_rank"], 2048, 8
     d = _attn_inputs(w, T)
@@ -596,6 +599,32 @@ def test_dense_causal_graph_replays():
         _sync()
         assert torch.equal(out, eager), f"replay {i} differs from the eager call"
         mla.mla_attention_fwd(q, kv, kr, eager, w.N, w.R, w.V, scale)   # eager work between replays
+        _sync()
+
+
+def test_unpacked_output_graph_replays():
+    """A captured call writing the restored layout gives the eager result on every replay."""
+    base = mi.WORKLOADS["dsv3_rank"]
+    T, H, sp = 2048, 16, 8
+    w = mi.Workload(base.name, base.cfg, T=T, H=H, L=base.L, N=base.N, R=base.R, V=base.V, heads_total=H)
+    d = _attn_inputs(w, T)
+    q, kv, kr = dev(d["q"]), dev(d["kv"]), dev(d["k_rope"])
+    scale = 1 / math.sqrt(w.K)
+    eager = torch.empty((T // sp, sp * H, w.V), dtype=torch.bfloat16, device="cuda")
+    mla.mla_attention_fwd(q, kv, kr, eager, w.N, w.R, w.V, scale, unpack_sp=sp)
+    _sync()
+    y = torch.full_like(eager, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mla.mla_attention_fwd(q, kv, kr, y, w.N, w.R, w.V, scale, unpack_sp=sp)
+    for i in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        _sync()
+        assert torch.equal(y, eager), f"replay {i} differs from the eager call"
+        mla.mla_attention_fwd(q, kv, kr, eager, w.N, w.R, w.V, scale, unpack_sp=sp)
         _sync()
 
 
